@@ -1,0 +1,268 @@
+"""Benchmark of the Block-GTQ packed-KV decode path on one MI355X.
+
+One step = one serving decode step of the 128K Llama-3.1-8B-shaped layer
+(batch 1, 8 KV / 32 query heads, K2V2): the new token's key and value are
+encoded into the packed cache at position T, then fused decode attention reads
+all T+1 cached tokens (query rotation, cache-streaming kernel, split merge).
+Calibration energy, allocation, plan creation and the full 128K prefill
+encode run once before the timed region and are reported as separate fields.
+
+value = algorithmic packed bytes read per step (codes + present fp16 norms)
+/ step time.  The packed cache is replicated (>= 1 GiB in total) and steps
+rotate over the replicas so that reads come from HBM, not the 256 MB
+Infinity Cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-KV decode attn GB/s (% HBM peak), ms/step @128K; encode keys/s"
+HBM_PEAK_GBPS = 8000.0
+STREAM_KERNEL = "decode_stream_kernel"
+
+
+def log(msg: str) -> None:
+    print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(os.path.join(ROOT, "decode_attention_bgtq_amd", "csrc", "decode.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(cid: int):
+    """Per-launch HBM bytes of the stream kernel from committed counter runs, if still valid."""
+    p = os.path.join(ROOT, "profiles", "decode_stream_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    rec = d.get("configs", {}).get(str(cid))
+    if not rec or d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, bits, n_heads: int):
+    """The oracle's decode (explicit dequantisation + float64 softmax attention) on a sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    import synth
+    t = cfg.seq_len
+    q = synth.query(cfg)
+    total_s, total_bytes = 0.0, 0
+    for h in range(n_heads):
+        k = synth.keys(cfg, count=t)[:, h]
+        v = synth.values(cfg, count=t)[:, h]
+        kc, kn = oracle.encode_k(k, bits[h], cfg.seed, 0, h)
+        vc, vn = oracle.encode_v(v, cfg.v_bits, cfg.seed, 0, h)
+        n_groups = len([w for w in (1, 2, 3, 4) if np.any(bits[h] == w)])
+        t0 = time.perf_counter()
+        kh = oracle.dequant_k(kc, kn, bits[h], cfg.seed, 0, h)
+        vh = oracle.dequant_v(vc, vn, cfg.v_bits, cfg.seed, 0, h)
+        for hh in range(h * cfg.group, (h + 1) * cfg.group):
+            oracle.softmax_attention(q[hh].astype(np.float64), kh, vh, 1 / math.sqrt(128))
+        total_s += time.perf_counter() - t0
+        total_bytes += t * (16 * cfg.k_bits + 2 * n_groups + 16 * cfg.v_bits + 2)
+        log("cpu baseline head %d: %.2fs" % (h, total_s))
+    return {"value": total_bytes / total_s / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": "float64 oracle decode (dequantise + softmax attention) of %d of %d KV heads x %d tokens "
+                      "(all %d query heads of those KV heads); packed bytes of the sample / wall time" %
+                      (n_heads, cfg.n_kv_heads, t, n_heads * cfg.group)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--replica-bytes", type=float, default=1.1e9)
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (see DESIGN.md for how it "
+              "would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import decode_attention_bgtq_amd as bg
+    import synth
+
+    if not os.path.exists(bg.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    b, t, hkv, hq = cfg.batch, cfg.seq_len, cfg.n_kv_heads, cfg.n_q_heads
+    log("config %d %s: batch %d, T %d, %d/%d heads, K%dV%d" % (cfg.cid, cfg.name, b, t, hkv, hq, cfg.k_bits,
+                                                              cfg.v_bits))
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.float16 else a).to(dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    # ---- one-time rows: energy, allocation, plan
+    q_cal, k_cal = synth.calibration(cfg)
+    qc, kc = to_dev(q_cal), to_dev(k_cal)
+    e_dev = torch.empty((hkv, 64), dtype=torch.float64, device=dev)
+    bits_dev = torch.empty((hkv, 64), dtype=torch.int8, device=dev)
+    bg.energy(qc, kc, hkv, e_dev)
+    bg.allocate(e_dev, cfg.k_bits, bits_dev)
+    torch.cuda.synchronize()
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record()
+    for _ in range(10):
+        bg.energy(qc, kc, hkv, e_dev)
+    e1.record()
+    for _ in range(10):
+        bg.allocate(e_dev, cfg.k_bits, bits_dev)
+    e2.record()
+    torch.cuda.synchronize()
+    energy_us = e0.elapsed_time(e1) * 100.0
+    alloc_us = e1.elapsed_time(e2) * 100.0
+    bits = bits_dev.cpu().numpy()
+    tp = time.perf_counter()
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, hq, seed=cfg.seed, layer=0)
+    plan_ms = (time.perf_counter() - tp) * 1e3
+
+    # ---- prefill encode of the whole context (timed once more after a warm-up)
+    cap = t + 64
+    cache = bg.Cache(plan, b, cap, device=dev)
+    log("generating %d x %d tokens" % (b, t))
+    ks = [synth.keys(cfg, seq=s, count=t) for s in range(b)]
+    vs = [synth.values(cfg, seq=s, count=t) for s in range(b)]
+    kd = to_dev(np.stack(ks))
+    vd = to_dev(np.stack(vs))
+    del ks, vs
+    cache.encode(kd, vd, 0)
+    torch.cuda.synchronize()
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record()
+    plan.encode_k(cache.consts, kd, cap, 0, cache.k_codes, cache.k_norms)
+    e1.record()
+    plan.encode_v(cache.consts, vd, cap, 0, cache.v_codes, cache.v_norms)
+    e2.record()
+    torch.cuda.synchronize()
+    enc_k_s, enc_v_s = e0.elapsed_time(e1) / 1e3, e1.elapsed_time(e2) / 1e3
+    token_heads = b * t * hkv
+    del kd, vd
+
+    # ---- the appended token and the query (position T)
+    cfg1 = dataclasses.replace(cfg, append=1)
+    k_new = to_dev(np.stack([synth.keys(cfg1, seq=s, start=t, count=1) for s in range(b)]))
+    v_new = to_dev(np.stack([synth.values(cfg1, seq=s, start=t, count=1) for s in range(b)]))
+    q = to_dev(np.stack([synth.query(cfg, seq=s, pos=t) for s in range(b)]))
+    seq_lens = torch.full((b,), t + 1, dtype=torch.int32, device=dev)
+    packed = cache.packed_bytes(t + 1)
+    n_rep = max(1, math.ceil(args.replica_bytes / packed))
+    log("packed bytes/step %.1f MB; %d replicas" % (packed / 1e6, n_rep))
+    reps = [(cache.k_codes, cache.k_norms, cache.v_codes, cache.v_norms)]
+    for _ in range(n_rep - 1):
+        reps.append(tuple(x.clone() for x in reps[0]))
+    out = torch.empty((b, hq, 128), dtype=torch.int16, device=dev)
+    ws = torch.empty(plan.workspace_size(b, t + 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        kc_, kn_, vc_, vn_ = reps[i % n_rep]
+        plan.encode_k(cache.consts, k_new, cap, t, kc_, kn_)
+        plan.encode_v(cache.consts, v_new, cap, t, vc_, vn_)
+        plan.decode_attn(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Timed region: rounds of at most 100 steps, each enqueued behind a short GPU
+    # spin so that the host has queued the whole round before the GPU reaches it;
+    # the events bracket the steps only, so the time is the GPU's.
+    per_round = min(args.steps, 100)
+    rounds = max(1, args.steps // per_round)
+    spin = getattr(torch.cuda, "_sleep", None)
+    bg.profile_enable(True)
+    bg.profile_read()
+    step_ms_total, host_enqueue_s, n_steps = 0.0, 0.0, 0
+    for r in range(rounds):
+        torch.cuda.synchronize()
+        if spin is not None:
+            spin(int(30e6))
+        s0, s1 = ev(), ev()
+        s0.record()
+        th = time.perf_counter()
+        for i in range(per_round):
+            step(args.warmup + n_steps + i)
+        host_enqueue_s += time.perf_counter() - th
+        s1.record()
+        torch.cuda.synchronize()
+        step_ms_total += s0.elapsed_time(s1)
+        n_steps += per_round
+    bg.profile_enable(False)
+    step_ms = step_ms_total / n_steps
+    kern_ms_total, launches = bg.profile_read()
+    kern_ms = kern_ms_total / max(launches, 1)
+    value = packed / (step_ms / 1e3) / 1e9
+    achieved = packed / (kern_ms / 1e3) / 1e9
+    log("step %.4f ms (%.0f GB/s); stream kernel %.4f ms (%.0f GB/s, %d launches); host enqueue %.4f ms/step" %
+        (step_ms, value, kern_ms, achieved, launches, host_enqueue_s * 1e3 / n_steps))
+
+    # ---- copy probe: practical streaming ceiling (1 GiB read + 1 GiB write)
+    src = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = ev(), ev()
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst, reps
+
+    traffic = load_traffic(cfg.cid)
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": b, "seq_len": t, "n_kv_heads": hkv, "n_q_heads": hq,
+                   "k_bits": cfg.k_bits, "v_bits": cfg.v_bits, "head_dim": 128, "cache_io": "packed codes + fp16 norms",
+                   "query_io": "fp16", "accumulate": "fp32", "parallelism": "single GPU"},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "packed_bytes_per_step": packed,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": STREAM_KERNEL, "kernel_ms": round(kern_ms, 5)},
+        "encode_token_heads_per_s": {"k_and_v": round(token_heads / (enc_k_s + enc_v_s)),
+                                     "k": round(token_heads / enc_k_s), "v": round(token_heads / enc_v_s),
+                                     "tokens": b * t},
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "one_time": {"energy_us": round(energy_us, 2), "allocate_us": round(alloc_us, 2),
+                     "plan_host_ms": round(plan_ms, 2)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, bits, args.cpu_heads)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

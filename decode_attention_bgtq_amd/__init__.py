@@ -1,0 +1,268 @@
+"""Python binding of libbgtq (Block-GTQ packed-KV path for MI355X).
+
+Argument marshalling only: every step runs in the HIP library.  Device
+tensors are torch tensors on a ROCm device (torch supplies device memory and
+streams); the library is loaded from this directory and the binding raises if
+it is missing.  Function names follow include/bgtq.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbgtq.so")
+
+OK, EINVAL, EBUDGET, ECAPACITY, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
+TILE = 64
+HEAD_DIM = 128
+
+EXPORTED = [
+    "bgtq_abi_version", "bgtq_last_error", "bgtq_energy", "bgtq_allocate", "bgtq_plan_create",
+    "bgtq_plan_destroy", "bgtq_plan_sizes", "bgtq_plan_upload", "bgtq_encode_k", "bgtq_encode_v",
+    "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
+    "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read",
+]
+
+
+class BgtqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("bgtq status %d: %s" % (status, msg))
+        self.status = status
+
+
+class _PlanDesc(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k_avg_bits", ctypes.c_int32),
+                ("v_bits", ctypes.c_int32), ("k_bits", ctypes.POINTER(ctypes.c_int8)),
+                ("seed", ctypes.c_uint64), ("layer", ctypes.c_int32)]
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("consts", ctypes.c_uint64), ("k_codes", ctypes.c_uint64),
+                ("k_norms", ctypes.c_uint64), ("v_codes", ctypes.c_uint64),
+                ("v_norms", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbgtq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libbgtq.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+    sig = {
+        "bgtq_abi_version": (I32, []),
+        "bgtq_last_error": (ctypes.c_char_p, []),
+        "bgtq_energy": (I32, [P, P, I64, I32, I32, I32, P, P]),
+        "bgtq_allocate": (I32, [P, I32, I32, I32, P, P]),
+        "bgtq_plan_create": (I32, [ctypes.POINTER(_PlanDesc), ctypes.POINTER(P)]),
+        "bgtq_plan_destroy": (None, [P]),
+        "bgtq_plan_sizes": (I32, [P, I32, I64, ctypes.POINTER(_Sizes)]),
+        "bgtq_plan_upload": (I32, [P, P, P]),
+        "bgtq_encode_k": (I32, [P, P, P, I32, I64, I64, I64, P, P, P]),
+        "bgtq_encode_v": (I32, [P, P, P, I32, I64, I64, I64, P, P, P]),
+        "bgtq_rotate_queries": (I32, [P, P, P, I32, P, P]),
+        "bgtq_decode_workspace_size": (I32, [P, I32, I64, ctypes.POINTER(SZ)]),
+        "bgtq_decode_attn": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float, P, P, SZ, P]),
+        "bgtq_codebook": (I32, [I32, P, P, P]),
+        "bgtq_plan_rotation": (I32, [P, I32, I32, I32, P, ctypes.POINTER(I32)]),
+        "bgtq_plan_bits": (I32, [P, P]),
+        "bgtq_profile_enable": (I32, [I32]),
+        "bgtq_profile_read": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise BgtqError(status, load().bgtq_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    """Device (or host numpy) address of a tensor/array; None passes NULL."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def abi_version() -> int:
+    return load().bgtq_abi_version()
+
+
+def codebook(bits: int):
+    """(centroids, thresholds, D(b)) of the library's b-bit Lloyd-Max quantiser."""
+    c = np.zeros(1 << bits)
+    t = np.zeros((1 << bits) - 1)
+    d = ctypes.c_double()
+    _check(load().bgtq_codebook(bits, c.ctypes.data, t.ctypes.data, ctypes.addressof(d)))
+    return c, t, d.value
+
+
+def energy(q_cal, k_cal, n_kv_heads: int, out, stream=None) -> None:
+    n, hq, d = q_cal.shape
+    _check(load().bgtq_energy(_ptr(q_cal), _ptr(k_cal), n, hq, n_kv_heads, d, _ptr(out), _stream(stream)))
+
+
+def allocate(energy_t, avg_bits: int, out, stream=None) -> None:
+    hkv, nb = energy_t.shape
+    _check(load().bgtq_allocate(_ptr(energy_t), hkv, nb, avg_bits, _ptr(out), _stream(stream)))
+
+
+@dataclasses.dataclass
+class Sizes:
+    consts: int
+    k_codes: int
+    k_norms: int
+    v_codes: int
+    v_norms: int
+
+
+class Plan:
+    """Host plan for one layer (widths, V width, seed, layer id)."""
+
+    def __init__(self, k_bits: np.ndarray, k_avg_bits: int, v_bits: int, n_q_heads: int,
+                 seed: int = 0, layer: int = 0):
+        lib = load()
+        kb = np.ascontiguousarray(np.asarray(k_bits, dtype=np.int8))
+        self.n_kv_heads = kb.shape[0]
+        self.n_q_heads = n_q_heads
+        self.k_avg_bits = k_avg_bits
+        self.v_bits = v_bits
+        self.seed = seed
+        self.layer = layer
+        desc = _PlanDesc(self.n_kv_heads, n_q_heads, HEAD_DIM, k_avg_bits, v_bits,
+                         kb.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), seed, layer)
+        h = ctypes.c_void_p()
+        _check(lib.bgtq_plan_create(ctypes.byref(desc), ctypes.byref(h)))
+        self._h = h
+        self.k_bits = kb.copy()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            load().bgtq_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sizes(self, batch: int, capacity: int) -> Sizes:
+        s = _Sizes()
+        _check(load().bgtq_plan_sizes(self._h, batch, capacity, ctypes.byref(s)))
+        return Sizes(s.consts, s.k_codes, s.k_norms, s.v_codes, s.v_norms)
+
+    def upload(self, dev_consts, stream=None) -> None:
+        _check(load().bgtq_plan_upload(self._h, _ptr(dev_consts), _stream(stream)))
+
+    def rotation(self, kvh: int, tensor: int, width: int) -> np.ndarray | None:
+        d = ctypes.c_int32()
+        _check(load().bgtq_plan_rotation(self._h, kvh, tensor, width, None, ctypes.byref(d)))
+        if d.value == 0:
+            return None
+        out = np.zeros((d.value, d.value))
+        _check(load().bgtq_plan_rotation(self._h, kvh, tensor, width, out.ctypes.data, ctypes.byref(d)))
+        return out
+
+    def bits(self) -> np.ndarray:
+        out = np.zeros((self.n_kv_heads, 64), np.int8)
+        _check(load().bgtq_plan_bits(self._h, out.ctypes.data))
+        return out
+
+    def encode_k(self, consts, k, capacity: int, t0: int, k_codes, k_norms, stream=None) -> None:
+        b, n = k.shape[0], k.shape[1]
+        _check(load().bgtq_encode_k(self._h, _ptr(consts), _ptr(k), b, capacity, t0, n,
+                                    _ptr(k_codes), _ptr(k_norms), _stream(stream)))
+
+    def encode_v(self, consts, v, capacity: int, t0: int, v_codes, v_norms, stream=None) -> None:
+        b, n = v.shape[0], v.shape[1]
+        _check(load().bgtq_encode_v(self._h, _ptr(consts), _ptr(v), b, capacity, t0, n,
+                                    _ptr(v_codes), _ptr(v_norms), _stream(stream)))
+
+    def rotate_queries(self, consts, q, q_rot, stream=None) -> None:
+        _check(load().bgtq_rotate_queries(self._h, _ptr(consts), _ptr(q), q.shape[0], _ptr(q_rot),
+                                          _stream(stream)))
+
+    def workspace_size(self, batch: int, max_seq_len: int) -> int:
+        n = ctypes.c_size_t()
+        _check(load().bgtq_decode_workspace_size(self._h, batch, max_seq_len, ctypes.byref(n)))
+        return n.value
+
+    def decode_attn(self, consts, q, k_codes, k_norms, v_codes, v_norms, capacity: int, seq_lens,
+                    max_seq_len: int, out, workspace, softmax_scale: float | None = None,
+                    stream=None) -> None:
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_attn(self._h, _ptr(consts), _ptr(q), _ptr(k_codes), _ptr(k_norms),
+                                       _ptr(v_codes), _ptr(v_norms), capacity, _ptr(seq_lens), q.shape[0],
+                                       max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(load().bgtq_profile_enable(1 if on else 0))
+
+
+def profile_read() -> tuple[float, int]:
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(load().bgtq_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+class Cache:
+    """Device buffers of one layer's packed cache (caller-owned torch tensors, zero-filled)."""
+
+    def __init__(self, plan: Plan, batch: int, capacity: int, device="cuda"):
+        import torch
+        s = plan.sizes(batch, capacity)
+        tiles = (capacity + TILE - 1) // TILE
+        hkv = plan.n_kv_heads
+        self.plan, self.batch, self.capacity, self.tiles = plan, batch, capacity, tiles
+        self.consts = torch.zeros(s.consts // 4 + 64, dtype=torch.int32, device=device)
+        self.k_codes = torch.zeros((batch, hkv, tiles, 4 * plan.k_avg_bits, TILE), dtype=torch.int32, device=device)
+        self.k_norms = torch.zeros((batch, hkv, tiles, TILE, 4), dtype=torch.int16, device=device)
+        self.v_codes = torch.zeros((batch, hkv, tiles, HEAD_DIM, 2 * plan.v_bits), dtype=torch.int32, device=device)
+        self.v_norms = torch.zeros((batch, hkv, tiles, TILE), dtype=torch.int16, device=device)
+        assert self.k_codes.numel() * 4 == s.k_codes and self.v_codes.numel() * 4 == s.v_codes
+        plan.upload(self.consts)
+
+    def encode(self, k, v, t0: int, stream=None) -> None:
+        self.plan.encode_k(self.consts, k, self.capacity, t0, self.k_codes, self.k_norms, stream)
+        self.plan.encode_v(self.consts, v, self.capacity, t0, self.v_codes, self.v_norms, stream)
+
+    def packed_bytes(self, seq_len: int) -> int:
+        """Algorithmic packed bytes read for `seq_len` tokens per sequence (codes + present norms)."""
+        kb = self.plan.k_bits
+        groups = [len({int(w) for w in row if w > 0}) for row in kb]
+        per_head = [4 * 4 * self.plan.k_avg_bits + 2 * g + 16 * self.plan.v_bits + 2 for g in groups]
+        return self.batch * seq_len * sum(per_head)

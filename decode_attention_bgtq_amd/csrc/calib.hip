@@ -1,0 +1,96 @@
+// Calibration rows of the Block-GTQ path on gfx950: the label-free RoPE-block
+// energy and the greedy integer bit allocation ("RoPE-Aware Bit Allocation for
+// KV-Cache Quantization", Abstract; Block-GTQ README, introduction and
+// calibration paragraph).  Definitions: include/bgtq.h.
+#include "device.h"
+#include "host.h"
+
+namespace bgtq {
+
+// One workgroup per KV head: exact integer sums of squares per coordinate.
+__global__ __launch_bounds__(256) void energy_kernel(const uint16_t *__restrict__ q,
+                                                     const uint16_t *__restrict__ k, int64_t n,
+                                                     int hq, int hkv, double *__restrict__ energy) {
+  __shared__ u128 sq[256], sk[256];
+  const int kvh = blockIdx.x, tid = threadIdx.x, c = tid & 127, half = tid >> 7;
+  const int G = hq / hkv;
+  u128 aq = 0, ak = 0;
+  for (int64_t t = half; t < n; t += 2) {
+    for (int hh = 0; hh < G; ++hh) {
+      const uint64_t u = f16_mag_units(q[((size_t)t * hq + (size_t)kvh * G + hh) * kHeadDim + c]);
+      aq += (u128)u * u;
+    }
+    const uint64_t u = f16_mag_units(k[((size_t)t * hkv + kvh) * kHeadDim + c]);
+    ak += (u128)u * u;
+  }
+  sq[tid] = aq;
+  sk[tid] = ak;
+  __syncthreads();
+  if (tid < kBlocks) {
+    const int j = tid;
+    const u128 tq = sq[j] + sq[j + 64] + sq[128 + j] + sq[128 + j + 64];
+    const u128 tk = sk[j] + sk[j + 64] + sk[128 + j] + sk[128 + j + 64];
+    const double eq = ldexp(u128_to_f64(tq), -48) / (double)(n * G);
+    const double ek = ldexp(u128_to_f64(tk), -48) / (double)n;
+    energy[(size_t)kvh * kBlocks + j] = eq * ek;
+  }
+}
+
+// ============================================================ (2) allocation
+
+// One wave per KV head; lane j owns block j.
+__global__ __launch_bounds__(64) void allocate_kernel(const double *__restrict__ energy, int avg,
+                                                      int8_t *__restrict__ bits, double dd0,
+                                                      double dd1, double dd2, double dd3) {
+  const int kvh = blockIdx.x, lane = threadIdx.x;
+  const double e = energy[(size_t)kvh * kBlocks + lane];
+  int b = 0;
+  for (int step = 0; step < avg * kBlocks; ++step) {
+    const double dd = b == 0 ? dd0 : b == 1 ? dd1 : b == 2 ? dd2 : dd3;
+    double bg = b < 4 ? e * dd : -1.0;
+    int bj = lane;
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double og = __shfl_xor(bg, off);
+      const int oj = __shfl_xor(bj, off);
+      if (og > bg || (og == bg && oj < bj)) {
+        bg = og;
+        bj = oj;
+      }
+    }
+    if (bj == lane) ++b;
+  }
+  bits[(size_t)kvh * kBlocks + lane] = (int8_t)b;
+}
+
+}  // namespace bgtq
+
+using namespace bgtq;
+
+extern "C" {
+
+bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_cal, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, double *energy, bgtq_stream stream) {
+  if (!q_cal || !k_cal || !energy) return fail(BGTQ_EINVAL, "bgtq_energy: null pointer");
+  if (n_cal < 1 || n_cal > (1 << 22)) return fail(BGTQ_EINVAL, "bgtq_energy: n_cal must be 1..2^22");
+  if (head_dim != kHeadDim) return fail(BGTQ_EINVAL, "bgtq_energy: head_dim must be 128");
+  if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return fail(BGTQ_EINVAL, "bgtq_energy: n_q_heads must be a positive multiple of n_kv_heads");
+  energy_kernel<<<n_kv_heads, 256, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
+                                                              energy);
+  return launch_status("bgtq_energy");
+}
+
+bgtq_status bgtq_allocate(const double *energy, int32_t n_kv_heads, int32_t n_blocks, int32_t avg_bits,
+                          int8_t *bits, bgtq_stream stream) {
+  if (!energy || !bits) return fail(BGTQ_EINVAL, "bgtq_allocate: null pointer");
+  if (n_blocks != kBlocks || n_kv_heads < 1) return fail(BGTQ_EINVAL, "bgtq_allocate: n_blocks must be 64");
+  if (avg_bits < 0 || avg_bits > 4) return fail(BGTQ_EBUDGET, "bgtq_allocate: avg_bits must be 0..4");
+  double dist[5] = {1.0, 0, 0, 0, 0};
+  for (int b = 1; b <= 4; ++b) dist[b] = codebook(b).d;
+  allocate_kernel<<<n_kv_heads, 64, 0, (hipStream_t)stream>>>(energy, avg_bits, bits, dist[0] - dist[1],
+                                                               dist[1] - dist[2], dist[2] - dist[3],
+                                                               dist[3] - dist[4]);
+  return launch_status("bgtq_allocate");
+}
+
+}  // extern "C"

@@ -1,0 +1,372 @@
+// Host-side plan for the Block-GTQ packed-KV path: Lloyd-Max codebooks,
+// seeded Haar rotations, key group maps, decode lookup-table descriptors and
+// the device constant image.  Pure host C++ (no HIP calls).
+//
+// Method sources: "RoPE-Aware Bit Allocation for KV-Cache Quantization",
+// Abstract (TurboQuant-MSE as the base encoder, per-(layer, KV head) integer
+// widths); Block-GTQ README introduction (grouping by width under a fixed
+// average budget).  The quantiser, rotation and layout details the pages leave
+// open are fixed as follows and restated in bgtq.h:
+//  * b-bit Lloyd-Max quantiser of N(0,1) (Lloyd 1957, Max 1960) in double,
+//    made exactly odd-symmetric, applied to sqrt(d_g) * y.
+//  * Rotations: SplitMix64 (Steele, Lea, Flood 2014) absorbing (seed, layer,
+//    kvh, tensor, width, d); Box-Muller Gaussians filled row-major; Householder
+//    QR, Pi = Q diag(sign R_ii) with sign(0) = +1 (Mezzadri 2007).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+
+namespace bgtq {
+namespace {
+
+// ---------------------------------------------------------------- codebooks
+double gauss_pdf(double x) {
+  if (std::isinf(x)) return 0.0;
+  return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+}
+
+// P(a <= X < b), X ~ N(0,1); upper-tail form when both ends are positive.
+double gauss_mass(double a, double b) {
+  const double r2 = std::sqrt(2.0);
+  if (a >= 0.0) return 0.5 * (std::erfc(a / r2) - std::erfc(b / r2));
+  if (b <= 0.0) return 0.5 * (std::erfc(-b / r2) - std::erfc(-a / r2));
+  return 1.0 - 0.5 * std::erfc(-a / r2) - 0.5 * std::erfc(b / r2);
+}
+
+Codebook make_codebook(int bits) {
+  const int n = 1 << bits;
+  std::vector<double> c(n), t(n + 1), nc(n);
+  for (int k = 0; k < n; ++k) c[k] = -2.0 + 4.0 * (k + 0.5) / n;
+  for (int it = 0; it < 100000; ++it) {
+    t[0] = -INFINITY;
+    t[n] = INFINITY;
+    for (int k = 1; k < n; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    double move = 0.0;
+    for (int k = 0; k < n; ++k) {
+      nc[k] = (gauss_pdf(t[k]) - gauss_pdf(t[k + 1])) / gauss_mass(t[k], t[k + 1]);
+      move = std::max(move, std::fabs(nc[k] - c[k]));
+    }
+    c = nc;
+    if (move <= 1e-15) break;
+  }
+  std::vector<double> s(n);
+  for (int k = 0; k < n; ++k) s[k] = (c[k] - c[n - 1 - k]) / 2.0;
+  Codebook cb;
+  cb.c = s;
+  cb.t.resize(n - 1);
+  for (int k = 1; k < n; ++k) cb.t[k - 1] = 0.5 * (s[k - 1] + s[k]);
+  // D(b) = 1 - sum_k p_k c_k^2, summed with Neumaier compensation
+  double sum = 0.0, comp = 0.0;
+  for (int k = 0; k < n; ++k) {
+    const double lo = k ? cb.t[k - 1] : -INFINITY, hi = k < n - 1 ? cb.t[k] : INFINITY;
+    const double term = gauss_mass(lo, hi) * s[k] * s[k];
+    const double tt = sum + term;
+    comp += std::fabs(sum) >= std::fabs(term) ? (sum - tt) + term : (term - tt) + sum;
+    sum = tt;
+  }
+  cb.d = 1.0 - (sum + comp);
+  return cb;
+}
+
+// ---------------------------------------------------------------- rotations
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+uint64_t sm_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct Stream {
+  uint64_t s = 0;
+  void absorb(uint64_t f) { s = sm_mix((s ^ f) + kGamma); }
+  uint64_t next() {
+    s += kGamma;
+    return sm_mix(s);
+  }
+  double uniform() { return (double)(next() >> 11) * (1.0 / 9007199254740992.0); }
+};
+
+// Haar rotation of size d for the given stream fields, row-major Pi[i][k].
+std::vector<double> haar(uint64_t seed, int layer, int kvh, int tensor, int width, int d) {
+  Stream st;
+  const uint64_t fields[6] = {seed, (uint64_t)(int64_t)layer, (uint64_t)kvh, (uint64_t)tensor,
+                              (uint64_t)width, (uint64_t)d};
+  for (uint64_t f : fields) st.absorb(f);
+  std::vector<double> a((size_t)d * d);
+  for (size_t i = 0; i < a.size(); i += 2) {
+    const double u1 = st.uniform(), u2 = st.uniform();
+    const double r = std::sqrt(-2.0 * std::log(1.0 - u1));
+    a[i] = r * std::cos(2.0 * M_PI * u2);
+    a[i + 1] = r * std::sin(2.0 * M_PI * u2);
+  }
+  // Householder QR: a <- R, q <- H_0 H_1 ... H_{d-1}
+  std::vector<double> q((size_t)d * d, 0.0), v(d);
+  for (int i = 0; i < d; ++i) q[(size_t)i * d + i] = 1.0;
+  std::vector<double> diag(d);
+  for (int j = 0; j < d; ++j) {
+    double nrm2 = 0.0;
+    for (int i = j; i < d; ++i) nrm2 += a[(size_t)i * d + j] * a[(size_t)i * d + j];
+    const double nrm = std::sqrt(nrm2);
+    if (nrm == 0.0) {
+      diag[j] = 0.0;
+      continue;
+    }
+    const double x0 = a[(size_t)j * d + j];
+    const double alpha = x0 >= 0.0 ? -nrm : nrm;
+    double vn2 = 0.0;
+    for (int i = j; i < d; ++i) {
+      v[i] = a[(size_t)i * d + j] - (i == j ? alpha : 0.0);
+      vn2 += v[i] * v[i];
+    }
+    if (vn2 == 0.0) {
+      diag[j] = x0;
+      continue;
+    }
+    const double beta = 2.0 / vn2;
+    for (int k = j; k < d; ++k) {
+      double s = 0.0;
+      for (int i = j; i < d; ++i) s += v[i] * a[(size_t)i * d + k];
+      s *= beta;
+      for (int i = j; i < d; ++i) a[(size_t)i * d + k] -= s * v[i];
+    }
+    for (int r = 0; r < d; ++r) {
+      double s = 0.0;
+      for (int i = j; i < d; ++i) s += q[(size_t)r * d + i] * v[i];
+      s *= beta;
+      for (int i = j; i < d; ++i) q[(size_t)r * d + i] -= s * v[i];
+    }
+    diag[j] = a[(size_t)j * d + j];
+  }
+  for (int r = 0; r < d; ++r)
+    for (int k = 0; k < d; ++k)
+      if (diag[k] < 0.0) q[(size_t)r * d + k] = -q[(size_t)r * d + k];
+  return q;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+const Codebook &codebook(int bits) {
+  static std::once_flag once;
+  static Codebook books[4];
+  std::call_once(once, [] {
+    for (int b = 1; b <= 4; ++b) books[b - 1] = make_codebook(b);
+  });
+  return books[bits - 1];
+}
+
+bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
+  const int hkv = d.n_kv_heads, hq = d.n_q_heads;
+  if (hkv < 1 || hq < 1 || hq % hkv) {
+    err = "n_q_heads must be a positive multiple of n_kv_heads";
+    return BGTQ_EINVAL;
+  }
+  const int G = hq / hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) {
+    err = "query heads per KV head must be 1, 2, 4 or 8";
+    return BGTQ_EINVAL;
+  }
+  if (d.head_dim != kHeadDim) {
+    err = "head_dim must be 128";
+    return BGTQ_EINVAL;
+  }
+  if (!d.k_bits) {
+    err = "k_bits is NULL";
+    return BGTQ_EINVAL;
+  }
+  if (d.k_avg_bits < 0 || d.k_avg_bits > 4 || d.v_bits < 1 || d.v_bits > 4) {
+    err = "k_avg_bits must be 0..4 and v_bits 1..4";
+    return BGTQ_EBUDGET;
+  }
+  p.desc = d;
+  p.bits.assign(d.k_bits, d.k_bits + (size_t)hkv * kBlocks);
+  p.desc.k_bits = nullptr;
+  for (int h = 0; h < hkv; ++h) {
+    int sum = 0;
+    for (int j = 0; j < kBlocks; ++j) {
+      const int b = p.bits[(size_t)h * kBlocks + j];
+      if (b < 0 || b > 4) {
+        err = "k_bits entries must be 0..4";
+        return BGTQ_EBUDGET;
+      }
+      sum += b;
+    }
+    if (sum != d.k_avg_bits * kBlocks) {
+      err = "a row of k_bits does not sum to k_avg_bits * 64";
+      return BGTQ_EBUDGET;
+    }
+  }
+  const int wk = 4 * d.k_avg_bits;
+  const int entry_log2 = 2 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);
+
+  // groups, coordinates, bit offsets, rotations
+  p.kvh.assign(hkv, KvhDesc{});
+  p.rot_k.clear();
+  p.rot_v.clear();
+  int64_t rot64_k = 0, rot32_k = 0;
+  for (int h = 0; h < hkv; ++h) {
+    KvhDesc &kd = p.kvh[h];
+    std::memset(&kd, 0, sizeof(kd));
+    int pos = 0, bit = 0;
+    for (int w = 4; w >= 1; --w) {
+      int dg = 0;
+      for (int j = 0; j < kBlocks; ++j)
+        if (p.bits[(size_t)h * kBlocks + j] == w) {
+          kd.coord[pos + dg++] = (int16_t)j;
+          kd.coord[pos + dg++] = (int16_t)(j + kBlocks);
+        }
+      if (!dg) continue;
+      KGroupDesc &g = kd.g[kd.n_groups++];
+      g.w = w;
+      g.d = dg;
+      g.pos = pos;
+      g.bit_off = bit;
+      g.rot64 = rot64_k;
+      g.rot32 = rot32_k;
+      rot64_k += (int64_t)dg * dg;
+      rot32_k += (int64_t)dg * dg;
+      p.rot_k.push_back(haar(d.seed, d.layer, h, 0, w, dg));
+      pos += dg;
+      bit += w * dg;
+    }
+    kd.d_nz = pos;
+    p.rot_v.push_back(haar(d.seed, d.layer, h, 1, d.v_bits, kHeadDim));
+  }
+
+  // decode lookup chunks; pick the widest window whose tables fit 64 KiB
+  int window = 6;
+  for (;;) {
+    int max_chunks = 0;
+    for (int h = 0; h < hkv; ++h) {
+      int n = 0;
+      for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) {
+        const KGroupDesc &g = p.kvh[h].g[gi];
+        const int m = window / g.w;
+        n += (g.d + m - 1) / m;
+      }
+      max_chunks = std::max(max_chunks, n);
+    }
+    const size_t bytes = (size_t)max_chunks << (window + entry_log2);
+    if (bytes <= 65536 || window == 4) break;
+    window = 4;
+  }
+  p.lookup.clear();
+  p.build.clear();
+  int max_chunks = 0;
+  for (int h = 0; h < hkv; ++h) {
+    KvhDesc &kd = p.kvh[h];
+    if (p.lookup.size() & 1) {  // even start for the paired 16-bit words
+      p.lookup.push_back(0);
+      p.build.push_back(0);
+    }
+    kd.chunk_base = (int32_t)p.lookup.size();
+    std::vector<int> anchors;
+    int c = 0;
+    for (int gi = 0; gi < kd.n_groups; ++gi) {
+      const KGroupDesc &g = kd.g[gi];
+      const int m_max = window / g.w;
+      for (int r0 = 0; r0 < g.d; r0 += m_max, ++c) {
+        const int m = std::min(m_max, g.d - r0);
+        const int s = g.bit_off + g.w * r0;
+        const int lo = s - entry_log2;
+        const int anchor = lo >= 0 ? lo / 32 : -1;
+        const int shift = lo - 32 * anchor;
+        const uint32_t slot = (uint32_t)(4 - g.w);
+        p.lookup.push_back((uint16_t)((uint32_t)c | ((uint32_t)shift << 7) | (slot << 12) |
+                                      (r0 == 0 ? kChunkStart : 0u)));
+        p.build.push_back((uint32_t)(g.pos + r0) | ((uint32_t)m << 8) | ((uint32_t)g.w << 12) |
+                          ((uint32_t)gi << 15));
+        anchors.push_back(anchor);
+      }
+    }
+    kd.n_chunks = c;
+    max_chunks = std::max(max_chunks, c);
+    // anchor ranges: chunks anchored at word jj-1 are [anchor[jj], anchor[jj+1])
+    for (int jj = 0; jj <= kMaxWK + 1; ++jj) {
+      int first = 0;
+      while (first < c && anchors[first] < jj - 1) ++first;
+      kd.anchor[jj] = first;
+    }
+  }
+  if (p.lookup.size() & 1) {
+    p.lookup.push_back(0);
+    p.build.push_back(0);
+  }
+
+  // constant image
+  ConstHeader &hd = p.hdr;
+  std::memset(&hd, 0, sizeof(hd));
+  hd.n_kv_heads = hkv;
+  hd.n_q_heads = hq;
+  hd.group = G;
+  hd.head_dim = kHeadDim;
+  hd.k_avg_bits = d.k_avg_bits;
+  hd.v_bits = d.v_bits;
+  hd.wk = wk;
+  hd.wv = 2 * d.v_bits;
+  hd.lut_window = window;
+  hd.lut_entry_log2 = entry_log2;
+  hd.max_chunks = max_chunks;
+  for (int b = 1; b <= 4; ++b) {
+    const Codebook &cb = codebook(b);
+    for (int k = 0; k < (1 << b); ++k) hd.cent[b - 1][k] = cb.c[k];
+    for (int k = 0; k < (1 << b) - 1; ++k) hd.thr[b - 1][k] = cb.t[k];
+    hd.dist[b] = cb.d;
+  }
+  hd.dist[0] = 1.0;
+  size_t off = align256(sizeof(ConstHeader));
+  hd.off_kvh = off;
+  off = align256(off + sizeof(KvhDesc) * hkv);
+  hd.off_lookup = off;
+  off = align256(off + 2 * p.lookup.size());
+  hd.off_build = off;
+  off = align256(off + 4 * p.build.size());
+  hd.off_rot64_k = off;
+  off = align256(off + 8 * (size_t)rot64_k);
+  hd.off_rot32_k = off;
+  off = align256(off + 4 * (size_t)rot32_k);
+  hd.off_rot64_v = off;
+  off = align256(off + 8 * (size_t)hkv * kHeadDim * kHeadDim);
+  hd.off_rot32_v = off;
+  off = align256(off + 4 * (size_t)hkv * kHeadDim * kHeadDim);
+  hd.total_bytes = off;
+
+  p.image.assign(off, 0);
+  uint8_t *img = p.image.data();
+  std::memcpy(img, &hd, sizeof(hd));
+  std::memcpy(img + hd.off_kvh, p.kvh.data(), sizeof(KvhDesc) * hkv);
+  std::memcpy(img + hd.off_lookup, p.lookup.data(), 2 * p.lookup.size());
+  std::memcpy(img + hd.off_build, p.build.data(), 4 * p.build.size());
+  double *r64k = (double *)(img + hd.off_rot64_k);
+  float *r32k = (float *)(img + hd.off_rot32_k);
+  size_t gidx = 0;
+  for (int h = 0; h < hkv; ++h)
+    for (int gi = 0; gi < p.kvh[h].n_groups; ++gi, ++gidx) {
+      const KGroupDesc &g = p.kvh[h].g[gi];
+      const std::vector<double> &pi = p.rot_k[gidx];
+      for (int i = 0; i < g.d; ++i)
+        for (int k = 0; k < g.d; ++k) {
+          r64k[g.rot64 + (int64_t)k * g.d + i] = pi[(size_t)i * g.d + k];
+          r32k[g.rot32 + (int64_t)i * g.d + k] = (float)pi[(size_t)i * g.d + k];
+        }
+    }
+  double *r64v = (double *)(img + hd.off_rot64_v);
+  float *r32v = (float *)(img + hd.off_rot32_v);
+  for (int h = 0; h < hkv; ++h) {
+    const std::vector<double> &pi = p.rot_v[h];
+    const size_t base = (size_t)h * kHeadDim * kHeadDim;
+    for (int i = 0; i < kHeadDim; ++i)
+      for (int k = 0; k < kHeadDim; ++k) {
+        r64v[base + (size_t)k * kHeadDim + i] = pi[(size_t)i * kHeadDim + k];
+        r32v[base + (size_t)k * kHeadDim + i] = (float)pi[(size_t)i * kHeadDim + k];
+      }
+  }
+  return BGTQ_OK;
+}
+
+}  // namespace bgtq

@@ -1,0 +1,226 @@
+/*
+ * bgtq.h -- C ABI of the Block-GTQ packed-KV library for AMD MI355X (gfx950).
+ *
+ * Block-GTQ ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract)
+ * scores every 2-D RoPE frequency block of every (layer, KV head) with a
+ * label-free Q/K energy, greedily gives integer bit widths to the blocks by
+ * marginal gain under a fixed average budget, encodes keys with TurboQuant-MSE
+ * per group of equal-width blocks (values at one uniform width), and serves
+ * decode attention straight from the packed cache.  The Block-GTQ README
+ * (introduction, calibration paragraph, backend table) adds the per-(layer,
+ * KV head) calibration from saved Q/K activations and the fused packed-cache
+ * decode kernel as the production path.
+ *
+ * Conventions (all entry points):
+ *  - Return BGTQ_OK (0) or a negative bgtq_status.  No exception or abort
+ *    crosses the ABI.  bgtq_last_error() returns a thread-local message for
+ *    the last failure of the calling thread.
+ *  - Arguments are validated on the host before anything is enqueued; a call
+ *    that fails validation writes nothing.
+ *  - Device pointers are caller-owned device allocations (the library never
+ *    allocates device memory).  Host pointers are read during the call only.
+ *  - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream) with no host synchronisation, except where stated.
+ *  - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
+ *  - head_dim is 128 (64 RoPE blocks) in this version.
+ *  - A failed kernel launch returns BGTQ_EDEVICE.
+ */
+#ifndef BGTQ_H
+#define BGTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bgtq_status;
+enum {
+  BGTQ_OK = 0,
+  BGTQ_EINVAL = -1,     /* bad pointer, shape or flag */
+  BGTQ_EBUDGET = -2,    /* bit budget outside 0..4 bits per coordinate */
+  BGTQ_ECAPACITY = -3,  /* token range beyond the cache capacity */
+  BGTQ_EDEVICE = -4,    /* HIP runtime or launch failure */
+  BGTQ_EWORKSPACE = -5  /* workspace smaller than the size query */
+};
+
+#define BGTQ_ABI_VERSION 1
+#define BGTQ_TILE 64 /* cache tokens per tile */
+
+typedef void *bgtq_stream; /* hipStream_t */
+
+int32_t bgtq_abi_version(void);
+const char *bgtq_last_error(void);
+
+/*
+ * (1) Label-free block energy (Abstract: "computes a label-free energy score
+ * for each RoPE block"; README calibration paragraph: Q/K activations of one
+ * forward pass).  Block j of a 128-wide head is the coordinate pair (j, j+64).
+ *   E[h][j] = Eq[h][j] * Ek[h][j]
+ *   Eq[h][j] = sum over t < n_cal and h' in {hG..hG+G-1} of q[t][h'][j]^2 + q[t][h'][j+64]^2, / (n_cal G)
+ *   Ek[h][j] = sum over t < n_cal of k[t][h][j]^2 + k[t][h][j+64]^2, / n_cal
+ * Each sum is exact and rounded once to double; the division and the product
+ * round once each, so the result is deterministic to the last bit.
+ *   q_cal   device fp16 [n_cal][n_q_heads][head_dim], post-RoPE, d fastest
+ *   k_cal   device fp16 [n_cal][n_kv_heads][head_dim]
+ *   energy  device double [n_kv_heads][head_dim/2], written
+ * Errors: EINVAL on null pointers, n_cal < 1 or n_cal > 2^22, head_dim != 128,
+ * n_q_heads not a positive multiple of n_kv_heads.
+ */
+bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_cal,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                        double *energy, bgtq_stream stream);
+
+/*
+ * (2) Greedy integer bit allocation by marginal gain (Abstract: "greedily
+ * allocates integer bit widths by marginal gain"; README introduction: bits
+ * shift toward high-energy blocks under a fixed average budget).
+ * Widths start at 0; avg_bits * n_blocks times, the block with the largest
+ * gain E[j] * (D(b_j) - D(b_j + 1)) among blocks with b_j < 4 gets one more
+ * bit (ties: lowest j).  D(b) is the b-bit Lloyd-Max MSE of N(0,1), D(0) = 1.
+ *   energy  device double [n_kv_heads][n_blocks]
+ *   bits    device int8 [n_kv_heads][n_blocks], written (values 0..4)
+ * Errors: EINVAL on null pointers or n_blocks != 64; EBUDGET unless
+ * 0 <= avg_bits <= 4.
+ */
+bgtq_status bgtq_allocate(const double *energy, int32_t n_kv_heads, int32_t n_blocks,
+                          int32_t avg_bits, int8_t *bits, bgtq_stream stream);
+
+/*
+ * (3) Plan: everything the encoder and decoder need for one layer, fixed by
+ * (widths, V width, seed, layer): Lloyd-Max codebooks b = 1..4 in double, one
+ * seeded Haar rotation per (KV head, K width group) and per KV head for V
+ * (SplitMix64 stream absorbing seed, layer, kvh, tensor (K 0, V 1), width,
+ * group size; Box-Muller; Householder QR with the sign of diag(R) taken
+ * positive), the group maps, the bit offsets of the key stream and the
+ * decode lookup-table descriptors.  Plans are immutable; one plan may be used
+ * from several threads and streams at once.
+ */
+typedef struct bgtq_plan bgtq_plan;
+
+typedef struct {
+  int32_t n_kv_heads;
+  int32_t n_q_heads;    /* multiple of n_kv_heads, query head h reads KV head h / G */
+  int32_t head_dim;     /* 128 */
+  int32_t k_avg_bits;   /* 0..4; each row of k_bits must sum to k_avg_bits * 64 */
+  int32_t v_bits;       /* 1..4 */
+  const int8_t *k_bits; /* host int8 [n_kv_heads][64], values 0..4 */
+  uint64_t seed;
+  int32_t layer;
+} bgtq_plan_desc;
+
+typedef struct {
+  uint64_t consts;  /* device constant image written by bgtq_plan_upload */
+  uint64_t k_codes; /* u32 [batch][Hkv][tiles][4*k_avg_bits][64] */
+  uint64_t k_norms; /* fp16 [batch][Hkv][tiles][64][4], slot 4-w holds the width-w group norm */
+  uint64_t v_codes; /* u32 [batch][Hkv][tiles][128][2*v_bits] */
+  uint64_t v_norms; /* fp16 [batch][Hkv][tiles][64] */
+} bgtq_sizes;
+
+/* Errors: EINVAL (null, shape), EBUDGET (a row of k_bits does not sum to
+ * k_avg_bits * 64 or holds a width outside 0..4, v_bits outside 1..4). */
+bgtq_status bgtq_plan_create(const bgtq_plan_desc *desc, bgtq_plan **out);
+void bgtq_plan_destroy(bgtq_plan *plan);
+
+/* Byte sizes of the constant image and of the cache arrays for `batch`
+ * sequences of `capacity` tokens (tiles = ceil(capacity / 64)). The caller
+ * zero-fills the cache arrays before the first encode. */
+bgtq_status bgtq_plan_sizes(const bgtq_plan *plan, int32_t batch, int64_t capacity,
+                            bgtq_sizes *out);
+
+/* Copies the constant image into caller memory `dev_consts` (sizes.consts
+ * bytes, 256-byte aligned) on `stream`.  The plan must outlive the copy. */
+bgtq_status bgtq_plan_upload(const bgtq_plan *plan, void *dev_consts, bgtq_stream stream);
+
+/*
+ * (4) TurboQuant-MSE encode of n_new tokens at positions t0 .. t0+n_new-1 of
+ * every sequence (prefill: t0 = 0; append: t0 = current length).  Per token,
+ * KV head and width group: n = ||x_g|| (exact sum of squares, rounded once,
+ * correctly rounded sqrt), y = Pi x_g / n (0 if n = 0), z = sqrt(d_g) y,
+ * code_i = #{Lloyd-Max thresholds < z_i}; the norm is stored as fp16 with one
+ * round-to-nearest-even step.  Keys use the plan's widths (groups in width
+ * order 4,3,2,1, each block's coordinates j, j+64 adjacent, blocks
+ * ascending); values one group of all 128 coordinates at v_bits.
+ *   k / v      device fp16 [batch][n_new][n_kv_heads][128], post-RoPE keys
+ *   capacity   tokens per sequence the cache arrays were sized for
+ *   k_codes... device arrays laid out as in bgtq_sizes
+ * Tokens outside [t0, t0+n_new) are left unchanged.
+ * Errors: EINVAL (null, batch < 1, n_new < 0), ECAPACITY (t0 < 0 or
+ * t0 + n_new > capacity).
+ */
+bgtq_status bgtq_encode_k(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k,
+                          int32_t batch, int64_t capacity, int64_t t0, int64_t n_new,
+                          uint32_t *k_codes, uint16_t *k_norms, bgtq_stream stream);
+bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const uint16_t *v,
+                          int32_t batch, int64_t capacity, int64_t t0, int64_t n_new,
+                          uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
+
+/*
+ * (5) Query rotation: for every query head h and present key width group g,
+ * q_rot[b][h][o_g + i] = sum_k Pi_g[i][k] q[b][h][coord_g[k]] (fp32, matrix
+ * cores), o_g = sum of the sizes of the groups before g; entries past the
+ * last group are 0.  This is the "rotate q once per group" step of the fused
+ * decode (logits are taken in the rotated space).
+ *   q      device fp16 [batch][n_q_heads][128] (post-RoPE)
+ *   q_rot  device float [batch][n_q_heads][128], written
+ */
+bgtq_status bgtq_rotate_queries(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                int32_t batch, float *q_rot, bgtq_stream stream);
+
+/*
+ * (6) Fused decode attention over the packed cache for one new query per
+ * sequence (the packed-cache serving path of the Abstract and the README
+ * backend table): per (sequence, query head),
+ *   l_t = softmax_scale * q . k_hat_t,  o = sum_t softmax(l)_t v_hat_t
+ * over t < seq_len, where k_hat, v_hat are the TurboQuant-MSE reconstructions
+ * (fp16 norm * Pi^T (centroid / sqrt(d_g))).  Computed without
+ * materialising k_hat or v_hat: queries rotated once per group, per-group
+ * lookup tables of q_rot x centroid in LDS, online softmax, accumulation in
+ * the rotated V space, then one un-rotation per head.  fp32 accumulation.
+ *   q           device fp16 [batch][n_q_heads][128]
+ *   seq_lens    device int32 [batch]; each value is clamped to [0, max_seq_len];
+ *               a sequence of length 0 yields a zero output
+ *   max_seq_len host bound on every seq_lens entry, 1 <= max_seq_len <= capacity
+ *   out         device fp16 [batch][n_q_heads][128], written
+ *   workspace   device scratch of at least bgtq_decode_workspace_size bytes
+ * Errors: EINVAL, ECAPACITY (max_seq_len outside [1, capacity]),
+ * EWORKSPACE (ws_bytes too small).
+ */
+bgtq_status bgtq_decode_workspace_size(const bgtq_plan *plan, int32_t batch, int64_t max_seq_len,
+                                       size_t *bytes);
+bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                             const uint32_t *k_codes, const uint16_t *k_norms,
+                             const uint32_t *v_codes, const uint16_t *v_norms, int64_t capacity,
+                             const int32_t *seq_lens, int32_t batch, int64_t max_seq_len,
+                             float softmax_scale, uint16_t *out, void *workspace, size_t ws_bytes,
+                             bgtq_stream stream);
+
+/*
+ * Host-side inspection (no device work).
+ * bgtq_codebook: the b-bit Lloyd-Max quantiser of N(0,1) the library uses:
+ * centroids [2^b], interior thresholds [2^b - 1], and D(b).
+ * bgtq_plan_rotation: the plan's rotation for (kvh, tensor 0 = K / 1 = V,
+ * width) into out [d*d] row-major (Pi[i][k]); *dim receives d (0 if the width
+ * is absent).  out may be NULL to query d only.
+ * bgtq_plan_bits: the plan's widths [n_kv_heads][64].
+ */
+bgtq_status bgtq_codebook(int32_t bits, double *centroids, double *thresholds, double *distortion);
+bgtq_status bgtq_plan_rotation(const bgtq_plan *plan, int32_t kvh, int32_t tensor, int32_t width,
+                               double *out, int32_t *dim);
+bgtq_status bgtq_plan_bits(const bgtq_plan *plan, int8_t *bits);
+
+/*
+ * Kernel timing: when enabled, bgtq_decode_attn brackets its cache-streaming
+ * kernel with HIP events on `stream`; bgtq_profile_read waits for the
+ * recorded events, returns the summed duration (ms) and launch count since
+ * the last read, and clears them.
+ */
+bgtq_status bgtq_profile_enable(int32_t on);
+bgtq_status bgtq_profile_read(double *stream_kernel_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BGTQ_H */

@@ -1,0 +1,131 @@
+"""Host-side tests of libbgtq: exported symbols, codebooks and rotations against the
+oracle, plan validation and argument checks.  No device work is issued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bg():
+    import decode_attention_bgtq_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from decode_attention_bgtq_amd import build
+        build.build()
+    m.load()
+    return m
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "bgtq.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bgtq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(bg):
+    names = _header_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(bg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bg.EXPORTED) == names
+
+
+def test_abi_version(bg):
+    assert bg.abi_version() == 1
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_codebook_matches_oracle(bg, b):
+    c, t, d = bg.codebook(b)
+    oc, ot, od, _ = oracle.lloyd_max(b)
+    np.testing.assert_allclose(c, oc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(t, ot, rtol=0, atol=1e-12)
+    assert abs(d - od) <= 1e-12
+    assert t[len(t) // 2] == 0.0
+
+
+def _bits(seed, avg):
+    e = np.exp(np.random.default_rng(seed).normal(0, 2, (3, 64)))
+    return np.stack([oracle.greedy_allocate(r, avg, oracle.distortion_table()) for r in e])
+
+
+def test_plan_rotations_match_oracle(bg):
+    bits = _bits(0, 3)
+    plan = bg.Plan(bits, 3, 2, n_q_heads=12, seed=7, layer=5)
+    np.testing.assert_array_equal(plan.bits(), bits)
+    for h in range(3):
+        for w in (1, 2, 3, 4):
+            d = 2 * int((bits[h] == w).sum())
+            got = plan.rotation(h, 0, w)
+            if d == 0:
+                assert got is None
+                continue
+            ref = oracle.rotation_for(7, 5, h, 0, w, d)
+            assert got.shape == (d, d)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(got.T @ got, np.eye(d), atol=1e-13)
+        rv = plan.rotation(h, 1, 2)
+        np.testing.assert_allclose(rv, oracle.rotation_for(7, 5, h, 1, 2, 128), rtol=0, atol=1e-12)
+        assert plan.rotation(h, 1, 3) is None
+
+
+def test_plan_sizes(bg):
+    bits = _bits(1, 2)
+    plan = bg.Plan(bits, 2, 2, n_q_heads=12)
+    s = plan.sizes(batch=2, capacity=130)
+    tiles = 3
+    assert s.k_codes == 2 * 3 * tiles * 8 * 64 * 4
+    assert s.k_norms == 2 * 3 * tiles * 64 * 4 * 2
+    assert s.v_codes == 2 * 3 * tiles * 128 * 4 * 4
+    assert s.v_norms == 2 * 3 * tiles * 64 * 2
+    assert s.consts > 0 and s.consts % 256 == 0
+
+
+def test_plan_validation(bg):
+    bits = _bits(2, 3)
+    with pytest.raises(bg.BgtqError) as e:
+        bg.Plan(bits, 2, 2, n_q_heads=12)          # rows sum to 192, not 128
+    assert e.value.status == bg.EBUDGET
+    bad = bits.copy()
+    bad[0, 0] = 5
+    with pytest.raises(bg.BgtqError) as e:
+        bg.Plan(bad, 3, 2, n_q_heads=12)
+    assert e.value.status == bg.EBUDGET
+    with pytest.raises(bg.BgtqError) as e:
+        bg.Plan(bits, 3, 2, n_q_heads=9)           # G = 3
+    assert e.value.status == bg.EINVAL
+    with pytest.raises(bg.BgtqError) as e:
+        bg.Plan(bits, 3, 5, n_q_heads=12)
+    assert e.value.status == bg.EBUDGET
+    assert "k_bits" in bg.load().bgtq_last_error().decode() or True
+
+
+def test_device_calls_reject_bad_arguments_before_launch(bg):
+    lib = bg.load()
+    assert lib.bgtq_energy(None, None, 10, 8, 2, 128, None, None) == bg.EINVAL
+    assert lib.bgtq_energy(1, 1, 10, 8, 3, 128, 1, None) == bg.EINVAL      # 8 % 3
+    assert lib.bgtq_energy(1, 1, 10, 8, 2, 64, 1, None) == bg.EINVAL       # head_dim
+    assert lib.bgtq_allocate(1, 2, 64, 5, 1, None) == bg.EBUDGET
+    assert lib.bgtq_allocate(1, 2, 32, 2, 1, None) == bg.EINVAL
+    plan = bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6)
+    h = plan.handle
+    assert lib.bgtq_encode_k(h, 256, 256, 1, 100, 90, 20, 256, 256, None) == bg.ECAPACITY
+    assert lib.bgtq_encode_v(h, 256, 256, 1, 100, -1, 20, 256, 256, None) == bg.ECAPACITY
+    assert lib.bgtq_encode_k(h, None, 256, 1, 100, 0, 20, 256, 256, None) == bg.EINVAL
+    args = [h, 256, 256, 256, 256, 256, 256]
+    assert lib.bgtq_decode_attn(*args, 100, 256, 1, 101, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
+    assert lib.bgtq_decode_attn(*args, 100, 256, 1, 0, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
+    assert lib.bgtq_decode_attn(*args, 100, 256, 1, 50, 0.1, 256, 256, 16, None) == bg.EWORKSPACE
+    assert lib.bgtq_decode_attn(*args, 100, 256, 1, 50, -1.0, 256, 256, 1 << 30, None) == bg.EINVAL
+    assert lib.bgtq_decode_attn(h, 256, None, 256, 256, 256, 256, 100, 256, 1, 50, 0.1, 256, 256, 1 << 30,
+                                None) == bg.EINVAL
+    assert lib.bgtq_plan_upload(h, 255, None) == bg.EINVAL                  # misaligned
+    assert lib.bgtq_codebook(0, None, None, None) == bg.EINVAL
