@@ -75,15 +75,26 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                ROW_MASK, 0xF, false));
 }
 
-// Max over the 64 lanes of a wave, returned to every lane.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));         // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));         // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));        // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));        // row_mirror
-  v = fmaxf(v, dpp_f<0x142, 0xA>(v));   // row_bcast:15
-  v = fmaxf(v, dpp_f<0x143, 0xC>(v));   // row_bcast:31
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Max over the 64 lanes of a wave, returned to every lane.  Floats are mapped
+// to integers with the same order (negative values have their magnitude bits
+// flipped) so that each step is a single integer max with a DPP operand; the
+// inputs are finite or -inf.
+__device__ __forceinline__ float wave_max(float x) {
+  const int i = __builtin_bit_cast(int, x);
+  int v = i ^ ((i >> 31) & 0x7FFFFFFF);
+  v = max(v, dpp_i<0xB1>(v));        // quad_perm [1,0,3,2]
+  v = max(v, dpp_i<0x4E>(v));        // quad_perm [2,3,0,1]
+  v = max(v, dpp_i<0x141>(v));       // row_half_mirror
+  v = max(v, dpp_i<0x140>(v));       // row_mirror
+  v = max(v, dpp_i<0x142, 0xA>(v));  // row_bcast:15
+  v = max(v, dpp_i<0x143, 0xC>(v));  // row_bcast:31
+  v = __builtin_amdgcn_readlane(v, 63);
+  return __builtin_bit_cast(float, v ^ ((v >> 31) & 0x7FFFFFFF));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(128) void append_kernel(const uint8_t *__restrict__
     __syncthreads();
     if (tid < d_nz) {
       double acc = 0.0;
-#pragma unroll 16
+#pragma unroll 32
       for (int k = 0; k < d; ++k) {
         const int c = IS_V ? k : kd->coord[pos + k];
         acc = fma(pt[(size_t)k * d + i], (double)xs[c], acc);

@@ -22,12 +22,14 @@ constexpr int kMaxChunks = 128;     // one code per chunk at most
 // codes of one key group (m * w <= window bits).  Its table is indexed by the
 // `window` stream bits starting at the chunk's first bit.
 //
-// lookup (16 bits, two per 32-bit word): [0,7) table index, [7,12) funnel
-//   shift, [12,14) norm slot, [14] first chunk of a group
+// lookup (32 bits): [0,5) funnel shift that brings the chunk's window to bit
+//   log2(entry bytes), [5,23) byte offset of the chunk's table in LDS,
+//   [23] first chunk of a group, [24,26) norm slot (4 - width)
 // build (32 bits): [0,8) first code position (group order), [8,12) codes m,
 //   [12,15) width w, [15,17) group index
-// Each head's chunk list starts at an even index (padded with a null chunk).
-constexpr uint32_t kChunkStart = 1u << 14;
+constexpr uint32_t kChunkStart = 1u << 23;
+constexpr uint32_t kChunkTableMask = 0x007FFFE0u;
+constexpr int kLutBudget = 64 * 1024;  // LDS bytes for one head's key tables
 
 struct KGroupDesc {
   int32_t w;        // width 1..4
@@ -58,7 +60,7 @@ struct ConstHeader {
   int32_t max_chunks;        // largest chunk count over heads
   int32_t pad0;
   int64_t off_kvh;           // KvhDesc[n_kv_heads]
-  int64_t off_lookup;        // uint16 [total chunks]
+  int64_t off_lookup;        // uint32 [total chunks]
   int64_t off_build;         // uint32 [total chunks]
   int64_t off_rot64_k;       // double area (Pi^T per K group)
   int64_t off_rot32_k;       // float area (Pi per K group)
@@ -80,8 +82,7 @@ struct Plan {
   bgtq_plan_desc desc{};
   std::vector<int8_t> bits;             // [Hkv][64]
   std::vector<KvhDesc> kvh;
-  std::vector<uint16_t> lookup;         // chunk descriptors (see above)
-  std::vector<uint32_t> build;
+  std::vector<uint32_t> lookup, build;  // chunk descriptors (see above)
   std::vector<std::vector<double>> rot_k;  // per (kvh, group) Pi row-major
   std::vector<std::vector<double>> rot_v;  // per kvh Pi_V row-major
   std::vector<uint8_t> image;           // device constant image

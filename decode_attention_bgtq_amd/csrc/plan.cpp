@@ -238,10 +238,10 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     p.rot_v.push_back(haar(d.seed, d.layer, h, 1, d.v_bits, kHeadDim));
   }
 
-  // decode lookup chunks; pick the widest window whose tables fit 64 KiB
+  // decode lookup chunks; the widest window whose tables fit the LDS budget
   int window = 6;
   for (;;) {
-    int max_chunks = 0;
+    int max_c = 0;
     for (int h = 0; h < hkv; ++h) {
       int n = 0;
       for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) {
@@ -249,10 +249,10 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
         const int m = window / g.w;
         n += (g.d + m - 1) / m;
       }
-      max_chunks = std::max(max_chunks, n);
+      max_c = std::max(max_c, n);
     }
-    const size_t bytes = (size_t)max_chunks << (window + entry_log2);
-    if (bytes <= 65536 || window == 4) break;
+    const size_t bytes = (size_t)max_c << (window + entry_log2);
+    if (bytes <= (size_t)kLutBudget || window == 4) break;
     window = 4;
   }
   p.lookup.clear();
@@ -260,10 +260,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   int max_chunks = 0;
   for (int h = 0; h < hkv; ++h) {
     KvhDesc &kd = p.kvh[h];
-    if (p.lookup.size() & 1) {  // even start for the paired 16-bit words
-      p.lookup.push_back(0);
-      p.build.push_back(0);
-    }
     kd.chunk_base = (int32_t)p.lookup.size();
     std::vector<int> anchors;
     int c = 0;
@@ -275,10 +271,10 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
         const int s = g.bit_off + g.w * r0;
         const int lo = s - entry_log2;
         const int anchor = lo >= 0 ? lo / 32 : -1;
-        const int shift = lo - 32 * anchor;
+        const uint32_t shift = (uint32_t)(lo - 32 * anchor);
+        const uint32_t table = (uint32_t)c << (window + entry_log2);
         const uint32_t slot = (uint32_t)(4 - g.w);
-        p.lookup.push_back((uint16_t)((uint32_t)c | ((uint32_t)shift << 7) | (slot << 12) |
-                                      (r0 == 0 ? kChunkStart : 0u)));
+        p.lookup.push_back(shift | table | (r0 == 0 ? kChunkStart : 0u) | (slot << 24));
         p.build.push_back((uint32_t)(g.pos + r0) | ((uint32_t)m << 8) | ((uint32_t)g.w << 12) |
                           ((uint32_t)gi << 15));
         anchors.push_back(anchor);
@@ -292,10 +288,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
       while (first < c && anchors[first] < jj - 1) ++first;
       kd.anchor[jj] = first;
     }
-  }
-  if (p.lookup.size() & 1) {
-    p.lookup.push_back(0);
-    p.build.push_back(0);
   }
 
   // constant image
@@ -323,7 +315,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   hd.off_kvh = off;
   off = align256(off + sizeof(KvhDesc) * hkv);
   hd.off_lookup = off;
-  off = align256(off + 2 * p.lookup.size());
+  off = align256(off + 4 * p.lookup.size());
   hd.off_build = off;
   off = align256(off + 4 * p.build.size());
   hd.off_rot64_k = off;
@@ -340,7 +332,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   uint8_t *img = p.image.data();
   std::memcpy(img, &hd, sizeof(hd));
   std::memcpy(img + hd.off_kvh, p.kvh.data(), sizeof(KvhDesc) * hkv);
-  std::memcpy(img + hd.off_lookup, p.lookup.data(), 2 * p.lookup.size());
+  std::memcpy(img + hd.off_lookup, p.lookup.data(), 4 * p.lookup.size());
   std::memcpy(img + hd.off_build, p.build.data(), 4 * p.build.size());
   double *r64k = (double *)(img + hd.off_rot64_k);
   float *r32k = (float *)(img + hd.off_rot32_k);
