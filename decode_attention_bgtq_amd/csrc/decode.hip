@@ -46,36 +46,61 @@ __device__ __forceinline__ T lds_at(uint32_t off) {
 }
 
 // q_rot[h][pos_g + i] = sum_k Pi_g[i][k] q[h][coord_g[k]] for the key groups of
-// one KV head; qin [G][128] natural order, qs [G][128] group order (zeroed by
-// the caller past d_nz).  16x16x4 fp32 MFMA tiles, the G heads as columns;
-// `waves` waves of the workgroup share the row tiles.
+// one KV head.  qg [8][128]: the queries gathered into group order
+// (qg[h][pos_g + k] = q[h][coord_g[k]]), rows h >= G zero.  qs [G][128]: the
+// rotated queries in group order.  16x16x4 fp32 MFMA tiles with the query
+// heads as columns; the (group, 16-row tile) pairs of all groups are spread
+// over the `waves` waves, and each wave issues every operand load of a tile
+// before its first MFMA (clamped addresses, zero-masked values).
 __device__ __forceinline__ void rotate_queries(const ConstHeader *hd, const KvhDesc *kd, int G,
-                                               const float *qin, float *qs, int wave, int waves,
+                                               const float *qg, float *qs, int wave, int waves,
                                                int lane) {
-  for (int gi = 0; gi < kd->n_groups; ++gi) {
-    const KGroupDesc g = kd->g[gi];
-    const float *pi = (const float *)((const uint8_t *)hd + hd->off_rot32_k) + g.rot32;
-    const int n = lane & 15, kq = lane >> 4;
-    for (int i0 = 16 * wave; i0 < g.d; i0 += 16 * waves) {
-      f4v acc = {0.f, 0.f, 0.f, 0.f};
-      const int ia = i0 + n;
-      const int ic = ia < g.d ? ia : g.d - 1;
-#pragma unroll 8
-      for (int k0 = 0; k0 < g.d; k0 += 4) {
-        const int kk = k0 + kq;
-        const int kcl = kk < g.d ? kk : g.d - 1;
-        const float a0 = pi[(size_t)ic * g.d + kcl];
-        const float b0 = qin[(n & 7) * kHeadDim + kd->coord[g.pos + kcl]];
-        const float a = (ia < g.d && kk < g.d) ? a0 : 0.f;
-        const float bv = (kk < g.d && n < G) ? b0 : 0.f;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-      }
+  const int n = lane & 15, kq = lane >> 4;
+  int ng = kd->n_groups, tiles[kMaxGroups + 1];
+  tiles[0] = 0;
+  for (int gi = 0; gi < kMaxGroups; ++gi) tiles[gi + 1] = tiles[gi] + (gi < ng ? (kd->g[gi].d + 15) >> 4 : 0);
+  for (int t = wave; t < tiles[kMaxGroups]; t += waves) {
+    int gi = 0;
+    while (t >= tiles[gi + 1]) ++gi;
+    const int d = kd->g[gi].d, pos = kd->g[gi].pos;
+    const float *pi = (const float *)((const uint8_t *)hd + hd->off_rot32_k) + kd->g[gi].rot32;
+    const int ia = 16 * (t - tiles[gi]) + n;
+    const int ic = ia < d ? ia : d - 1;
+    float a[kHeadDim / 4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * kq + r;
-        if (i < g.d && n < G) qs[n * kHeadDim + g.pos + i] = acc[r];
+    for (int s = 0; s < kHeadDim / 4; ++s) {
+      const int kk = 4 * s + kq;
+      a[s] = pi[(size_t)ic * d + (kk < d ? kk : d - 1)];
+    }
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kHeadDim / 4; ++s) {
+      const int kk = 4 * s + kq;
+      if (4 * s < d) {  // wave-uniform
+        const float av = (ia < d && kk < d) ? a[s] : 0.f;
+        const float bq = qg[(n & 7) * kHeadDim + pos + (kk < d ? kk : d - 1)];
+        const float bv = kk < d ? bq : 0.f;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ia - n + 4 * kq + r;
+      if (i < d && n < G) qs[n * kHeadDim + pos + i] = acc[r];
+    }
+  }
+}
+
+// qg[h][p] = q[h][coord[p]] for p < d_nz, else 0, for h < 8 (rows h >= G zero).
+__device__ __forceinline__ void gather_queries(const KvhDesc *kd, int G, const uint16_t *qb, float *qg, int tid,
+                                               int threads) {
+  const int dnz = kd->d_nz;
+  for (int i = tid; i < 8 * kHeadDim; i += threads) {
+    const int h = i >> 7, p = i & (kHeadDim - 1);
+    const int pc = p < dnz ? p : 0;
+    const int hc = h < G ? h : 0;
+    const float v = h2f(qb[hc * kHeadDim + kd->coord[pc]]);
+    qg[i] = (h < G && p < dnz) ? v : 0.f;
   }
 }
 
@@ -84,7 +109,7 @@ __device__ __forceinline__ void rotate_queries(const ConstHeader *hd, const KvhD
 __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ consts,
                                                    const uint16_t *__restrict__ q, float *__restrict__ qrot) {
   __shared__ float qs[8 * kHeadDim];
-  __shared__ float qin[8 * kHeadDim];
+  __shared__ float qg[8 * kHeadDim];
   const ConstHeader *hd = hdr_of(consts);
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int G = hd->group, hq = hd->n_q_heads;
@@ -92,34 +117,100 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
   const int tid = threadIdx.x;
   const uint16_t *qb = q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim;
   const int nq = G * kHeadDim;
-  for (int i = tid; i < 8 * kHeadDim; i += 256) {
-    qs[i] = 0.f;
-    qin[i] = i < nq ? h2f(qb[i]) : 0.f;
-  }
+  for (int i = tid; i < 8 * kHeadDim; i += 256) qs[i] = 0.f;
+  gather_queries(kd, G, qb, qg, tid, 256);
   __syncthreads();
-  rotate_queries(hd, kd, G, qin, qs, tid >> 6, 4, tid & 63);
+  rotate_queries(hd, kd, G, qg, qs, tid >> 6, 4, tid & 63);
   __syncthreads();
   for (int idx = tid; idx < nq; idx += 256) qrot[((size_t)b * hq + (size_t)kvh * G) * kHeadDim + idx] = qs[idx];
 }
 
 // ------------------------------------------------------------------ stream
 
+// Cross-lane broadcast multiply-adds (inline VALU, no memory access).  The
+// broadcast operand is read through DPP row_newbcast:K, i.e. from lane K of
+// the reading lane's 16-lane row.  Each block starts with two wait states so
+// that a VALU write of a broadcast source just before it is visible to the
+// DPP read.
+#define BGTQ_DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define BGTQ_FM(A, S, B, K) "v_fmac_f32_dpp %" #A ", %" #S ", %" #B " row_newbcast:%" #K BGTQ_DPP
+#define BGTQ_D2(A, S, B, K) "v_dot2c_f32_f16_dpp %" #A ", %" #S ", %" #B " row_newbcast:%" #K BGTQ_DPP
+
+// a[h] += src[h](lane K) * b0 + src[h](lane K + 1) * b1, for the G heads
+template <int G, int K>
+__device__ __forceinline__ void fmac_bcast(float (&a)[G], const float (&src)[G], float b0, float b1) {
+  static_assert(K >= 0 && K + 1 < 16, "row lane");
+  if constexpr (G == 1) {
+    asm("s_nop 1\n\t" BGTQ_FM(0, 1, 2, 4) BGTQ_FM(0, 1, 3, 5)
+        : "+v"(a[0]) : "v"(src[0]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
+  } else if constexpr (G == 2) {
+    asm("s_nop 1\n\t" BGTQ_FM(0, 2, 4, 6) BGTQ_FM(0, 2, 5, 7) BGTQ_FM(1, 3, 4, 6) BGTQ_FM(1, 3, 5, 7)
+        : "+v"(a[0]), "+v"(a[1]) : "v"(src[0]), "v"(src[1]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      asm("s_nop 1\n\t" BGTQ_FM(0, 4, 8, 10) BGTQ_FM(0, 4, 9, 11) BGTQ_FM(1, 5, 8, 10) BGTQ_FM(1, 5, 9, 11)
+              BGTQ_FM(2, 6, 8, 10) BGTQ_FM(2, 6, 9, 11) BGTQ_FM(3, 7, 8, 10) BGTQ_FM(3, 7, 9, 11)
+          : "+v"(a[g]), "+v"(a[g + 1]), "+v"(a[g + 2]), "+v"(a[g + 3])
+          : "v"(src[g]), "v"(src[g + 1]), "v"(src[g + 2]), "v"(src[g + 3]), "v"(b0), "v"(b1), "n"(K),
+            "n"(K + 1));
+    }
+  }
+}
+
+// a0[h] += <src[h](lane K), c0>, a1[h] += <src[h](lane K), c1> (fp16 pairs, fp32 accumulate)
+template <int G, int K>
+__device__ __forceinline__ void dot2_bcast(float (&a0)[G], float (&a1)[G], const uint32_t (&src)[G], uint32_t c0,
+                                           uint32_t c1) {
+  static_assert(K >= 0 && K < 16, "row lane");
+  if constexpr (G == 1) {
+    asm("s_nop 1\n\t" BGTQ_D2(0, 2, 3, 5) BGTQ_D2(1, 2, 4, 5)
+        : "+v"(a0[0]), "+v"(a1[0]) : "v"(src[0]), "v"(c0), "v"(c1), "n"(K));
+  } else if constexpr (G == 2) {
+    asm("s_nop 1\n\t" BGTQ_D2(0, 4, 6, 8) BGTQ_D2(1, 4, 7, 8) BGTQ_D2(2, 5, 6, 8) BGTQ_D2(3, 5, 7, 8)
+        : "+v"(a0[0]), "+v"(a1[0]), "+v"(a0[1]), "+v"(a1[1]) : "v"(src[0]), "v"(src[1]), "v"(c0), "v"(c1),
+          "n"(K));
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      asm("s_nop 1\n\t" BGTQ_D2(0, 8, 12, 14) BGTQ_D2(1, 8, 13, 14) BGTQ_D2(2, 9, 12, 14) BGTQ_D2(3, 9, 13, 14)
+              BGTQ_D2(4, 10, 12, 14) BGTQ_D2(5, 10, 13, 14) BGTQ_D2(6, 11, 12, 14) BGTQ_D2(7, 11, 13, 14)
+          : "+v"(a0[g]), "+v"(a1[g]), "+v"(a0[g + 1]), "+v"(a1[g + 1]), "+v"(a0[g + 2]), "+v"(a1[g + 2]),
+            "+v"(a0[g + 3]), "+v"(a1[g + 3])
+          : "v"(src[g]), "v"(src[g + 1]), "v"(src[g + 2]), "v"(src[g + 3]), "v"(c0), "v"(c1), "n"(K));
+    }
+  }
+}
+#undef BGTQ_D2
+#undef BGTQ_FM
+#undef BGTQ_DPP
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
 struct StreamSmem {
-  int vlut, pbuf, scratch, total;
+  int c4, q4, vlut, scratch, total;
 };
 
-// LDS layout: [key tables | wave merge area] [value table] [P pairs per wave]
-//             [prologue scratch: qin, qs (G x 128 floats each), build words]
+// LDS layout (bytes):
+//   [key tables of the width-1..3 chunks, fp16 entry per query head | wave merge area]
+//   [4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32]
+//   [4-bit group queries: G x 128 fp32, scaled, zero past d4]
+//   [value table]
+//   [prologue scratch: gathered queries 8 x 128, rotated queries G x 128, build
+//    words, centroids 4 x 16, group scales 4, per-head table maxima G]
 template <int G, int VB>
 __host__ __device__ constexpr StreamSmem stream_layout(int table_bytes) {
   StreamSmem s{};
   const int merge = kStreamWaves * G * kPartStride * 4;
   int r0 = table_bytes > merge ? table_bytes : merge;
   r0 = (r0 + 15) & ~15;
-  s.vlut = r0;
-  s.pbuf = s.vlut + VLut<VB>::entries * VLut<VB>::bytes;
-  s.scratch = s.pbuf + kStreamWaves * 32 * G * 4;
-  s.total = s.scratch + 2 * G * kHeadDim * 4 + kMaxChunks * 4;
+  s.c4 = r0;
+  s.q4 = s.c4 + 256 * 8;
+  s.vlut = s.q4 + G * kHeadDim * 4;
+  s.scratch = s.vlut + VLut<VB>::entries * VLut<VB>::bytes;
+  s.total = s.scratch + (8 + G) * kHeadDim * 4 + kMaxChunks * 4 + (64 + kMaxGroups + 8) * 4;
   return s;
 }
 
@@ -174,90 +265,149 @@ __device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *_
   }
 }
 
-template <int G>
-__device__ __forceinline__ void lds_entry(uint32_t a, float (&t)[G]) {
-  if constexpr (G == 1) {
-    t[0] = lds_at<float>(a);
-  } else if constexpr (G == 2) {
-    const float2 v = lds_at<float2>(a);
-    t[0] = v.x, t[1] = v.y;
-  } else {
-#pragma unroll
-    for (int q4 = 0; q4 < G / 4; ++q4) {
-      const float4 v = lds_at<float4>(a + 16 * q4);
-      t[4 * q4 + 0] = v.x, t[4 * q4 + 1] = v.y, t[4 * q4 + 2] = v.z, t[4 * q4 + 3] = v.w;
-    }
-  }
-}
-
-template <int G>
-__device__ __forceinline__ void lds_pairs(uint32_t a, uint32_t (&o)[G]) {
-  if constexpr (G == 1) {
-    o[0] = lds_at<uint32_t>(a);
-  } else if constexpr (G == 2) {
-    const uint2 v = lds_at<uint2>(a);
-    o[0] = v.x, o[1] = v.y;
-  } else {
-#pragma unroll
-    for (int q4 = 0; q4 < G / 4; ++q4) {
-      const uint4 v = lds_at<uint4>(a + 16 * q4);
-      o[4 * q4 + 0] = v.x, o[4 * q4 + 1] = v.y, o[4 * q4 + 2] = v.z, o[4 * q4 + 3] = v.w;
-    }
-  }
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
-}
-
-// acc0/acc1[h] += <p' pair of head h, centroid pair> for token pair `pair`
-template <int G>
-__device__ __forceinline__ void pair_accum(uint32_t pbuf, int pair, uint32_t c0, uint32_t c1,
-                                           float (&acc0)[G], float (&acc1)[G]) {
-  uint32_t pv[G];
-  lds_pairs<G>(pbuf + pair * G * 4, pv);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    acc0[h] = dot2(pv[h], c0, acc0[h]);
-    acc1[h] = dot2(pv[h], c1, acc1[h]);
-  }
-}
-
 struct StreamState {
   uint32_t dv0, dv1;  // lane l: lookup descriptor of chunk l (dv0) and l + 64 (dv1)
   uint32_t av;        // lane jj: first chunk anchored at key word jj-1
   uint32_t fmask;     // window mask shifted to the entry offset (held in a VGPR)
-  int wk;
+  int wk, nb4;
   int64_t seq;
+  uint32_t c4, q4, vlut;  // LDS offsets
 };
 
-// One key chunk: funnel-shift the window out of (hi, lo), look up the table
-// entry of every head, accumulate norm * entry.
+// One table chunk (widths 1..3): funnel-shift the window out of (hi, lo), read
+// the fp16 entries of all heads, accumulate norm * entry with fp32 dot2.
+// nlo / nhi hold the group norm as the fp16 pair (n, 0) / (0, n).
 template <int G>
-__device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo, uint32_t fmask,
-                                          const float (&nf)[4], float &ncur, float (&lg)[G]) {
-  if (dsc & kChunkStart) {
+__device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo, uint32_t fmask, uint32_t n1,
+                                          uint32_t n2, uint32_t n3, uint32_t &nlo, uint32_t &nhi,
+                                          float (&lr)[G]) {
+  if (dsc & kChunkStart) {  // norm slot 1..3 = widths 3..1
     const uint32_t slot = (dsc >> 24) & 3;
-    ncur = slot == 0 ? nf[0] : slot == 1 ? nf[1] : slot == 2 ? nf[2] : nf[3];
+    nlo = slot == 1 ? n1 : (slot == 2 ? n2 : n3);
+    nhi = nlo << 16;
   }
   const uint32_t t = __builtin_amdgcn_alignbit(hi, lo, dsc);
-  float tv[G];
-  lds_entry<G>((t & fmask) | (dsc & kChunkTableMask), tv);
+  const uint32_t a = (t & fmask) | (dsc & kChunkTableMask);
+  if constexpr (G == 1) {
+    const uint32_t e = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a;
+    lr[0] = dot2(e, nlo, lr[0]);
+  } else if constexpr (G == 2) {
+    const uint32_t e = lds_at<uint32_t>(a);
+    lr[0] = dot2(e, nlo, lr[0]);
+    lr[1] = dot2(e, nhi, lr[1]);
+  } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h) lg[h] = fmaf(ncur, tv[h], lg[h]);
+    for (int q4 = 0; q4 < G / 4; ++q4) {
+      const uint2 e = lds_at<uint2>(a + 8 * q4);
+      lr[4 * q4 + 0] = dot2(e.x, nlo, lr[4 * q4 + 0]);
+      lr[4 * q4 + 1] = dot2(e.x, nhi, lr[4 * q4 + 1]);
+      lr[4 * q4 + 2] = dot2(e.y, nlo, lr[4 * q4 + 2]);
+      lr[4 * q4 + 3] = dot2(e.y, nhi, lr[4 * q4 + 3]);
+    }
+  }
+}
+
+// 4-bit group, one block of 16 codes (key words 2 blk, 2 blk + 1): lane =
+// token; a4[h] += sum_r q4[h][16 blk + r] * c4[code_r].  The queries of the
+// block sit row-replicated in one register per head (lane l holds code
+// 16 blk + l % 16) and are broadcast per code by DPP.
+template <int G, int WK, int BLK>
+__device__ __forceinline__ void key4_block(const uint32_t (&w)[WK], uint32_t c4, uint32_t q4, int lane,
+                                           float (&a4)[G]) {
+  float qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) qr[h] = lds_at<float>(q4 + (uint32_t)(h * kHeadDim + 16 * BLK + (lane & 15)) * 4);
+#pragma unroll
+  for (int wi = 0; wi < 2; ++wi) {
+    const uint32_t word = w[2 * BLK + wi];
+#define BGTQ_K4(BY)                                                          \
+  {                                                                          \
+    const float2 cp = lds_at<float2>(c4 + ((word >> (8 * BY)) & 255u) * 8); \
+    if (wi == 0) fmac_bcast<G, 2 * BY>(a4, qr, cp.x, cp.y);                 \
+    else fmac_bcast<G, 8 + 2 * BY>(a4, qr, cp.x, cp.y);                     \
+  }
+    BGTQ_K4(0) BGTQ_K4(1) BGTQ_K4(2) BGTQ_K4(3)
+#undef BGTQ_K4
+  }
+}
+
+template <int G, int WK, int BLK>
+__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], const StreamState &st, int lane,
+                                            float (&a4)[G]) {
+  if constexpr (2 * BLK < WK) {
+    if (BLK < st.nb4) {
+      key4_block<G, WK, BLK>(w, st.c4, st.q4, lane, a4);
+      key4_blocks<G, WK, BLK + 1>(w, st, lane, a4);
+    }
+  }
+}
+
+// Value accumulation for token pair J (0..31) from the row-replicated P'
+// registers: acc0/acc1[h] += <P'_h pair J, centroid pair of coordinate lane / lane + 64>.
+template <int G, int J>
+__device__ __forceinline__ void v_pair(const uint32_t (&pr)[2][G], uint32_t c0, uint32_t c1, float (&acc0)[G],
+                                       float (&acc1)[G]) {
+  dot2_bcast<G, J & 15>(acc0, acc1, pr[J >> 4], c0, c1);
+}
+
+template <int G, int VB, int Y>
+__device__ __forceinline__ void v_step(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+                                       const uint32_t (&pr)[2][G], float (&acc0)[G], float (&acc1)[G]) {
+  if constexpr (VB == 3) {  // Y = token pair, 6 bits per coordinate
+    constexpr int bit = 6 * Y, wi = bit >> 5, sh = bit & 31;
+    uint32_t s0, s1;
+    if constexpr (sh <= 26) {
+      s0 = (va[wi] >> sh) & 63u;
+      s1 = (vb[wi] >> sh) & 63u;
+    } else {
+      s0 = __builtin_amdgcn_alignbit(va[wi + 1], va[wi], sh) & 63u;
+      s1 = __builtin_amdgcn_alignbit(vb[wi + 1], vb[wi], sh) & 63u;
+    }
+    v_pair<G, Y>(pr, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
+  } else if constexpr (VB == 4) {  // Y = token pair, one byte
+    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    v_pair<G, Y>(pr, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
+  } else if constexpr (VB == 2) {  // Y = byte: token pairs 2Y, 2Y + 1
+    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    const uint2 e0 = lds_at<uint2>(vlut + 8 * s0), e1 = lds_at<uint2>(vlut + 8 * s1);
+    v_pair<G, 2 * Y>(pr, e0.x, e1.x, acc0, acc1);
+    v_pair<G, 2 * Y + 1>(pr, e0.y, e1.y, acc0, acc1);
+  } else {  // VB == 1, Y = byte: token pairs 4Y .. 4Y + 3
+    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
+    const uint4 e0 = lds_at<uint4>(vlut + 16 * s0), e1 = lds_at<uint4>(vlut + 16 * s1);
+    v_pair<G, 4 * Y + 0>(pr, e0.x, e1.x, acc0, acc1);
+    v_pair<G, 4 * Y + 1>(pr, e0.y, e1.y, acc0, acc1);
+    v_pair<G, 4 * Y + 2>(pr, e0.z, e1.z, acc0, acc1);
+    v_pair<G, 4 * Y + 3>(pr, e0.w, e1.w, acc0, acc1);
+  }
+}
+
+template <int G, int VB, int Y>
+__device__ __forceinline__ void v_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+                                        const uint32_t (&pr)[2][G], float (&acc0)[G], float (&acc1)[G]) {
+  constexpr int n = VB == 3 || VB == 4 ? 32 : VB == 2 ? 16 : 8;
+  if constexpr (Y < n) {
+    v_step<G, VB, Y>(va, vb, vlut, pr, acc0, acc1);
+    if constexpr ((Y & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the lookups in flight
+    v_steps<G, VB, Y + 1>(va, vb, vlut, pr, acc0, acc1);
+  }
 }
 
 template <int G, int VB, int WK>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
-                                             uint32_t vlut, uint32_t pbuf, float (&mrun)[G], float (&lsum)[G],
+                                             const float (&rinv)[G], float (&mrun)[G], float (&lsum)[G],
                                              float (&acc0)[G], float (&acc1)[G], int lane) {
-  // ---- keys: lane = token; log2-domain logits from the chunk tables
-  const float nf[4] = {h2f((uint16_t)(r.nr.x & 0xFFFF)), h2f((uint16_t)(r.nr.x >> 16)),
-                       h2f((uint16_t)(r.nr.y & 0xFFFF)), h2f((uint16_t)(r.nr.y >> 16))};
-  float lg[G];
+  // ---- keys, lane = token.  4-bit group: direct centroid sums.
+  float a4[G], lr[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) lg[h] = 0.f;
-  float ncur = 0.f;
+  for (int h = 0; h < G; ++h) a4[h] = 0.f, lr[h] = 0.f;
+  key4_blocks<G, WK, 0>(r.w, st, lane, a4);
+  // widths 1..3: table chunks, grouped by the key word their window starts in
+  uint32_t nlo = 0, nhi = 0;
+  const uint32_t n1 = r.nr.x >> 16, n2 = r.nr.y & 0xFFFFu, n3 = r.nr.y >> 16;
 #pragma unroll
   for (int jj = 0; jj <= WK; ++jj) {
     if (jj <= st.wk) {
@@ -266,79 +416,55 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
       const int c1 = __builtin_amdgcn_readlane((int)st.av, jj + 1);
       const int m1 = c1 < 64 ? c1 : 64;
       for (int c = c0; c < m1; ++c)
-        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c), hi, lo, st.fmask, nf, ncur, lg);
+        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c), hi, lo, st.fmask, n1, n2, n3, nlo, nhi,
+                     lr);
       for (int c = c0 > 64 ? c0 : 64; c < c1; ++c)
-        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv1, c - 64), hi, lo, st.fmask, nf, ncur, lg);
+        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv1, c - 64), hi, lo, st.fmask, n1, n2, n3, nlo,
+                     nhi, lr);
     }
   }
   const bool valid = (int64_t)tile * kTile + lane < st.seq;
+  const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
+  // ---- online softmax (log2 domain); P' = p * value norm as fp16 token pairs
   float alpha[G];
+  uint32_t pr[2][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float l = valid ? lg[h] : -INFINITY;
+    const float lg = fmaf(n4, a4[h], lr[h] * rinv[h]);
+    const float l = valid ? lg : -INFINITY;
     const float mn = fmaxf(mrun[h], wave_max(l));
     alpha[h] = __builtin_amdgcn_exp2f(mrun[h] - mn);
     const float p = __builtin_amdgcn_exp2f(l - mn);
     lsum[h] = fmaf(lsum[h], alpha[h], p);
     mrun[h] = mn;
-    *(__attribute__((address_space(3))) _Float16 *)(size_t)(pbuf + ((lane >> 1) * G + h) * 4 + (lane & 1) * 2) =
-        (_Float16)(p * nv);
+    const uint32_t mine = __builtin_bit_cast(uint16_t, (_Float16)(p * nv));
+    const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+    const uint32_t pair = mine | (nb << 16);  // lane 2k: tokens 2k, 2k + 1
+    // row-replicated: lane l of register half t holds pair 16 t + l % 16
+    pr[0][h] = (uint32_t)__builtin_amdgcn_ds_bpermute((lane & 15) << 3, (int)pair);
+    pr[1][h] = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane & 15) + 16) << 3, (int)pair);
   }
-  wave_sync_lds();
   // ---- values: lane = coordinates lane and lane + 64
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     acc0[h] *= alpha[h];
     acc1[h] *= alpha[h];
   }
-  if constexpr (VB == 3) {
-#pragma unroll
-    for (int y = 0; y < 32; ++y) {
-      const int bit = 6 * y, wi = bit >> 5, sh = bit & 31;
-      uint32_t s0, s1;
-      if (sh <= 26) {
-        s0 = (r.va[wi] >> sh) & 63u;
-        s1 = (r.vb[wi] >> sh) & 63u;
-      } else {
-        s0 = __builtin_amdgcn_alignbit(r.va[wi + 1], r.va[wi], sh) & 63u;
-        s1 = __builtin_amdgcn_alignbit(r.vb[wi + 1], r.vb[wi], sh) & 63u;
-      }
-      pair_accum<G>(pbuf, y, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
-    }
-  } else if constexpr (VB == 4) {
-#pragma unroll
-    for (int y = 0; y < 32; ++y) {
-      const uint32_t s0 = (r.va[y >> 2] >> (8 * (y & 3))) & 255u;
-      const uint32_t s1 = (r.vb[y >> 2] >> (8 * (y & 3))) & 255u;
-      pair_accum<G>(pbuf, y, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
-    }
-  } else if constexpr (VB == 2) {
-#pragma unroll
-    for (int y = 0; y < 16; ++y) {
-      const uint32_t s0 = (r.va[y >> 2] >> (8 * (y & 3))) & 255u;
-      const uint32_t s1 = (r.vb[y >> 2] >> (8 * (y & 3))) & 255u;
-      const uint2 e0 = lds_at<uint2>(vlut + 8 * s0), e1 = lds_at<uint2>(vlut + 8 * s1);
-      pair_accum<G>(pbuf, 2 * y, e0.x, e1.x, acc0, acc1);
-      pair_accum<G>(pbuf, 2 * y + 1, e0.y, e1.y, acc0, acc1);
-    }
-  } else {
-#pragma unroll
-    for (int y = 0; y < 8; ++y) {
-      const uint32_t s0 = (r.va[y >> 2] >> (8 * (y & 3))) & 255u;
-      const uint32_t s1 = (r.vb[y >> 2] >> (8 * (y & 3))) & 255u;
-      const uint4 e0 = lds_at<uint4>(vlut + 16 * s0), e1 = lds_at<uint4>(vlut + 16 * s1);
-      pair_accum<G>(pbuf, 4 * y + 0, e0.x, e1.x, acc0, acc1);
-      pair_accum<G>(pbuf, 4 * y + 1, e0.y, e1.y, acc0, acc1);
-      pair_accum<G>(pbuf, 4 * y + 2, e0.z, e1.z, acc0, acc1);
-      pair_accum<G>(pbuf, 4 * y + 3, e0.w, e1.w, acc0, acc1);
-    }
-  }
-  wave_sync_lds();
+  v_steps<G, VB, 0>(r.va, r.vb, st.vlut, pr, acc0, acc1);
 }
 
+// Waves per SIMD the register allocation aims at: four (two workgroups per CU,
+// at most 128 VGPRs) for up to four query heads per KV head and up to eight key
+// words per token; fewer for the larger register sets.
+template <int G, int WK>
+struct StreamOcc {
+  static constexpr int v = G <= 4 ? (WK <= 8 ? 4 : 3) : 2;
+};
+
 template <int G, int VB, int WK>
-__global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
+void decode_stream_kernel(
     const uint8_t *__restrict__ consts, const uint16_t *__restrict__ q, const uint32_t *__restrict__ kc,
     const uint16_t *__restrict__ kn, const uint32_t *__restrict__ vc, const uint16_t *__restrict__ vn,
     int64_t tiles_cap, const int32_t *__restrict__ seq_lens, int64_t max_seq_len, int tiles_per_split,
@@ -354,33 +480,81 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(
   const int win = hd->lut_window;
   const int nch = kd->n_chunks;
   const StreamSmem sm = stream_layout<G, VB>(hd->max_chunks << (win + L));
-  const uint32_t pbuf = (uint32_t)(sm.pbuf + wave * 32 * G * 4);
 
-  // ---- prologue: rotated queries and key lookup tables of this head
+  // ---- prologue: rotated queries, 4-bit group queries and centroid pairs,
+  // key lookup tables of this head
+  float *qg = (float *)(smem + sm.scratch);
+  float *qs = qg + 8 * kHeadDim;
+  uint32_t *bld = (uint32_t *)(qs + G * kHeadDim);
+  float *cs = (float *)(bld + kMaxChunks);  // centroids [4][16], group scales [4], per-head maxima [G]
+  uint32_t *hmax = (uint32_t *)(cs + 64 + kMaxGroups);
+  const int d4 = kd->d4;
   {
-    float *qin = (float *)(smem + sm.scratch);
-    float *qs = qin + G * kHeadDim;
-    uint32_t *bld = (uint32_t *)(qs + G * kHeadDim);
     const uint16_t *qb = q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim;
-    for (int i = tid; i < G * kHeadDim; i += kStreamThreads) {
-      qin[i] = h2f(qb[i]);
-      qs[i] = 0.f;
-    }
+    gather_queries(kd, G, qb, qg, tid, kStreamThreads);
     const uint32_t *bsrc = (const uint32_t *)(consts + hd->off_build) + kd->chunk_base;
     if (tid < nch) bld[tid] = bsrc[tid];
-    __syncthreads();
-    rotate_queries(hd, kd, G, qin, qs, wave, kStreamWaves, lane);
-    __syncthreads();
-    const int ne = 1 << win;
-    float *tab = (float *)smem;
-    for (int idx = tid; idx < nch * ne * G; idx += kStreamThreads) {
-      const int h = idx % G, f = (idx / G) % ne, c = idx / (G * ne);
+    if (tid < 64) cs[tid] = (float)hd->cent[tid >> 4][tid & 15];
+    if (tid < kd->n_groups) cs[64 + tid] = kscale / sqrtf((float)kd->g[tid].d);
+    if (tid < G) hmax[tid] = 0u;
+    // 4-bit centroid pairs
+    float2 *c4 = (float2 *)(smem + sm.c4);
+    for (int e = tid; e < 256; e += kStreamThreads)
+      c4[e] = make_float2((float)hd->cent[3][e & 15], (float)hd->cent[3][e >> 4]);
+  }
+  __syncthreads();
+  rotate_queries(hd, kd, G, qg, qs, wave, kStreamWaves, lane);
+  __syncthreads();
+  constexpr int lg = L - 1;  // log2 G (an entry holds G fp16 values)
+  const int ne = 1 << win, sh = win + lg;
+  {
+    // 4-bit group queries, scaled by kscale / sqrt(d4), zero past d4
+    float *q4 = (float *)(smem + sm.q4);
+    const float s4 = d4 > 0 ? kscale / sqrtf((float)d4) : 0.f;
+    for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
+      const int h = idx >> 7, r = idx & (kHeadDim - 1);
+      q4[idx] = r < d4 ? qs[h * kHeadDim + r] * s4 : 0.f;
+    }
+    // per-head bound of the table entries: scale_g * max|c_w| * sum_r |q_rot[h][pos + r]|
+    for (int idx = tid; idx < nch * G; idx += kStreamThreads) {
+      const int h = idx & (G - 1), c = idx >> lg;
       const uint32_t bw = bld[c];
       const int pos = bw & 255, m = (bw >> 8) & 15, w = (bw >> 12) & 7, gi = (bw >> 15) & 3;
       float s = 0.f;
-      for (int r = 0; r < m; ++r)
-        s = fmaf(qs[h * kHeadDim + pos + r], (float)hd->cent[w - 1][(f >> (w * r)) & ((1 << w) - 1)], s);
-      tab[idx] = kscale / sqrtf((float)kd->g[gi].d) * s;
+      for (int r = 0; r < m; ++r) s += fabsf(qs[h * kHeadDim + pos + r]);
+      const float bound = s * cs[64 + gi] * fabsf(cs[16 * (w - 1) + (1 << w) - 1]);
+      atomicMax(&hmax[h], __float_as_uint(bound));
+    }
+  }
+  __syncthreads();
+  // per-head power-of-two factor bringing every entry below 2^14 (fp16 range)
+  float fac[G], rinv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float m = __uint_as_float(hmax[h]);
+    int e = 0;
+    (void)frexpf(m, &e);
+    e = m > 0.f ? e : 0;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    fac[h] = ldexpf(1.f, 14 - e);
+    rinv[h] = ldexpf(1.f, e - 14);
+  }
+  {
+    // entry [c][f][h] = fac_h * scale_g * sum_r q_rot[h][pos + r] * centroid_w[(f >> w r) & (2^w - 1)]
+    _Float16 *tab = (_Float16 *)smem;
+    for (int idx = tid; idx < (nch << sh); idx += kStreamThreads) {
+      const int h = idx & (G - 1), f = (idx >> lg) & (ne - 1), c = idx >> sh;
+      const uint32_t bw = bld[c];
+      const int pos = bw & 255, m = (bw >> 8) & 15, w = (bw >> 12) & 7, gi = (bw >> 15) & 3;
+      const float *cw = cs + 16 * (w - 1);
+      const float *qh = qs + h * kHeadDim + pos;
+      const int mask = (1 << w) - 1;
+      float acc = 0.f;
+      for (int r = 0; r < m; ++r) acc = fmaf(qh[r], cw[(f >> (w * r)) & mask], acc);
+      float fh = fac[0];
+#pragma unroll
+      for (int k = 1; k < G; ++k) fh = h == k ? fac[k] : fh;
+      tab[idx] = (_Float16)(fh * (cs[64 + gi] * acc));
     }
   }
   // value table: fp16 centroid pairs for the tokens of one code chunk
@@ -414,6 +588,10 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(
     st.av = lane <= kMaxWK + 1 ? (uint32_t)kd->anchor[lane] : 0u;
     st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
     st.wk = hd->wk;
+    st.nb4 = kd->n4blk;
+    st.c4 = (uint32_t)sm.c4;
+    st.q4 = (uint32_t)sm.q4;
+    st.vlut = (uint32_t)sm.vlut;
   }
   __syncthreads();
 
@@ -427,18 +605,17 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(
   const size_t head_base = ((size_t)b * hkv + kvh) * (size_t)tiles_cap;
   const uint32_t *ksrc = st.wk ? kc : (const uint32_t *)kn;
   const int wkl = st.wk ? st.wk : 1;
-  const uint32_t vlut = (uint32_t)sm.vlut;
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
   if (tile < tile_hi) {
     load_tile(ra, ksrc, kn, vc, vn, head_base + tile, st.wk, wkl, lane);
     for (;;) {
       load_tile(rb, ksrc, kn, vc, vn, head_base + min(tile + kStreamWaves, tile_hi - 1), st.wk, wkl, lane);
-      process_tile<G, VB, WK>(ra, tile, st, vlut, pbuf, mrun, lsum, acc0, acc1, lane);
+      process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
       tile += kStreamWaves;
       if (tile >= tile_hi) break;
       load_tile(ra, ksrc, kn, vc, vn, head_base + min(tile + kStreamWaves, tile_hi - 1), st.wk, wkl, lane);
-      process_tile<G, VB, WK>(rb, tile, st, vlut, pbuf, mrun, lsum, acc0, acc1, lane);
+      process_tile<G, VB, WK>(rb, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
       tile += kStreamWaves;
       if (tile >= tile_hi) break;
     }
@@ -478,64 +655,71 @@ __global__ __launch_bounds__(kStreamThreads) void decode_stream_kernel(
   }
 }
 
-// One workgroup per (sequence, KV head): log-sum-exp merge of the splits of
-// its G query heads, normalisation and un-rotation by Pi_V^T, fp16 output.
-__global__ __launch_bounds__(kStreamThreads) void merge_kernel(const uint8_t *__restrict__ consts,
-                                                             const float *__restrict__ part, int n_splits,
-                                                             uint16_t *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) float ws_s[8 * kMaxSplits];
-  __shared__ float ls_s[8 * kMaxSplits];
-  __shared__ __attribute__((aligned(16))) float ys[8 * kHeadDim];
+// One workgroup per (query head, sequence).  Thread s < n_splits owns split
+// s's (m, l); thread t accumulates value coordinate t % 128 over the splits of
+// parity t / 128; the un-rotation out[j] = sum_k Pi_V[k][j] y[k] gives each
+// output two threads (k halves), whose rows are fetched at the start.
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint8_t *__restrict__ consts,
+                                                              const float *__restrict__ part, int n_splits,
+                                                              uint16_t *__restrict__ out) {
+  __shared__ float wsm[kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float ys[2 * kHeadDim];
+  __shared__ float red[2 * (kMergeThreads / 64)];
   const ConstHeader *hd = hdr_of(consts);
-  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int G = hd->group, hq = hd->n_q_heads;
-  const int gs = G * n_splits;
-  const size_t pbase = ((size_t)b * hq + (size_t)kvh * G) * n_splits;
-  for (int idx = tid; idx < gs; idx += kStreamThreads) {
-    const float2 ml = *(const float2 *)(part + (pbase + idx) * kPartStride);
-    ws_s[idx] = ml.x;
-    ls_s[idx] = ml.y;
-  }
-  __syncthreads();
-  if (tid < G) {  // per head: max, then weights exp2(m_s - M) / (L sqrt(128))
-    float mx = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ws_s[tid * n_splits + s]);
-    float l = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float f = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ws_s[tid * n_splits + s] - mx);
-      ws_s[tid * n_splits + s] = f;
-      l = fmaf(f, ls_s[tid * n_splits + s], l);
-    }
-    const float inv = l > 0.f ? 1.0f / (l * sqrtf((float)kHeadDim)) : 0.f;
-    for (int s = 0; s < n_splits; ++s) ws_s[tid * n_splits + s] *= inv;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
-    const int h = idx / kHeadDim, i = idx % kHeadDim;
-    const float *p = part + (pbase + (size_t)h * n_splits) * kPartStride + 4 + i;
-    const float *wv = ws_s + h * n_splits;
-    float a = 0.f;
-#pragma unroll 16
-    for (int s = 0; s < n_splits; ++s) a = fmaf(wv[s], p[(size_t)s * kPartStride], a);
-    ys[idx] = a;
-  }
-  __syncthreads();
-  const float *pvt = (const float *)(consts + hd->off_rot32_v) + (size_t)kvh * kHeadDim * kHeadDim;
-  for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
-    const int h = idx / kHeadDim, j = idx % kHeadDim;
-    const float4 *row = (const float4 *)(pvt + (size_t)j * kHeadDim);  // Pi_V[k][j], k = 0..127
-    const float4 *yv = (const float4 *)(ys + h * kHeadDim);
-    float o = 0.f;
+  const int hqi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hq = hd->n_q_heads, kvh = hqi / hd->group;
+  const float *ph = part + ((size_t)b * hq + hqi) * (size_t)n_splits * kPartStride;
+  const int j = tid >> 1, kh = (tid & 1) * (kHeadDim / 2);
+  const float4 *row =
+      (const float4 *)((const float *)(consts + hd->off_rot32_v) + ((size_t)kvh * kHeadDim + j) * kHeadDim + kh);
+  float4 pr[kHeadDim / 8];
 #pragma unroll
-    for (int k4 = 0; k4 < kHeadDim / 4; ++k4) {
-      const float4 pv = row[k4], y4 = yv[k4];
-      o = fmaf(pv.x, y4.x, o);
-      o = fmaf(pv.y, y4.y, o);
-      o = fmaf(pv.z, y4.z, o);
-      o = fmaf(pv.w, y4.w, o);
-    }
-    out[((size_t)b * hq + (size_t)kvh * G + h) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
+  for (int u = 0; u < kHeadDim / 8; ++u) pr[u] = row[u];
+  float m = -INFINITY, l = 0.f;
+  if (tid < n_splits) {
+    const float2 ml = *(const float2 *)(ph + (size_t)tid * kPartStride);
+    m = ml.x;
+    l = ml.y;
   }
+  const float wm = wave_max(m);
+  if (lane == 0) red[wave] = wm;
+  __syncthreads();
+  float mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+  const float f = (mx == -INFINITY || m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+  const float wl = wave_sum(f * l);
+  if (lane == 0) red[kMergeThreads / 64 + wave] = wl;
+  __syncthreads();
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) lsum += red[kMergeThreads / 64 + w];
+  const float inv = lsum > 0.f ? 1.0f / (lsum * sqrtf((float)kHeadDim)) : 0.f;
+  if (tid < n_splits) wsm[tid] = f * inv;
+  __syncthreads();
+  {
+    const int i = tid & (kHeadDim - 1), par = tid >> 7;
+    const float *p = ph + 4 + i;
+    float a = 0.f;
+#pragma unroll 8
+    for (int s = par; s < n_splits; s += 2) a = fmaf(wsm[s], p[(size_t)s * kPartStride], a);
+    ys[par * kHeadDim + i] = a;
+  }
+  __syncthreads();
+  const float4 *y0 = (const float4 *)(ys + kh), *y1 = (const float4 *)(ys + kHeadDim + kh);
+  float o = 0.f;
+#pragma unroll
+  for (int u = 0; u < kHeadDim / 8; ++u) {
+    const float4 a0 = y0[u], a1 = y1[u];
+    o = fmaf(pr[u].x, a0.x + a1.x, o);
+    o = fmaf(pr[u].y, a0.y + a1.y, o);
+    o = fmaf(pr[u].z, a0.z + a1.z, o);
+    o = fmaf(pr[u].w, a0.w + a1.w, o);
+  }
+  o += __shfl_xor(o, 1);
+  if ((tid & 1) == 0) out[((size_t)b * hq + hqi) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
 }
 
 // ------------------------------------------------------------------ host
@@ -691,7 +875,7 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
     pr.pending.emplace_back(e0, e1);
   }
   if (s != BGTQ_OK) return s;
-  merge_kernel<<<dim3(p.desc.n_kv_heads, batch), kStreamThreads, 0, st>>>((const uint8_t *)dev_consts, part,
+  merge_kernel<<<dim3(p.desc.n_q_heads, batch), kMergeThreads, 0, st>>>((const uint8_t *)dev_consts, part,
                                                                          lay.n_splits, out);
   return launch_status("bgtq_decode_attn (merge)");
 }

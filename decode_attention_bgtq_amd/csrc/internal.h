@@ -16,11 +16,13 @@ constexpr int kBlocks = 64;
 constexpr int kTile = 64;
 constexpr int kMaxGroups = 4;
 constexpr int kMaxWK = 16;          // key words per token at 4 bits per coordinate
-constexpr int kMaxChunks = 128;     // one code per chunk at most
+constexpr int kMaxChunks = 128;     // bound on lookup chunks per head (widths 1..3)
 
-// Decode lookup-table chunk descriptors.  A chunk is a run of m consecutive
-// codes of one key group (m * w <= window bits).  Its table is indexed by the
-// `window` stream bits starting at the chunk's first bit.
+// Decode lookup-table chunk descriptors, for the key groups of width 1..3 (the
+// 4-bit group is summed directly from its centroids).  A chunk is a run of m
+// consecutive codes of one key group (m * w <= window bits).  Its table, one
+// fp16 entry per query head of the group, is indexed by the `window` stream
+// bits starting at the chunk's first bit.
 //
 // lookup (32 bits): [0,5) funnel shift that brings the chunk's window to bit
 //   log2(entry bytes), [5,23) byte offset of the chunk's table in LDS,
@@ -45,6 +47,8 @@ struct KvhDesc {
   int32_t d_nz;
   int32_t n_chunks;
   int32_t chunk_base;          // index of this head's first chunk in the chunk arrays
+  int32_t d4;                  // coordinates of the 4-bit group (group 0 when present), else 0
+  int32_t n4blk;               // 16-code blocks of the 4-bit group, ceil(d4 / 16)
   KGroupDesc g[kMaxGroups];
   int16_t coord[kHeadDim];     // original coordinate of each group-order position
   int16_t pad_[4];
@@ -56,7 +60,7 @@ struct ConstHeader {
   int32_t n_kv_heads, n_q_heads, group, head_dim;
   int32_t k_avg_bits, v_bits, wk, wv;
   int32_t lut_window;        // key lookup window bits (4 or 6)
-  int32_t lut_entry_log2;    // log2 of the table entry size in bytes (4 * group)
+  int32_t lut_entry_log2;    // log2 of the table entry size in bytes (2 * group: fp16 per head)
   int32_t max_chunks;        // largest chunk count over heads
   int32_t pad0;
   int64_t off_kvh;           // KvhDesc[n_kv_heads]

@@ -202,7 +202,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     }
   }
   const int wk = 4 * d.k_avg_bits;
-  const int entry_log2 = 2 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);
+  const int entry_log2 = 1 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);  // fp16 per head
 
   // groups, coordinates, bit offsets, rotations
   p.kvh.assign(hkv, KvhDesc{});
@@ -246,6 +246,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
       int n = 0;
       for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) {
         const KGroupDesc &g = p.kvh[h].g[gi];
+        if (g.w == 4) continue;
         const int m = window / g.w;
         n += (g.d + m - 1) / m;
       }
@@ -263,8 +264,11 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     kd.chunk_base = (int32_t)p.lookup.size();
     std::vector<int> anchors;
     int c = 0;
+    kd.d4 = (kd.n_groups > 0 && kd.g[0].w == 4) ? kd.g[0].d : 0;
+    kd.n4blk = (kd.d4 + 15) / 16;
     for (int gi = 0; gi < kd.n_groups; ++gi) {
       const KGroupDesc &g = kd.g[gi];
+      if (g.w == 4) continue;  // summed directly in the decode, no tables
       const int m_max = window / g.w;
       for (int r0 = 0; r0 < g.d; r0 += m_max, ++c) {
         const int m = std::min(m_max, g.d - r0);
