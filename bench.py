@@ -2,8 +2,9 @@
 
 One step = one serving decode step of the 128K Llama-3.1-8B-shaped layer
 (batch 1, 8 KV / 32 query heads, K2V2): the new token's key and value are
-encoded into the packed cache at position T, then fused decode attention reads
-all T+1 cached tokens (query rotation, cache-streaming kernel, split merge).
+encoded into the packed cache at position T and the query prepared (one launch),
+then the fused decode attention reads all T+1 cached tokens (cache-streaming
+kernel, split merge): bgtq_decode_step.
 Calibration energy, allocation, plan creation and the full 128K prefill
 encode run once before the timed region and are reported as separate fields.
 
@@ -174,7 +175,6 @@ def main() -> int:
     k_new = to_dev(np.stack([synth.keys(cfg1, seq=s, start=t, count=1) for s in range(b)]))
     v_new = to_dev(np.stack([synth.values(cfg1, seq=s, start=t, count=1) for s in range(b)]))
     q = to_dev(np.stack([synth.query(cfg, seq=s, pos=t) for s in range(b)]))
-    seq_lens = torch.full((b,), t + 1, dtype=torch.int32, device=dev)
     packed = cache.packed_bytes(t + 1)
     n_rep = max(1, math.ceil(args.replica_bytes / packed))
     log("packed bytes/step %.1f MB; %d replicas" % (packed / 1e6, n_rep))
@@ -184,11 +184,11 @@ def main() -> int:
     out = torch.empty((b, hq, 128), dtype=torch.int16, device=dev)
     ws = torch.empty(plan.workspace_size(b, t + 1), dtype=torch.uint8, device=dev)
 
-    def step(i):
+    pos = torch.full((b,), t, dtype=torch.int32, device=dev)
+
+    def step(i):  # one fused decode step: append at position t, attend over t + 1 tokens
         kc_, kn_, vc_, vn_ = reps[i % n_rep]
-        plan.encode_k(cache.consts, k_new, cap, t, kc_, kn_)
-        plan.encode_v(cache.consts, v_new, cap, t, vc_, vn_)
-        plan.decode_attn(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, out, ws)
+        plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
 
     for i in range(args.warmup):
         step(i)

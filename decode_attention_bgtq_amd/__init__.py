@@ -24,7 +24,7 @@ EXPORTED = [
     "bgtq_abi_version", "bgtq_last_error", "bgtq_energy", "bgtq_allocate", "bgtq_plan_create",
     "bgtq_plan_destroy", "bgtq_plan_sizes", "bgtq_plan_upload", "bgtq_encode_k", "bgtq_encode_v",
     "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
-    "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read",
+    "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
 ]
 
 
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_rotate_queries": (I32, [P, P, P, I32, P, P]),
         "bgtq_decode_workspace_size": (I32, [P, I32, I64, ctypes.POINTER(SZ)]),
         "bgtq_decode_attn": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float, P, P, SZ, P]),
+        "bgtq_decode_step": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, I64, ctypes.c_float, P, P, SZ, P]),
         "bgtq_codebook": (I32, [I32, P, P, P]),
         "bgtq_plan_rotation": (I32, [P, I32, I32, I32, P, ctypes.POINTER(I32)]),
         "bgtq_plan_bits": (I32, [P, P]),
@@ -227,6 +228,17 @@ class Plan:
                                        max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
 
+    def decode_step(self, consts, q, k_new, v_new, pos, max_seq_len: int, k_codes, k_norms, v_codes, v_norms,
+                    capacity: int, out, workspace, softmax_scale: float | None = None, stream=None) -> None:
+        """Append k_new / v_new at token pos[b] of each sequence, then attend q over pos[b] + 1 tokens."""
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_step(self._h, _ptr(consts), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos),
+                                       q.shape[0], max_seq_len, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                       _ptr(v_norms), capacity, softmax_scale, _ptr(out), _ptr(workspace),
+                                       ws_bytes, _stream(stream)))
+
 
 def profile_enable(on: bool = True) -> None:
     _check(load().bgtq_profile_enable(1 if on else 0))
@@ -259,6 +271,10 @@ class Cache:
     def encode(self, k, v, t0: int, stream=None) -> None:
         self.plan.encode_k(self.consts, k, self.capacity, t0, self.k_codes, self.k_norms, stream)
         self.plan.encode_v(self.consts, v, self.capacity, t0, self.v_codes, self.v_norms, stream)
+
+    def step(self, q, k_new, v_new, pos, max_seq_len: int, out, workspace, softmax_scale=None, stream=None) -> None:
+        self.plan.decode_step(self.consts, q, k_new, v_new, pos, max_seq_len, self.k_codes, self.k_norms,
+                              self.v_codes, self.v_norms, self.capacity, out, workspace, softmax_scale, stream)
 
     def packed_bytes(self, seq_len: int) -> int:
         """Algorithmic packed bytes read for `seq_len` tokens per sequence (codes + present norms)."""

@@ -19,6 +19,7 @@
 //          splits, normalisation, un-rotation by Pi_V^T, fp16 output.
 #include "device.h"
 #include "host.h"
+#include "prep.h"
 
 namespace bgtq {
 
@@ -27,7 +28,6 @@ constexpr int kStreamThreads = 64 * kStreamWaves;
 constexpr int kPartStride = 132;  // m, l, pad, pad, acc[128]
 constexpr int kMaxSplits = 256;
 
-typedef float f4v __attribute__((ext_vector_type(4)));
 
 // LDS access by raw byte offset.  The stream kernel has no static LDS, so its
 // dynamic allocation starts at offset 0 (checked on the host before launch).
@@ -42,65 +42,6 @@ __device__ __forceinline__ T lds_at(uint32_t off) {
   } else {
     static_assert(sizeof(T) == 16, "LDS reads of 4, 8 or 16 bytes");
     return __builtin_bit_cast(T, *(const __attribute__((address_space(3))) u4v *)(size_t)off);
-  }
-}
-
-// q_rot[h][pos_g + i] = sum_k Pi_g[i][k] q[h][coord_g[k]] for the key groups of
-// one KV head.  qg [8][128]: the queries gathered into group order
-// (qg[h][pos_g + k] = q[h][coord_g[k]]), rows h >= G zero.  qs [G][128]: the
-// rotated queries in group order.  16x16x4 fp32 MFMA tiles with the query
-// heads as columns; the (group, 16-row tile) pairs of all groups are spread
-// over the `waves` waves, and each wave issues every operand load of a tile
-// before its first MFMA (clamped addresses, zero-masked values).
-__device__ __forceinline__ void rotate_queries(const ConstHeader *hd, const KvhDesc *kd, int G,
-                                               const float *qg, float *qs, int wave, int waves,
-                                               int lane) {
-  const int n = lane & 15, kq = lane >> 4;
-  int ng = kd->n_groups, tiles[kMaxGroups + 1];
-  tiles[0] = 0;
-  for (int gi = 0; gi < kMaxGroups; ++gi) tiles[gi + 1] = tiles[gi] + (gi < ng ? (kd->g[gi].d + 15) >> 4 : 0);
-  for (int t = wave; t < tiles[kMaxGroups]; t += waves) {
-    int gi = 0;
-    while (t >= tiles[gi + 1]) ++gi;
-    const int d = kd->g[gi].d, pos = kd->g[gi].pos;
-    const float *pi = (const float *)((const uint8_t *)hd + hd->off_rot32_k) + kd->g[gi].rot32;
-    const int ia = 16 * (t - tiles[gi]) + n;
-    const int ic = ia < d ? ia : d - 1;
-    float a[kHeadDim / 4];
-#pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) {
-      const int kk = 4 * s + kq;
-      a[s] = pi[(size_t)ic * d + (kk < d ? kk : d - 1)];
-    }
-    f4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) {
-      const int kk = 4 * s + kq;
-      if (4 * s < d) {  // wave-uniform
-        const float av = (ia < d && kk < d) ? a[s] : 0.f;
-        const float bq = qg[(n & 7) * kHeadDim + pos + (kk < d ? kk : d - 1)];
-        const float bv = kk < d ? bq : 0.f;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ia - n + 4 * kq + r;
-      if (i < d && n < G) qs[n * kHeadDim + pos + i] = acc[r];
-    }
-  }
-}
-
-// qg[h][p] = q[h][coord[p]] for p < d_nz, else 0, for h < 8 (rows h >= G zero).
-__device__ __forceinline__ void gather_queries(const KvhDesc *kd, int G, const uint16_t *qb, float *qg, int tid,
-                                               int threads) {
-  const int dnz = kd->d_nz;
-  for (int i = tid; i < 8 * kHeadDim; i += threads) {
-    const int h = i >> 7, p = i & (kHeadDim - 1);
-    const int pc = p < dnz ? p : 0;
-    const int hc = h < G ? h : 0;
-    const float v = h2f(qb[hc * kHeadDim + kd->coord[pc]]);
-    qg[i] = (h < G && p < dnz) ? v : 0.f;
   }
 }
 
@@ -190,16 +131,14 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 struct StreamSmem {
-  int c4, q4, vlut, scratch, total;
+  int c4, q4, vlut, total;
 };
 
-// LDS layout (bytes):
+// LDS layout of the stream kernel (bytes):
 //   [key tables of the width-1..3 chunks, fp16 entry per query head | wave merge area]
 //   [4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32]
 //   [4-bit group queries: G x 128 fp32, scaled, zero past d4]
 //   [value table]
-//   [prologue scratch: gathered queries 8 x 128, rotated queries G x 128, build
-//    words, centroids 4 x 16, group scales 4, per-head table maxima G]
 template <int G, int VB>
 __host__ __device__ constexpr StreamSmem stream_layout(int table_bytes) {
   StreamSmem s{};
@@ -209,9 +148,15 @@ __host__ __device__ constexpr StreamSmem stream_layout(int table_bytes) {
   s.c4 = r0;
   s.q4 = s.c4 + 256 * 8;
   s.vlut = s.q4 + G * kHeadDim * 4;
-  s.scratch = s.vlut + VLut<VB>::entries * VLut<VB>::bytes;
-  s.total = s.scratch + (8 + G) * kHeadDim * 4 + kMaxChunks * 4 + (64 + kMaxGroups + 8) * 4;
+  s.total = s.vlut + VLut<VB>::entries * VLut<VB>::bytes;
   return s;
+}
+
+// Per (sequence, KV head) output of the prep kernel, read by every split of
+// the stream kernel: [key tables: table_bytes][4-bit queries: G x 128 fp32]
+// [1 / table factor: G fp32], 256-byte aligned.
+__host__ __device__ constexpr int64_t prep_stride(int G, int table_bytes) {
+  return ((int64_t)table_bytes + G * kHeadDim * 4 + G * 4 + 255) & ~(int64_t)255;
 }
 
 template <int VB, int WK>
@@ -462,132 +407,73 @@ struct StreamOcc {
   static constexpr int v = G <= 4 ? (WK <= 8 ? 4 : 3) : 2;
 };
 
+// ------------------------------------------------------------------ prep
+
+// Grid (KV head, sequence, slice), see prep_role.
+template <int G>
+__global__ __launch_bounds__(kStreamThreads) void prep_kernel(const PrepArgs a) {
+  prep_role<G>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// ------------------------------------------------------------------ stream kernel
+
+// Launch arguments of the stream kernel (by value; the host fills in what it
+// knows so that the kernel starts without dependent loads).
+struct StreamArgs {
+  const uint8_t *consts;
+  const uint8_t *prep;  // prep kernel output
+  const uint32_t *kc;
+  const uint16_t *kn;
+  const uint32_t *vc;
+  const uint16_t *vn;
+  const int32_t *seq_lens;
+  float *part;
+  int64_t tiles_cap, max_seq_len, off_kvh, off_lookup, off_c4, off_vlut, prep_stride;
+  int hkv, hq, wk, win, tiles_per_split, n_splits, table_bytes;
+  int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
+};
+
+// 16-byte copy from global memory into LDS by the whole workgroup.
+__device__ __forceinline__ void copy_to_lds(uint8_t *dst, const uint8_t *__restrict__ src, int bytes, int tid) {
+  const uint4 *s4 = (const uint4 *)src;
+  uint4 *d4 = (uint4 *)dst;
+  for (int i = tid; i < (bytes >> 4); i += kStreamThreads) d4[i] = s4[i];
+}
+
 template <int G, int VB, int WK>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
-void decode_stream_kernel(
-    const uint8_t *__restrict__ consts, const uint16_t *__restrict__ q, const uint32_t *__restrict__ kc,
-    const uint16_t *__restrict__ kn, const uint32_t *__restrict__ vc, const uint16_t *__restrict__ vn,
-    int64_t tiles_cap, const int32_t *__restrict__ seq_lens, int64_t max_seq_len, int tiles_per_split,
-    float kscale, float *__restrict__ part, int n_splits) {
+void decode_stream_kernel(const StreamArgs a) {
   constexpr int L = GLog<G>::v;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint8_t *consts = a.consts;
   const ConstHeader *hd = hdr_of(consts);
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hkv = hd->n_kv_heads, hq = hd->n_q_heads;
-  const KvhDesc *kd = (const KvhDesc *)(consts + hd->off_kvh) + kvh;
-  const int win = hd->lut_window;
-  const int nch = kd->n_chunks;
-  const StreamSmem sm = stream_layout<G, VB>(hd->max_chunks << (win + L));
+  const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
+  const int win = a.win;
+  const StreamSmem sm = stream_layout<G, VB>(a.table_bytes);
 
-  // ---- prologue: rotated queries, 4-bit group queries and centroid pairs,
-  // key lookup tables of this head
-  float *qg = (float *)(smem + sm.scratch);
-  float *qs = qg + 8 * kHeadDim;
-  uint32_t *bld = (uint32_t *)(qs + G * kHeadDim);
-  float *cs = (float *)(bld + kMaxChunks);  // centroids [4][16], group scales [4], per-head maxima [G]
-  uint32_t *hmax = (uint32_t *)(cs + 64 + kMaxGroups);
-  const int d4 = kd->d4;
-  {
-    const uint16_t *qb = q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim;
-    gather_queries(kd, G, qb, qg, tid, kStreamThreads);
-    const uint32_t *bsrc = (const uint32_t *)(consts + hd->off_build) + kd->chunk_base;
-    if (tid < nch) bld[tid] = bsrc[tid];
-    if (tid < 64) cs[tid] = (float)hd->cent[tid >> 4][tid & 15];
-    if (tid < kd->n_groups) cs[64 + tid] = kscale / sqrtf((float)kd->g[tid].d);
-    if (tid < G) hmax[tid] = 0u;
-    // 4-bit centroid pairs
-    float2 *c4 = (float2 *)(smem + sm.c4);
-    for (int e = tid; e < 256; e += kStreamThreads)
-      c4[e] = make_float2((float)hd->cent[3][e & 15], (float)hd->cent[3][e >> 4]);
-  }
-  __syncthreads();
-  rotate_queries(hd, kd, G, qg, qs, wave, kStreamWaves, lane);
-  __syncthreads();
-  constexpr int lg = L - 1;  // log2 G (an entry holds G fp16 values)
-  const int ne = 1 << win, sh = win + lg;
-  {
-    // 4-bit group queries, scaled by kscale / sqrt(d4), zero past d4
-    float *q4 = (float *)(smem + sm.q4);
-    const float s4 = d4 > 0 ? kscale / sqrtf((float)d4) : 0.f;
-    for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
-      const int h = idx >> 7, r = idx & (kHeadDim - 1);
-      q4[idx] = r < d4 ? qs[h * kHeadDim + r] * s4 : 0.f;
-    }
-    // per-head bound of the table entries: scale_g * max|c_w| * sum_r |q_rot[h][pos + r]|
-    for (int idx = tid; idx < nch * G; idx += kStreamThreads) {
-      const int h = idx & (G - 1), c = idx >> lg;
-      const uint32_t bw = bld[c];
-      const int pos = bw & 255, m = (bw >> 8) & 15, w = (bw >> 12) & 7, gi = (bw >> 15) & 3;
-      float s = 0.f;
-      for (int r = 0; r < m; ++r) s += fabsf(qs[h * kHeadDim + pos + r]);
-      const float bound = s * cs[64 + gi] * fabsf(cs[16 * (w - 1) + (1 << w) - 1]);
-      atomicMax(&hmax[h], __float_as_uint(bound));
-    }
-  }
-  __syncthreads();
-  // per-head power-of-two factor bringing every entry below 2^14 (fp16 range)
-  float fac[G], rinv[G];
+  // ---- prologue: the shared query state of this (sequence, KV head) and the
+  // plan's centroid tables into LDS
+  const uint8_t *pr = a.prep + ((size_t)b * a.hkv + kvh) * (size_t)a.prep_stride;
+  copy_to_lds(smem, pr, a.table_bytes, tid);
+  copy_to_lds(smem + sm.q4, pr + a.table_bytes, G * kHeadDim * 4, tid);
+  copy_to_lds(smem + sm.c4, consts + a.off_c4, 256 * 8, tid);
+  copy_to_lds(smem + sm.vlut, consts + a.off_vlut, VLut<VB>::entries * VLut<VB>::bytes, tid);
+  float rinv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float m = __uint_as_float(hmax[h]);
-    int e = 0;
-    (void)frexpf(m, &e);
-    e = m > 0.f ? e : 0;
-    e = e < -100 ? -100 : (e > 100 ? 100 : e);
-    fac[h] = ldexpf(1.f, 14 - e);
-    rinv[h] = ldexpf(1.f, e - 14);
-  }
-  {
-    // entry [c][f][h] = fac_h * scale_g * sum_r q_rot[h][pos + r] * centroid_w[(f >> w r) & (2^w - 1)]
-    _Float16 *tab = (_Float16 *)smem;
-    for (int idx = tid; idx < (nch << sh); idx += kStreamThreads) {
-      const int h = idx & (G - 1), f = (idx >> lg) & (ne - 1), c = idx >> sh;
-      const uint32_t bw = bld[c];
-      const int pos = bw & 255, m = (bw >> 8) & 15, w = (bw >> 12) & 7, gi = (bw >> 15) & 3;
-      const float *cw = cs + 16 * (w - 1);
-      const float *qh = qs + h * kHeadDim + pos;
-      const int mask = (1 << w) - 1;
-      float acc = 0.f;
-      for (int r = 0; r < m; ++r) acc = fmaf(qh[r], cw[(f >> (w * r)) & mask], acc);
-      float fh = fac[0];
-#pragma unroll
-      for (int k = 1; k < G; ++k) fh = h == k ? fac[k] : fh;
-      tab[idx] = (_Float16)(fh * (cs[64 + gi] * acc));
-    }
-  }
-  // value table: fp16 centroid pairs for the tokens of one code chunk
-  {
-    uint16_t c16[1 << VB];
-#pragma unroll
-    for (int k = 0; k < (1 << VB); ++k) c16[k] = f64_to_f16(hd->cent[VB - 1][k]);
-    uint32_t *vl = (uint32_t *)(smem + sm.vlut);
-    for (int y = tid; y < VLut<VB>::entries; y += kStreamThreads) {
-      if constexpr (VB == 1) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          vl[4 * y + u] = (uint32_t)c16[(y >> (2 * u)) & 1] | ((uint32_t)c16[(y >> (2 * u + 1)) & 1] << 16);
-      } else if constexpr (VB == 2) {
-        vl[2 * y + 0] = (uint32_t)c16[y & 3] | ((uint32_t)c16[(y >> 2) & 3] << 16);
-        vl[2 * y + 1] = (uint32_t)c16[(y >> 4) & 3] | ((uint32_t)c16[(y >> 6) & 3] << 16);
-      } else if constexpr (VB == 3) {
-        vl[y] = (uint32_t)c16[y & 7] | ((uint32_t)c16[(y >> 3) & 7] << 16);
-      } else {
-        vl[y] = (uint32_t)c16[y & 15] | ((uint32_t)c16[(y >> 4) & 15] << 16);
-      }
-    }
-  }
+  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + a.table_bytes + G * kHeadDim * 4))[h];
   StreamState st;
   {
-    int64_t s = seq_lens[b];
-    st.seq = s < 0 ? 0 : (s > max_seq_len ? max_seq_len : s);
-    const uint32_t *lk = (const uint32_t *)(consts + hd->off_lookup) + kd->chunk_base;
-    st.dv0 = lane < nch ? lk[lane] : 0u;
-    st.dv1 = lane + 64 < nch ? lk[lane + 64] : 0u;
+    int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
+    st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
+    const uint32_t *lk = (const uint32_t *)(consts + a.off_lookup) + kvh * kMaxChunks;
+    st.dv0 = lk[lane];  // zero past the head's chunks
+    st.dv1 = lk[lane + 64];
     st.av = lane <= kMaxWK + 1 ? (uint32_t)kd->anchor[lane] : 0u;
     st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
-    st.wk = hd->wk;
+    st.wk = a.wk;
     st.nb4 = kd->n4blk;
     st.c4 = (uint32_t)sm.c4;
     st.q4 = (uint32_t)sm.q4;
@@ -595,26 +481,26 @@ void decode_stream_kernel(
   }
   __syncthreads();
 
+  // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
-  const int tile_lo = split * tiles_per_split;
-  const int tile_hi = min(tile_lo + tiles_per_split, ntile);
+  const int tile_lo = split * a.tiles_per_split;
+  const int tile_hi = min(tile_lo + a.tiles_per_split, ntile);
+  const size_t head_base = ((size_t)b * a.hkv + kvh) * (size_t)a.tiles_cap;
+  const uint32_t *ksrc = a.wk ? a.kc : (const uint32_t *)a.kn;
+  const int wkl = a.wk ? a.wk : 1;
   float mrun[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f, acc0[h] = 0.f, acc1[h] = 0.f;
-
-  const size_t head_base = ((size_t)b * hkv + kvh) * (size_t)tiles_cap;
-  const uint32_t *ksrc = st.wk ? kc : (const uint32_t *)kn;
-  const int wkl = st.wk ? st.wk : 1;
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
   if (tile < tile_hi) {
-    load_tile(ra, ksrc, kn, vc, vn, head_base + tile, st.wk, wkl, lane);
+    load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + tile, a.wk, wkl, lane);
     for (;;) {
-      load_tile(rb, ksrc, kn, vc, vn, head_base + min(tile + kStreamWaves, tile_hi - 1), st.wk, wkl, lane);
+      load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
       process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
       tile += kStreamWaves;
       if (tile >= tile_hi) break;
-      load_tile(ra, ksrc, kn, vc, vn, head_base + min(tile + kStreamWaves, tile_hi - 1), st.wk, wkl, lane);
+      load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
       process_tile<G, VB, WK>(rb, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
       tile += kStreamWaves;
       if (tile >= tile_hi) break;
@@ -649,7 +535,7 @@ void decode_stream_kernel(
         l = fmaf(f, rr[1], l);
       }
     }
-    float *o = part + (((size_t)b * hq + (size_t)kvh * G + h) * n_splits + split) * kPartStride;
+    float *o = a.part + (((size_t)b * a.hq + (size_t)kvh * G + h) * a.n_splits + split) * kPartStride;
     o[4 + i] = s;
     if (i == 0) o[0] = mx, o[1] = l;
   }
@@ -658,22 +544,22 @@ void decode_stream_kernel(
 // One workgroup per (query head, sequence).  Thread s < n_splits owns split
 // s's (m, l); thread t accumulates value coordinate t % 128 over the splits of
 // parity t / 128; the un-rotation out[j] = sum_k Pi_V[k][j] y[k] gives each
-// output two threads (k halves), whose rows are fetched at the start.
+// output two threads (k halves).  Every global load (rotation rows, split
+// statistics, split accumulators) is issued before the first reduction.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeRegs = 16;  // split accumulators per thread held in registers (n_splits <= 32)
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint8_t *__restrict__ consts,
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ pvt_all,
                                                               const float *__restrict__ part, int n_splits,
-                                                              uint16_t *__restrict__ out) {
+                                                              int group, int hq, uint16_t *__restrict__ out) {
   __shared__ float wsm[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float ys[2 * kHeadDim];
   __shared__ float red[2 * (kMergeThreads / 64)];
-  const ConstHeader *hd = hdr_of(consts);
   const int hqi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hq = hd->n_q_heads, kvh = hqi / hd->group;
+  const int kvh = hqi / group;
   const float *ph = part + ((size_t)b * hq + hqi) * (size_t)n_splits * kPartStride;
   const int j = tid >> 1, kh = (tid & 1) * (kHeadDim / 2);
-  const float4 *row =
-      (const float4 *)((const float *)(consts + hd->off_rot32_v) + ((size_t)kvh * kHeadDim + j) * kHeadDim + kh);
+  const float4 *row = (const float4 *)(pvt_all + ((size_t)kvh * kHeadDim + j) * kHeadDim + kh);
   float4 pr[kHeadDim / 8];
 #pragma unroll
   for (int u = 0; u < kHeadDim / 8; ++u) pr[u] = row[u];
@@ -682,6 +568,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint8_t *__r
     const float2 ml = *(const float2 *)(ph + (size_t)tid * kPartStride);
     m = ml.x;
     l = ml.y;
+  }
+  const int i = tid & (kHeadDim - 1), par = tid >> 7;
+  const float *pv = ph + 4 + i;
+  float av[kMergeRegs];
+#pragma unroll
+  for (int u = 0; u < kMergeRegs; ++u) {
+    const int sp = par + 2 * u;
+    av[u] = pv[(size_t)(sp < n_splits ? sp : 0) * kPartStride];
   }
   const float wm = wave_max(m);
   if (lane == 0) red[wave] = wm;
@@ -700,12 +594,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint8_t *__r
   if (tid < n_splits) wsm[tid] = f * inv;
   __syncthreads();
   {
-    const int i = tid & (kHeadDim - 1), par = tid >> 7;
-    const float *p = ph + 4 + i;
-    float a = 0.f;
-#pragma unroll 8
-    for (int s = par; s < n_splits; s += 2) a = fmaf(wsm[s], p[(size_t)s * kPartStride], a);
-    ys[par * kHeadDim + i] = a;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMergeRegs; ++u) {
+      const int sp = par + 2 * u;
+      if (sp < n_splits) acc = fmaf(wsm[sp], av[u], acc);
+    }
+    for (int sp = par + 2 * kMergeRegs; sp < n_splits; sp += 2) acc = fmaf(wsm[sp], pv[(size_t)sp * kPartStride], acc);
+    ys[par * kHeadDim + i] = acc;
   }
   __syncthreads();
   const float4 *y0 = (const float4 *)(ys + kh), *y1 = (const float4 *)(ys + kHeadDim + kh);
@@ -724,8 +620,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint8_t *__r
 
 // ------------------------------------------------------------------ host
 
-typedef void (*stream_fn)(const uint8_t *, const uint16_t *, const uint32_t *, const uint16_t *, const uint32_t *,
-                          const uint16_t *, int64_t, const int32_t *, int64_t, int, float, float *, int);
+typedef void (*stream_fn)(const StreamArgs);
+typedef void (*prep_fn)(const PrepArgs);
+constexpr int kPrepChunks = 8;  // lookup chunks built per prep workgroup
+
+prep_fn pick_prep(int g) {
+  switch (g) {
+    case 1: return prep_kernel<1>;
+    case 2: return prep_kernel<2>;
+    case 4: return prep_kernel<4>;
+    default: return prep_kernel<8>;
+  }
+}
 
 template <int G, int VB>
 stream_fn pick_wk(int wk) {
@@ -766,7 +672,9 @@ int stream_smem_bytes(int g, int vb, int table_bytes) {
 
 struct DecodeLayout {
   int n_splits, tiles_per_split;
-  size_t total;  // workspace bytes (split partials)
+  size_t prep_off;     // workspace offset of the prep output
+  int64_t prep_stride;  // bytes per (sequence, KV head)
+  size_t total;         // workspace bytes: split partials, then prep output
 };
 
 DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
@@ -779,7 +687,9 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   const int tps = (tiles + s - 1) / s;
   d.n_splits = (tiles + tps - 1) / tps;
   d.tiles_per_split = tps;
-  d.total = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
+  d.prep_off = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
+  d.prep_stride = prep_stride(p.hdr.group, p.hdr.max_chunks << (p.hdr.lut_window + p.hdr.lut_entry_log2));
+  d.total = d.prep_off + (size_t)batch * hkv * (size_t)d.prep_stride;
   return d;
 }
 
@@ -794,6 +704,118 @@ bool stream_static_lds_ok(stream_fn fn) {
   if (hipFuncGetAttributes(&attr, (const void *)fn) != hipSuccess || attr.sharedSizeBytes != 0) return false;
   checked.push_back(fn);
   return true;
+}
+
+float kscale_of(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }  // logits in log2 units
+
+int table_bytes_of(const Plan &p) { return p.hdr.max_chunks << (p.hdr.lut_window + p.hdr.lut_entry_log2); }
+
+int prep_slices(const Plan &p) { return std::max(1, (p.hdr.max_chunks + kPrepChunks - 1) / kPrepChunks); }
+
+PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
+                   int64_t max_seq_len, float softmax_scale) {
+  const DecodeLayout lay = decode_layout(p, batch, max_seq_len);
+  PrepArgs pa;
+  pa.consts = (const uint8_t *)dev_consts;
+  pa.q = q;
+  pa.out = (uint8_t *)workspace + lay.prep_off;
+  pa.off_kvh = p.hdr.off_kvh;
+  pa.off_build = p.hdr.off_build;
+  pa.stride = lay.prep_stride;
+  pa.hkv = p.desc.n_kv_heads;
+  pa.hq = p.desc.n_q_heads;
+  pa.win = p.hdr.lut_window;
+  pa.table_bytes = table_bytes_of(p);
+  pa.chunks_per_wg = kPrepChunks;
+  pa.kscale = kscale_of(softmax_scale);
+  return pa;
+}
+
+bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
+                         const void *workspace, size_t ws_bytes, const char *nm) {
+  if (batch < 1 || batch > 65535) return fail(BGTQ_EINVAL, std::string(nm) + ": batch must be 1..65535");
+  if (max_seq_len < 1 || max_seq_len > capacity)
+    return fail(BGTQ_ECAPACITY, std::string(nm) + ": max_seq_len must be in [1, capacity]");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": softmax_scale must be positive and finite");
+  if ((uintptr_t)workspace & 255) return fail(BGTQ_EINVAL, std::string(nm) + ": workspace must be 256-byte aligned");
+  if (ws_bytes < decode_layout(p, batch, max_seq_len).total)
+    return fail(BGTQ_EWORKSPACE, std::string(nm) + ": workspace too small");
+  return BGTQ_OK;
+}
+
+bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
+  const DecodeLayout lay = decode_layout(p, c.batch, c.max_seq_len);
+  const int G = p.hdr.group, vb = p.hdr.v_bits;
+  const int table_bytes = table_bytes_of(p);
+  const int smem = stream_smem_bytes(G, vb, table_bytes);
+  stream_fn fn = pick_stream(G, vb, p.hdr.wk);
+  if (!stream_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: stream kernel has static LDS");
+  if (smem > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: lookup tables exceed the LDS limit");
+  }
+  hipStream_t st = (hipStream_t)c.stream;
+  float *part = (float *)c.workspace;
+  if (with_prep) {
+    const PrepArgs pa = prep_args(p, c.dev_consts, c.q, c.workspace, c.batch, c.max_seq_len, c.softmax_scale);
+    pick_prep(G)<<<dim3(p.desc.n_kv_heads, c.batch, prep_slices(p)), kPrepThreads, 0, st>>>(pa);
+    const bgtq_status ps = launch_status("decode (prep)");
+    if (ps != BGTQ_OK) return ps;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    Prof &pr = prof();
+    std::lock_guard<std::mutex> lk(pr.mu);
+    if (pr.on) {
+      if (!pr.pool.empty()) {
+        e0 = pr.pool.back().first;
+        e1 = pr.pool.back().second;
+        pr.pool.pop_back();
+      } else if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        return fail(BGTQ_EDEVICE, "decode: event creation failed");
+      }
+    }
+  }
+  StreamArgs sa;
+  sa.consts = (const uint8_t *)c.dev_consts;
+  sa.prep = (const uint8_t *)c.workspace + lay.prep_off;
+  sa.kc = c.k_codes;
+  sa.kn = c.k_norms;
+  sa.vc = c.v_codes;
+  sa.vn = c.v_norms;
+  sa.seq_lens = c.seq_lens;
+  sa.part = part;
+  sa.tiles_cap = (c.capacity + kTile - 1) / kTile;
+  sa.max_seq_len = c.max_seq_len;
+  sa.off_kvh = p.hdr.off_kvh;
+  sa.off_lookup = p.hdr.off_lookup;
+  sa.off_c4 = p.hdr.off_c4;
+  sa.off_vlut = p.hdr.off_vlut;
+  sa.prep_stride = lay.prep_stride;
+  sa.hkv = p.desc.n_kv_heads;
+  sa.hq = p.desc.n_q_heads;
+  sa.wk = p.hdr.wk;
+  sa.win = p.hdr.lut_window;
+  sa.tiles_per_split = lay.tiles_per_split;
+  sa.n_splits = lay.n_splits;
+  sa.table_bytes = table_bytes;
+  sa.seq_add = c.seq_add;
+  const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
+  if (e0) (void)hipEventRecord(e0, st);
+  fn<<<grid, kStreamThreads, smem, st>>>(sa);
+  bgtq_status s = launch_status("decode (stream)");
+  if (e1) {
+    (void)hipEventRecord(e1, st);
+    Prof &pr = prof();
+    std::lock_guard<std::mutex> lk(pr.mu);
+    pr.pending.emplace_back(e0, e1);
+  }
+  if (s != BGTQ_OK) return s;
+  merge_kernel<<<dim3(p.desc.n_q_heads, c.batch), kMergeThreads, 0, st>>>(
+      (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v), part, lay.n_splits, G, p.desc.n_q_heads,
+      c.out);
+  return launch_status("decode (merge)");
 }
 
 }  // namespace bgtq
@@ -826,58 +848,12 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
   if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace ||
       (!k_codes && plan->p.hdr.wk > 0))
     return fail(BGTQ_EINVAL, "bgtq_decode_attn: null pointer");
-  if (batch < 1 || batch > 65535) return fail(BGTQ_EINVAL, "bgtq_decode_attn: batch must be 1..65535");
-  if (max_seq_len < 1 || max_seq_len > capacity)
-    return fail(BGTQ_ECAPACITY, "bgtq_decode_attn: max_seq_len must be in [1, capacity]");
-  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-    return fail(BGTQ_EINVAL, "bgtq_decode_attn: softmax_scale must be positive and finite");
-  if ((uintptr_t)workspace & 255) return fail(BGTQ_EINVAL, "bgtq_decode_attn: workspace must be 256-byte aligned");
-  const Plan &p = plan->p;
-  const DecodeLayout lay = decode_layout(p, batch, max_seq_len);
-  if (ws_bytes < lay.total) return fail(BGTQ_EWORKSPACE, "bgtq_decode_attn: workspace too small");
-  const int G = p.hdr.group, vb = p.hdr.v_bits;
-  const int table_bytes = p.hdr.max_chunks << (p.hdr.lut_window + p.hdr.lut_entry_log2);
-  const int smem = stream_smem_bytes(G, vb, table_bytes);
-  stream_fn fn = pick_stream(G, vb, p.hdr.wk);
-  if (!stream_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "bgtq_decode_attn: stream kernel has static LDS");
-  if (smem > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return fail(BGTQ_EDEVICE, "bgtq_decode_attn: lookup tables exceed the LDS limit");
-  }
-  hipStream_t st = (hipStream_t)stream;
-  float *part = (float *)workspace;
-  const int64_t tiles_cap = (capacity + kTile - 1) / kTile;
-  const float kscale = softmax_scale * 1.4426950408889634f;  // logits in log2 units
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  {
-    Prof &pr = prof();
-    std::lock_guard<std::mutex> lk(pr.mu);
-    if (pr.on) {
-      if (!pr.pool.empty()) {
-        e0 = pr.pool.back().first;
-        e1 = pr.pool.back().second;
-        pr.pool.pop_back();
-      } else if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-        return fail(BGTQ_EDEVICE, "bgtq_decode_attn: event creation failed");
-      }
-    }
-  }
-  if (e0) (void)hipEventRecord(e0, st);
-  const dim3 grid(lay.n_splits, p.desc.n_kv_heads, batch);
-  fn<<<grid, kStreamThreads, smem, st>>>((const uint8_t *)dev_consts, q, k_codes, k_norms, v_codes, v_norms,
-                                         tiles_cap, seq_lens, max_seq_len, lay.tiles_per_split, kscale, part,
-                                         lay.n_splits);
-  bgtq_status s = launch_status("bgtq_decode_attn (stream)");
-  if (e1) {
-    (void)hipEventRecord(e1, st);
-    Prof &pr = prof();
-    std::lock_guard<std::mutex> lk(pr.mu);
-    pr.pending.emplace_back(e0, e1);
-  }
-  if (s != BGTQ_OK) return s;
-  merge_kernel<<<dim3(p.desc.n_q_heads, batch), kMergeThreads, 0, st>>>((const uint8_t *)dev_consts, part,
-                                                                         lay.n_splits, out);
-  return launch_status("bgtq_decode_attn (merge)");
+  const bgtq_status v = decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes,
+                                     "bgtq_decode_attn");
+  if (v != BGTQ_OK) return v;
+  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
+               softmax_scale, out, workspace, stream};
+  return decode_launch(plan->p, c, true);
 }
 
 }  // extern "C"

@@ -24,4 +24,34 @@ struct Prof {
 };
 Prof &prof();
 
+// Decode launches shared by bgtq_decode_attn and bgtq_decode_step.
+struct DecodeCall {
+  const void *dev_consts;
+  const uint16_t *q;
+  const uint32_t *k_codes;
+  const uint16_t *k_norms;
+  const uint32_t *v_codes;
+  const uint16_t *v_norms;
+  int64_t capacity;
+  const int32_t *seq_lens;
+  int seq_add;
+  int32_t batch;
+  int64_t max_seq_len;
+  float softmax_scale;
+  uint16_t *out;
+  void *workspace;
+  bgtq_stream stream;
+};
+struct PrepArgs;
+bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
+                         const void *workspace, size_t ws_bytes, const char *nm);
+bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep);  // [prep], stream, merge
+PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
+                   int64_t max_seq_len, float softmax_scale);
+int prep_slices(const Plan &p);
+
+struct AppendArgs;
+AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,
+                       int64_t tiles_cap, bool is_v);
+
 }  // namespace bgtq

@@ -46,7 +46,7 @@ struct KvhDesc {
   int32_t n_groups;
   int32_t d_nz;
   int32_t n_chunks;
-  int32_t chunk_base;          // index of this head's first chunk in the chunk arrays
+  int32_t chunk_base;          // index of this head's first chunk in the chunk arrays (head * kMaxChunks)
   int32_t d4;                  // coordinates of the 4-bit group (group 0 when present), else 0
   int32_t n4blk;               // 16-code blocks of the 4-bit group, ceil(d4 / 16)
   KGroupDesc g[kMaxGroups];
@@ -70,6 +70,9 @@ struct ConstHeader {
   int64_t off_rot32_k;       // float area (Pi per K group)
   int64_t off_rot64_v;       // double [n_kv_heads][128][128], Pi_V^T ([k][i])
   int64_t off_rot32_v;       // float [n_kv_heads][128][128], Pi_V^T ([j][k] = Pi_V[k][j])
+  int64_t off_c4;            // float2 [256]: (c4[b & 15], c4[b >> 4]), 4-bit centroid pairs of a code byte
+  int64_t off_vlut;          // value-width table: fp16 centroid pairs of the tokens of one code chunk
+  int64_t vlut_bytes;
   int64_t total_bytes;
   double thr[4][16];         // interior thresholds of the b-bit quantiser, row b-1
   double cent[4][16];        // centroids, row b-1

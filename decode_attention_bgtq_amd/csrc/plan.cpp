@@ -149,6 +149,45 @@ std::vector<double> haar(uint64_t seed, int layer, int kvh, int tensor, int widt
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// float64 -> fp16 bits, round to nearest even (finite inputs of any size).
+uint16_t f16_bits(double x) {
+  const uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+  const double a = std::fabs(x);
+  if (std::isnan(x)) return 0x7E00;
+  if (a >= 65520.0) return sign | 0x7C00;
+  if (a < std::ldexp(1.0, -14)) return sign | (uint16_t)std::nearbyint(std::ldexp(a, 24));  // 1024 = min normal
+  int e = 0;
+  const double f = std::frexp(a, &e);  // a = f 2^e, f in [0.5, 1)
+  double m = std::nearbyint((2.0 * f - 1.0) * 1024.0);
+  int ex = e - 1;
+  if (m >= 1024.0) m = 0.0, ++ex;
+  if (ex > 15) return sign | 0x7C00;
+  return sign | (uint16_t)((ex + 15) << 10) | (uint16_t)m;
+}
+
+// Value lookup table of width vb: for a code byte (or 6-bit pair for vb = 3)
+// of one coordinate, the fp16 centroids of its tokens packed in pairs.
+std::vector<uint32_t> value_table(int vb) {
+  uint16_t c16[16];
+  const Codebook &cb = codebook(vb);
+  for (int k = 0; k < (1 << vb); ++k) c16[k] = f16_bits(cb.c[k]);
+  std::vector<uint32_t> t;
+  if (vb == 1) {
+    for (int y = 0; y < 256; ++y)
+      for (int u = 0; u < 4; ++u) t.push_back(c16[(y >> (2 * u)) & 1] | ((uint32_t)c16[(y >> (2 * u + 1)) & 1] << 16));
+  } else if (vb == 2) {
+    for (int y = 0; y < 256; ++y) {
+      t.push_back(c16[y & 3] | ((uint32_t)c16[(y >> 2) & 3] << 16));
+      t.push_back(c16[(y >> 4) & 3] | ((uint32_t)c16[(y >> 6) & 3] << 16));
+    }
+  } else if (vb == 3) {
+    for (int y = 0; y < 64; ++y) t.push_back(c16[y & 7] | ((uint32_t)c16[(y >> 3) & 7] << 16));
+  } else {
+    for (int y = 0; y < 256; ++y) t.push_back(c16[y & 15] | ((uint32_t)c16[(y >> 4) & 15] << 16));
+  }
+  return t;
+}
+
 }  // namespace
 
 const Codebook &codebook(int bits) {
@@ -261,7 +300,9 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   int max_chunks = 0;
   for (int h = 0; h < hkv; ++h) {
     KvhDesc &kd = p.kvh[h];
-    kd.chunk_base = (int32_t)p.lookup.size();
+    kd.chunk_base = h * kMaxChunks;  // fixed stride: the kernels address a head's chunks from its index
+    p.lookup.resize((size_t)h * kMaxChunks, 0u);
+    p.build.resize((size_t)h * kMaxChunks, 0u);
     std::vector<int> anchors;
     int c = 0;
     kd.d4 = (kd.n_groups > 0 && kd.g[0].w == 4) ? kd.g[0].d : 0;
@@ -284,8 +325,14 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
         anchors.push_back(anchor);
       }
     }
+    if (c > kMaxChunks) {
+      err = "internal: too many lookup chunks";
+      return BGTQ_EINVAL;
+    }
     kd.n_chunks = c;
     max_chunks = std::max(max_chunks, c);
+    p.lookup.resize((size_t)(h + 1) * kMaxChunks, 0u);
+    p.build.resize((size_t)(h + 1) * kMaxChunks, 0u);
     // anchor ranges: chunks anchored at word jj-1 are [anchor[jj], anchor[jj+1])
     for (int jj = 0; jj <= kMaxWK + 1; ++jj) {
       int first = 0;
@@ -330,6 +377,12 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   off = align256(off + 8 * (size_t)hkv * kHeadDim * kHeadDim);
   hd.off_rot32_v = off;
   off = align256(off + 4 * (size_t)hkv * kHeadDim * kHeadDim);
+  const std::vector<uint32_t> vlut = value_table(d.v_bits);
+  hd.off_c4 = off;
+  off = align256(off + 8 * 256);
+  hd.off_vlut = off;
+  hd.vlut_bytes = 4 * (int64_t)vlut.size();
+  off = align256(off + 4 * vlut.size());
   hd.total_bytes = off;
 
   p.image.assign(off, 0);
@@ -351,6 +404,13 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
           r32k[g.rot32 + (int64_t)i * g.d + k] = (float)pi[(size_t)i * g.d + k];
         }
     }
+  float *c4 = (float *)(img + hd.off_c4);
+  const Codebook &cb4 = codebook(4);
+  for (int e = 0; e < 256; ++e) {
+    c4[2 * e] = (float)cb4.c[e & 15];
+    c4[2 * e + 1] = (float)cb4.c[e >> 4];
+  }
+  std::memcpy(img + hd.off_vlut, vlut.data(), 4 * vlut.size());
   double *r64v = (double *)(img + hd.off_rot64_v);
   float *r32v = (float *)(img + hd.off_rot32_v);
   for (int h = 0; h < hkv; ++h) {

@@ -197,6 +197,28 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
                              bgtq_stream stream);
 
 /*
+ * (7) Decode step: appends one new key and value per sequence to the packed
+ * cache and attends the new query over the cache including that token.  For
+ * each sequence b with 0 <= pos[b] < capacity, k_new[b] and v_new[b] are
+ * encoded at token pos[b] exactly as bgtq_encode_k / bgtq_encode_v would
+ * (sequences with pos[b] outside that range append nothing); then the output
+ * is bgtq_decode_attn's with seq_lens[b] = pos[b] + 1 (clamped to
+ * [0, max_seq_len]).  The appends and the query preparation share one launch,
+ * followed by the cache-streaming and merge launches of the decode.
+ *   q            device fp16 [batch][n_q_heads][128]
+ *   k_new, v_new device fp16 [batch][n_kv_heads][128]
+ *   pos          device int32 [batch]
+ *   caches       as for bgtq_encode_k / bgtq_encode_v (written) and bgtq_decode_attn (read)
+ *   workspace    bgtq_decode_workspace_size(plan, batch, max_seq_len) bytes, 256-byte aligned
+ * Errors: as bgtq_decode_attn.
+ */
+bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                             const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, int32_t batch,
+                             int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms, uint32_t *v_codes,
+                             uint16_t *v_norms, int64_t capacity, float softmax_scale, uint16_t *out,
+                             void *workspace, size_t ws_bytes, bgtq_stream stream);
+
+/*
  * Host-side inspection (no device work).
  * bgtq_codebook: the b-bit Lloyd-Max quantiser of N(0,1) the library uses:
  * centroids [2^b], interior thresholds [2^b - 1], and D(b).
