@@ -85,13 +85,13 @@ __device__ __forceinline__ void fmac_bcast(float (&a)[G], const float (&src)[G],
     asm("s_nop 1\n\t" BGTQ_FM(0, 1, 2, 4) BGTQ_FM(0, 1, 3, 5)
         : "+v"(a[0]) : "v"(src[0]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
   } else if constexpr (G == 2) {
-    asm("s_nop 1\n\t" BGTQ_FM(0, 2, 4, 6) BGTQ_FM(0, 2, 5, 7) BGTQ_FM(1, 3, 4, 6) BGTQ_FM(1, 3, 5, 7)
+    asm("s_nop 1\n\t" BGTQ_FM(0, 2, 4, 6) BGTQ_FM(1, 3, 4, 6) BGTQ_FM(0, 2, 5, 7) BGTQ_FM(1, 3, 5, 7)
         : "+v"(a[0]), "+v"(a[1]) : "v"(src[0]), "v"(src[1]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
   } else {
 #pragma unroll
     for (int g = 0; g < G; g += 4) {
-      asm("s_nop 1\n\t" BGTQ_FM(0, 4, 8, 10) BGTQ_FM(0, 4, 9, 11) BGTQ_FM(1, 5, 8, 10) BGTQ_FM(1, 5, 9, 11)
-              BGTQ_FM(2, 6, 8, 10) BGTQ_FM(2, 6, 9, 11) BGTQ_FM(3, 7, 8, 10) BGTQ_FM(3, 7, 9, 11)
+      asm("s_nop 1\n\t" BGTQ_FM(0, 4, 8, 10) BGTQ_FM(1, 5, 8, 10) BGTQ_FM(2, 6, 8, 10) BGTQ_FM(3, 7, 8, 10)
+              BGTQ_FM(0, 4, 9, 11) BGTQ_FM(1, 5, 9, 11) BGTQ_FM(2, 6, 9, 11) BGTQ_FM(3, 7, 9, 11)
           : "+v"(a[g]), "+v"(a[g + 1]), "+v"(a[g + 2]), "+v"(a[g + 3])
           : "v"(src[g]), "v"(src[g + 1]), "v"(src[g + 2]), "v"(src[g + 3]), "v"(b0), "v"(b1), "n"(K),
             "n"(K + 1));
@@ -130,27 +130,22 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
-struct StreamSmem {
-  int c4, q4, vlut, total;
-};
-
-// LDS layout of the stream kernel (bytes):
-//   [key tables of the width-1..3 chunks, fp16 entry per query head | wave merge area]
-//   [4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32]
-//   [4-bit group queries: G x 128 fp32, scaled, zero past d4]
-//   [value table]
+// LDS layout of the stream kernel (bytes; fixed offsets first, so that the
+// compiler folds them into the LDS instruction offsets):
+//   [0, 2048)      4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32
+//   [2048, +G 512) 4-bit group queries: G x 128 fp32, scaled, zero past d4
+//   [.., +vlut)    value table
+//   [tab0, ..)     key tables of the width-1..3 chunks, fp16 entry per query head
+// After the tile loop the whole area is reused for the wave merge.
 template <int G, int VB>
-__host__ __device__ constexpr StreamSmem stream_layout(int table_bytes) {
-  StreamSmem s{};
-  const int merge = kStreamWaves * G * kPartStride * 4;
-  int r0 = table_bytes > merge ? table_bytes : merge;
-  r0 = (r0 + 15) & ~15;
-  s.c4 = r0;
-  s.q4 = s.c4 + 256 * 8;
-  s.vlut = s.q4 + G * kHeadDim * 4;
-  s.total = s.vlut + VLut<VB>::entries * VLut<VB>::bytes;
-  return s;
-}
+struct StreamLds {
+  static constexpr int c4 = 0;
+  static constexpr int q4 = 2048;
+  static constexpr int vlut = q4 + G * kHeadDim * 4;
+  static constexpr int tab0 = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
+  static constexpr int merge = kStreamWaves * G * kPartStride * 4;
+  static constexpr int total(int table_bytes) { return tab0 + table_bytes > merge ? tab0 + table_bytes : merge; }
+};
 
 // Per (sequence, KV head) output of the prep kernel, read by every split of
 // the stream kernel: [key tables: table_bytes][4-bit queries: G x 128 fp32]
@@ -214,25 +209,20 @@ struct StreamState {
   uint32_t dv0, dv1;  // lane l: lookup descriptor of chunk l (dv0) and l + 64 (dv1)
   uint32_t av;        // lane jj: first chunk anchored at key word jj-1
   uint32_t fmask;     // window mask shifted to the entry offset (held in a VGPR)
-  int wk, nb4;
+  uint32_t cgrp, jrng;  // chunk boundaries and word-slot ranges of the width-3, 2, 1 groups
+  int wk, n4w;
   int64_t seq;
-  uint32_t c4, q4, vlut;  // LDS offsets
 };
 
 // One table chunk (widths 1..3): funnel-shift the window out of (hi, lo), read
-// the fp16 entries of all heads, accumulate norm * entry with fp32 dot2.
-// nlo / nhi hold the group norm as the fp16 pair (n, 0) / (0, n).
-template <int G>
-__device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo, uint32_t fmask, uint32_t n1,
-                                          uint32_t n2, uint32_t n3, uint32_t &nlo, uint32_t &nhi,
-                                          float (&lr)[G]) {
-  if (dsc & kChunkStart) {  // norm slot 1..3 = widths 3..1
-    const uint32_t slot = (dsc >> 24) & 3;
-    nlo = slot == 1 ? n1 : (slot == 2 ? n2 : n3);
-    nhi = nlo << 16;
-  }
+// the fp16 entries of all heads at LDS byte tab0 + offset, accumulate
+// norm * entry with fp32 dot2.  nlo / nhi hold the group norm as the fp16
+// pair (n, 0) / (0, n).
+template <int G, int TAB0>
+__device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo, uint32_t fmask, uint32_t nlo,
+                                          uint32_t nhi, float (&lr)[G]) {
   const uint32_t t = __builtin_amdgcn_alignbit(hi, lo, dsc);
-  const uint32_t a = (t & fmask) | (dsc & kChunkTableMask);
+  const uint32_t a = ((t & fmask) | (dsc & kChunkTableMask)) + TAB0;
   if constexpr (G == 1) {
     const uint32_t e = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a;
     lr[0] = dot2(e, nlo, lr[0]);
@@ -252,40 +242,141 @@ __device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo
   }
 }
 
-// 4-bit group, one block of 16 codes (key words 2 blk, 2 blk + 1): lane =
-// token; a4[h] += sum_r q4[h][16 blk + r] * c4[code_r].  The queries of the
-// block sit row-replicated in one register per head (lane l holds code
-// 16 blk + l % 16) and are broadcast per code by DPP.
-template <int G, int WK, int BLK>
-__device__ __forceinline__ void key4_block(const uint32_t (&w)[WK], uint32_t c4, uint32_t q4, int lane,
-                                           float (&a4)[G]) {
-  float qr[G];
+// Two table chunks of one group and key-word pair, both reads issued first.
+template <int G, int TAB0>
+__device__ __forceinline__ void key_chunk2(uint32_t d0, uint32_t d1, uint32_t hi, uint32_t lo, uint32_t fmask,
+                                           uint32_t nlo, uint32_t nhi, float (&lr)[G]) {
+  const uint32_t a0 = ((__builtin_amdgcn_alignbit(hi, lo, d0) & fmask) | (d0 & kChunkTableMask)) + TAB0;
+  const uint32_t a1 = ((__builtin_amdgcn_alignbit(hi, lo, d1) & fmask) | (d1 & kChunkTableMask)) + TAB0;
+  if constexpr (G == 1) {
+    const uint32_t e0 = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a0;
+    const uint32_t e1 = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a1;
+    lr[0] = dot2(e0, nlo, lr[0]);
+    lr[0] = dot2(e1, nlo, lr[0]);
+  } else if constexpr (G == 2) {
+    const uint32_t e0 = lds_at<uint32_t>(a0), e1 = lds_at<uint32_t>(a1);
+    lr[0] = dot2(e0, nlo, lr[0]);
+    lr[1] = dot2(e0, nhi, lr[1]);
+    lr[0] = dot2(e1, nlo, lr[0]);
+    lr[1] = dot2(e1, nhi, lr[1]);
+  } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h) qr[h] = lds_at<float>(q4 + (uint32_t)(h * kHeadDim + 16 * BLK + (lane & 15)) * 4);
-#pragma unroll
-  for (int wi = 0; wi < 2; ++wi) {
-    const uint32_t word = w[2 * BLK + wi];
-#define BGTQ_K4(BY)                                                          \
-  {                                                                          \
-    const float2 cp = lds_at<float2>(c4 + ((word >> (8 * BY)) & 255u) * 8); \
-    if (wi == 0) fmac_bcast<G, 2 * BY>(a4, qr, cp.x, cp.y);                 \
-    else fmac_bcast<G, 8 + 2 * BY>(a4, qr, cp.x, cp.y);                     \
-  }
-    BGTQ_K4(0) BGTQ_K4(1) BGTQ_K4(2) BGTQ_K4(3)
-#undef BGTQ_K4
-  }
-}
-
-template <int G, int WK, int BLK>
-__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], const StreamState &st, int lane,
-                                            float (&a4)[G]) {
-  if constexpr (2 * BLK < WK) {
-    if (BLK < st.nb4) {
-      key4_block<G, WK, BLK>(w, st.c4, st.q4, lane, a4);
-      key4_blocks<G, WK, BLK + 1>(w, st, lane, a4);
+    for (int q4 = 0; q4 < G / 4; ++q4) {
+      const uint2 e0 = lds_at<uint2>(a0 + 8 * q4), e1 = lds_at<uint2>(a1 + 8 * q4);
+      lr[4 * q4 + 0] = dot2(e0.x, nlo, lr[4 * q4 + 0]);
+      lr[4 * q4 + 1] = dot2(e0.x, nhi, lr[4 * q4 + 1]);
+      lr[4 * q4 + 2] = dot2(e0.y, nlo, lr[4 * q4 + 2]);
+      lr[4 * q4 + 3] = dot2(e0.y, nhi, lr[4 * q4 + 3]);
+      lr[4 * q4 + 0] = dot2(e1.x, nlo, lr[4 * q4 + 0]);
+      lr[4 * q4 + 1] = dot2(e1.x, nhi, lr[4 * q4 + 1]);
+      lr[4 * q4 + 2] = dot2(e1.y, nlo, lr[4 * q4 + 2]);
+      lr[4 * q4 + 3] = dot2(e1.y, nhi, lr[4 * q4 + 3]);
     }
   }
 }
+
+// 4-bit group, key word J (codes 8 J .. 8 J + 7; lanes K0 .. K0 + 7 of the
+// block's query registers): lane = token, a4[h] += sum_r q4[h][r] * c4[code_r]
+// over the code pairs of the word's bytes (centroid pairs at LDS byte 8 * byte).
+template <int G, int WK, int J, int K0>
+__device__ __forceinline__ void key4_word(const uint32_t (&w)[WK], const float (&qr)[G], float (&a4)[G]) {
+  const uint32_t word = w[J];
+#define BGTQ_K4(BY)                                                           \
+  {                                                                           \
+    const float2 cp = lds_at<float2>(((word >> (8 * BY)) & 255u) << 3);      \
+    fmac_bcast<G, K0 + 2 * BY>(a4, qr, cp.x, cp.y);                           \
+  }
+  BGTQ_K4(0) BGTQ_K4(1) BGTQ_K4(2) BGTQ_K4(3)
+#undef BGTQ_K4
+}
+
+// Blocks of 16 codes (two key words): the block's queries sit row-replicated
+// in one register per head (lane l holds code 16 BLK + l % 16) and are
+// broadcast per code by DPP.  Only the words that hold 4-bit codes are read.
+template <int G, int VB, int WK, int BLK>
+__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, int lane, float (&a4)[G]) {
+  if constexpr (2 * BLK < WK) {
+    if (2 * BLK < n4w) {
+      float qr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        qr[h] = lds_at<float>(StreamLds<G, VB>::q4 + (uint32_t)(h * kHeadDim + 16 * BLK + (lane & 15)) * 4);
+      key4_word<G, WK, 2 * BLK, 0>(w, qr, a4);
+      if (2 * BLK + 1 < n4w) key4_word<G, WK, 2 * BLK + 1, 8>(w, qr, a4);
+      key4_blocks<G, VB, WK, BLK + 1>(w, n4w, lane, a4);
+    }
+  }
+}
+
+// Chunks of one width group (rest group R = width 3 - R, norm slot R + 1),
+// grouped by the key word their window starts in.
+template <int G, int VB, int WK, int R>
+__device__ __forceinline__ void key_group(const uint32_t (&w)[WK], const StreamState &st, uint32_t nlo,
+                                          float (&lr)[G]) {
+  constexpr int TAB0 = StreamLds<G, VB>::tab0;
+  const int cb = (st.cgrp >> (8 * R)) & 255, ce = (st.cgrp >> (8 * R + 8)) & 255;
+  if (cb >= ce) return;
+  const int jl = (st.jrng >> (10 * R)) & 31, jh = (st.jrng >> (10 * R + 5)) & 31;
+  const uint32_t nhi = nlo << 16;
+#pragma unroll
+  for (int jj = 0; jj <= WK; ++jj) {
+    if (jj >= jl && jj <= jh) {
+      const uint32_t lo = jj ? w[jj - 1] : 0u, hi = jj < WK ? w[jj] : 0u;
+      const int a0 = __builtin_amdgcn_readlane((int)st.av, jj);
+      const int a1 = __builtin_amdgcn_readlane((int)st.av, jj + 1);
+      const int c0 = a0 > cb ? a0 : cb, c1 = a1 < ce ? a1 : ce;
+      const int m1 = c1 < 64 ? c1 : 64;
+      int c = c0;
+      for (; c + 1 < m1; c += 2) {  // two chunks per step: both table reads in flight
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c);
+        const uint32_t d1 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c + 1);
+        key_chunk2<G, TAB0>(d0, d1, hi, lo, st.fmask, nlo, nhi, lr);
+      }
+      if (c < m1)
+        key_chunk<G, TAB0>((uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c), hi, lo, st.fmask, nlo, nhi, lr);
+      for (int c = c0 > 64 ? c0 : 64; c < c1; ++c)
+        key_chunk<G, TAB0>((uint32_t)__builtin_amdgcn_readlane((int)st.dv1, c - 64), hi, lo, st.fmask, nlo, nhi,
+                           lr);
+    }
+  }
+}
+
+// In-place maximum over the 64 lanes of each v[h] (every lane receives it):
+// fused DPP max steps, heads interleaved so that consecutive steps of one head
+// are at least two instructions apart.
+#define BGTQ_MX(V, CTL) "v_max_f32_dpp %" #V ", %" #V ", %" #V " " CTL " bank_mask:0xf\n\t"
+#define BGTQ_MX4(CTL) BGTQ_MX(0, CTL) BGTQ_MX(1, CTL) BGTQ_MX(2, CTL) BGTQ_MX(3, CTL)
+#define BGTQ_MX2(CTL) BGTQ_MX(0, CTL) "s_nop 0\n\t" BGTQ_MX(1, CTL)
+template <int G>
+__device__ __forceinline__ void wave_max_heads(float (&v)[G]) {
+  if constexpr (G == 1) {
+    asm("s_nop 1\n\t" BGTQ_MX(0, "quad_perm:[1,0,3,2] row_mask:0xf") "s_nop 1\n\t"
+        BGTQ_MX(0, "quad_perm:[2,3,0,1] row_mask:0xf") "s_nop 1\n\t" BGTQ_MX(0, "row_half_mirror row_mask:0xf")
+        "s_nop 1\n\t" BGTQ_MX(0, "row_mirror row_mask:0xf") "s_nop 1\n\t" BGTQ_MX(0, "row_bcast:15 row_mask:0xa")
+        "s_nop 1\n\t" BGTQ_MX(0, "row_bcast:31 row_mask:0xc")
+        : "+v"(v[0]));
+  } else if constexpr (G == 2) {
+    asm("s_nop 1\n\t" BGTQ_MX2("quad_perm:[1,0,3,2] row_mask:0xf") "s_nop 0\n\t"
+        BGTQ_MX2("quad_perm:[2,3,0,1] row_mask:0xf") "s_nop 0\n\t" BGTQ_MX2("row_half_mirror row_mask:0xf")
+        "s_nop 0\n\t" BGTQ_MX2("row_mirror row_mask:0xf") "s_nop 0\n\t" BGTQ_MX2("row_bcast:15 row_mask:0xa")
+        "s_nop 0\n\t" BGTQ_MX2("row_bcast:31 row_mask:0xc")
+        : "+v"(v[0]), "+v"(v[1]));
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      asm("s_nop 1\n\t" BGTQ_MX4("quad_perm:[1,0,3,2] row_mask:0xf") BGTQ_MX4("quad_perm:[2,3,0,1] row_mask:0xf")
+              BGTQ_MX4("row_half_mirror row_mask:0xf") BGTQ_MX4("row_mirror row_mask:0xf")
+                  BGTQ_MX4("row_bcast:15 row_mask:0xa") BGTQ_MX4("row_bcast:31 row_mask:0xc")
+          : "+v"(v[g]), "+v"(v[g + 1]), "+v"(v[g + 2]), "+v"(v[g + 3]));
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    v[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[h]), 63));
+}
+#undef BGTQ_MX2
+#undef BGTQ_MX4
+#undef BGTQ_MX
 
 // Value accumulation for token pair J (0..31) from the row-replicated P'
 // registers: acc0/acc1[h] += <P'_h pair J, centroid pair of coordinate lane / lane + 64>.
@@ -349,38 +440,29 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   float a4[G], lr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) a4[h] = 0.f, lr[h] = 0.f;
-  key4_blocks<G, WK, 0>(r.w, st, lane, a4);
-  // widths 1..3: table chunks, grouped by the key word their window starts in
-  uint32_t nlo = 0, nhi = 0;
-  const uint32_t n1 = r.nr.x >> 16, n2 = r.nr.y & 0xFFFFu, n3 = r.nr.y >> 16;
-#pragma unroll
-  for (int jj = 0; jj <= WK; ++jj) {
-    if (jj <= st.wk) {
-      const uint32_t lo = jj ? r.w[jj - 1] : 0u, hi = jj < WK ? r.w[jj] : 0u;
-      const int c0 = __builtin_amdgcn_readlane((int)st.av, jj);
-      const int c1 = __builtin_amdgcn_readlane((int)st.av, jj + 1);
-      const int m1 = c1 < 64 ? c1 : 64;
-      for (int c = c0; c < m1; ++c)
-        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c), hi, lo, st.fmask, n1, n2, n3, nlo, nhi,
-                     lr);
-      for (int c = c0 > 64 ? c0 : 64; c < c1; ++c)
-        key_chunk<G>((uint32_t)__builtin_amdgcn_readlane((int)st.dv1, c - 64), hi, lo, st.fmask, n1, n2, n3, nlo,
-                     nhi, lr);
-    }
-  }
+  key4_blocks<G, VB, WK, 0>(r.w, st.n4w, lane, a4);
+  // widths 3, 2, 1: table chunks, norm slots 1, 2, 3
+  key_group<G, VB, WK, 0>(r.w, st, r.nr.x >> 16, lr);
+  key_group<G, VB, WK, 1>(r.w, st, r.nr.y & 0xFFFFu, lr);
+  key_group<G, VB, WK, 2>(r.w, st, r.nr.y >> 16, lr);
   const bool valid = (int64_t)tile * kTile + lane < st.seq;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
   // ---- online softmax (log2 domain); P' = p * value norm as fp16 token pairs
+  float l[G], mx[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = valid ? fmaf(n4, a4[h], lr[h] * rinv[h]) : -INFINITY;
+    mx[h] = l[h];
+  }
+  wave_max_heads<G>(mx);
   float alpha[G];
   uint32_t pr[2][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float lg = fmaf(n4, a4[h], lr[h] * rinv[h]);
-    const float l = valid ? lg : -INFINITY;
-    const float mn = fmaxf(mrun[h], wave_max(l));
+    const float mn = fmaxf(mrun[h], mx[h]);
     alpha[h] = __builtin_amdgcn_exp2f(mrun[h] - mn);
-    const float p = __builtin_amdgcn_exp2f(l - mn);
+    const float p = __builtin_amdgcn_exp2f(l[h] - mn);
     lsum[h] = fmaf(lsum[h], alpha[h], p);
     mrun[h] = mn;
     const uint32_t mine = __builtin_bit_cast(uint16_t, (_Float16)(p * nv));
@@ -396,7 +478,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
     acc0[h] *= alpha[h];
     acc1[h] *= alpha[h];
   }
-  v_steps<G, VB, 0>(r.va, r.vb, st.vlut, pr, acc0, acc1);
+  v_steps<G, VB, 0>(r.va, r.vb, (uint32_t)StreamLds<G, VB>::vlut, pr, acc0, acc1);
 }
 
 // Waves per SIMD the register allocation aims at: four (two workgroups per CU,
@@ -433,13 +515,6 @@ struct StreamArgs {
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
 };
 
-// 16-byte copy from global memory into LDS by the whole workgroup.
-__device__ __forceinline__ void copy_to_lds(uint8_t *dst, const uint8_t *__restrict__ src, int bytes, int tid) {
-  const uint4 *s4 = (const uint4 *)src;
-  uint4 *d4 = (uint4 *)dst;
-  for (int i = tid; i < (bytes >> 4); i += kStreamThreads) d4[i] = s4[i];
-}
-
 template <int G, int VB, int WK>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
 void decode_stream_kernel(const StreamArgs a) {
@@ -452,49 +527,81 @@ void decode_stream_kernel(const StreamArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
   const int win = a.win;
-  const StreamSmem sm = stream_layout<G, VB>(a.table_bytes);
+  typedef StreamLds<G, VB> Lds;
 
   // ---- prologue: the shared query state of this (sequence, KV head) and the
-  // plan's centroid tables into LDS
+  // plan's centroid tables into LDS.  The first 32 KB of the copy are loaded
+  // into registers before the first tile is requested, so that waiting for
+  // them does not wait for the tile (loads complete in order).
   const uint8_t *pr = a.prep + ((size_t)b * a.hkv + kvh) * (size_t)a.prep_stride;
-  copy_to_lds(smem, pr, a.table_bytes, tid);
-  copy_to_lds(smem + sm.q4, pr + a.table_bytes, G * kHeadDim * 4, tid);
-  copy_to_lds(smem + sm.c4, consts + a.off_c4, 256 * 8, tid);
-  copy_to_lds(smem + sm.vlut, consts + a.off_vlut, VLut<VB>::entries * VLut<VB>::bytes, tid);
-  float rinv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + a.table_bytes + G * kHeadDim * 4))[h];
+  const int n0 = a.table_bytes >> 4;
+  const int n1 = n0 + ((G * kHeadDim * 4) >> 4);
+  const int n2 = n1 + ((256 * 8) >> 4);
+  const int n3 = n2 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
+  const uint4 *cs0 = (const uint4 *)pr, *cs1 = (const uint4 *)(pr + a.table_bytes) - n0;
+  const uint4 *cs2 = (const uint4 *)(consts + a.off_c4) - n1, *cs3 = (const uint4 *)(consts + a.off_vlut) - n2;
+  constexpr int kCopyRegs = 4;
+  uint4 cr0, cr1, cr2, cr3;
+#define BGTQ_CSRC(I) ((I) < n0 ? cs0 + (I) : (I) < n1 ? cs1 + (I) : (I) < n2 ? cs2 + (I) : cs3 + (I))
+#define BGTQ_CDST(I)                                                                                              \
+  ((uint4 *)(smem + ((I) < n0 ? Lds::tab0 + 16 * (I)                                                              \
+                              : (I) < n1 ? Lds::q4 + 16 * ((I) - n0)                                              \
+                                         : (I) < n2 ? Lds::c4 + 16 * ((I) - n1)                                   \
+                                                    : (I) < n3 ? Lds::vlut + 16 * ((I) - n2) : Lds::total(a.table_bytes))))
+  {
+    const int i0 = min(tid, n3 - 1), i1 = min(tid + kStreamThreads, n3 - 1);
+    const int i2 = min(tid + 2 * kStreamThreads, n3 - 1), i3 = min(tid + 3 * kStreamThreads, n3 - 1);
+    cr0 = *BGTQ_CSRC(i0);
+    cr1 = *BGTQ_CSRC(i1);
+    cr2 = *BGTQ_CSRC(i2);
+    cr3 = *BGTQ_CSRC(i3);
+  }
   StreamState st;
   {
-    int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
-    st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
     const uint32_t *lk = (const uint32_t *)(consts + a.off_lookup) + kvh * kMaxChunks;
     st.dv0 = lk[lane];  // zero past the head's chunks
     st.dv1 = lk[lane + 64];
-    st.av = lane <= kMaxWK + 1 ? (uint32_t)kd->anchor[lane] : 0u;
-    st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
-    st.wk = a.wk;
-    st.nb4 = kd->n4blk;
-    st.c4 = (uint32_t)sm.c4;
-    st.q4 = (uint32_t)sm.q4;
-    st.vlut = (uint32_t)sm.vlut;
+    st.av = (uint32_t)kd->anchor[min(lane, kMaxWK + 1)];
   }
-  __syncthreads();
-
-  // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers
-  const int ntile = (int)((st.seq + kTile - 1) / kTile);
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tile request
+  // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers.
+  // The first is requested now, its range bounded by max_seq_len (in memory).
   const int tile_lo = split * a.tiles_per_split;
-  const int tile_hi = min(tile_lo + a.tiles_per_split, ntile);
+  const int tile_end = min(tile_lo + a.tiles_per_split, (int)((a.max_seq_len + kTile - 1) / kTile));
   const size_t head_base = ((size_t)b * a.hkv + kvh) * (size_t)a.tiles_cap;
   const uint32_t *ksrc = a.wk ? a.kc : (const uint32_t *)a.kn;
   const int wkl = a.wk ? a.wk : 1;
+  TileRegs<VB, WK> ra, rb;
+  int tile = tile_lo + wave;
+  load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), a.wk, wkl, lane);
+  // past the copy: a spare 16 bytes at the end of the allocation takes the stores
+  *BGTQ_CDST(tid) = cr0;
+  *BGTQ_CDST(tid + kStreamThreads) = cr1;
+  *BGTQ_CDST(tid + 2 * kStreamThreads) = cr2;
+  *BGTQ_CDST(tid + 3 * kStreamThreads) = cr3;
+  for (int i = tid + kCopyRegs * kStreamThreads; i < n3; i += kStreamThreads) *BGTQ_CDST(i) = *BGTQ_CSRC(i);
+#undef BGTQ_CDST
+#undef BGTQ_CSRC
+  float rinv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + a.table_bytes + G * kHeadDim * 4))[h];
+  {
+    int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
+    st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
+    st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
+    st.wk = a.wk;
+    st.n4w = kd->n4w;
+    st.cgrp = kd->cgrp;
+    st.jrng = kd->jrng;
+  }
+  __syncthreads();
+
+  const int ntile = (int)((st.seq + kTile - 1) / kTile);
+  const int tile_hi = min(tile_end, ntile);
   float mrun[G], lsum[G], acc0[G], acc1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f, acc0[h] = 0.f, acc1[h] = 0.f;
-  TileRegs<VB, WK> ra, rb;
-  int tile = tile_lo + wave;
   if (tile < tile_hi) {
-    load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + tile, a.wk, wkl, lane);
     for (;;) {
       load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
       process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
@@ -661,7 +768,7 @@ stream_fn pick_stream(int g, int vb, int wk) {
 
 int stream_smem_bytes(int g, int vb, int table_bytes) {
 #define BGTQ_SM(G_, VB_) \
-  if (g == G_ && vb == VB_) return stream_layout<G_, VB_>(table_bytes).total;
+  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::total(table_bytes) + 16;
   BGTQ_SM(1, 1) BGTQ_SM(1, 2) BGTQ_SM(1, 3) BGTQ_SM(1, 4)
   BGTQ_SM(2, 1) BGTQ_SM(2, 2) BGTQ_SM(2, 3) BGTQ_SM(2, 4)
   BGTQ_SM(4, 1) BGTQ_SM(4, 2) BGTQ_SM(4, 3) BGTQ_SM(4, 4)

@@ -49,6 +49,9 @@ struct KvhDesc {
   int32_t chunk_base;          // index of this head's first chunk in the chunk arrays (head * kMaxChunks)
   int32_t d4;                  // coordinates of the 4-bit group (group 0 when present), else 0
   int32_t n4blk;               // 16-code blocks of the 4-bit group, ceil(d4 / 16)
+  int32_t n4w;                 // key words holding 4-bit codes, ceil(d4 / 8)
+  uint32_t cgrp;               // byte r (r = 0..3): first chunk of the width-(3-r) group; byte 3 = n_chunks
+  uint32_t jrng;               // bits [10r, 10r+5) / [10r+5, 10r+10): first / last word slot jj of group r's chunks
   KGroupDesc g[kMaxGroups];
   int16_t coord[kHeadDim];     // original coordinate of each group-order position
   int16_t pad_[4];

@@ -307,9 +307,14 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     int c = 0;
     kd.d4 = (kd.n_groups > 0 && kd.g[0].w == 4) ? kd.g[0].d : 0;
     kd.n4blk = (kd.d4 + 15) / 16;
+    kd.n4w = (kd.d4 + 7) / 8;
+    int cfirst[4] = {-1, -1, -1, -1};  // first chunk of the width-3, 2, 1 groups
+    int jlo[3] = {31, 31, 31}, jhi[3] = {0, 0, 0};
     for (int gi = 0; gi < kd.n_groups; ++gi) {
       const KGroupDesc &g = kd.g[gi];
       if (g.w == 4) continue;  // summed directly in the decode, no tables
+      const int rg = 3 - g.w;   // rest-group index
+      cfirst[rg] = c;
       const int m_max = window / g.w;
       for (int r0 = 0; r0 < g.d; r0 += m_max, ++c) {
         const int m = std::min(m_max, g.d - r0);
@@ -323,6 +328,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
         p.build.push_back((uint32_t)(g.pos + r0) | ((uint32_t)m << 8) | ((uint32_t)g.w << 12) |
                           ((uint32_t)gi << 15));
         anchors.push_back(anchor);
+        jlo[rg] = std::min(jlo[rg], anchor + 1);
+        jhi[rg] = std::max(jhi[rg], anchor + 1);
       }
     }
     if (c > kMaxChunks) {
@@ -331,6 +338,15 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     }
     kd.n_chunks = c;
     max_chunks = std::max(max_chunks, c);
+    {
+      // chunk boundaries of the width-3, 2, 1 groups (an absent group is an empty range)
+      int bnd[4];
+      bnd[3] = c;
+      for (int rg = 2; rg >= 0; --rg) bnd[rg] = cfirst[rg] >= 0 ? cfirst[rg] : bnd[rg + 1];
+      kd.cgrp = (uint32_t)bnd[0] | ((uint32_t)bnd[1] << 8) | ((uint32_t)bnd[2] << 16) | ((uint32_t)bnd[3] << 24);
+      kd.jrng = 0;
+      for (int rg = 0; rg < 3; ++rg) kd.jrng |= ((uint32_t)jlo[rg] | ((uint32_t)jhi[rg] << 5)) << (10 * rg);
+    }
     p.lookup.resize((size_t)(h + 1) * kMaxChunks, 0u);
     p.build.resize((size_t)(h + 1) * kMaxChunks, 0u);
     // anchor ranges: chunks anchored at word jj-1 are [anchor[jj], anchor[jj+1])
