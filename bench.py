@@ -1,10 +1,11 @@
 """Benchmark of the Block-GTQ packed-KV decode path on one MI355X.
 
-One step = one serving decode step of the 128K Llama-3.1-8B-shaped layer
-(batch 1, 8 KV / 32 query heads, K2V2): the new token's key and value are
-encoded into the packed cache at position T and the query prepared (one launch),
-then the fused decode attention reads all T+1 cached tokens (cache-streaming
-kernel, split merge): bgtq_decode_step.
+One step = one decode-attention call (bgtq_decode_attn: query preparation,
+cache-streaming kernel, split merge) of the 128K Llama-3.1-8B-shaped layer
+(batch 1, 8 KV / 32 query heads, K2V2) over the T+1 cached tokens.  The serving
+step (bgtq_decode_step: the new token's key and value appended at position T in
+the same launch as the query preparation, then the decode) is timed as well and
+reported under "serving_step".
 Calibration energy, allocation, plan creation and the full 128K prefill
 encode run once before the timed region and are reported as separate fields.
 
@@ -90,6 +91,52 @@ def cpu_baseline(cfg, bits, n_heads: int):
                       (n_heads, cfg.n_kv_heads, t, n_heads * cfg.group)}
 
 
+def traffic_from(fetch_dir: str, write_dir: str, cid: int, packed: int | None, out_path: str) -> int:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) into
+    profiles/decode_stream_traffic.json.  Both counters are scaled by what they read for the
+    1 GiB device copy of the copy probe (1 GiB read, 1 GiB written)."""
+    import csv
+    import glob
+
+    def rows(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit("no counter_collection.csv under %s" % d)
+        return list(csv.DictReader(open(f[0])))
+
+    def per_kernel(rs, counter):
+        copy, stream = [], []
+        for r in rs:
+            if r["Counter_Name"] != counter:
+                continue
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append((dur, float(r["Counter_Value"])))
+            elif STREAM_KERNEL in r["Kernel_Name"]:
+                stream.append(float(r["Counter_Value"]))
+        top = max(d for d, _ in copy)
+        big = [v for d, v in copy if d >= top / 2]  # the 1 GiB copies
+        return sum(big) / len(big), sum(stream) / len(stream), len(big), len(stream)
+
+    fc, fs, nfc, nfs = per_kernel(rows(fetch_dir), "FETCH_SIZE")
+    wc, ws, nwc, nws = per_kernel(rows(write_dir), "WRITE_SIZE")
+    gib = float(1 << 30)
+    rscale, wscale = gib / (fc * 1024), gib / (wc * 1024)
+    rec = {"fetch_bytes": round(fs * 1024 * rscale), "write_bytes": round(ws * 1024 * wscale),
+           "fetch_kib_raw": fs, "write_kib_raw": ws, "launches": [nfs, nws]}
+    rec["hbm_bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    if packed:
+        rec["algorithmic_bytes_per_launch"] = packed
+    out = {"kernel": STREAM_KERNEL, "kernel_source_sha256_16": kernel_source_hash(),
+           "copy_scale": {"fetch": rscale, "write": wscale, "copy_fetch_kib_raw": fc, "copy_write_kib_raw": wc,
+                          "copies": [nfc, nwc]},
+           "configs": {str(cid): rec}}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,10 +146,18 @@ def main() -> int:
     ap.add_argument("--replica-bytes", type=float, default=1.1e9)
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/decode_stream_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--packed-bytes", type=int, default=None)
+    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "decode_stream_traffic.json"))
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_from(args.traffic_from[0], args.traffic_from[1], args.config, args.packed_bytes,
+                            args.traffic_out)
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode (see DESIGN.md for how it "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the decode path has no multi-GPU mode here (KV heads, "
+              "sequences and token ranges would shard with one partial merge); run with --gpus 1",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -185,22 +240,25 @@ def main() -> int:
     ws = torch.empty(plan.workspace_size(b, t + 1), dtype=torch.uint8, device=dev)
 
     pos = torch.full((b,), t, dtype=torch.int32, device=dev)
+    seq_lens = torch.full((b,), t + 1, dtype=torch.int32, device=dev)
+    for i in range(n_rep):  # every replica holds token t before the timed decode calls
+        kc_, kn_, vc_, vn_ = reps[i]
+        plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
+    torch.cuda.synchronize()
 
-    def step(i):  # one fused decode step: append at position t, attend over t + 1 tokens
+    def attn(i):  # one decode-attention call over t + 1 tokens: query prep, cache stream, split merge
+        kc_, kn_, vc_, vn_ = reps[i % n_rep]
+        plan.decode_attn(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, out, ws)
+
+    def serve(i):  # one serving step: append the new key / value at t, then attend (fused entry point)
         kc_, kn_, vc_, vn_ = reps[i % n_rep]
         plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Timed region: rounds of at most 100 steps, each enqueued behind a short GPU
-    # spin so that the host has queued the whole round before the GPU reaches it;
-    # the events bracket the steps only, so the time is the GPU's.
-    per_round = min(args.steps, 100)
-    rounds = max(1, args.steps // per_round)
     spin = getattr(torch.cuda, "_sleep", None)
 
-    def timed_round(i0, n):
+    def timed_round(fn, i0, n):
+        # one round: n calls enqueued behind a short GPU spin so that the host has queued
+        # them all before the GPU reaches them; the events bracket the calls only
         torch.cuda.synchronize()
         if spin is not None:
             spin(int(30e6))
@@ -208,33 +266,41 @@ def main() -> int:
         s0.record()
         th = time.perf_counter()
         for i in range(n):
-            step(i0 + i)
+            fn(i0 + i)
         th = time.perf_counter() - th
         s1.record()
         torch.cuda.synchronize()
         return s0.elapsed_time(s1), th
 
-    step_ms_total, host_enqueue_s, n_steps = 0.0, 0.0, 0
+    for i in range(args.warmup):
+        attn(i)
+        serve(i)
+    torch.cuda.synchronize()
+    per_round = min(args.steps, 100)
+    rounds = max(1, args.steps // per_round)
+    round_ms, host_enqueue_s, n_steps = [], 0.0, 0
     for r in range(rounds):
-        ms, th = timed_round(args.warmup + n_steps, per_round)
-        step_ms_total += ms
+        ms, th = timed_round(attn, args.warmup + n_steps, per_round)
+        round_ms.append(ms / per_round)
         host_enqueue_s += th
         n_steps += per_round
-    step_ms = step_ms_total / n_steps
-    # Stream-kernel duration: the same steps once more with the library's HIP events
-    # around every cache-streaming launch (on the launch stream).  Kept out of the
-    # step timing above because each event record adds a queue packet.
+    step_ms = sum(round_ms) / len(round_ms)
+    serve_ms = sum(timed_round(serve, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
+    # Stream-kernel duration: the same decode calls once more with the library's HIP events
+    # around every cache-streaming launch (on the launch stream); kept out of the timings
+    # above because each event record adds a queue packet.
     bg.profile_enable(True)
     bg.profile_read()
     for r in range(rounds):
-        timed_round(args.warmup + n_steps + r * per_round, per_round)
+        timed_round(attn, r * per_round, per_round)
     bg.profile_enable(False)
     kern_ms_total, launches = bg.profile_read()
     kern_ms = kern_ms_total / max(launches, 1)
     value = packed / (step_ms / 1e3) / 1e9
     achieved = packed / (kern_ms / 1e3) / 1e9
-    log("step %.4f ms (%.0f GB/s); stream kernel %.4f ms (%.0f GB/s, %d launches); host enqueue %.4f ms/step" %
-        (step_ms, value, kern_ms, achieved, launches, host_enqueue_s * 1e3 / n_steps))
+    log("decode %.4f ms (%.0f GB/s); serving step %.4f ms; stream kernel %.4f ms (%.0f GB/s, %d launches); "
+        "host enqueue %.4f ms/call" % (step_ms, value, serve_ms, kern_ms, achieved, launches,
+                                       host_enqueue_s * 1e3 / n_steps))
 
     # ---- copy probe: practical streaming ceiling (1 GiB read + 1 GiB write)
     src = torch.empty(1 << 28, dtype=torch.int32, device=dev)
@@ -253,11 +319,15 @@ def main() -> int:
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "step_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(round_ms, [10, 50, 90])],
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": b, "seq_len": t, "n_kv_heads": hkv, "n_q_heads": hq,
                    "k_bits": cfg.k_bits, "v_bits": cfg.v_bits, "head_dim": 128, "cache_io": "packed codes + fp16 norms",
                    "query_io": "fp16", "accumulate": "fp32", "parallelism": "single GPU"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "serving_step": {"what": "bgtq_decode_step: the new token's key and value appended at position T, then "
+                                 "decode attention over T + 1 tokens", "ms": round(serve_ms, 5),
+                         "GBps": round(packed / (serve_ms / 1e3) / 1e9, 2)},
         "packed_bytes_per_step": packed,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,

@@ -58,10 +58,11 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
   const int tid = threadIdx.x;
   const uint16_t *qb = q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim;
   const int nq = G * kHeadDim;
-  for (int i = tid; i < 8 * kHeadDim; i += 256) qs[i] = 0.f;
+  RotRows<4> rr;
+  rot_rows<4>((const float *)(consts + hd->off_rot32_k) + (size_t)kvh * kHeadDim * kHeadDim, tid >> 6, tid & 63, rr);
   gather_queries(kd, G, qb, qg, tid, 256);
   __syncthreads();
-  rotate_queries(hd, kd, G, qg, qs, tid >> 6, 4, tid & 63);
+  rot_tiles<4>(rr, G, qg, qs, tid >> 6, tid & 63);
   __syncthreads();
   for (int idx = tid; idx < nq; idx += 256) qrot[((size_t)b * hq + (size_t)kvh * G) * kHeadDim + idx] = qs[idx];
 }
@@ -648,28 +649,30 @@ void decode_stream_kernel(const StreamArgs a) {
   }
 }
 
-// One workgroup per (query head, sequence).  Thread s < n_splits owns split
-// s's (m, l); thread t accumulates value coordinate t % 128 over the splits of
-// parity t / 128; the un-rotation out[j] = sum_k Pi_V[k][j] y[k] gives each
-// output two threads (k halves).  Every global load (rotation rows, split
-// statistics, split accumulators) is issued before the first reduction.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeRegs = 16;  // split accumulators per thread held in registers (n_splits <= 32)
+// One workgroup of 512 threads per (query head, sequence).  Every global load
+// is issued first: thread t holds the split accumulators of coordinate t % 128
+// for the splits s = t / 128 (mod 4) (up to kMergeRegs of them in registers),
+// the (m, l) of split t, and a quarter (32 values) of row t / 4 of Pi_V^T.
+// Then: M = max_s m_s, w_s = 2^(m_s - M) / (sum_s 2^(m_s - M) l_s sqrt(128)),
+// y = sum_s w_s acc_s, out[j] = sum_k Pi_V[k][j] y[k] (four threads per j).
+constexpr int kMergeThreads = 512;
+constexpr int kMergeRegs = 16;  // split accumulators per thread held in registers (n_splits <= 64)
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ pvt_all,
                                                               const float *__restrict__ part, int n_splits,
                                                               int group, int hq, uint16_t *__restrict__ out) {
   __shared__ float wsm[kMaxSplits];
-  __shared__ __attribute__((aligned(16))) float ys[2 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float ys[4 * kHeadDim];
   __shared__ float red[2 * (kMergeThreads / 64)];
   const int hqi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvh = hqi / group;
   const float *ph = part + ((size_t)b * hq + hqi) * (size_t)n_splits * kPartStride;
-  const int j = tid >> 1, kh = (tid & 1) * (kHeadDim / 2);
-  const float4 *row = (const float4 *)(pvt_all + ((size_t)kvh * kHeadDim + j) * kHeadDim + kh);
-  float4 pr[kHeadDim / 8];
+  // rotation quarter: output j = tid / 4, k in [32 (tid % 4), 32 (tid % 4) + 32)
+  const int j = tid >> 2, kq = tid & 3;
+  const float4 *row = (const float4 *)(pvt_all + ((size_t)kvh * kHeadDim + j) * kHeadDim + 32 * kq);
+  float4 pr[8];
 #pragma unroll
-  for (int u = 0; u < kHeadDim / 8; ++u) pr[u] = row[u];
+  for (int u = 0; u < 8; ++u) pr[u] = row[u];
   float m = -INFINITY, l = 0.f;
   if (tid < n_splits) {
     const float2 ml = *(const float2 *)(ph + (size_t)tid * kPartStride);
@@ -681,7 +684,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
   float av[kMergeRegs];
 #pragma unroll
   for (int u = 0; u < kMergeRegs; ++u) {
-    const int sp = par + 2 * u;
+    const int sp = par + 4 * u;
     av[u] = pv[(size_t)(sp < n_splits ? sp : 0) * kPartStride];
   }
   const float wm = wave_max(m);
@@ -704,25 +707,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
     float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < kMergeRegs; ++u) {
-      const int sp = par + 2 * u;
+      const int sp = par + 4 * u;
       if (sp < n_splits) acc = fmaf(wsm[sp], av[u], acc);
     }
-    for (int sp = par + 2 * kMergeRegs; sp < n_splits; sp += 2) acc = fmaf(wsm[sp], pv[(size_t)sp * kPartStride], acc);
+    for (int sp = par + 4 * kMergeRegs; sp < n_splits; sp += 4) acc = fmaf(wsm[sp], pv[(size_t)sp * kPartStride], acc);
     ys[par * kHeadDim + i] = acc;
   }
   __syncthreads();
-  const float4 *y0 = (const float4 *)(ys + kh), *y1 = (const float4 *)(ys + kHeadDim + kh);
   float o = 0.f;
 #pragma unroll
-  for (int u = 0; u < kHeadDim / 8; ++u) {
-    const float4 a0 = y0[u], a1 = y1[u];
-    o = fmaf(pr[u].x, a0.x + a1.x, o);
-    o = fmaf(pr[u].y, a0.y + a1.y, o);
-    o = fmaf(pr[u].z, a0.z + a1.z, o);
-    o = fmaf(pr[u].w, a0.w + a1.w, o);
+  for (int u = 0; u < 8; ++u) {
+    const int k = 32 * kq + 4 * u;
+    const float y0 = ys[k] + ys[kHeadDim + k] + ys[2 * kHeadDim + k] + ys[3 * kHeadDim + k];
+    const float y1 = ys[k + 1] + ys[kHeadDim + k + 1] + ys[2 * kHeadDim + k + 1] + ys[3 * kHeadDim + k + 1];
+    const float y2 = ys[k + 2] + ys[kHeadDim + k + 2] + ys[2 * kHeadDim + k + 2] + ys[3 * kHeadDim + k + 2];
+    const float y3 = ys[k + 3] + ys[kHeadDim + k + 3] + ys[2 * kHeadDim + k + 3] + ys[3 * kHeadDim + k + 3];
+    o = fmaf(pr[u].x, y0, o);
+    o = fmaf(pr[u].y, y1, o);
+    o = fmaf(pr[u].z, y2, o);
+    o = fmaf(pr[u].w, y3, o);
   }
   o += __shfl_xor(o, 1);
-  if ((tid & 1) == 0) out[((size_t)b * hq + hqi) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
+  o += __shfl_xor(o, 2);
+  if (kq == 0) out[((size_t)b * hq + hqi) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
 }
 
 // ------------------------------------------------------------------ host
@@ -828,6 +835,7 @@ PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, voi
   pa.out = (uint8_t *)workspace + lay.prep_off;
   pa.off_kvh = p.hdr.off_kvh;
   pa.off_build = p.hdr.off_build;
+  pa.off_rot32 = p.hdr.off_rot32_k;
   pa.stride = lay.prep_stride;
   pa.hkv = p.desc.n_kv_heads;
   pa.hq = p.desc.n_q_heads;

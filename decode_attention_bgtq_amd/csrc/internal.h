@@ -39,7 +39,7 @@ struct KGroupDesc {
   int32_t pos;      // first position in group order
   int32_t bit_off;  // first bit in the key stream
   int64_t rot64;    // element offset of Pi^T (double, [k][i]) in the K double-rotation area
-  int64_t rot32;    // element offset of Pi (float, [i][k]) in the K float-rotation area
+  int64_t rot32;    // unused (the float rotations are one block-diagonal matrix per head)
 };
 
 struct KvhDesc {
@@ -70,7 +70,7 @@ struct ConstHeader {
   int64_t off_lookup;        // uint32 [total chunks]
   int64_t off_build;         // uint32 [total chunks]
   int64_t off_rot64_k;       // double area (Pi^T per K group)
-  int64_t off_rot32_k;       // float area (Pi per K group)
+  int64_t off_rot32_k;       // float [n_kv_heads][128][128]: block-diagonal R, R[pos_g + i][pos_g + k] = Pi_g[i][k]
   int64_t off_rot64_v;       // double [n_kv_heads][128][128], Pi_V^T ([k][i])
   int64_t off_rot32_v;       // float [n_kv_heads][128][128], Pi_V^T ([j][k] = Pi_V[k][j])
   int64_t off_c4;            // float2 [256]: (c4[b & 15], c4[b >> 4]), 4-bit centroid pairs of a code byte

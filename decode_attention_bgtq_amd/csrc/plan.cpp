@@ -388,7 +388,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   hd.off_rot64_k = off;
   off = align256(off + 8 * (size_t)rot64_k);
   hd.off_rot32_k = off;
-  off = align256(off + 4 * (size_t)rot32_k);
+  off = align256(off + 4 * (size_t)hkv * kHeadDim * kHeadDim);
   hd.off_rot64_v = off;
   off = align256(off + 8 * (size_t)hkv * kHeadDim * kHeadDim);
   hd.off_rot32_v = off;
@@ -417,7 +417,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
       for (int i = 0; i < g.d; ++i)
         for (int k = 0; k < g.d; ++k) {
           r64k[g.rot64 + (int64_t)k * g.d + i] = pi[(size_t)i * g.d + k];
-          r32k[g.rot32 + (int64_t)i * g.d + k] = (float)pi[(size_t)i * g.d + k];
+          r32k[((size_t)h * kHeadDim + g.pos + i) * kHeadDim + g.pos + k] = (float)pi[(size_t)i * g.d + k];
         }
     }
   float *c4 = (float *)(img + hd.off_c4);

@@ -14,48 +14,46 @@ constexpr int kPrepThreads = 64 * kPrepWaves;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-// q_rot[h][pos_g + i] = sum_k Pi_g[i][k] q[h][coord_g[k]] for the key groups of
-// one KV head.  qg [8][128]: the queries gathered into group order
-// (qg[h][pos_g + k] = q[h][coord_g[k]]), rows h >= G zero.  qs [G][128]: the
-// rotated queries in group order.  16x16x4 fp32 MFMA tiles with the query
-// heads as columns; the (group, 16-row tile) pairs of all groups are spread
-// over the `waves` waves, and each wave issues every operand load of a tile
-// before its first MFMA (clamped addresses, zero-masked values).
-__device__ __forceinline__ void rotate_queries(const ConstHeader *hd, const KvhDesc *kd, int G,
-                                               const float *qg, float *qs, int wave, int waves,
-                                               int lane) {
+// q_rot[h][p] = sum_k R[p][k] qg[h][k]: the rotation of every key width group
+// at once, R being the head's block-diagonal matrix of the group rotations
+// (rows and columns in group order, zero outside the blocks and past d_nz).
+// qg [8][128]: the queries in group order, rows h >= G zero; qs [G][128].
+// 16x16x4 fp32 MFMA tiles, the query heads as columns; the 8 row tiles of 16
+// are spread over the WAVES waves (8 / WAVES tiles each).  The operand rows of R are fetched by
+// rot_rows (addresses independent of the descriptor), the MFMAs run in
+// rot_tiles.
+template <int WAVES>
+struct RotRows {
+  static constexpr int nt = 8 / WAVES;  // row tiles per wave
+  float a[nt][kHeadDim / 4];
+};
+
+template <int WAVES>
+__device__ __forceinline__ void rot_rows(const float *R, int wave, int lane, RotRows<WAVES> &rr) {
   const int n = lane & 15, kq = lane >> 4;
-  int ng = kd->n_groups, tiles[kMaxGroups + 1];
-  tiles[0] = 0;
-  for (int gi = 0; gi < kMaxGroups; ++gi) tiles[gi + 1] = tiles[gi] + (gi < ng ? (kd->g[gi].d + 15) >> 4 : 0);
-  for (int t = wave; t < tiles[kMaxGroups]; t += waves) {
-    int gi = 0;
-    while (t >= tiles[gi + 1]) ++gi;
-    const int d = kd->g[gi].d, pos = kd->g[gi].pos;
-    const float *pi = (const float *)((const uint8_t *)hd + hd->off_rot32_k) + kd->g[gi].rot32;
-    const int ia = 16 * (t - tiles[gi]) + n;
-    const int ic = ia < d ? ia : d - 1;
-    float a[kHeadDim / 4];
 #pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) {
-      const int kk = 4 * s + kq;
-      a[s] = pi[(size_t)ic * d + (kk < d ? kk : d - 1)];
-    }
-    f4v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) {
+    const int t = wave + t2 * WAVES;
 #pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) {
-      const int kk = 4 * s + kq;
-      if (4 * s < d) {  // wave-uniform
-        const float av = (ia < d && kk < d) ? a[s] : 0.f;
-        const float bq = qg[(n & 7) * kHeadDim + pos + (kk < d ? kk : d - 1)];
-        const float bv = kk < d ? bq : 0.f;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-      }
-    }
+    for (int s = 0; s < kHeadDim / 4; ++s) rr.a[t2][s] = R[(16 * t + n) * kHeadDim + 4 * s + kq];
+  }
+}
+
+template <int WAVES>
+__device__ __forceinline__ void rot_tiles(const RotRows<WAVES> &rr, int G, const float *qg, float *qs, int wave,
+                                          int lane) {
+  const int n = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ia - n + 4 * kq + r;
-      if (i < d && n < G) qs[n * kHeadDim + pos + i] = acc[r];
+  for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) {
+    const int t = wave + t2 * WAVES;
+    {
+      f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kHeadDim / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rr.a[t2][s], qg[(n & 7) * kHeadDim + 4 * s + kq], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n < G) qs[n * kHeadDim + 16 * t + 4 * kq + r] = acc[r];
     }
   }
 }
@@ -77,7 +75,7 @@ struct PrepArgs {
   const uint8_t *consts;
   const uint16_t *q;
   uint8_t *out;
-  int64_t off_kvh, off_build, stride;
+  int64_t off_kvh, off_build, off_rot32, stride;
   int hkv, hq, win, table_bytes, chunks_per_wg;
   float kscale;
 };
@@ -106,15 +104,24 @@ __device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b, int
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t *out = a.out + ((size_t)b * a.hkv + kvh) * (size_t)a.stride;
-  // ---- round 1: descriptor, queries (natural order, in the rotated-query area), centroids, build words
-  {
-    const uint32_t *src = (const uint32_t *)((const KvhDesc *)(consts + a.off_kvh) + kvh);
-    for (int i = tid; i < (int)(sizeof(KvhDesc) / 4); i += kPrepThreads) ((uint32_t *)&kds)[i] = src[i];
-    const uint16_t *qb = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim;
-    for (int i = tid; i < G * kHeadDim; i += kPrepThreads) qs[i] = h2f(qb[i]);
-    if (tid < 64) cs[tid] = (float)hd->cent[tid >> 4][tid & 15];
-    if (tid < kMaxChunks) bld[tid] = ((const uint32_t *)(consts + a.off_build))[kvh * kMaxChunks + tid];
-  }
+  // ---- one round of loads: descriptor, queries (natural order, in the
+  // rotated-query area), centroids and build words first, then the rotation
+  // rows (fixed addresses), so that staging the former waits for them only.
+  constexpr int kDescWords = (int)(sizeof(KvhDesc) / 4);
+  static_assert(kDescWords <= kPrepThreads && G * kHeadDim <= 2 * kPrepThreads, "one pass of staging loads");
+  const uint32_t dw = ((const uint32_t *)((const KvhDesc *)(consts + a.off_kvh) + kvh))[min(tid, kDescWords - 1)];
+  const uint16_t *qb = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim;
+  const uint16_t q0 = qb[min(tid, G * kHeadDim - 1)];
+  const uint16_t q1 = qb[min(tid + kPrepThreads, G * kHeadDim - 1)];
+  const float c0 = (float)hd->cent[(tid >> 4) & 3][tid & 15];
+  const uint32_t bw0 = ((const uint32_t *)(consts + a.off_build))[kvh * kMaxChunks + (tid & (kMaxChunks - 1))];
+  RotRows<kPrepWaves> rr;
+  rot_rows<kPrepWaves>((const float *)(consts + a.off_rot32) + (size_t)kvh * kHeadDim * kHeadDim, wave, lane, rr);
+  if (tid < kDescWords) ((uint32_t *)&kds)[tid] = dw;
+  if (tid < G * kHeadDim) qs[tid] = h2f(q0);
+  if (tid + kPrepThreads < G * kHeadDim) qs[tid + kPrepThreads] = h2f(q1);
+  if (tid < 64) cs[tid] = c0;
+  if (tid < kMaxChunks) bld[tid] = bw0;
   __syncthreads();
   const int nch = kds.n_chunks, d4 = kds.d4, dnz = kds.d_nz;
   if (tid < kds.n_groups) cs[64 + tid] = a.kscale / sqrtf((float)kds.g[tid].d);
@@ -129,8 +136,7 @@ __device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b, int
     }
   }
   __syncthreads();
-  // ---- round 2: rotation rows
-  rotate_queries(hd, &kds, G, qg, qs, wave, kPrepWaves, lane);
+  rot_tiles<kPrepWaves>(rr, G, qg, qs, wave, lane);
   __syncthreads();
   // per head: sum of |q_rot| over the table groups, one wave per head, fixed order
   for (int h = wave; h < G; h += kPrepWaves) {
