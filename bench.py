@@ -287,8 +287,9 @@ def main() -> int:
     step_ms = sum(round_ms) / len(round_ms)
     serve_ms = sum(timed_round(serve, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
     # Stream-kernel duration: the same decode calls once more with the library's HIP events
-    # around every cache-streaming launch (on the launch stream); kept out of the timings
-    # above because each event record adds a queue packet.
+    # bound to every cache-streaming launch (hipExtLaunchKernel on the launch stream, so the
+    # elapsed time is the kernel's own start-to-end time); a pass of its own because event
+    # timing can slow the dispatch of the launches around it.
     bg.profile_enable(True)
     bg.profile_read()
     for r in range(rounds):

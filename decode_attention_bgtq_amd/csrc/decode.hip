@@ -17,6 +17,8 @@
 //          one partial (m, l, acc) per split and query head.
 //  merge   one workgroup per (sequence, KV head): log-sum-exp merge of the
 //          splits, normalisation, un-rotation by Pi_V^T, fp16 output.
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "host.h"
 #include "prep.h"
@@ -76,7 +78,6 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 // DPP read.
 #define BGTQ_DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
 #define BGTQ_FM(A, S, B, K) "v_fmac_f32_dpp %" #A ", %" #S ", %" #B " row_newbcast:%" #K BGTQ_DPP
-#define BGTQ_D2(A, S, B, K) "v_dot2c_f32_f16_dpp %" #A ", %" #S ", %" #B " row_newbcast:%" #K BGTQ_DPP
 
 // a[h] += src[h](lane K) * b0 + src[h](lane K + 1) * b1, for the G heads
 template <int G, int K>
@@ -100,30 +101,6 @@ __device__ __forceinline__ void fmac_bcast(float (&a)[G], const float (&src)[G],
   }
 }
 
-// a0[h] += <src[h](lane K), c0>, a1[h] += <src[h](lane K), c1> (fp16 pairs, fp32 accumulate)
-template <int G, int K>
-__device__ __forceinline__ void dot2_bcast(float (&a0)[G], float (&a1)[G], const uint32_t (&src)[G], uint32_t c0,
-                                           uint32_t c1) {
-  static_assert(K >= 0 && K < 16, "row lane");
-  if constexpr (G == 1) {
-    asm("s_nop 1\n\t" BGTQ_D2(0, 2, 3, 5) BGTQ_D2(1, 2, 4, 5)
-        : "+v"(a0[0]), "+v"(a1[0]) : "v"(src[0]), "v"(c0), "v"(c1), "n"(K));
-  } else if constexpr (G == 2) {
-    asm("s_nop 1\n\t" BGTQ_D2(0, 4, 6, 8) BGTQ_D2(1, 4, 7, 8) BGTQ_D2(2, 5, 6, 8) BGTQ_D2(3, 5, 7, 8)
-        : "+v"(a0[0]), "+v"(a1[0]), "+v"(a0[1]), "+v"(a1[1]) : "v"(src[0]), "v"(src[1]), "v"(c0), "v"(c1),
-          "n"(K));
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; g += 4) {
-      asm("s_nop 1\n\t" BGTQ_D2(0, 8, 12, 14) BGTQ_D2(1, 8, 13, 14) BGTQ_D2(2, 9, 12, 14) BGTQ_D2(3, 9, 13, 14)
-              BGTQ_D2(4, 10, 12, 14) BGTQ_D2(5, 10, 13, 14) BGTQ_D2(6, 11, 12, 14) BGTQ_D2(7, 11, 13, 14)
-          : "+v"(a0[g]), "+v"(a1[g]), "+v"(a0[g + 1]), "+v"(a1[g + 1]), "+v"(a0[g + 2]), "+v"(a1[g + 2]),
-            "+v"(a0[g + 3]), "+v"(a1[g + 3])
-          : "v"(src[g]), "v"(src[g + 1]), "v"(src[g + 2]), "v"(src[g + 3]), "v"(c0), "v"(c1), "n"(K));
-    }
-  }
-}
-#undef BGTQ_D2
 #undef BGTQ_FM
 #undef BGTQ_DPP
 
@@ -136,6 +113,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 //   [0, 2048)      4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32
 //   [2048, +G 512) 4-bit group queries: G x 128 fp32, scaled, zero past d4
 //   [.., +vlut)    value table
+//   [pt, ..)       per wave: the tile's softmax weights x value norm, fp16 [G][64]
 //   [tab0, ..)     key tables of the width-1..3 chunks, fp16 entry per query head
 // After the tile loop the whole area is reused for the wave merge.
 template <int G, int VB>
@@ -143,7 +121,8 @@ struct StreamLds {
   static constexpr int c4 = 0;
   static constexpr int q4 = 2048;
   static constexpr int vlut = q4 + G * kHeadDim * 4;
-  static constexpr int tab0 = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
+  static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
+  static constexpr int tab0 = pt + kStreamWaves * G * kTile * 2;
   static constexpr int merge = kStreamWaves * G * kPartStride * 4;
   static constexpr int total(int table_bytes) { return tab0 + table_bytes > merge ? tab0 + table_bytes : merge; }
 };
@@ -211,6 +190,7 @@ struct StreamState {
   uint32_t av;        // lane jj: first chunk anchored at key word jj-1
   uint32_t fmask;     // window mask shifted to the entry offset (held in a VGPR)
   uint32_t cgrp, jrng;  // chunk boundaries and word-slot ranges of the width-3, 2, 1 groups
+  uint32_t ptw;  // LDS byte offset of this wave's weight rows
   int wk, n4w;
   int64_t seq;
 };
@@ -379,64 +359,70 @@ __device__ __forceinline__ void wave_max_heads(float (&v)[G]) {
 #undef BGTQ_MX4
 #undef BGTQ_MX
 
-// Value accumulation for token pair J (0..31) from the row-replicated P'
-// registers: acc0/acc1[h] += <P'_h pair J, centroid pair of coordinate lane / lane + 64>.
-template <int G, int J>
-__device__ __forceinline__ void v_pair(const uint32_t (&pr)[2][G], uint32_t c0, uint32_t c1, float (&acc0)[G],
-                                       float (&acc1)[G]) {
-  dot2_bcast<G, J & 15>(acc0, acc1, pr[J >> 4], c0, c1);
+// Value accumulation on the matrix cores: per tile, acc[h][i] += sum_t P'[h][t] v[t][i]
+// with P' = softmax weight x value norm (fp16) and v the fp16 centroids of the
+// lane's coordinate i, as 16 steps of v_mfma_f32_4x4x4f16 (16 blocks of 4 x 4,
+// K = 4 tokens).  Block k of a step is lanes 4k .. 4k + 3: its B operand is the
+// four tokens of coordinate (lane) and its output row m is head m, so lane i
+// keeps acc[h][i] in register h.  The A operand (P' of tokens 4S .. 4S + 3) is
+// broadcast from block S (CBSZ 4, ABID S), whose lane 4S + m holds head m.
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+template <int G>
+struct VQuads {
+  static constexpr int v = (G + 3) / 4;  // accumulator registers of 4 heads
+};
+
+template <int BIT, int N>
+__device__ __forceinline__ uint32_t bits6(const uint32_t (&c)[N]) {
+  constexpr int wi = BIT >> 5, sh = BIT & 31;
+  if constexpr (sh <= 26)
+    return (c[wi] >> sh) & 63u;
+  else
+    return __builtin_amdgcn_alignbit(c[wi + 1], c[wi], sh) & 63u;
 }
 
-template <int G, int VB, int Y>
-__device__ __forceinline__ void v_step(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
-                                       const uint32_t (&pr)[2][G], float (&acc0)[G], float (&acc1)[G]) {
-  if constexpr (VB == 3) {  // Y = token pair, 6 bits per coordinate
-    constexpr int bit = 6 * Y, wi = bit >> 5, sh = bit & 31;
-    uint32_t s0, s1;
-    if constexpr (sh <= 26) {
-      s0 = (va[wi] >> sh) & 63u;
-      s1 = (vb[wi] >> sh) & 63u;
-    } else {
-      s0 = __builtin_amdgcn_alignbit(va[wi + 1], va[wi], sh) & 63u;
-      s1 = __builtin_amdgcn_alignbit(vb[wi + 1], vb[wi], sh) & 63u;
-    }
-    v_pair<G, Y>(pr, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
-  } else if constexpr (VB == 4) {  // Y = token pair, one byte
-    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    v_pair<G, Y>(pr, lds_at<uint32_t>(vlut + 4 * s0), lds_at<uint32_t>(vlut + 4 * s1), acc0, acc1);
-  } else if constexpr (VB == 2) {  // Y = byte: token pairs 2Y, 2Y + 1
-    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    const uint2 e0 = lds_at<uint2>(vlut + 8 * s0), e1 = lds_at<uint2>(vlut + 8 * s1);
-    v_pair<G, 2 * Y>(pr, e0.x, e1.x, acc0, acc1);
-    v_pair<G, 2 * Y + 1>(pr, e0.y, e1.y, acc0, acc1);
-  } else {  // VB == 1, Y = byte: token pairs 4Y .. 4Y + 3
-    const uint32_t s0 = (va[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    const uint32_t s1 = (vb[Y >> 2] >> (8 * (Y & 3))) & 255u;
-    const uint4 e0 = lds_at<uint4>(vlut + 16 * s0), e1 = lds_at<uint4>(vlut + 16 * s1);
-    v_pair<G, 4 * Y + 0>(pr, e0.x, e1.x, acc0, acc1);
-    v_pair<G, 4 * Y + 1>(pr, e0.y, e1.y, acc0, acc1);
-    v_pair<G, 4 * Y + 2>(pr, e0.z, e1.z, acc0, acc1);
-    v_pair<G, 4 * Y + 3>(pr, e0.w, e1.w, acc0, acc1);
+// B operand of step S: the fp16 centroids of tokens 4S .. 4S + 3 (bits 4 VB S ..
+// 4 VB (S + 1) of the coordinate's code stream) from the value table.
+template <int VB, int S>
+__device__ __forceinline__ h4v v_operand(const uint32_t (&c)[2 * VB], uint32_t vlut) {
+  if constexpr (VB == 1) {  // entry = one byte (8 tokens) x 16 bytes
+    const uint32_t y = (c[S >> 3] >> (8 * ((S >> 1) & 3))) & 255u;
+    return lds_at<h4v>(vlut + 16 * y + 8 * (S & 1));
+  } else if constexpr (VB == 2) {  // entry = one byte (4 tokens) x 8 bytes
+    const uint32_t y = (c[S >> 2] >> (8 * (S & 3))) & 255u;
+    return lds_at<h4v>(vlut + 8 * y);
+  } else if constexpr (VB == 3) {  // entry = 6 bits (2 tokens) x 4 bytes
+    const uint32_t y0 = bits6<12 * S>(c), y1 = bits6<12 * S + 6>(c);
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(vlut + 4 * y0), lds_at<uint32_t>(vlut + 4 * y1)});
+  } else {  // entry = one byte (2 tokens) x 4 bytes
+    const uint32_t w = c[S >> 1] >> (16 * (S & 1));
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(vlut + 4 * (w & 255u)),
+                                         lds_at<uint32_t>(vlut + 4 * ((w >> 8) & 255u))});
   }
 }
 
-template <int G, int VB, int Y>
-__device__ __forceinline__ void v_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
-                                        const uint32_t (&pr)[2][G], float (&acc0)[G], float (&acc1)[G]) {
-  constexpr int n = VB == 3 || VB == 4 ? 32 : VB == 2 ? 16 : 8;
-  if constexpr (Y < n) {
-    v_step<G, VB, Y>(va, vb, vlut, pr, acc0, acc1);
-    if constexpr ((Y & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the lookups in flight
-    v_steps<G, VB, Y + 1>(va, vb, vlut, pr, acc0, acc1);
+template <int G, int VB, int S>
+__device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+                                             const h4v (&pa)[VQuads<G>::v], f4v (&acc0)[VQuads<G>::v],
+                                             f4v (&acc1)[VQuads<G>::v]) {
+  if constexpr (S < kTile / 4) {
+    const h4v b0 = v_operand<VB, S>(va, vlut), b1 = v_operand<VB, S>(vb, vlut);
+#pragma unroll
+    for (int g = 0; g < VQuads<G>::v; ++g) {
+      acc0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b0, acc0[g], 4, S, 0);
+      acc1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b1, acc1[g], 4, S, 0);
+    }
+    constexpr int kBatch = VB <= 2 ? 4 : 2;  // steps whose lookups may be in flight together
+    if constexpr (S % kBatch == kBatch - 1) __builtin_amdgcn_sched_barrier(0);
+    v_mfma_steps<G, VB, S + 1>(va, vb, vlut, pa, acc0, acc1);
   }
 }
 
 template <int G, int VB, int WK>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
                                              const float (&rinv)[G], float (&mrun)[G], float (&lsum)[G],
-                                             float (&acc0)[G], float (&acc1)[G], int lane) {
+                                             f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v], int lane) {
   // ---- keys, lane = token.  4-bit group: direct centroid sums.
   float a4[G], lr[G];
 #pragma unroll
@@ -449,7 +435,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   const bool valid = (int64_t)tile * kTile + lane < st.seq;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
-  // ---- online softmax (log2 domain); P' = p * value norm as fp16 token pairs
+  // ---- online softmax (log2 domain); P' = p * value norm, fp16, to the wave's
+  // LDS rows [h][token]
   float l[G], mx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -458,7 +445,6 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   }
   wave_max_heads<G>(mx);
   float alpha[G];
-  uint32_t pr[2][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float mn = fmaxf(mrun[h], mx[h]);
@@ -466,20 +452,21 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
     const float p = __builtin_amdgcn_exp2f(l[h] - mn);
     lsum[h] = fmaf(lsum[h], alpha[h], p);
     mrun[h] = mn;
-    const uint32_t mine = __builtin_bit_cast(uint16_t, (_Float16)(p * nv));
-    const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);  // lane ^ 1
-    const uint32_t pair = mine | (nb << 16);  // lane 2k: tokens 2k, 2k + 1
-    // row-replicated: lane l of register half t holds pair 16 t + l % 16
-    pr[0][h] = (uint32_t)__builtin_amdgcn_ds_bpermute((lane & 15) << 3, (int)pair);
-    pr[1][h] = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane & 15) + 16) << 3, (int)pair);
+    *(__attribute__((address_space(3))) _Float16 *)(size_t)(st.ptw + h * (2 * kTile) + 2 * lane) = (_Float16)(p * nv);
   }
+  // A operands: lane 4k + m holds head m's weights of tokens 4k .. 4k + 3 (heads
+  // past G repeat a valid row; their output rows are never read)
+  h4v pa[VQuads<G>::v];
+#pragma unroll
+  for (int g = 0; g < VQuads<G>::v; ++g)
+    pa[g] = lds_at<h4v>(st.ptw + ((4 * g + (lane & 3)) & (G - 1)) * (2 * kTile) + (lane >> 2) * 8);
   // ---- values: lane = coordinates lane and lane + 64
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    acc0[h] *= alpha[h];
-    acc1[h] *= alpha[h];
+    acc0[h >> 2][h & 3] *= alpha[h];
+    acc1[h >> 2][h & 3] *= alpha[h];
   }
-  v_steps<G, VB, 0>(r.va, r.vb, (uint32_t)StreamLds<G, VB>::vlut, pr, acc0, acc1);
+  v_mfma_steps<G, VB, 0>(r.va, r.vb, (uint32_t)StreamLds<G, VB>::vlut, pa, acc0, acc1);
 }
 
 // Waves per SIMD the register allocation aims at: four (two workgroups per CU,
@@ -522,7 +509,6 @@ void decode_stream_kernel(const StreamArgs a) {
   constexpr int L = GLog<G>::v;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint8_t *consts = a.consts;
-  const ConstHeader *hd = hdr_of(consts);
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -591,6 +577,7 @@ void decode_stream_kernel(const StreamArgs a) {
     st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
     st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
     st.wk = a.wk;
+    st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
     st.n4w = kd->n4w;
     st.cgrp = kd->cgrp;
     st.jrng = kd->jrng;
@@ -599,9 +586,12 @@ void decode_stream_kernel(const StreamArgs a) {
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
-  float mrun[G], lsum[G], acc0[G], acc1[G];
+  float mrun[G], lsum[G];
+  f4v acc0[VQuads<G>::v], acc1[VQuads<G>::v];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f, acc0[h] = 0.f, acc1[h] = 0.f;
+  for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f;
+#pragma unroll
+  for (int g = 0; g < VQuads<G>::v; ++g) acc0[g] = (f4v){0.f, 0.f, 0.f, 0.f}, acc1[g] = acc0[g];
   if (tile < tile_hi) {
     for (;;) {
       load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
@@ -624,8 +614,8 @@ void decode_stream_kernel(const StreamArgs a) {
   for (int h = 0; h < G; ++h) {
     float *rr = mrg + (wave * G + h) * kPartStride;
     if (lane == 0) rr[0] = mrun[h], rr[1] = lsum[h];
-    rr[4 + lane] = acc0[h];
-    rr[4 + 64 + lane] = acc1[h];
+    rr[4 + lane] = acc0[h >> 2][h & 3];
+    rr[4 + 64 + lane] = acc1[h >> 2][h & 3];
   }
   __syncthreads();
   for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
@@ -917,11 +907,14 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
   sa.table_bytes = table_bytes;
   sa.seq_add = c.seq_add;
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
-  if (e0) (void)hipEventRecord(e0, st);
-  fn<<<grid, kStreamThreads, smem, st>>>(sa);
+  // With profiling on, the events are bound to the launch itself, so their elapsed time is the
+  // kernel's own start-to-end time (no queue packets of their own between the kernels).
+  if (e0)
+    hipExtLaunchKernelGGL(fn, grid, dim3(kStreamThreads), (uint32_t)smem, st, e0, e1, 0, sa);
+  else
+    fn<<<grid, kStreamThreads, smem, st>>>(sa);
   bgtq_status s = launch_status("decode (stream)");
   if (e1) {
-    (void)hipEventRecord(e1, st);
     Prof &pr = prof();
     std::lock_guard<std::mutex> lk(pr.mu);
     pr.pending.emplace_back(e0, e1);
