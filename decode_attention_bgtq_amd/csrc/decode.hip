@@ -71,39 +71,6 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 
 // ------------------------------------------------------------------ stream
 
-// Cross-lane broadcast multiply-adds (inline VALU, no memory access).  The
-// broadcast operand is read through DPP row_newbcast:K, i.e. from lane K of
-// the reading lane's 16-lane row.  Each block starts with two wait states so
-// that a VALU write of a broadcast source just before it is visible to the
-// DPP read.
-#define BGTQ_DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-#define BGTQ_FM(A, S, B, K) "v_fmac_f32_dpp %" #A ", %" #S ", %" #B " row_newbcast:%" #K BGTQ_DPP
-
-// a[h] += src[h](lane K) * b0 + src[h](lane K + 1) * b1, for the G heads
-template <int G, int K>
-__device__ __forceinline__ void fmac_bcast(float (&a)[G], const float (&src)[G], float b0, float b1) {
-  static_assert(K >= 0 && K + 1 < 16, "row lane");
-  if constexpr (G == 1) {
-    asm("s_nop 1\n\t" BGTQ_FM(0, 1, 2, 4) BGTQ_FM(0, 1, 3, 5)
-        : "+v"(a[0]) : "v"(src[0]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
-  } else if constexpr (G == 2) {
-    asm("s_nop 1\n\t" BGTQ_FM(0, 2, 4, 6) BGTQ_FM(1, 3, 4, 6) BGTQ_FM(0, 2, 5, 7) BGTQ_FM(1, 3, 5, 7)
-        : "+v"(a[0]), "+v"(a[1]) : "v"(src[0]), "v"(src[1]), "v"(b0), "v"(b1), "n"(K), "n"(K + 1));
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; g += 4) {
-      asm("s_nop 1\n\t" BGTQ_FM(0, 4, 8, 10) BGTQ_FM(1, 5, 8, 10) BGTQ_FM(2, 6, 8, 10) BGTQ_FM(3, 7, 8, 10)
-              BGTQ_FM(0, 4, 9, 11) BGTQ_FM(1, 5, 9, 11) BGTQ_FM(2, 6, 9, 11) BGTQ_FM(3, 7, 9, 11)
-          : "+v"(a[g]), "+v"(a[g + 1]), "+v"(a[g + 2]), "+v"(a[g + 3])
-          : "v"(src[g]), "v"(src[g + 1]), "v"(src[g + 2]), "v"(src[g + 3]), "v"(b0), "v"(b1), "n"(K),
-            "n"(K + 1));
-    }
-  }
-}
-
-#undef BGTQ_FM
-#undef BGTQ_DPP
-
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
@@ -256,34 +223,50 @@ __device__ __forceinline__ void key_chunk2(uint32_t d0, uint32_t d1, uint32_t hi
   }
 }
 
-// 4-bit group, key word J (codes 8 J .. 8 J + 7; lanes K0 .. K0 + 7 of the
-// block's query registers): lane = token, a4[h] += sum_r q4[h][r] * c4[code_r]
-// over the code pairs of the word's bytes (centroid pairs at LDS byte 8 * byte).
-template <int G, int WK, int J, int K0>
-__device__ __forceinline__ void key4_word(const uint32_t (&w)[WK], const float (&qr)[G], float (&a4)[G]) {
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+template <int G>
+struct VQuads {
+  static constexpr int v = (G + 3) / 4;  // matrix-core registers of 4 query heads
+};
+
+// 4-bit group on the matrix cores, one v_mfma_f32_4x4x1f32 per code r (16 blocks
+// of 4 x 4 x 1): block k is lanes 4k .. 4k + 3 = tokens 4k .. 4k + 3, its B operand
+// the token's centroid c4[code_r] (centroid pairs at LDS byte 8 x code byte) and
+// its output row m head m, so the token's lane keeps a4[h] in register h.  The A
+// operand, head m's query value of code r, is broadcast from block r % 16 of a
+// register whose lane 4k + m holds code 16 (r / 16) + k (CBSZ 4, ABID r % 16).
+// Key word J holds codes 8 J .. 8 J + 7, two per byte (low nibble first).
+template <int G, int WK, int J>
+__device__ __forceinline__ void key4_word(const uint32_t (&w)[WK], const float (&qa)[VQuads<G>::v],
+                                          f4v (&a4)[VQuads<G>::v]) {
   const uint32_t word = w[J];
-#define BGTQ_K4(BY)                                                           \
-  {                                                                           \
-    const float2 cp = lds_at<float2>(((word >> (8 * BY)) & 255u) << 3);      \
-    fmac_bcast<G, K0 + 2 * BY>(a4, qr, cp.x, cp.y);                           \
+  constexpr int S0 = 8 * (J & 1);
+  float2 cp[4];  // all four lookups in flight before the first product
+#pragma unroll
+  for (int by = 0; by < 4; ++by) cp[by] = lds_at<float2>(((word >> (8 * by)) & 255u) << 3);
+  __builtin_amdgcn_sched_barrier(0);
+#define BGTQ_K4(BY)                                                                          \
+  _Pragma("unroll") for (int g = 0; g < VQuads<G>::v; ++g) {                                 \
+    a4[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[g], cp[BY].x, a4[g], 4, S0 + 2 * BY, 0);     \
+    a4[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[g], cp[BY].y, a4[g], 4, S0 + 2 * BY + 1, 0); \
   }
   BGTQ_K4(0) BGTQ_K4(1) BGTQ_K4(2) BGTQ_K4(3)
 #undef BGTQ_K4
 }
 
-// Blocks of 16 codes (two key words): the block's queries sit row-replicated
-// in one register per head (lane l holds code 16 BLK + l % 16) and are
-// broadcast per code by DPP.  Only the words that hold 4-bit codes are read.
+// Blocks of 16 codes (two key words); only the words that hold 4-bit codes are read.
 template <int G, int VB, int WK, int BLK>
-__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, int lane, float (&a4)[G]) {
+__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, int lane, f4v (&a4)[VQuads<G>::v]) {
   if constexpr (2 * BLK < WK) {
     if (2 * BLK < n4w) {
-      float qr[G];
+      float qa[VQuads<G>::v];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        qr[h] = lds_at<float>(StreamLds<G, VB>::q4 + (uint32_t)(h * kHeadDim + 16 * BLK + (lane & 15)) * 4);
-      key4_word<G, WK, 2 * BLK, 0>(w, qr, a4);
-      if (2 * BLK + 1 < n4w) key4_word<G, WK, 2 * BLK + 1, 8>(w, qr, a4);
+      for (int g = 0; g < VQuads<G>::v; ++g)
+        qa[g] = lds_at<float>(StreamLds<G, VB>::q4 +
+                              (uint32_t)(((4 * g + (lane & 3)) & (G - 1)) * kHeadDim + 16 * BLK + (lane >> 2)) * 4);
+      key4_word<G, WK, 2 * BLK>(w, qa, a4);
+      if (2 * BLK + 1 < n4w) key4_word<G, WK, 2 * BLK + 1>(w, qa, a4);
       key4_blocks<G, VB, WK, BLK + 1>(w, n4w, lane, a4);
     }
   }
@@ -366,13 +349,6 @@ __device__ __forceinline__ void wave_max_heads(float (&v)[G]) {
 // four tokens of coordinate (lane) and its output row m is head m, so lane i
 // keeps acc[h][i] in register h.  The A operand (P' of tokens 4S .. 4S + 3) is
 // broadcast from block S (CBSZ 4, ABID S), whose lane 4S + m holds head m.
-typedef _Float16 h4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-template <int G>
-struct VQuads {
-  static constexpr int v = (G + 3) / 4;  // accumulator registers of 4 heads
-};
-
 template <int BIT, int N>
 __device__ __forceinline__ uint32_t bits6(const uint32_t (&c)[N]) {
   constexpr int wi = BIT >> 5, sh = BIT & 31;
@@ -424,9 +400,12 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
                                              const float (&rinv)[G], float (&mrun)[G], float (&lsum)[G],
                                              f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v], int lane) {
   // ---- keys, lane = token.  4-bit group: direct centroid sums.
-  float a4[G], lr[G];
+  float lr[G];
+  f4v a4[VQuads<G>::v];
 #pragma unroll
-  for (int h = 0; h < G; ++h) a4[h] = 0.f, lr[h] = 0.f;
+  for (int h = 0; h < G; ++h) lr[h] = 0.f;
+#pragma unroll
+  for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
   key4_blocks<G, VB, WK, 0>(r.w, st.n4w, lane, a4);
   // widths 3, 2, 1: table chunks, norm slots 1, 2, 3
   key_group<G, VB, WK, 0>(r.w, st, r.nr.x >> 16, lr);
@@ -440,7 +419,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   float l[G], mx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] = valid ? fmaf(n4, a4[h], lr[h] * rinv[h]) : -INFINITY;
+    l[h] = valid ? fmaf(n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
     mx[h] = l[h];
   }
   wave_max_heads<G>(mx);
