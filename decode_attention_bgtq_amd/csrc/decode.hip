@@ -71,34 +71,34 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 
 // ------------------------------------------------------------------ stream
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
-}
-
-// LDS layout of the stream kernel (bytes; fixed offsets first, so that the
-// compiler folds them into the LDS instruction offsets):
-//   [0, 2048)      4-bit centroid pairs: 256 x (c[b & 15], c[b >> 4]) fp32
-//   [2048, +G 512) 4-bit group queries: G x 128 fp32, scaled, zero past d4
-//   [.., +vlut)    value table
-//   [pt, ..)       per wave: the tile's softmax weights x value norm, fp16 [G][64]
-//   [tab0, ..)     key tables of the width-1..3 chunks, fp16 entry per query head
-// After the tile loop the whole area is reused for the wave merge.
+// LDS layout of the stream kernel (bytes, fixed offsets that the compiler
+// folds into the LDS instruction offsets):
+//   [0, kDtabBytes)  decode tables of the plan: 4-bit centroid pairs (c4),
+//                    four fp16 centroids of a width-2 byte (t2) / width-1
+//                    nibble (t1), two of six width-3 bits (t3)
+//   [q4, +G 512)     4-bit group queries: G x 128 fp32, scaled, zero past d4
+//   [qr, ..)         k-step query operands of the width-1..3 groups (prep layout)
+//   [vlut, ..)       value table
+//   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
+// After the tile loop the area is reused for the wave merge.
 template <int G, int VB>
 struct StreamLds {
-  static constexpr int c4 = 0;
-  static constexpr int q4 = 2048;
-  static constexpr int vlut = q4 + G * kHeadDim * 4;
+  static constexpr int c4 = kDtabC4, t2 = kDtabT2, t1 = kDtabT1, t3 = kDtabT3;
+  static constexpr int q4 = kDtabBytes;
+  static constexpr int qr = q4 + PrepOut<G>::qr;
+  static constexpr int vlut = q4 + PrepOut<G>::rinv;
   static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
-  static constexpr int tab0 = pt + kStreamWaves * G * kTile * 2;
+  static constexpr int end = pt + kStreamWaves * G * kTile * 2;
   static constexpr int merge = kStreamWaves * G * kPartStride * 4;
-  static constexpr int total(int table_bytes) { return tab0 + table_bytes > merge ? tab0 + table_bytes : merge; }
+  static constexpr int total = end > merge ? end : merge;
+  static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0, "table bases above the index bits");
 };
 
 // Per (sequence, KV head) output of the prep kernel, read by every split of
-// the stream kernel: [key tables: table_bytes][4-bit queries: G x 128 fp32]
-// [1 / table factor: G fp32], 256-byte aligned.
-__host__ __device__ constexpr int64_t prep_stride(int G, int table_bytes) {
-  return ((int64_t)table_bytes + G * kHeadDim * 4 + G * 4 + 255) & ~(int64_t)255;
+// the stream kernel (PrepOut layout), 256-byte aligned.
+__host__ __device__ constexpr int64_t prep_stride_of(int G) {
+  const int nq = (G + 3) / 4;
+  return ((int64_t)G * kHeadDim * 4 + kMaxKSteps * nq * 32 + G * 4 + 255) & ~(int64_t)255;
 }
 
 template <int VB, int WK>
@@ -153,75 +153,14 @@ __device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *_
 }
 
 struct StreamState {
-  uint32_t dv0, dv1;  // lane l: lookup descriptor of chunk l (dv0) and l + 64 (dv1)
-  uint32_t av;        // lane jj: first chunk anchored at key word jj-1
-  uint32_t fmask;     // window mask shifted to the entry offset (held in a VGPR)
-  uint32_t cgrp, jrng;  // chunk boundaries and word-slot ranges of the width-3, 2, 1 groups
-  uint32_t ptw;  // LDS byte offset of this wave's weight rows
+  uint32_t dv0;       // lane c: descriptor of k-step c
+  uint32_t av;        // lane jj: first k-step anchored at key word jj-1
+  uint32_t laneoff;   // (lane & 3) * 8: this lane's query row inside a k-step operand
+  uint32_t cgrp, jrng;  // k-step boundaries and word-slot ranges of the width-3, 2, 1 groups
+  uint32_t ptw;       // LDS byte offset of this wave's weight rows
   int wk, n4w;
   int64_t seq;
 };
-
-// One table chunk (widths 1..3): funnel-shift the window out of (hi, lo), read
-// the fp16 entries of all heads at LDS byte tab0 + offset, accumulate
-// norm * entry with fp32 dot2.  nlo / nhi hold the group norm as the fp16
-// pair (n, 0) / (0, n).
-template <int G, int TAB0>
-__device__ __forceinline__ void key_chunk(uint32_t dsc, uint32_t hi, uint32_t lo, uint32_t fmask, uint32_t nlo,
-                                          uint32_t nhi, float (&lr)[G]) {
-  const uint32_t t = __builtin_amdgcn_alignbit(hi, lo, dsc);
-  const uint32_t a = ((t & fmask) | (dsc & kChunkTableMask)) + TAB0;
-  if constexpr (G == 1) {
-    const uint32_t e = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a;
-    lr[0] = dot2(e, nlo, lr[0]);
-  } else if constexpr (G == 2) {
-    const uint32_t e = lds_at<uint32_t>(a);
-    lr[0] = dot2(e, nlo, lr[0]);
-    lr[1] = dot2(e, nhi, lr[1]);
-  } else {
-#pragma unroll
-    for (int q4 = 0; q4 < G / 4; ++q4) {
-      const uint2 e = lds_at<uint2>(a + 8 * q4);
-      lr[4 * q4 + 0] = dot2(e.x, nlo, lr[4 * q4 + 0]);
-      lr[4 * q4 + 1] = dot2(e.x, nhi, lr[4 * q4 + 1]);
-      lr[4 * q4 + 2] = dot2(e.y, nlo, lr[4 * q4 + 2]);
-      lr[4 * q4 + 3] = dot2(e.y, nhi, lr[4 * q4 + 3]);
-    }
-  }
-}
-
-// Two table chunks of one group and key-word pair, both reads issued first.
-template <int G, int TAB0>
-__device__ __forceinline__ void key_chunk2(uint32_t d0, uint32_t d1, uint32_t hi, uint32_t lo, uint32_t fmask,
-                                           uint32_t nlo, uint32_t nhi, float (&lr)[G]) {
-  const uint32_t a0 = ((__builtin_amdgcn_alignbit(hi, lo, d0) & fmask) | (d0 & kChunkTableMask)) + TAB0;
-  const uint32_t a1 = ((__builtin_amdgcn_alignbit(hi, lo, d1) & fmask) | (d1 & kChunkTableMask)) + TAB0;
-  if constexpr (G == 1) {
-    const uint32_t e0 = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a0;
-    const uint32_t e1 = *(const __attribute__((address_space(3))) uint16_t *)(size_t)a1;
-    lr[0] = dot2(e0, nlo, lr[0]);
-    lr[0] = dot2(e1, nlo, lr[0]);
-  } else if constexpr (G == 2) {
-    const uint32_t e0 = lds_at<uint32_t>(a0), e1 = lds_at<uint32_t>(a1);
-    lr[0] = dot2(e0, nlo, lr[0]);
-    lr[1] = dot2(e0, nhi, lr[1]);
-    lr[0] = dot2(e1, nlo, lr[0]);
-    lr[1] = dot2(e1, nhi, lr[1]);
-  } else {
-#pragma unroll
-    for (int q4 = 0; q4 < G / 4; ++q4) {
-      const uint2 e0 = lds_at<uint2>(a0 + 8 * q4), e1 = lds_at<uint2>(a1 + 8 * q4);
-      lr[4 * q4 + 0] = dot2(e0.x, nlo, lr[4 * q4 + 0]);
-      lr[4 * q4 + 1] = dot2(e0.x, nhi, lr[4 * q4 + 1]);
-      lr[4 * q4 + 2] = dot2(e0.y, nlo, lr[4 * q4 + 2]);
-      lr[4 * q4 + 3] = dot2(e0.y, nhi, lr[4 * q4 + 3]);
-      lr[4 * q4 + 0] = dot2(e1.x, nlo, lr[4 * q4 + 0]);
-      lr[4 * q4 + 1] = dot2(e1.x, nhi, lr[4 * q4 + 1]);
-      lr[4 * q4 + 2] = dot2(e1.y, nlo, lr[4 * q4 + 2]);
-      lr[4 * q4 + 3] = dot2(e1.y, nhi, lr[4 * q4 + 3]);
-    }
-  }
-}
 
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
@@ -272,16 +211,40 @@ __device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, in
   }
 }
 
-// Chunks of one width group (rest group R = width 3 - R, norm slot R + 1),
-// grouped by the key word their window starts in.
+// Width-1..3 groups on the matrix cores: per k-step (four positions of one
+// group), v_mfma_f32_4x4x4f16 adds sum_i q[m][i] c[code_i] for every token.
+// Block k is lanes 4k .. 4k + 3 = tokens; its B operand is the token's four
+// fp16 centroids, looked up from the k-step's code bits (funnel-shifted out of
+// the key words hi:lo so that they start at bit kstep_bit(W)), and every block
+// takes the same A operand, head m's four scaled query values, from the LDS
+// operand row of the k-step (lane 4k + m reads row m).
+template <int G, int VB, int W>
+__device__ __forceinline__ h4v kstep_b(uint32_t dsc, uint32_t hi, uint32_t lo) {
+  typedef StreamLds<G, VB> Lds;
+  const uint32_t t = __builtin_amdgcn_alignbit(hi, lo, dsc);
+  if constexpr (W == 3)
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(Lds::t3 + (t & 0xFCu)),
+                                         lds_at<uint32_t>(Lds::t3 + ((t >> 6) & 0xFCu))});
+  else if constexpr (W == 2)
+    return lds_at<h4v>(Lds::t2 + (t & 0x7F8u));
+  else
+    return lds_at<h4v>(Lds::t1 + (t & 0x78u));
+}
+
+template <int G, int VB>
+__device__ __forceinline__ uint32_t kstep_a(uint32_t dsc, uint32_t laneoff) {
+  return (uint32_t)StreamLds<G, VB>::qr + ((dsc >> 5) & 63u) * (VQuads<G>::v * 32) + laneoff;
+}
+
+// K-steps of one width group (rest group R = width 3 - R), grouped by the key
+// word their window starts in; two k-steps per iteration with all their
+// lookups in flight.
 template <int G, int VB, int WK, int R>
-__device__ __forceinline__ void key_group(const uint32_t (&w)[WK], const StreamState &st, uint32_t nlo,
-                                          float (&lr)[G]) {
-  constexpr int TAB0 = StreamLds<G, VB>::tab0;
+__device__ __forceinline__ void key_group(const uint32_t (&w)[WK], const StreamState &st, f4v (&acc)[VQuads<G>::v]) {
+  constexpr int W = 3 - R, NQ = VQuads<G>::v;
   const int cb = (st.cgrp >> (8 * R)) & 255, ce = (st.cgrp >> (8 * R + 8)) & 255;
   if (cb >= ce) return;
   const int jl = (st.jrng >> (10 * R)) & 31, jh = (st.jrng >> (10 * R + 5)) & 31;
-  const uint32_t nhi = nlo << 16;
 #pragma unroll
   for (int jj = 0; jj <= WK; ++jj) {
     if (jj >= jl && jj <= jh) {
@@ -289,18 +252,29 @@ __device__ __forceinline__ void key_group(const uint32_t (&w)[WK], const StreamS
       const int a0 = __builtin_amdgcn_readlane((int)st.av, jj);
       const int a1 = __builtin_amdgcn_readlane((int)st.av, jj + 1);
       const int c0 = a0 > cb ? a0 : cb, c1 = a1 < ce ? a1 : ce;
-      const int m1 = c1 < 64 ? c1 : 64;
       int c = c0;
-      for (; c + 1 < m1; c += 2) {  // two chunks per step: both table reads in flight
+      for (; c + 1 < c1; c += 2) {
         const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c);
         const uint32_t d1 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c + 1);
-        key_chunk2<G, TAB0>(d0, d1, hi, lo, st.fmask, nlo, nhi, lr);
+        const h4v b0 = kstep_b<G, VB, W>(d0, hi, lo), b1 = kstep_b<G, VB, W>(d1, hi, lo);
+        const uint32_t r0 = kstep_a<G, VB>(d0, st.laneoff), r1 = kstep_a<G, VB>(d1, st.laneoff);
+        h4v q0[NQ], q1[NQ];
+#pragma unroll
+        for (int g = 0; g < NQ; ++g) q0[g] = lds_at<h4v>(r0 + 32 * g), q1[g] = lds_at<h4v>(r1 + 32 * g);
+#pragma unroll
+        for (int g = 0; g < NQ; ++g) {
+          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(q0[g], b0, acc[g], 0, 0, 0);
+          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(q1[g], b1, acc[g], 0, 0, 0);
+        }
       }
-      if (c < m1)
-        key_chunk<G, TAB0>((uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c), hi, lo, st.fmask, nlo, nhi, lr);
-      for (int c = c0 > 64 ? c0 : 64; c < c1; ++c)
-        key_chunk<G, TAB0>((uint32_t)__builtin_amdgcn_readlane((int)st.dv1, c - 64), hi, lo, st.fmask, nlo, nhi,
-                           lr);
+      if (c < c1) {
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c);
+        const h4v b0 = kstep_b<G, VB, W>(d0, hi, lo);
+        const uint32_t r0 = kstep_a<G, VB>(d0, st.laneoff);
+#pragma unroll
+        for (int g = 0; g < NQ; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(lds_at<h4v>(r0 + 32 * g), b0, acc[g], 0, 0, 0);
+      }
     }
   }
 }
@@ -399,18 +373,25 @@ template <int G, int VB, int WK>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
                                              const float (&rinv)[G], float (&mrun)[G], float (&lsum)[G],
                                              f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v], int lane) {
-  // ---- keys, lane = token.  4-bit group: direct centroid sums.
-  float lr[G];
+  // ---- keys, lane = token.  4-bit group: one fp32 step per code.
   f4v a4[VQuads<G>::v];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lr[h] = 0.f;
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
   key4_blocks<G, VB, WK, 0>(r.w, st.n4w, lane, a4);
-  // widths 3, 2, 1: table chunks, norm slots 1, 2, 3
-  key_group<G, VB, WK, 0>(r.w, st, r.nr.x >> 16, lr);
-  key_group<G, VB, WK, 1>(r.w, st, r.nr.y & 0xFFFFu, lr);
-  key_group<G, VB, WK, 2>(r.w, st, r.nr.y >> 16, lr);
+  // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w
+  float lr[G];
+  {
+    f4v ak[VQuads<G>::v];
+#define BGTQ_KG(R, NORM)                                                              \
+  {                                                                                   \
+    _Pragma("unroll") for (int g = 0; g < VQuads<G>::v; ++g) ak[g] = (f4v){0.f, 0.f, 0.f, 0.f}; \
+    key_group<G, VB, WK, R>(r.w, st, ak);                                             \
+    const float nw = h2f((uint16_t)(NORM));                                           \
+    _Pragma("unroll") for (int h = 0; h < G; ++h) lr[h] = R == 0 ? nw * ak[h >> 2][h & 3] : fmaf(nw, ak[h >> 2][h & 3], lr[h]); \
+  }
+    BGTQ_KG(0, r.nr.x >> 16) BGTQ_KG(1, r.nr.y & 0xFFFFu) BGTQ_KG(2, r.nr.y >> 16)
+#undef BGTQ_KG
+  }
   const bool valid = (int64_t)tile * kTile + lane < st.seq;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
@@ -458,10 +439,10 @@ struct StreamOcc {
 
 // ------------------------------------------------------------------ prep
 
-// Grid (KV head, sequence, slice), see prep_role.
+// Grid (KV head, sequence), see prep_role.
 template <int G>
-__global__ __launch_bounds__(kStreamThreads) void prep_kernel(const PrepArgs a) {
-  prep_role<G>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
+  prep_role<G>(a, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ stream kernel
@@ -477,58 +458,50 @@ struct StreamArgs {
   const uint16_t *vn;
   const int32_t *seq_lens;
   float *part;
-  int64_t tiles_cap, max_seq_len, off_kvh, off_lookup, off_c4, off_vlut, prep_stride;
-  int hkv, hq, wk, win, tiles_per_split, n_splits, table_bytes;
+  int64_t tiles_cap, max_seq_len, off_kvh, off_ksd, off_dtab, off_vlut, prep_stride;
+  int hkv, hq, wk, tiles_per_split, n_splits;
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
 };
 
 template <int G, int VB, int WK>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
 void decode_stream_kernel(const StreamArgs a) {
-  constexpr int L = GLog<G>::v;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint8_t *consts = a.consts;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
-  const int win = a.win;
   typedef StreamLds<G, VB> Lds;
+  typedef PrepOut<G> PO;
 
-  // ---- prologue: the shared query state of this (sequence, KV head) and the
-  // plan's centroid tables into LDS.  The first 32 KB of the copy are loaded
-  // into registers before the first tile is requested, so that waiting for
-  // them does not wait for the tile (loads complete in order).
+  // ---- prologue: the plan's decode tables, the shared query operands of this
+  // (sequence, KV head) and the value table into LDS, 16 bytes per thread and
+  // range.  The copy is loaded into registers before the first tile is
+  // requested, so that waiting for it does not wait for the tile (loads
+  // complete in order).
   const uint8_t *pr = a.prep + ((size_t)b * a.hkv + kvh) * (size_t)a.prep_stride;
-  const int n0 = a.table_bytes >> 4;
-  const int n1 = n0 + ((G * kHeadDim * 4) >> 4);
-  const int n2 = n1 + ((256 * 8) >> 4);
-  const int n3 = n2 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
-  const uint4 *cs0 = (const uint4 *)pr, *cs1 = (const uint4 *)(pr + a.table_bytes) - n0;
-  const uint4 *cs2 = (const uint4 *)(consts + a.off_c4) - n1, *cs3 = (const uint4 *)(consts + a.off_vlut) - n2;
-  constexpr int kCopyRegs = 4;
+  constexpr int n0 = kDtabBytes >> 4;
+  constexpr int n1 = n0 + (PO::rinv >> 4);
+  constexpr int n2 = n1 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
+  static_assert(n2 <= 4 * kStreamThreads, "four copy rounds");
+  const uint4 *cs0 = (const uint4 *)(consts + a.off_dtab), *cs1 = (const uint4 *)pr - n0;
+  const uint4 *cs2 = (const uint4 *)(consts + a.off_vlut) - n1;
   uint4 cr0, cr1, cr2, cr3;
-#define BGTQ_CSRC(I) ((I) < n0 ? cs0 + (I) : (I) < n1 ? cs1 + (I) : (I) < n2 ? cs2 + (I) : cs3 + (I))
-#define BGTQ_CDST(I)                                                                                              \
-  ((uint4 *)(smem + ((I) < n0 ? Lds::tab0 + 16 * (I)                                                              \
-                              : (I) < n1 ? Lds::q4 + 16 * ((I) - n0)                                              \
-                                         : (I) < n2 ? Lds::c4 + 16 * ((I) - n1)                                   \
-                                                    : (I) < n3 ? Lds::vlut + 16 * ((I) - n2) : Lds::total(a.table_bytes))))
+#define BGTQ_CSRC(I) ((I) < n0 ? cs0 + (I) : (I) < n1 ? cs1 + (I) : cs2 + (I))
+#define BGTQ_CDST(I) \
+  ((uint4 *)(smem + ((I) < n1 ? 16 * (I) : (I) < n2 ? Lds::vlut + 16 * ((I) - n1) : Lds::total)))
   {
-    const int i0 = min(tid, n3 - 1), i1 = min(tid + kStreamThreads, n3 - 1);
-    const int i2 = min(tid + 2 * kStreamThreads, n3 - 1), i3 = min(tid + 3 * kStreamThreads, n3 - 1);
+    const int i0 = min(tid, n2 - 1), i1 = min(tid + kStreamThreads, n2 - 1);
+    const int i2 = min(tid + 2 * kStreamThreads, n2 - 1), i3 = min(tid + 3 * kStreamThreads, n2 - 1);
     cr0 = *BGTQ_CSRC(i0);
     cr1 = *BGTQ_CSRC(i1);
     cr2 = *BGTQ_CSRC(i2);
     cr3 = *BGTQ_CSRC(i3);
   }
   StreamState st;
-  {
-    const uint32_t *lk = (const uint32_t *)(consts + a.off_lookup) + kvh * kMaxChunks;
-    st.dv0 = lk[lane];  // zero past the head's chunks
-    st.dv1 = lk[lane + 64];
-    st.av = (uint32_t)kd->anchor[min(lane, kMaxWK + 1)];
-  }
+  st.dv0 = ((const uint32_t *)(consts + a.off_ksd))[kvh * kMaxKSteps + min(lane, kMaxKSteps - 1)];
+  st.av = (uint32_t)kd->anchor[min(lane, kMaxWK + 1)];
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tile request
   // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers.
   // The first is requested now, its range bounded by max_seq_len (in memory).
@@ -545,17 +518,16 @@ void decode_stream_kernel(const StreamArgs a) {
   *BGTQ_CDST(tid + kStreamThreads) = cr1;
   *BGTQ_CDST(tid + 2 * kStreamThreads) = cr2;
   *BGTQ_CDST(tid + 3 * kStreamThreads) = cr3;
-  for (int i = tid + kCopyRegs * kStreamThreads; i < n3; i += kStreamThreads) *BGTQ_CDST(i) = *BGTQ_CSRC(i);
 #undef BGTQ_CDST
 #undef BGTQ_CSRC
   float rinv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + a.table_bytes + G * kHeadDim * 4))[h];
+  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + PO::rinv))[h];
   {
     int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
     st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
-    st.fmask = (uint32_t)__builtin_amdgcn_mov_dpp((int)(((1u << win) - 1) << L), 0xE4, 0xF, 0xF, false);
     st.wk = a.wk;
+    st.laneoff = (uint32_t)(lane & 3) * 8;
     st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
     st.n4w = kd->n4w;
     st.cgrp = kd->cgrp;
@@ -705,7 +677,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
 
 typedef void (*stream_fn)(const StreamArgs);
 typedef void (*prep_fn)(const PrepArgs);
-constexpr int kPrepChunks = 8;  // lookup chunks built per prep workgroup
 
 prep_fn pick_prep(int g) {
   switch (g) {
@@ -742,9 +713,9 @@ stream_fn pick_stream(int g, int vb, int wk) {
   }
 }
 
-int stream_smem_bytes(int g, int vb, int table_bytes) {
+int stream_smem_bytes(int g, int vb) {
 #define BGTQ_SM(G_, VB_) \
-  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::total(table_bytes) + 16;
+  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::total + 16;
   BGTQ_SM(1, 1) BGTQ_SM(1, 2) BGTQ_SM(1, 3) BGTQ_SM(1, 4)
   BGTQ_SM(2, 1) BGTQ_SM(2, 2) BGTQ_SM(2, 3) BGTQ_SM(2, 4)
   BGTQ_SM(4, 1) BGTQ_SM(4, 2) BGTQ_SM(4, 3) BGTQ_SM(4, 4)
@@ -771,7 +742,7 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   d.n_splits = (tiles + tps - 1) / tps;
   d.tiles_per_split = tps;
   d.prep_off = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
-  d.prep_stride = prep_stride(p.hdr.group, p.hdr.max_chunks << (p.hdr.lut_window + p.hdr.lut_entry_log2));
+  d.prep_stride = prep_stride_of(p.hdr.group);
   d.total = d.prep_off + (size_t)batch * hkv * (size_t)d.prep_stride;
   return d;
 }
@@ -791,10 +762,6 @@ bool stream_static_lds_ok(stream_fn fn) {
 
 float kscale_of(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }  // logits in log2 units
 
-int table_bytes_of(const Plan &p) { return p.hdr.max_chunks << (p.hdr.lut_window + p.hdr.lut_entry_log2); }
-
-int prep_slices(const Plan &p) { return std::max(1, (p.hdr.max_chunks + kPrepChunks - 1) / kPrepChunks); }
-
 PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
                    int64_t max_seq_len, float softmax_scale) {
   const DecodeLayout lay = decode_layout(p, batch, max_seq_len);
@@ -803,14 +770,10 @@ PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, voi
   pa.q = q;
   pa.out = (uint8_t *)workspace + lay.prep_off;
   pa.off_kvh = p.hdr.off_kvh;
-  pa.off_build = p.hdr.off_build;
   pa.off_rot32 = p.hdr.off_rot32_k;
   pa.stride = lay.prep_stride;
   pa.hkv = p.desc.n_kv_heads;
   pa.hq = p.desc.n_q_heads;
-  pa.win = p.hdr.lut_window;
-  pa.table_bytes = table_bytes_of(p);
-  pa.chunks_per_wg = kPrepChunks;
   pa.kscale = kscale_of(softmax_scale);
   return pa;
 }
@@ -831,19 +794,18 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
 bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
   const DecodeLayout lay = decode_layout(p, c.batch, c.max_seq_len);
   const int G = p.hdr.group, vb = p.hdr.v_bits;
-  const int table_bytes = table_bytes_of(p);
-  const int smem = stream_smem_bytes(G, vb, table_bytes);
+  const int smem = stream_smem_bytes(G, vb);
   stream_fn fn = pick_stream(G, vb, p.hdr.wk);
   if (!stream_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: stream kernel has static LDS");
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: lookup tables exceed the LDS limit");
+    if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: LDS request above the limit");
   }
   hipStream_t st = (hipStream_t)c.stream;
   float *part = (float *)c.workspace;
   if (with_prep) {
     const PrepArgs pa = prep_args(p, c.dev_consts, c.q, c.workspace, c.batch, c.max_seq_len, c.softmax_scale);
-    pick_prep(G)<<<dim3(p.desc.n_kv_heads, c.batch, prep_slices(p)), kPrepThreads, 0, st>>>(pa);
+    pick_prep(G)<<<dim3(p.desc.n_kv_heads, c.batch), kPrepThreads, 0, st>>>(pa);
     const bgtq_status ps = launch_status("decode (prep)");
     if (ps != BGTQ_OK) return ps;
   }
@@ -873,17 +835,15 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
   sa.tiles_cap = (c.capacity + kTile - 1) / kTile;
   sa.max_seq_len = c.max_seq_len;
   sa.off_kvh = p.hdr.off_kvh;
-  sa.off_lookup = p.hdr.off_lookup;
-  sa.off_c4 = p.hdr.off_c4;
+  sa.off_ksd = p.hdr.off_ksd;
+  sa.off_dtab = p.hdr.off_dtab;
   sa.off_vlut = p.hdr.off_vlut;
   sa.prep_stride = lay.prep_stride;
   sa.hkv = p.desc.n_kv_heads;
   sa.hq = p.desc.n_q_heads;
   sa.wk = p.hdr.wk;
-  sa.win = p.hdr.lut_window;
   sa.tiles_per_split = lay.tiles_per_split;
   sa.n_splits = lay.n_splits;
-  sa.table_bytes = table_bytes;
   sa.seq_add = c.seq_add;
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
   // With profiling on, the events are bound to the launch itself, so their elapsed time is the

@@ -126,10 +126,4 @@ template <> struct VLut<2> { static constexpr int entries = 256, bytes = 8; };
 template <> struct VLut<3> { static constexpr int entries = 64, bytes = 4; };
 template <> struct VLut<4> { static constexpr int entries = 256, bytes = 4; };
 
-template <int G> struct GLog;  // log2 of the key-table entry size (2 * G bytes: fp16 per head)
-template <> struct GLog<1> { static constexpr int v = 1; };
-template <> struct GLog<2> { static constexpr int v = 2; };
-template <> struct GLog<4> { static constexpr int v = 3; };
-template <> struct GLog<8> { static constexpr int v = 4; };
-
 }  // namespace bgtq

@@ -48,7 +48,6 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
 bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep);  // [prep], stream, merge
 PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
                    int64_t max_seq_len, float softmax_scale);
-int prep_slices(const Plan &p);
 
 struct AppendArgs;
 AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,

@@ -1,6 +1,6 @@
 // Host-side plan for the Block-GTQ packed-KV path: Lloyd-Max codebooks,
-// seeded Haar rotations, key group maps, decode lookup-table descriptors and
-// the device constant image.  Pure host C++ (no HIP calls).
+// seeded Haar rotations, key group maps, decode k-step descriptors and tables,
+// and the device constant image.  Pure host C++ (no HIP calls).
 //
 // Method sources: "RoPE-Aware Bit Allocation for KV-Cache Quantization",
 // Abstract (TurboQuant-MSE as the base encoder, per-(layer, KV head) integer
@@ -241,7 +241,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     }
   }
   const int wk = 4 * d.k_avg_bits;
-  const int entry_log2 = 1 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);  // fp16 per head
 
   // groups, coordinates, bit offsets, rotations
   p.kvh.assign(hkv, KvhDesc{});
@@ -277,79 +276,47 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     p.rot_v.push_back(haar(d.seed, d.layer, h, 1, d.v_bits, kHeadDim));
   }
 
-  // decode lookup chunks; the widest window whose tables fit the LDS budget
-  int window = 6;
-  for (;;) {
-    int max_c = 0;
-    for (int h = 0; h < hkv; ++h) {
-      int n = 0;
-      for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) {
-        const KGroupDesc &g = p.kvh[h].g[gi];
-        if (g.w == 4) continue;
-        const int m = window / g.w;
-        n += (g.d + m - 1) / m;
-      }
-      max_c = std::max(max_c, n);
-    }
-    const size_t bytes = (size_t)max_c << (window + entry_log2);
-    if (bytes <= (size_t)kLutBudget || window == 4) break;
-    window = 4;
-  }
-  p.lookup.clear();
-  p.build.clear();
-  int max_chunks = 0;
+  // decode k-steps of the width-1..3 groups (four positions each)
+  p.ksd.assign((size_t)hkv * kMaxKSteps, 0u);
+  int max_ksteps = 0;
   for (int h = 0; h < hkv; ++h) {
     KvhDesc &kd = p.kvh[h];
-    kd.chunk_base = h * kMaxChunks;  // fixed stride: the kernels address a head's chunks from its index
-    p.lookup.resize((size_t)h * kMaxChunks, 0u);
-    p.build.resize((size_t)h * kMaxChunks, 0u);
     std::vector<int> anchors;
     int c = 0;
     kd.d4 = (kd.n_groups > 0 && kd.g[0].w == 4) ? kd.g[0].d : 0;
     kd.n4blk = (kd.d4 + 15) / 16;
     kd.n4w = (kd.d4 + 7) / 8;
-    int cfirst[4] = {-1, -1, -1, -1};  // first chunk of the width-3, 2, 1 groups
+    int cfirst[3] = {-1, -1, -1};  // first k-step of the width-3, 2, 1 groups
     int jlo[3] = {31, 31, 31}, jhi[3] = {0, 0, 0};
     for (int gi = 0; gi < kd.n_groups; ++gi) {
       const KGroupDesc &g = kd.g[gi];
-      if (g.w == 4) continue;  // summed directly in the decode, no tables
-      const int rg = 3 - g.w;   // rest-group index
+      if (g.w == 4) continue;  // one matrix-core step per code in the decode
+      const int rg = 3 - g.w;  // rest-group index
       cfirst[rg] = c;
-      const int m_max = window / g.w;
-      for (int r0 = 0; r0 < g.d; r0 += m_max, ++c) {
-        const int m = std::min(m_max, g.d - r0);
-        const int s = g.bit_off + g.w * r0;
-        const int lo = s - entry_log2;
+      for (int r0 = 0; r0 < g.d; r0 += 4, ++c) {
+        if (c >= kMaxKSteps) {
+          err = "internal: too many k-steps";
+          return BGTQ_EINVAL;
+        }
+        const int lo = g.bit_off + g.w * r0 - kstep_bit(g.w);  // window start, may be -2 or -3
         const int anchor = lo >= 0 ? lo / 32 : -1;
         const uint32_t shift = (uint32_t)(lo - 32 * anchor);
-        const uint32_t table = (uint32_t)c << (window + entry_log2);
-        const uint32_t slot = (uint32_t)(4 - g.w);
-        p.lookup.push_back(shift | table | (r0 == 0 ? kChunkStart : 0u) | (slot << 24));
-        p.build.push_back((uint32_t)(g.pos + r0) | ((uint32_t)m << 8) | ((uint32_t)g.w << 12) |
-                          ((uint32_t)gi << 15));
+        p.ksd[(size_t)h * kMaxKSteps + c] = shift | ((uint32_t)c << 5);
         anchors.push_back(anchor);
         jlo[rg] = std::min(jlo[rg], anchor + 1);
         jhi[rg] = std::max(jhi[rg], anchor + 1);
       }
     }
-    if (c > kMaxChunks) {
-      err = "internal: too many lookup chunks";
-      return BGTQ_EINVAL;
-    }
-    kd.n_chunks = c;
-    max_chunks = std::max(max_chunks, c);
-    {
-      // chunk boundaries of the width-3, 2, 1 groups (an absent group is an empty range)
-      int bnd[4];
-      bnd[3] = c;
-      for (int rg = 2; rg >= 0; --rg) bnd[rg] = cfirst[rg] >= 0 ? cfirst[rg] : bnd[rg + 1];
-      kd.cgrp = (uint32_t)bnd[0] | ((uint32_t)bnd[1] << 8) | ((uint32_t)bnd[2] << 16) | ((uint32_t)bnd[3] << 24);
-      kd.jrng = 0;
-      for (int rg = 0; rg < 3; ++rg) kd.jrng |= ((uint32_t)jlo[rg] | ((uint32_t)jhi[rg] << 5)) << (10 * rg);
-    }
-    p.lookup.resize((size_t)(h + 1) * kMaxChunks, 0u);
-    p.build.resize((size_t)(h + 1) * kMaxChunks, 0u);
-    // anchor ranges: chunks anchored at word jj-1 are [anchor[jj], anchor[jj+1])
+    kd.n_ksteps = c;
+    max_ksteps = std::max(max_ksteps, c);
+    // k-step boundaries of the width-3, 2, 1 groups (an absent group is an empty range)
+    int bnd[4];
+    bnd[3] = c;
+    for (int rg = 2; rg >= 0; --rg) bnd[rg] = cfirst[rg] >= 0 ? cfirst[rg] : bnd[rg + 1];
+    kd.cgrp = (uint32_t)bnd[0] | ((uint32_t)bnd[1] << 8) | ((uint32_t)bnd[2] << 16) | ((uint32_t)bnd[3] << 24);
+    kd.jrng = 0;
+    for (int rg = 0; rg < 3; ++rg) kd.jrng |= ((uint32_t)jlo[rg] | ((uint32_t)jhi[rg] << 5)) << (10 * rg);
+    // anchor ranges: k-steps whose window starts in word jj-1 are [anchor[jj], anchor[jj+1])
     for (int jj = 0; jj <= kMaxWK + 1; ++jj) {
       int first = 0;
       while (first < c && anchors[first] < jj - 1) ++first;
@@ -368,9 +335,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   hd.v_bits = d.v_bits;
   hd.wk = wk;
   hd.wv = 2 * d.v_bits;
-  hd.lut_window = window;
-  hd.lut_entry_log2 = entry_log2;
-  hd.max_chunks = max_chunks;
+  hd.max_ksteps = max_ksteps;
   for (int b = 1; b <= 4; ++b) {
     const Codebook &cb = codebook(b);
     for (int k = 0; k < (1 << b); ++k) hd.cent[b - 1][k] = cb.c[k];
@@ -381,10 +346,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   size_t off = align256(sizeof(ConstHeader));
   hd.off_kvh = off;
   off = align256(off + sizeof(KvhDesc) * hkv);
-  hd.off_lookup = off;
-  off = align256(off + 4 * p.lookup.size());
-  hd.off_build = off;
-  off = align256(off + 4 * p.build.size());
+  hd.off_ksd = off;
+  off = align256(off + 4 * p.ksd.size());
   hd.off_rot64_k = off;
   off = align256(off + 8 * (size_t)rot64_k);
   hd.off_rot32_k = off;
@@ -394,8 +357,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   hd.off_rot32_v = off;
   off = align256(off + 4 * (size_t)hkv * kHeadDim * kHeadDim);
   const std::vector<uint32_t> vlut = value_table(d.v_bits);
-  hd.off_c4 = off;
-  off = align256(off + 8 * 256);
+  hd.off_dtab = off;
+  off = align256(off + kDtabBytes);
   hd.off_vlut = off;
   hd.vlut_bytes = 4 * (int64_t)vlut.size();
   off = align256(off + 4 * vlut.size());
@@ -405,8 +368,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   uint8_t *img = p.image.data();
   std::memcpy(img, &hd, sizeof(hd));
   std::memcpy(img + hd.off_kvh, p.kvh.data(), sizeof(KvhDesc) * hkv);
-  std::memcpy(img + hd.off_lookup, p.lookup.data(), 4 * p.lookup.size());
-  std::memcpy(img + hd.off_build, p.build.data(), 4 * p.build.size());
+  std::memcpy(img + hd.off_ksd, p.ksd.data(), 4 * p.ksd.size());
   double *r64k = (double *)(img + hd.off_rot64_k);
   float *r32k = (float *)(img + hd.off_rot32_k);
   size_t gidx = 0;
@@ -420,11 +382,22 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
           r32k[((size_t)h * kHeadDim + g.pos + i) * kHeadDim + g.pos + k] = (float)pi[(size_t)i * g.d + k];
         }
     }
-  float *c4 = (float *)(img + hd.off_c4);
-  const Codebook &cb4 = codebook(4);
-  for (int e = 0; e < 256; ++e) {
-    c4[2 * e] = (float)cb4.c[e & 15];
-    c4[2 * e + 1] = (float)cb4.c[e >> 4];
+  {
+    uint8_t *dt = img + hd.off_dtab;
+    float *c4 = (float *)(dt + kDtabC4);
+    const Codebook &cb4 = codebook(4);
+    for (int e = 0; e < 256; ++e) {
+      c4[2 * e] = (float)cb4.c[e & 15];
+      c4[2 * e + 1] = (float)cb4.c[e >> 4];
+    }
+    uint16_t *t2 = (uint16_t *)(dt + kDtabT2), *t1 = (uint16_t *)(dt + kDtabT1), *t3 = (uint16_t *)(dt + kDtabT3);
+    const Codebook &cb1 = codebook(1), &cb2 = codebook(2), &cb3 = codebook(3);
+    for (int y = 0; y < 256; ++y)
+      for (int k = 0; k < 4; ++k) t2[4 * y + k] = f16_bits(cb2.c[(y >> (2 * k)) & 3]);
+    for (int y = 0; y < 16; ++y)
+      for (int k = 0; k < 4; ++k) t1[4 * y + k] = f16_bits(cb1.c[(y >> k) & 1]);
+    for (int y = 0; y < 64; ++y)
+      for (int k = 0; k < 2; ++k) t3[2 * y + k] = f16_bits(cb3.c[(y >> (3 * k)) & 7]);
   }
   std::memcpy(img + hd.off_vlut, vlut.data(), 4 * vlut.size());
   double *r64v = (double *)(img + hd.off_rot64_v);

@@ -1,8 +1,8 @@
 // Query preparation for the fused decode: rotation of the queries once per
-// key width group (fp32 MFMA, the only matrix-core use) and the per-chunk
-// lookup tables of q_rot x centroid ("RoPE-Aware Bit Allocation for KV-Cache
-// Quantization", Abstract; Block-GTQ README, backend table).  Internal header,
-// shared by the decode launches and the fused decode step.
+// key width group (fp32 MFMA) and their matrix-core operands for the stream
+// kernel ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract;
+// Block-GTQ README, backend table).  Internal header, shared by the decode
+// launches and the fused decode step.
 #pragma once
 
 #include "device.h"
@@ -75,56 +75,57 @@ struct PrepArgs {
   const uint8_t *consts;
   const uint16_t *q;
   uint8_t *out;
-  int64_t off_kvh, off_build, off_rot32, stride;
-  int hkv, hq, win, table_bytes, chunks_per_wg;
+  int64_t off_kvh, off_rot32, stride;
+  int hkv, hq;
   float kscale;
 };
 
-// One workgroup per (KV head, sequence, slice): the query-dependent state that every split
-// of the stream kernel shares.  Each workgroup rotates the G queries once per
-// key group (fp32 MFMA) and builds the lookup tables of its slice of the
-// width-1..3 chunks: per chunk, fac_h * kscale / sqrt(d_g) * sum_r
-// q_rot[h][pos + r] * c_w[code_r] over every value of the chunk's window, as
-// fp16.  fac_h is the power of two that brings
-// max_g(kscale c_max,w / sqrt(d_g)) * sum_p |q_rot[h][p]| (over the positions
-// of those groups, summed in a fixed order so that every slice finds the same
-// factor) below 2^14.  Slice 0 also writes the 4-bit group queries scaled by
-// kscale / sqrt(d4) and 1 / fac_h.
 template <int G>
-__device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b, int slice) {
-  constexpr int lg = GLog<G>::v - 1;  // log2 G
+struct PrepOut {  // byte offsets in one (sequence, KV head) block of the prep output
+  static constexpr int nq = (G + 3) / 4;            // query-head quads
+  static constexpr int q4 = 0;                      // fp32 [G][128]
+  static constexpr int qr = G * kHeadDim * 4;       // fp16 [kMaxKSteps][nq][4][4]
+  static constexpr int rinv = qr + kMaxKSteps * nq * 32;  // fp32 [G]
+  static constexpr int bytes = rinv + G * 4;
+};
+
+// One workgroup per (KV head, sequence): the query-dependent state that every
+// split of the stream kernel shares.  The G queries are rotated once per key
+// group (fp32 MFMA, block-diagonal rotation) and written as
+//  * q4[h][r] = kscale / sqrt(d4) q_rot[h][r] for the 4-bit group (r < d4, else 0);
+//  * qr[k][quad][m][i] = fp16(fac_h kscale / sqrt(d_g) q_rot[h][pos_g + 4 s + i]),
+//    h = 4 quad + m, for k-step k = (group g, step s) of the width-1..3 groups
+//    (0 past the group, for h >= G and for k past the head's k-steps);
+//  * rinv[h] = 1 / fac_h, fac_h the power of two that brings the largest
+//    |kscale / sqrt(d_g) q_rot[h][p]| over those groups to [2^13, 2^14).
+template <int G>
+__device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b) {
+  typedef PrepOut<G> PO;
   __shared__ KvhDesc kds;
   __shared__ float qg[8 * kHeadDim];
   __shared__ float qs[G * kHeadDim];
-  __shared__ uint32_t bld[kMaxChunks];
-  __shared__ float cs[64 + kMaxGroups];
-  __shared__ float hsum[G];
+  __shared__ float gsc[kHeadDim];  // kscale / sqrt(d_g) of the group of each position
+  __shared__ float hmax[G];
   const uint8_t *consts = a.consts;
-  const ConstHeader *hd = hdr_of(consts);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t *out = a.out + ((size_t)b * a.hkv + kvh) * (size_t)a.stride;
-  // ---- one round of loads: descriptor, queries (natural order, in the
-  // rotated-query area), centroids and build words first, then the rotation
-  // rows (fixed addresses), so that staging the former waits for them only.
+  // ---- one round of loads: descriptor and queries (natural order, in the
+  // rotated-query area) first, then the rotation rows (fixed addresses), so
+  // that staging the former waits for them only.
   constexpr int kDescWords = (int)(sizeof(KvhDesc) / 4);
   static_assert(kDescWords <= kPrepThreads && G * kHeadDim <= 2 * kPrepThreads, "one pass of staging loads");
   const uint32_t dw = ((const uint32_t *)((const KvhDesc *)(consts + a.off_kvh) + kvh))[min(tid, kDescWords - 1)];
   const uint16_t *qb = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim;
   const uint16_t q0 = qb[min(tid, G * kHeadDim - 1)];
   const uint16_t q1 = qb[min(tid + kPrepThreads, G * kHeadDim - 1)];
-  const float c0 = (float)hd->cent[(tid >> 4) & 3][tid & 15];
-  const uint32_t bw0 = ((const uint32_t *)(consts + a.off_build))[kvh * kMaxChunks + (tid & (kMaxChunks - 1))];
   RotRows<kPrepWaves> rr;
   rot_rows<kPrepWaves>((const float *)(consts + a.off_rot32) + (size_t)kvh * kHeadDim * kHeadDim, wave, lane, rr);
   if (tid < kDescWords) ((uint32_t *)&kds)[tid] = dw;
   if (tid < G * kHeadDim) qs[tid] = h2f(q0);
   if (tid + kPrepThreads < G * kHeadDim) qs[tid + kPrepThreads] = h2f(q1);
-  if (tid < 64) cs[tid] = c0;
-  if (tid < kMaxChunks) bld[tid] = bw0;
   __syncthreads();
-  const int nch = kds.n_chunks, d4 = kds.d4, dnz = kds.d_nz;
-  if (tid < kds.n_groups) cs[64 + tid] = a.kscale / sqrtf((float)kds.g[tid].d);
+  const int d4 = kds.d4, dnz = kds.d_nz;
   {
     // group order: qg[h][p] = q[h][coord[p]] (rows h >= G and positions >= d_nz zero)
     const int p = tid & (kHeadDim - 1);
@@ -134,19 +135,25 @@ __device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b, int
       const float v = qs[(h < G ? h : 0) * kHeadDim + cp];
       qg[i] = (h < G && p < dnz) ? v : 0.f;
     }
+    if (tid < kHeadDim) {
+      float sc = 0.f;
+      for (int gi = 0; gi < kds.n_groups; ++gi)
+        if (tid >= kds.g[gi].pos && tid < kds.g[gi].pos + kds.g[gi].d) sc = a.kscale / sqrtf((float)kds.g[gi].d);
+      gsc[tid] = sc;
+    }
   }
   __syncthreads();
   rot_tiles<kPrepWaves>(rr, G, qg, qs, wave, lane);
   __syncthreads();
-  // per head: sum of |q_rot| over the table groups, one wave per head, fixed order
+  // per head: the largest scaled |q_rot| over the width-1..3 groups, one wave per head
   for (int h = wave; h < G; h += kPrepWaves) {
     float v = 0.f;
-    for (int p = d4 + lane; p < dnz; p += 64) v += fabsf(qs[h * kHeadDim + p]);
-    v = wave_sum(v);
-    if (lane == 0) hsum[h] = v;
+    for (int p = d4 + lane; p < dnz; p += 64) v = fmaxf(v, fabsf(qs[h * kHeadDim + p] * gsc[p]));
+    v = wave_max(v);
+    if (lane == 0) hmax[h] = v;
   }
-  if (slice == 0) {
-    float *q4 = (float *)(out + a.table_bytes);
+  {
+    float *q4 = (float *)(out + PO::q4);
     const float s4 = d4 > 0 ? a.kscale / sqrtf((float)d4) : 0.f;
     for (int idx = tid; idx < G * kHeadDim; idx += kPrepThreads) {
       const int h = idx >> 7, r = idx & (kHeadDim - 1);
@@ -154,39 +161,38 @@ __device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b, int
     }
   }
   __syncthreads();
-  float smax = 0.f;
-  for (int gi = 0; gi < kds.n_groups; ++gi) {
-    const int w = kds.g[gi].w;
-    if (w < 4) smax = fmaxf(smax, cs[64 + gi] * fabsf(cs[16 * (w - 1) + (1 << w) - 1]));
-  }
   float fac[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float m = smax * hsum[h];
+    const float m = hmax[h];
     int e = 0;
     (void)frexpf(m, &e);
     e = m > 0.f ? e : 0;
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
     fac[h] = ldexpf(1.f, 14 - e);
-    if (slice == 0 && tid == h) ((float *)(out + a.table_bytes + G * kHeadDim * 4))[h] = ldexpf(1.f, e - 14);
+    if (tid == h) ((float *)(out + PO::rinv))[h] = ldexpf(1.f, e - 14);
   }
-  const int ne = 1 << a.win, sh = a.win + lg;
-  const int c_lo = slice * a.chunks_per_wg;
-  const int c_hi = min(nch, c_lo + a.chunks_per_wg);
-  _Float16 *tab = (_Float16 *)out;
-  for (int idx = (c_lo << sh) + tid; idx < (c_hi << sh); idx += kPrepThreads) {
-    const int h = idx & (G - 1), f = (idx >> lg) & (ne - 1), c = idx >> sh;
-    const uint32_t bw = bld[c];
-    const int pos = bw & 255, m = (bw >> 8) & 15, w = (bw >> 12) & 7, gi = (bw >> 15) & 3;
-    const float *cw = cs + 16 * (w - 1);
-    const float *qh = qs + h * kHeadDim + pos;
-    const int mask = (1 << w) - 1;
-    float acc = 0.f;
-    for (int r = 0; r < m; ++r) acc = fmaf(qh[r], cw[(f >> (w * r)) & mask], acc);
-    float fh = fac[0];
+  // k-step operand rows, in group order 3, 2, 1
+  _Float16 *qr = (_Float16 *)(out + PO::qr);
+  for (int idx = tid; idx < kMaxKSteps * PO::nq * 16; idx += kPrepThreads) {
+    const int i = idx & 3, m = (idx >> 2) & 3, quad = (idx >> 4) % PO::nq, k = (idx >> 4) / PO::nq;
+    const int h = 4 * quad + m;
+    int p = -1, k0 = 0;
+    for (int gi = 0; gi < kds.n_groups; ++gi) {
+      const KGroupDesc &g = kds.g[gi];
+      if (g.w == 4) continue;
+      const int ns = (g.d + 3) >> 2;
+      if (k >= k0 && k < k0 + ns && 4 * (k - k0) + i < g.d) p = g.pos + 4 * (k - k0) + i;
+      k0 += ns;
+    }
+    float v = 0.f;
+    if (h < G && p >= 0) {
+      float fh = fac[0];
 #pragma unroll
-    for (int k = 1; k < G; ++k) fh = h == k ? fac[k] : fh;
-    tab[idx] = (_Float16)(fh * (cs[64 + gi] * acc));
+      for (int u = 1; u < G; ++u) fh = h == u ? fac[u] : fh;
+      v = fh * (gsc[p] * qs[h * kHeadDim + p]);
+    }
+    qr[idx] = (_Float16)v;
   }
 }
 

@@ -11,8 +11,8 @@
 namespace bgtq {
 
 // Workgroups [0, n): key append of (sequence, KV head) = (r / hkv, r % hkv);
-// [n, 2n): value append; [2n, 2n + n * slices): query preparation, slice-major.
-// n = batch * hkv.  Every role is independent of the others.
+// [n, 2n): value append; [2n, 3n): query preparation.  n = batch * hkv.  Every
+// role is independent of the others.
 template <int G>
 __global__ __launch_bounds__(kAppendThreads) void step_kernel(const AppendArgs ka, const AppendArgs va,
                                                               const PrepArgs pa, const int32_t *__restrict__ pos,
@@ -33,8 +33,7 @@ __global__ __launch_bounds__(kAppendThreads) void step_kernel(const AppendArgs k
     }
   } else {
     const int r = role - 2 * n;
-    const int slice = r / n, rr = r % n;
-    prep_role<G>(pa, rr % hkv, rr / hkv, slice);
+    prep_role<G>(pa, r % hkv, r / hkv);
   }
 }
 
@@ -68,7 +67,7 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
       decode_check(p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, "bgtq_decode_step");
   if (v != BGTQ_OK) return v;
   const int n = batch * p.desc.n_kv_heads;
-  const int64_t blocks = (int64_t)n * (2 + prep_slices(p));
+  const int64_t blocks = (int64_t)n * 3;
   if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, "bgtq_decode_step: grid too large");
   const int64_t tiles_cap = (capacity + kTile - 1) / kTile;
   const uint8_t *c = (const uint8_t *)dev_consts;
