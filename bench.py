@@ -1,11 +1,11 @@
 """Benchmark of the Block-GTQ packed-KV decode path on one MI355X.
 
-One step = one decode-attention call (bgtq_decode_attn: query preparation,
-cache-streaming kernel, split merge) of the 128K Llama-3.1-8B-shaped layer
-(batch 1, 8 KV / 32 query heads, K2V2) over the T+1 cached tokens.  The serving
-step (bgtq_decode_step: the new token's key and value appended at position T in
-the same launch as the query preparation, then the decode) is timed as well and
-reported under "serving_step".
+One step = one decode-attention call (bgtq_decode_attn: the decode kernel, which
+prepares the queries and streams the packed cache, then the split merge) of the
+128K Llama-3.1-8B-shaped layer (batch 1, 8 KV / 32 query heads, K2V2) over the
+T+1 cached tokens.  The serving step (bgtq_decode_step: the new token's key and
+value appended at position T, then the decode) is timed as well and reported
+under "serving_step".
 Calibration energy, allocation, plan creation and the full 128K prefill
 encode run once before the timed region and are reported as separate fields.
 
@@ -34,21 +34,28 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-KV decode attn GB/s (% HBM peak), ms/step @128K; encode keys/s"
 HBM_PEAK_GBPS = 8000.0
-STREAM_KERNEL = "decode_stream_kernel"
+STREAM_KERNEL = "decode_kernel"
 
 
 def log(msg: str) -> None:
     print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("decode.hip", "prep.h", "device.h", "internal.h")
+
+
 def kernel_source_hash() -> str:
-    with open(os.path.join(ROOT, "decode_attention_bgtq_amd", "csrc", "decode.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 prefix of the sources the decode kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_bgtq_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(cid: int):
-    """Per-launch HBM bytes of the stream kernel from committed counter runs, if still valid."""
-    p = os.path.join(ROOT, "profiles", "decode_stream_traffic.json")
+    """Per-launch HBM bytes of the decode kernel from committed counter runs, if still valid."""
+    p = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -93,7 +100,7 @@ def cpu_baseline(cfg, bits, n_heads: int):
 
 def traffic_from(fetch_dir: str, write_dir: str, cid: int, packed: int | None, out_path: str) -> int:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE) into
-    profiles/decode_stream_traffic.json.  Both counters are scaled by what they read for the
+    profiles/decode_kernel_traffic.json.  Both counters are scaled by what they read for the
     1 GiB device copy of the copy probe (1 GiB read, 1 GiB written)."""
     import csv
     import glob
@@ -147,9 +154,9 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/decode_stream_traffic.json from two rocprofv3 --pmc runs and exit")
+                    help="write profiles/decode_kernel_traffic.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--packed-bytes", type=int, default=None)
-    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "decode_stream_traffic.json"))
+    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "decode_kernel_traffic.json"))
     args = ap.parse_args()
     if args.traffic_from:
         return traffic_from(args.traffic_from[0], args.traffic_from[1], args.config, args.packed_bytes,
@@ -246,7 +253,7 @@ def main() -> int:
         plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
     torch.cuda.synchronize()
 
-    def attn(i):  # one decode-attention call over t + 1 tokens: query prep, cache stream, split merge
+    def attn(i):  # one decode-attention call over t + 1 tokens: decode kernel, split merge
         kc_, kn_, vc_, vn_ = reps[i % n_rep]
         plan.decode_attn(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, out, ws)
 
@@ -286,8 +293,8 @@ def main() -> int:
         n_steps += per_round
     step_ms = sum(round_ms) / len(round_ms)
     serve_ms = sum(timed_round(serve, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
-    # Stream-kernel duration: the same decode calls once more with the library's HIP events
-    # bound to every cache-streaming launch (hipExtLaunchKernel on the launch stream, so the
+    # Decode-kernel duration: the same decode calls once more with the library's HIP events
+    # bound to every decode-kernel launch (hipExtLaunchKernel on the launch stream, so the
     # elapsed time is the kernel's own start-to-end time); a pass of its own because event
     # timing can slow the dispatch of the launches around it.
     bg.profile_enable(True)
@@ -299,7 +306,7 @@ def main() -> int:
     kern_ms = kern_ms_total / max(launches, 1)
     value = packed / (step_ms / 1e3) / 1e9
     achieved = packed / (kern_ms / 1e3) / 1e9
-    log("decode %.4f ms (%.0f GB/s); serving step %.4f ms; stream kernel %.4f ms (%.0f GB/s, %d launches); "
+    log("decode %.4f ms (%.0f GB/s); serving step %.4f ms; decode kernel %.4f ms (%.0f GB/s, %d launches); "
         "host enqueue %.4f ms/call" % (step_ms, value, serve_ms, kern_ms, achieved, launches,
                                        host_enqueue_s * 1e3 / n_steps))
 

@@ -2,21 +2,26 @@
 // packed-cache serving path of "RoPE-Aware Bit Allocation for KV-Cache
 // Quantization", Abstract, and of the Block-GTQ README backend table).
 //
-// Two launches per call:
-//  stream  one workgroup per (split of the sequence, KV head, sequence).
-//          Prologue: rotates the G queries of the KV head once per key width
-//          group with fp32 MFMA (the only matrix-core use) and builds in LDS,
-//          per lookup chunk of the key stream, a table of
-//          scale * sum_r q_rot[h][pos + r] * centroid_w[code_r] / sqrt(d_g) over
-//          every value of the chunk's stream window.  Per 64-token tile: lane =
-//          token reads the key words (coalesced, word-major) and sums table
-//          entries times group norms into log2-domain logits; online softmax
-//          with wavefront reductions; lane = value coordinate accumulates fp16
-//          (p * value norm) token pairs against fp16 centroid pairs from an LDS
-//          table (v_dot2, fp32 accumulate) in the rotated value space.  Writes
-//          one partial (m, l, acc) per split and query head.
-//  merge   one workgroup per (sequence, KV head): log-sum-exp merge of the
-//          splits, normalisation, un-rotation by Pi_V^T, fp16 output.
+// Two launches per call.  The decode kernel, one workgroup of 8 waves per
+// (split of the sequence, KV head, sequence):
+//  prologue  the plan's decode tables into LDS; the G queries of the KV head
+//            rotated once per key width group (fp32, from the group rotations
+//            stored as bands) into the scaled 4-bit-group queries and the
+//            k-step operands of the width-1..3 groups (prep.h), in LDS.
+//  tiles     per 64-token tile (lane = token): key words read coalesced
+//            (word-major); logits on the matrix cores (the 4-bit group one
+//            fp32 4x4x1 step per code, the width-1..3 groups one fp16 4x4x4
+//            k-step per four codes, both with LDS centroid lookups) times the
+//            group norms, in log2 units; online softmax with wavefront
+//            reductions; the value codes (lane = coordinate) accumulated on the
+//            matrix cores against the fp16 softmax weights in the rotated value
+//            space.  The waves of a workgroup merge into one partial
+//            (m, l, acc[128]) per query head.
+// The merge kernel, one workgroup per (query head, sequence): log-sum-exp
+// merge of the splits, normalisation, un-rotation by Pi_V^T, fp16 output.
+// (Merging inside the decode kernel, by the last workgroup to arrive, costs
+// more: its chain of device-coherent stores, atomics and loads sits on the
+// critical path at the end of the grid.)
 #include <hip/hip_ext.h>
 
 #include "device.h"
@@ -51,8 +56,8 @@ __device__ __forceinline__ T lds_at(uint32_t off) {
 // per (KV head, sequence).
 __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ consts,
                                                    const uint16_t *__restrict__ q, float *__restrict__ qrot) {
-  __shared__ float qs[8 * kHeadDim];
-  __shared__ float qg[8 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float qs[8 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float qg[8 * kHeadDim];
   const ConstHeader *hd = hdr_of(consts);
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int G = hd->group, hq = hd->n_q_heads;
@@ -71,35 +76,38 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 
 // ------------------------------------------------------------------ stream
 
-// LDS layout of the stream kernel (bytes, fixed offsets that the compiler
+// LDS layout of the decode kernel (bytes, fixed offsets that the compiler
 // folds into the LDS instruction offsets):
 //   [0, kDtabBytes)  decode tables of the plan: 4-bit centroid pairs (c4),
 //                    four fp16 centroids of a width-2 byte (t2) / width-1
 //                    nibble (t1), two of six width-3 bits (t3)
 //   [q4, +G 512)     4-bit group queries: G x 128 fp32, scaled, zero past d4
-//   [qr, ..)         k-step query operands of the width-1..3 groups (prep layout)
+//   [qr, ..)         k-step query operands of the width-1..3 groups (PrepOut)
+//   [rinv, ..)       per head: 1 / the power-of-two scale of its k-step operands
 //   [vlut, ..)       value table
 //   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
-// After the tile loop the area is reused for the wave merge.
+// The query preparation uses [scr, ..) (from pt on) as scratch before the tile
+// loop; after it the area from 0 is reused for the wave merge.  Past `total`:
+// 16 spare bytes that take the stores of the table copy falling outside the
+// tables.
 template <int G, int VB>
 struct StreamLds {
   static constexpr int c4 = kDtabC4, t2 = kDtabT2, t1 = kDtabT1, t3 = kDtabT3;
   static constexpr int q4 = kDtabBytes;
   static constexpr int qr = q4 + PrepOut<G>::qr;
-  static constexpr int vlut = q4 + PrepOut<G>::rinv;
+  static constexpr int rinv = q4 + PrepOut<G>::rinv;
+  static constexpr int vlut = q4 + PrepOut<G>::bytes;
   static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
   static constexpr int end = pt + kStreamWaves * G * kTile * 2;
+  static constexpr int scr = pt;
+  static constexpr int scr_end = scr + PrepScratch<G>::bytes;
   static constexpr int merge = kStreamWaves * G * kPartStride * 4;
-  static constexpr int total = end > merge ? end : merge;
+  static constexpr int m1 = end > scr_end ? end : scr_end;
+  static constexpr int total = m1 > merge ? m1 : merge;
+  static constexpr int spare = total, alloc = total + 16;
   static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0, "table bases above the index bits");
+  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && scr % 16 == 0, "16-byte aligned areas");
 };
-
-// Per (sequence, KV head) output of the prep kernel, read by every split of
-// the stream kernel (PrepOut layout), 256-byte aligned.
-__host__ __device__ constexpr int64_t prep_stride_of(int G) {
-  const int nq = (G + 3) / 4;
-  return ((int64_t)G * kHeadDim * 4 + kMaxKSteps * nq * 32 + G * 4 + 255) & ~(int64_t)255;
-}
 
 template <int VB, int WK>
 struct TileRegs {
@@ -437,35 +445,28 @@ struct StreamOcc {
   static constexpr int v = G <= 4 ? (WK <= 8 ? 4 : 3) : 2;
 };
 
-// ------------------------------------------------------------------ prep
+// ------------------------------------------------------------------ decode kernel
 
-// Grid (KV head, sequence), see prep_role.
-template <int G>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepArgs a) {
-  prep_role<G>(a, blockIdx.x, blockIdx.y);
-}
-
-// ------------------------------------------------------------------ stream kernel
-
-// Launch arguments of the stream kernel (by value; the host fills in what it
-// knows so that the kernel starts without dependent loads).
-struct StreamArgs {
+// Launch arguments (by value; the host fills in what it knows so that the
+// kernel starts without dependent loads).
+struct DecodeArgs {
   const uint8_t *consts;
-  const uint8_t *prep;  // prep kernel output
+  const uint16_t *q;
   const uint32_t *kc;
   const uint16_t *kn;
   const uint32_t *vc;
   const uint16_t *vn;
   const int32_t *seq_lens;
-  float *part;
-  int64_t tiles_cap, max_seq_len, off_kvh, off_ksd, off_dtab, off_vlut, prep_stride;
+  float *part;  // split partials [batch][hq][n_splits][kPartStride]
+  int64_t tiles_cap, max_seq_len, off_kvh, off_ksd, off_dtab, off_vlut, off_rowk, off_bandk;
   int hkv, hq, wk, tiles_per_split, n_splits;
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
+  float kscale;
 };
 
 template <int G, int VB, int WK>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
-void decode_stream_kernel(const StreamArgs a) {
+void decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint8_t *consts = a.consts;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -473,31 +474,23 @@ void decode_stream_kernel(const StreamArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
   typedef StreamLds<G, VB> Lds;
-  typedef PrepOut<G> PO;
 
-  // ---- prologue: the plan's decode tables, the shared query operands of this
-  // (sequence, KV head) and the value table into LDS, 16 bytes per thread and
-  // range.  The copy is loaded into registers before the first tile is
-  // requested, so that waiting for it does not wait for the tile (loads
-  // complete in order).
-  const uint8_t *pr = a.prep + ((size_t)b * a.hkv + kvh) * (size_t)a.prep_stride;
+  // ---- prologue loads, in this order so that waiting for an earlier group
+  // does not wait for a later one (loads complete in order): query-prep
+  // inputs, the plan's decode and value tables (16 bytes per thread and
+  // round), the k-step descriptors, then the first tile.
+  PrepLoads pl;
+  prep_load_row<G>(pl, (const uint2 *)(consts + a.off_rowk) + (size_t)kvh * kHeadDim, kd,
+                   a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid);
   constexpr int n0 = kDtabBytes >> 4;
-  constexpr int n1 = n0 + (PO::rinv >> 4);
-  constexpr int n2 = n1 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
-  static_assert(n2 <= 4 * kStreamThreads, "four copy rounds");
-  const uint4 *cs0 = (const uint4 *)(consts + a.off_dtab), *cs1 = (const uint4 *)pr - n0;
-  const uint4 *cs2 = (const uint4 *)(consts + a.off_vlut) - n1;
-  uint4 cr0, cr1, cr2, cr3;
-#define BGTQ_CSRC(I) ((I) < n0 ? cs0 + (I) : (I) < n1 ? cs1 + (I) : cs2 + (I))
-#define BGTQ_CDST(I) \
-  ((uint4 *)(smem + ((I) < n1 ? 16 * (I) : (I) < n2 ? Lds::vlut + 16 * ((I) - n1) : Lds::total)))
-  {
-    const int i0 = min(tid, n2 - 1), i1 = min(tid + kStreamThreads, n2 - 1);
-    const int i2 = min(tid + 2 * kStreamThreads, n2 - 1), i3 = min(tid + 3 * kStreamThreads, n2 - 1);
-    cr0 = *BGTQ_CSRC(i0);
-    cr1 = *BGTQ_CSRC(i1);
-    cr2 = *BGTQ_CSRC(i2);
-    cr3 = *BGTQ_CSRC(i3);
+  constexpr int n1 = n0 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
+  constexpr int kRounds = (n1 + kStreamThreads - 1) / kStreamThreads;
+  const uint4 *cs0 = (const uint4 *)(consts + a.off_dtab), *cs1 = (const uint4 *)(consts + a.off_vlut) - n0;
+  uint4 cr[kRounds];
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int i = min(tid + k * kStreamThreads, n1 - 1);
+    cr[k] = *(i < n0 ? cs0 + i : cs1 + i);
   }
   StreamState st;
   st.dv0 = ((const uint32_t *)(consts + a.off_ksd))[kvh * kMaxKSteps + min(lane, kMaxKSteps - 1)];
@@ -513,16 +506,17 @@ void decode_stream_kernel(const StreamArgs a) {
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
   load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), a.wk, wkl, lane);
-  // past the copy: a spare 16 bytes at the end of the allocation takes the stores
-  *BGTQ_CDST(tid) = cr0;
-  *BGTQ_CDST(tid + kStreamThreads) = cr1;
-  *BGTQ_CDST(tid + 2 * kStreamThreads) = cr2;
-  *BGTQ_CDST(tid + 3 * kStreamThreads) = cr3;
-#undef BGTQ_CDST
-#undef BGTQ_CSRC
+  prep_load_band(pl, (const float *)(consts + a.off_bandk), tid);
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int i = tid + k * kStreamThreads;
+    *(uint4 *)(smem + (i < n0 ? 16 * i : i < n1 ? Lds::vlut + 16 * (i - n0) : Lds::spare)) = cr[k];
+  }
+  // the queries of this (sequence, KV head), rotated and scaled (ends with a barrier)
+  prep_build_rows<G>(pl, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
   float rinv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(pr + PO::rinv))[h];
+  for (int h = 0; h < G; ++h) rinv[h] = lds_at<float>(Lds::rinv + 4 * h);
   {
     int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
     st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
@@ -533,7 +527,6 @@ void decode_stream_kernel(const StreamArgs a) {
     st.cgrp = kd->cgrp;
     st.jrng = kd->jrng;
   }
-  __syncthreads();
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
@@ -569,6 +562,7 @@ void decode_stream_kernel(const StreamArgs a) {
     rr[4 + 64 + lane] = acc1[h >> 2][h & 3];
   }
   __syncthreads();
+  const size_t head0 = (size_t)b * a.hq + (size_t)kvh * G;  // first query head of this (sequence, KV head)
   for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
     const int h = idx / kHeadDim, i = idx % kHeadDim;
     float mx = -INFINITY;
@@ -584,7 +578,7 @@ void decode_stream_kernel(const StreamArgs a) {
         l = fmaf(f, rr[1], l);
       }
     }
-    float *o = a.part + (((size_t)b * a.hq + (size_t)kvh * G + h) * a.n_splits + split) * kPartStride;
+    float *o = a.part + ((head0 + h) * a.n_splits + split) * kPartStride;
     o[4 + i] = s;
     if (i == 0) o[0] = mx, o[1] = l;
   }
@@ -597,7 +591,7 @@ void decode_stream_kernel(const StreamArgs a) {
 // Then: M = max_s m_s, w_s = 2^(m_s - M) / (sum_s 2^(m_s - M) l_s sqrt(128)),
 // y = sum_s w_s acc_s, out[j] = sum_k Pi_V[k][j] y[k] (four threads per j).
 constexpr int kMergeThreads = 512;
-constexpr int kMergeRegs = 16;  // split accumulators per thread held in registers (n_splits <= 64)
+constexpr int kMergeRegs = 16;  // split accumulators per thread loaded before the weights (n_splits <= 64)
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ pvt_all,
                                                               const float *__restrict__ part, int n_splits,
@@ -651,7 +645,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
       const int sp = par + 4 * u;
       if (sp < n_splits) acc = fmaf(wsm[sp], av[u], acc);
     }
-    for (int sp = par + 4 * kMergeRegs; sp < n_splits; sp += 4) acc = fmaf(wsm[sp], pv[(size_t)sp * kPartStride], acc);
+    // further splits: chunks of kMergeRegs independent loads
+    for (int c0 = par + 4 * kMergeRegs; c0 < n_splits; c0 += 4 * kMergeRegs) {
+      float v[kMergeRegs];
+#pragma unroll
+      for (int u = 0; u < kMergeRegs; ++u) v[u] = pv[(size_t)min(c0 + 4 * u, n_splits - 1) * kPartStride];
+#pragma unroll
+      for (int u = 0; u < kMergeRegs; ++u)
+        if (c0 + 4 * u < n_splits) acc = fmaf(wsm[c0 + 4 * u], v[u], acc);
+    }
     ys[par * kHeadDim + i] = acc;
   }
   __syncthreads();
@@ -674,28 +676,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
 }
 
 // ------------------------------------------------------------------ host
+// ------------------------------------------------------------------ host
 
-typedef void (*stream_fn)(const StreamArgs);
-typedef void (*prep_fn)(const PrepArgs);
-
-prep_fn pick_prep(int g) {
-  switch (g) {
-    case 1: return prep_kernel<1>;
-    case 2: return prep_kernel<2>;
-    case 4: return prep_kernel<4>;
-    default: return prep_kernel<8>;
-  }
-}
+typedef void (*decode_fn)(const DecodeArgs);
 
 template <int G, int VB>
-stream_fn pick_wk(int wk) {
-  if (wk <= 8) return decode_stream_kernel<G, VB, 8>;
-  if (wk <= 12) return decode_stream_kernel<G, VB, 12>;
-  return decode_stream_kernel<G, VB, 16>;
+decode_fn pick_wk(int wk) {
+  if (wk <= 8) return decode_kernel<G, VB, 8>;
+  if (wk <= 12) return decode_kernel<G, VB, 12>;
+  return decode_kernel<G, VB, 16>;
 }
 
 template <int G>
-stream_fn pick_vb(int vb, int wk) {
+decode_fn pick_vb(int vb, int wk) {
   switch (vb) {
     case 1: return pick_wk<G, 1>(wk);
     case 2: return pick_wk<G, 2>(wk);
@@ -704,7 +697,7 @@ stream_fn pick_vb(int vb, int wk) {
   }
 }
 
-stream_fn pick_stream(int g, int vb, int wk) {
+decode_fn pick_decode(int g, int vb, int wk) {
   switch (g) {
     case 1: return pick_vb<1>(vb, wk);
     case 2: return pick_vb<2>(vb, wk);
@@ -713,9 +706,9 @@ stream_fn pick_stream(int g, int vb, int wk) {
   }
 }
 
-int stream_smem_bytes(int g, int vb) {
+int decode_smem_bytes(int g, int vb) {
 #define BGTQ_SM(G_, VB_) \
-  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::total + 16;
+  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::alloc;
   BGTQ_SM(1, 1) BGTQ_SM(1, 2) BGTQ_SM(1, 3) BGTQ_SM(1, 4)
   BGTQ_SM(2, 1) BGTQ_SM(2, 2) BGTQ_SM(2, 3) BGTQ_SM(2, 4)
   BGTQ_SM(4, 1) BGTQ_SM(4, 2) BGTQ_SM(4, 3) BGTQ_SM(4, 4)
@@ -724,11 +717,10 @@ int stream_smem_bytes(int g, int vb) {
   return -1;
 }
 
+// Workspace: the split partials [batch][hq][n_splits][kPartStride] f32.
 struct DecodeLayout {
   int n_splits, tiles_per_split;
-  size_t prep_off;     // workspace offset of the prep output
-  int64_t prep_stride;  // bytes per (sequence, KV head)
-  size_t total;         // workspace bytes: split partials, then prep output
+  size_t total;
 };
 
 DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
@@ -741,18 +733,16 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   const int tps = (tiles + s - 1) / s;
   d.n_splits = (tiles + tps - 1) / tps;
   d.tiles_per_split = tps;
-  d.prep_off = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
-  d.prep_stride = prep_stride_of(p.hdr.group);
-  d.total = d.prep_off + (size_t)batch * hkv * (size_t)d.prep_stride;
+  d.total = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
   return d;
 }
 
-// The stream kernels address LDS from offset 0: they must have no static LDS.
-bool stream_static_lds_ok(stream_fn fn) {
+// The decode kernels address LDS from offset 0: they must have no static LDS.
+bool decode_static_lds_ok(decode_fn fn) {
   static std::mutex mu;
-  static std::vector<stream_fn> checked;
+  static std::vector<decode_fn> checked;
   std::lock_guard<std::mutex> lk(mu);
-  for (stream_fn f : checked)
+  for (decode_fn f : checked)
     if (f == fn) return true;
   hipFuncAttributes attr{};
   if (hipFuncGetAttributes(&attr, (const void *)fn) != hipSuccess || attr.sharedSizeBytes != 0) return false;
@@ -761,22 +751,6 @@ bool stream_static_lds_ok(stream_fn fn) {
 }
 
 float kscale_of(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }  // logits in log2 units
-
-PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
-                   int64_t max_seq_len, float softmax_scale) {
-  const DecodeLayout lay = decode_layout(p, batch, max_seq_len);
-  PrepArgs pa;
-  pa.consts = (const uint8_t *)dev_consts;
-  pa.q = q;
-  pa.out = (uint8_t *)workspace + lay.prep_off;
-  pa.off_kvh = p.hdr.off_kvh;
-  pa.off_rot32 = p.hdr.off_rot32_k;
-  pa.stride = lay.prep_stride;
-  pa.hkv = p.desc.n_kv_heads;
-  pa.hq = p.desc.n_q_heads;
-  pa.kscale = kscale_of(softmax_scale);
-  return pa;
-}
 
 bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
                          const void *workspace, size_t ws_bytes, const char *nm) {
@@ -791,24 +765,17 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
   return BGTQ_OK;
 }
 
-bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
+bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   const DecodeLayout lay = decode_layout(p, c.batch, c.max_seq_len);
   const int G = p.hdr.group, vb = p.hdr.v_bits;
-  const int smem = stream_smem_bytes(G, vb);
-  stream_fn fn = pick_stream(G, vb, p.hdr.wk);
-  if (!stream_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: stream kernel has static LDS");
+  const int smem = decode_smem_bytes(G, vb);
+  decode_fn fn = pick_decode(G, vb, p.hdr.wk);
+  if (smem < 0 || !decode_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: LDS request above the limit");
   }
   hipStream_t st = (hipStream_t)c.stream;
-  float *part = (float *)c.workspace;
-  if (with_prep) {
-    const PrepArgs pa = prep_args(p, c.dev_consts, c.q, c.workspace, c.batch, c.max_seq_len, c.softmax_scale);
-    pick_prep(G)<<<dim3(p.desc.n_kv_heads, c.batch), kPrepThreads, 0, st>>>(pa);
-    const bgtq_status ps = launch_status("decode (prep)");
-    if (ps != BGTQ_OK) return ps;
-  }
   hipEvent_t e0 = nullptr, e1 = nullptr;
   {
     Prof &pr = prof();
@@ -823,36 +790,39 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
       }
     }
   }
-  StreamArgs sa;
-  sa.consts = (const uint8_t *)c.dev_consts;
-  sa.prep = (const uint8_t *)c.workspace + lay.prep_off;
-  sa.kc = c.k_codes;
-  sa.kn = c.k_norms;
-  sa.vc = c.v_codes;
-  sa.vn = c.v_norms;
-  sa.seq_lens = c.seq_lens;
-  sa.part = part;
-  sa.tiles_cap = (c.capacity + kTile - 1) / kTile;
-  sa.max_seq_len = c.max_seq_len;
-  sa.off_kvh = p.hdr.off_kvh;
-  sa.off_ksd = p.hdr.off_ksd;
-  sa.off_dtab = p.hdr.off_dtab;
-  sa.off_vlut = p.hdr.off_vlut;
-  sa.prep_stride = lay.prep_stride;
-  sa.hkv = p.desc.n_kv_heads;
-  sa.hq = p.desc.n_q_heads;
-  sa.wk = p.hdr.wk;
-  sa.tiles_per_split = lay.tiles_per_split;
-  sa.n_splits = lay.n_splits;
-  sa.seq_add = c.seq_add;
+  uint8_t *ws = (uint8_t *)c.workspace;
+  DecodeArgs a;
+  a.consts = (const uint8_t *)c.dev_consts;
+  a.q = c.q;
+  a.kc = c.k_codes;
+  a.kn = c.k_norms;
+  a.vc = c.v_codes;
+  a.vn = c.v_norms;
+  a.seq_lens = c.seq_lens;
+  a.part = (float *)ws;
+  a.tiles_cap = (c.capacity + kTile - 1) / kTile;
+  a.max_seq_len = c.max_seq_len;
+  a.off_kvh = p.hdr.off_kvh;
+  a.off_ksd = p.hdr.off_ksd;
+  a.off_dtab = p.hdr.off_dtab;
+  a.off_vlut = p.hdr.off_vlut;
+  a.off_rowk = p.hdr.off_rowk;
+  a.off_bandk = p.hdr.off_bandk;
+  a.hkv = p.desc.n_kv_heads;
+  a.hq = p.desc.n_q_heads;
+  a.wk = p.hdr.wk;
+  a.tiles_per_split = lay.tiles_per_split;
+  a.n_splits = lay.n_splits;
+  a.seq_add = c.seq_add;
+  a.kscale = kscale_of(c.softmax_scale);
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
   // With profiling on, the events are bound to the launch itself, so their elapsed time is the
-  // kernel's own start-to-end time (no queue packets of their own between the kernels).
+  // kernel's own start-to-end time (no queue packets of their own around the kernel).
   if (e0)
-    hipExtLaunchKernelGGL(fn, grid, dim3(kStreamThreads), (uint32_t)smem, st, e0, e1, 0, sa);
+    hipExtLaunchKernelGGL(fn, grid, dim3(kStreamThreads), (uint32_t)smem, st, e0, e1, 0, a);
   else
-    fn<<<grid, kStreamThreads, smem, st>>>(sa);
-  bgtq_status s = launch_status("decode (stream)");
+    fn<<<grid, kStreamThreads, smem, st>>>(a);
+  const bgtq_status s = launch_status("decode");
   if (e1) {
     Prof &pr = prof();
     std::lock_guard<std::mutex> lk(pr.mu);
@@ -860,8 +830,8 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep) {
   }
   if (s != BGTQ_OK) return s;
   merge_kernel<<<dim3(p.desc.n_q_heads, c.batch), kMergeThreads, 0, st>>>(
-      (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v), part, lay.n_splits, G, p.desc.n_q_heads,
-      c.out);
+      (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v), (const float *)ws, lay.n_splits, G,
+      p.desc.n_q_heads, c.out);
   return launch_status("decode (merge)");
 }
 
@@ -900,7 +870,7 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
   if (v != BGTQ_OK) return v;
   DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
                softmax_scale, out, workspace, stream};
-  return decode_launch(plan->p, c, true);
+  return decode_launch(plan->p, c);
 }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ bgtq_status fail(bgtq_status s, const std::string &m);
 bgtq_status launch_status(const char *what);
 int device_cus();
 
-// Events bracketing the cache-streaming kernel while profiling is on.
+// Events bracketing the decode kernel while profiling is on.
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -42,12 +42,9 @@ struct DecodeCall {
   void *workspace;
   bgtq_stream stream;
 };
-struct PrepArgs;
 bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
                          const void *workspace, size_t ws_bytes, const char *nm);
-bgtq_status decode_launch(const Plan &p, const DecodeCall &c, bool with_prep);  // [prep], stream, merge
-PrepArgs prep_args(const Plan &p, const void *dev_consts, const uint16_t *q, void *workspace, int batch,
-                   int64_t max_seq_len, float softmax_scale);
+bgtq_status decode_launch(const Plan &p, const DecodeCall &c);  // the fused decode kernel
 
 struct AppendArgs;
 AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,

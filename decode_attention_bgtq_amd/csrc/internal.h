@@ -74,6 +74,10 @@ struct ConstHeader {
   int64_t off_dtab;          // decode tables, kDtabBytes (layout above)
   int64_t off_vlut;          // value-width table: fp16 centroid pairs of the tokens of one code chunk
   int64_t vlut_bytes;
+  int64_t off_rowk;          // uint2 [n_kv_heads][128]: per group-order row p of the key rotation, x = float
+                             // offset of its band in the band area, y = d_g | pos_g << 8 | w << 16 | kbase << 19
+                             // (kbase: first k-step of a width-1..3 group); y = 0 past d_nz
+  int64_t off_bandk;         // float: per KV head and group, Pi_g row-major (d_g x d_g), groups in order
   int64_t total_bytes;
   double thr[4][16];         // interior thresholds of the b-bit quantiser, row b-1
   double cent[4][16];        // centroids, row b-1

@@ -278,6 +278,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
 
   // decode k-steps of the width-1..3 groups (four positions each)
   p.ksd.assign((size_t)hkv * kMaxKSteps, 0u);
+  std::vector<int> kbase((size_t)hkv * kMaxGroups, 0);  // first k-step of each width-1..3 group
   int max_ksteps = 0;
   for (int h = 0; h < hkv; ++h) {
     KvhDesc &kd = p.kvh[h];
@@ -293,6 +294,7 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
       if (g.w == 4) continue;  // one matrix-core step per code in the decode
       const int rg = 3 - g.w;  // rest-group index
       cfirst[rg] = c;
+      kbase[(size_t)h * kMaxGroups + gi] = c;
       for (int r0 = 0; r0 < g.d; r0 += 4, ++c) {
         if (c >= kMaxKSteps) {
           err = "internal: too many k-steps";
@@ -362,6 +364,13 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   hd.off_vlut = off;
   hd.vlut_bytes = 4 * (int64_t)vlut.size();
   off = align256(off + 4 * vlut.size());
+  hd.off_rowk = off;
+  off = align256(off + 8 * (size_t)hkv * kHeadDim);
+  hd.off_bandk = off;
+  int64_t band_floats = 0;
+  for (int h = 0; h < hkv; ++h)
+    for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) band_floats += (int64_t)p.kvh[h].g[gi].d * p.kvh[h].g[gi].d;
+  off = align256(off + 4 * (size_t)std::max<int64_t>(band_floats, 4));
   hd.total_bytes = off;
 
   p.image.assign(off, 0);
@@ -382,6 +391,26 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
           r32k[((size_t)h * kHeadDim + g.pos + i) * kHeadDim + g.pos + k] = (float)pi[(size_t)i * g.d + k];
         }
     }
+  {
+    // key rotation bands for the decode's query preparation
+    uint32_t *rowk = (uint32_t *)(img + hd.off_rowk);
+    float *band = (float *)(img + hd.off_bandk);
+    size_t gi_all = 0;
+    int64_t boff = 0;
+    for (int h = 0; h < hkv; ++h)
+      for (int gi = 0; gi < p.kvh[h].n_groups; ++gi, ++gi_all) {
+        const KGroupDesc &g = p.kvh[h].g[gi];
+        const std::vector<double> &pi = p.rot_k[gi_all];
+        const uint32_t kb = g.w < 4 ? (uint32_t)kbase[(size_t)h * kMaxGroups + gi] : 0u;
+        for (int i = 0; i < g.d; ++i) {
+          const size_t r = (size_t)h * kHeadDim + g.pos + i;
+          rowk[2 * r] = (uint32_t)(boff + (int64_t)i * g.d);
+          rowk[2 * r + 1] = (uint32_t)g.d | ((uint32_t)g.pos << 8) | ((uint32_t)g.w << 16) | (kb << 19);
+          for (int k = 0; k < g.d; ++k) band[boff + (int64_t)i * g.d + k] = (float)pi[(size_t)i * g.d + k];
+        }
+        boff += (int64_t)g.d * g.d;
+      }
+  }
   {
     uint8_t *dt = img + hd.off_dtab;
     float *c4 = (float *)(dt + kDtabC4);

@@ -1,16 +1,15 @@
 // Query preparation for the fused decode: rotation of the queries once per
-// key width group (fp32 MFMA) and their matrix-core operands for the stream
-// kernel ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract;
-// Block-GTQ README, backend table).  Internal header, shared by the decode
-// launches and the fused decode step.
+// key width group and their matrix-core operands for the tile loop
+// ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract; Block-GTQ
+// README, backend table).  Internal header.  The decode kernel prepares the
+// queries of its (sequence, KV head) in its own prologue from the group
+// rotations stored as bands (fp32 VALU); the query-rotation entry point rotates
+// batches of queries with fp32 MFMA over the block-diagonal matrix.
 #pragma once
 
 #include "device.h"
 
 namespace bgtq {
-
-constexpr int kPrepWaves = 8;
-constexpr int kPrepThreads = 64 * kPrepWaves;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -19,13 +18,15 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // (rows and columns in group order, zero outside the blocks and past d_nz).
 // qg [8][128]: the queries in group order, rows h >= G zero; qs [G][128].
 // 16x16x4 fp32 MFMA tiles, the query heads as columns; the 8 row tiles of 16
-// are spread over the WAVES waves (8 / WAVES tiles each).  The operand rows of R are fetched by
-// rot_rows (addresses independent of the descriptor), the MFMAs run in
-// rot_tiles.
+// are spread over the WAVES waves (8 / WAVES tiles each).  Step (u, e) of a
+// tile contracts column 16 u + 4 kq + e in the lanes of quarter kq (the sum
+// runs over every column once), so that A and B are read as float4.  The
+// operand rows of R are fetched by rot_rows (addresses independent of the
+// group layout), the MFMAs run in rot_tiles.
 template <int WAVES>
 struct RotRows {
   static constexpr int nt = 8 / WAVES;  // row tiles per wave
-  float a[nt][kHeadDim / 4];
+  float4 a[nt][kHeadDim / 16];
 };
 
 template <int WAVES>
@@ -34,8 +35,9 @@ __device__ __forceinline__ void rot_rows(const float *R, int wave, int lane, Rot
 #pragma unroll
   for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) {
     const int t = wave + t2 * WAVES;
+    const float4 *row = (const float4 *)(R + (16 * t + n) * kHeadDim + 4 * kq);
 #pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) rr.a[t2][s] = R[(16 * t + n) * kHeadDim + 4 * s + kq];
+    for (int u = 0; u < kHeadDim / 16; ++u) rr.a[t2][u] = row[4 * u];
   }
 }
 
@@ -43,18 +45,22 @@ template <int WAVES>
 __device__ __forceinline__ void rot_tiles(const RotRows<WAVES> &rr, int G, const float *qg, float *qs, int wave,
                                           int lane) {
   const int n = lane & 15, kq = lane >> 4;
+  const float4 *bq = (const float4 *)(qg + (n & 7) * kHeadDim + 4 * kq);
 #pragma unroll
   for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) {
     const int t = wave + t2 * WAVES;
-    {
-      f4v acc = {0.f, 0.f, 0.f, 0.f};
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kHeadDim / 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rr.a[t2][s], qg[(n & 7) * kHeadDim + 4 * s + kq], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n < G) qs[n * kHeadDim + 16 * t + 4 * kq + r] = acc[r];
+    for (int u = 0; u < kHeadDim / 16; ++u) {
+      const float4 a = rr.a[t2][u], b = bq[4 * u];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n < G) qs[n * kHeadDim + 16 * t + 4 * kq + r] = acc[r];
   }
 }
 
@@ -71,129 +77,145 @@ __device__ __forceinline__ void gather_queries(const KvhDesc *kd, int G, const u
   }
 }
 
-struct PrepArgs {
-  const uint8_t *consts;
-  const uint16_t *q;
-  uint8_t *out;
-  int64_t off_kvh, off_rot32, stride;
-  int hkv, hq;
-  float kscale;
+// Byte offsets of the prepared query state in the decode kernel's LDS, relative
+// to its start.
+template <int G>
+struct PrepOut {
+  static constexpr int nq = (G + 3) / 4;                  // query-head quads
+  static constexpr int q4 = 0;                            // fp32 [G][128]
+  static constexpr int qr = G * kHeadDim * 4;             // fp16 [kMaxKSteps][nq][4][4]
+  static constexpr int rinv = qr + kMaxKSteps * nq * 32;  // fp32 [G]
+  static constexpr int bytes = (rinv + G * 4 + 15) & ~15;
+};
+
+// LDS scratch of the preparation (prologue only), byte offsets from its base.
+template <int G>
+struct PrepScratch {
+  static constexpr int kds = 0;                                 // KvhDesc
+  static constexpr int qs = ((int)sizeof(KvhDesc) + 15) & ~15;  // fp32 [G][128], natural coordinate order
+  static constexpr int hm = qs + G * kHeadDim * 4;              // fp32 [8 waves][G]
+  static constexpr int bytes = (hm + 8 * G * 4 + 15) & ~15;
+};
+
+// Global loads of the preparation, issued at the start of the prologue so that
+// their latency overlaps the first cache tile's.  Thread t works on row
+// p = t / 4 of the head's group-order rotation and on its columns
+// k = 2 (t % 4) + 8 u + e (u < 16, e < 2).
+struct PrepLoads {
+  uint2 row;         // row table entry of p (band offset; d_g, pos_g, width, first k-step)
+  uint32_t dw;       // one word of the KvhDesc
+  uint16_t q0, q1;   // two query values (natural order)
+  float2 r[16];      // Pi_g[p - pos_g][k], 0 past d_g
 };
 
 template <int G>
-struct PrepOut {  // byte offsets in one (sequence, KV head) block of the prep output
-  static constexpr int nq = (G + 3) / 4;            // query-head quads
-  static constexpr int q4 = 0;                      // fp32 [G][128]
-  static constexpr int qr = G * kHeadDim * 4;       // fp16 [kMaxKSteps][nq][4][4]
-  static constexpr int rinv = qr + kMaxKSteps * nq * 32;  // fp32 [G]
-  static constexpr int bytes = rinv + G * 4;
-};
+__device__ __forceinline__ void prep_load_row(PrepLoads &l, const uint2 *rows, const KvhDesc *kd, const uint16_t *qb,
+                                              int tid) {
+  constexpr int kDescWords = (int)(sizeof(KvhDesc) / 4);
+  static_assert(kDescWords <= 512 && G * kHeadDim <= 1024, "one pass of staging loads (512 threads)");
+  l.row = rows[tid >> 2];
+  l.dw = ((const uint32_t *)kd)[min(tid, kDescWords - 1)];
+  l.q0 = qb[min(tid, G * kHeadDim - 1)];
+  l.q1 = qb[min(tid + 512, G * kHeadDim - 1)];
+}
 
-// One workgroup per (KV head, sequence): the query-dependent state that every
-// split of the stream kernel shares.  The G queries are rotated once per key
-// group (fp32 MFMA, block-diagonal rotation) and written as
-//  * q4[h][r] = kscale / sqrt(d4) q_rot[h][r] for the 4-bit group (r < d4, else 0);
+// The band of row p (addresses depend on the row entry): unconditional loads at
+// clamped addresses, zeroed past d_g.
+__device__ __forceinline__ void prep_load_band(PrepLoads &l, const float *band, int tid) {
+  const int d = (int)(l.row.y & 255u), kq = tid & 3;
+  const float2 *src = (const float2 *)(band + l.row.x);
+  const int last = d > 1 ? (d - 2) >> 1 : 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) l.r[u] = src[min(kq + 4 * u, last)];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (2 * kq + 8 * u >= d) l.r[u] = make_float2(0.f, 0.f);
+}
+
+// The query-dependent state of one (sequence, KV head), built in LDS by a
+// workgroup of 512 threads from the loads above.  The G queries are rotated
+// once per key group, q_rot[h][p] = sum_k Pi_g[p - pos_g][k] q[h][coord[pos_g + k]]
+// (fp32; four threads per row, each a quarter of the columns, summed by DPP), and
+// written as
+//  * q4[h][p] = kscale / sqrt(d4) q_rot[h][p] for the 4-bit group (p < d4, else 0);
 //  * qr[k][quad][m][i] = fp16(fac_h kscale / sqrt(d_g) q_rot[h][pos_g + 4 s + i]),
 //    h = 4 quad + m, for k-step k = (group g, step s) of the width-1..3 groups
 //    (0 past the group, for h >= G and for k past the head's k-steps);
 //  * rinv[h] = 1 / fac_h, fac_h the power of two that brings the largest
 //    |kscale / sqrt(d_g) q_rot[h][p]| over those groups to [2^13, 2^14).
+// `out` and `scr` are LDS addresses (PrepOut and PrepScratch layouts).  Ends
+// with a workgroup barrier.
 template <int G>
-__device__ __forceinline__ void prep_role(const PrepArgs &a, int kvh, int b) {
+__device__ __forceinline__ void prep_build_rows(const PrepLoads &l, uint8_t *out, uint8_t *scr, float kscale,
+                                                int tid, int wave, int lane) {
   typedef PrepOut<G> PO;
-  __shared__ KvhDesc kds;
-  __shared__ float qg[8 * kHeadDim];
-  __shared__ float qs[G * kHeadDim];
-  __shared__ float gsc[kHeadDim];  // kscale / sqrt(d_g) of the group of each position
-  __shared__ float hmax[G];
-  const uint8_t *consts = a.consts;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t *out = a.out + ((size_t)b * a.hkv + kvh) * (size_t)a.stride;
-  // ---- one round of loads: descriptor and queries (natural order, in the
-  // rotated-query area) first, then the rotation rows (fixed addresses), so
-  // that staging the former waits for them only.
+  typedef PrepScratch<G> PS;
   constexpr int kDescWords = (int)(sizeof(KvhDesc) / 4);
-  static_assert(kDescWords <= kPrepThreads && G * kHeadDim <= 2 * kPrepThreads, "one pass of staging loads");
-  const uint32_t dw = ((const uint32_t *)((const KvhDesc *)(consts + a.off_kvh) + kvh))[min(tid, kDescWords - 1)];
-  const uint16_t *qb = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim;
-  const uint16_t q0 = qb[min(tid, G * kHeadDim - 1)];
-  const uint16_t q1 = qb[min(tid + kPrepThreads, G * kHeadDim - 1)];
-  RotRows<kPrepWaves> rr;
-  rot_rows<kPrepWaves>((const float *)(consts + a.off_rot32) + (size_t)kvh * kHeadDim * kHeadDim, wave, lane, rr);
-  if (tid < kDescWords) ((uint32_t *)&kds)[tid] = dw;
-  if (tid < G * kHeadDim) qs[tid] = h2f(q0);
-  if (tid + kPrepThreads < G * kHeadDim) qs[tid + kPrepThreads] = h2f(q1);
+  const KvhDesc &kds = *(const KvhDesc *)(scr + PS::kds);
+  float *qs = (float *)(scr + PS::qs), *hm = (float *)(scr + PS::hm);
+  // ---- stage the descriptor and the queries; clear the k-step operands
+  if (tid < kDescWords) ((uint32_t *)(scr + PS::kds))[tid] = l.dw;
+  if (tid < G * kHeadDim) qs[tid] = h2f(l.q0);
+  if (tid + 512 < G * kHeadDim) qs[tid + 512] = h2f(l.q1);
+  constexpr int kQrVec = kMaxKSteps * PO::nq * 32 / 16;
+  for (int i = tid; i < kQrVec; i += 512) ((uint4 *)(out + PO::qr))[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  const int d4 = kds.d4, dnz = kds.d_nz;
-  {
-    // group order: qg[h][p] = q[h][coord[p]] (rows h >= G and positions >= d_nz zero)
-    const int p = tid & (kHeadDim - 1);
-    const int cp = kds.coord[p < dnz ? p : 0];
-    for (int i = tid; i < 8 * kHeadDim; i += kPrepThreads) {
-      const int h = i >> 7;
-      const float v = qs[(h < G ? h : 0) * kHeadDim + cp];
-      qg[i] = (h < G && p < dnz) ? v : 0.f;
-    }
-    if (tid < kHeadDim) {
-      float sc = 0.f;
-      for (int gi = 0; gi < kds.n_groups; ++gi)
-        if (tid >= kds.g[gi].pos && tid < kds.g[gi].pos + kds.g[gi].d) sc = a.kscale / sqrtf((float)kds.g[gi].d);
-      gsc[tid] = sc;
-    }
-  }
-  __syncthreads();
-  rot_tiles<kPrepWaves>(rr, G, qg, qs, wave, lane);
-  __syncthreads();
-  // per head: the largest scaled |q_rot| over the width-1..3 groups, one wave per head
-  for (int h = wave; h < G; h += kPrepWaves) {
-    float v = 0.f;
-    for (int p = d4 + lane; p < dnz; p += 64) v = fmaxf(v, fabsf(qs[h * kHeadDim + p] * gsc[p]));
-    v = wave_max(v);
-    if (lane == 0) hmax[h] = v;
-  }
-  {
-    float *q4 = (float *)(out + PO::q4);
-    const float s4 = d4 > 0 ? a.kscale / sqrtf((float)d4) : 0.f;
-    for (int idx = tid; idx < G * kHeadDim; idx += kPrepThreads) {
-      const int h = idx >> 7, r = idx & (kHeadDim - 1);
-      q4[idx] = r < d4 ? qs[h * kHeadDim + r] * s4 : 0.f;
+  // ---- rotation of row p: this thread's quarter of the columns, then the quad sum
+  const int p = tid >> 2, kq = tid & 3;
+  const int d = (int)(l.row.y & 255u), pos = (int)((l.row.y >> 8) & 255u), w = (int)((l.row.y >> 16) & 7u);
+  const int kb = (int)(l.row.y >> 19);
+  float acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int k = 2 * kq + 8 * u;
+    if (k < d) {  // d is even: k + 1 < d too
+      const int c0 = kds.coord[pos + k], c1 = kds.coord[pos + k + 1];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h] = fmaf(l.r[u].x, qs[h * kHeadDim + c0], acc[h]);
+        acc[h] = fmaf(l.r[u].y, qs[h * kHeadDim + c1], acc[h]);
+      }
     }
   }
-  __syncthreads();
-  float fac[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float m = hmax[h];
+    acc[h] += dpp_f<0xB1>(acc[h]);  // quad_perm [1,0,3,2]
+    acc[h] += dpp_f<0x4E>(acc[h]);  // quad_perm [2,3,0,1]
+  }
+  const float gsc = d > 0 ? kscale / sqrtf((float)d) : 0.f;
+  // 4-bit rows -> q4 (every row written: 0 outside the 4-bit group); heads kq, kq + 4
+  float *q4 = (float *)(out + PO::q4);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if ((h & 3) == kq) q4[h * kHeadDim + p] = w == 4 ? acc[h] * gsc : 0.f;
+  // per head: the largest scaled |q_rot| over the width-1..3 rows (wave, then workgroup)
+  const bool low = d > 0 && w < 4;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float v = wave_max(low ? fabsf(acc[h] * gsc) : 0.f);
+    if (lane == 0) hm[wave * G + h] = v;
+  }
+  __syncthreads();
+  // ---- power-of-two operand scale per head; k-step operands of the width-1..3 rows
+  _Float16 *qr = (_Float16 *)(out + PO::qr);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 8; ++wv) m = fmaxf(m, hm[wv * G + h]);
     int e = 0;
     (void)frexpf(m, &e);
     e = m > 0.f ? e : 0;
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
-    fac[h] = ldexpf(1.f, 14 - e);
     if (tid == h) ((float *)(out + PO::rinv))[h] = ldexpf(1.f, e - 14);
-  }
-  // k-step operand rows, in group order 3, 2, 1
-  _Float16 *qr = (_Float16 *)(out + PO::qr);
-  for (int idx = tid; idx < kMaxKSteps * PO::nq * 16; idx += kPrepThreads) {
-    const int i = idx & 3, m = (idx >> 2) & 3, quad = (idx >> 4) % PO::nq, k = (idx >> 4) / PO::nq;
-    const int h = 4 * quad + m;
-    int p = -1, k0 = 0;
-    for (int gi = 0; gi < kds.n_groups; ++gi) {
-      const KGroupDesc &g = kds.g[gi];
-      if (g.w == 4) continue;
-      const int ns = (g.d + 3) >> 2;
-      if (k >= k0 && k < k0 + ns && 4 * (k - k0) + i < g.d) p = g.pos + 4 * (k - k0) + i;
-      k0 += ns;
+    if (low && (h & 3) == kq) {
+      const int r = p - pos, k = kb + (r >> 2);
+      qr[((k * PO::nq + (h >> 2)) * 4 + (h & 3)) * 4 + (r & 3)] = (_Float16)(ldexpf(1.f, 14 - e) * (acc[h] * gsc));
     }
-    float v = 0.f;
-    if (h < G && p >= 0) {
-      float fh = fac[0];
-#pragma unroll
-      for (int u = 1; u < G; ++u) fh = h == u ? fac[u] : fh;
-      v = fh * (gsc[p] * qs[h * kHeadDim + p]);
-    }
-    qr[idx] = (_Float16)v;
   }
+  __syncthreads();
 }
 
 }  // namespace bgtq

@@ -1,55 +1,33 @@
 // Fused decode step: the new token's key and value appended to the packed
-// cache and the query prepared in one launch, then the cache-streaming and
-// merge launches of the decode ("RoPE-Aware Bit Allocation for KV-Cache
-// Quantization", Abstract: packed-cache serving; Block-GTQ README, backend
-// table).
+// cache in one launch, then the fused decode over the cache including that
+// token ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract:
+// packed-cache serving; Block-GTQ README, backend table).
 #include "append.h"
 #include "device.h"
 #include "host.h"
-#include "prep.h"
 
 namespace bgtq {
 
 // Workgroups [0, n): key append of (sequence, KV head) = (r / hkv, r % hkv);
-// [n, 2n): value append; [2n, 3n): query preparation.  n = batch * hkv.  Every
-// role is independent of the others.
-template <int G>
-__global__ __launch_bounds__(kAppendThreads) void step_kernel(const AppendArgs ka, const AppendArgs va,
-                                                              const PrepArgs pa, const int32_t *__restrict__ pos,
-                                                              int64_t capacity, int n) {
-  static_assert(kAppendThreads == kPrepThreads, "one block size for every role");
-  const int role = blockIdx.x, hkv = pa.hkv;
-  if (role < 2 * n) {
-    const int r = role < n ? role : role - n;
-    const int kvh = r % hkv, b = r / hkv;
-    const int64_t t = pos[b];
-    if (t < 0 || t >= capacity) return;  // uniform per workgroup
-    const int64_t tile = t / kTile;
-    const int lo = (int)(t - tile * kTile);
-    if (role < n) {
-      if (ka.wk > 0) append_role<false>(ka, tile, kvh, b, lo, lo + 1, b);
-    } else {
-      append_role<true>(va, tile, kvh, b, lo, lo + 1, b);
-    }
+// [n, 2n): value append.  n = batch * hkv.
+__global__ __launch_bounds__(kAppendThreads) void step_append_kernel(const AppendArgs ka, const AppendArgs va,
+                                                                     const int32_t *__restrict__ pos,
+                                                                     int64_t capacity, int n) {
+  const int role = blockIdx.x, hkv = ka.hkv;
+  const int r = role < n ? role : role - n;
+  const int kvh = r % hkv, b = r / hkv;
+  const int64_t t = pos[b];
+  if (t < 0 || t >= capacity) return;  // uniform per workgroup
+  const int64_t tile = t / kTile;
+  const int lo = (int)(t - tile * kTile);
+  if (role < n) {
+    if (ka.wk > 0) append_role<false>(ka, tile, kvh, b, lo, lo + 1, b);
   } else {
-    const int r = role - 2 * n;
-    prep_role<G>(pa, r % hkv, r / hkv);
-  }
-}
-
-typedef void (*step_fn)(const AppendArgs, const AppendArgs, const PrepArgs, const int32_t *, int64_t, int);
-
-step_fn pick_step(int g) {
-  switch (g) {
-    case 1: return step_kernel<1>;
-    case 2: return step_kernel<2>;
-    case 4: return step_kernel<4>;
-    default: return step_kernel<8>;
+    append_role<true>(va, tile, kvh, b, lo, lo + 1, b);
   }
 }
 
 }  // namespace bgtq
-
 using namespace bgtq;
 
 extern "C" {
@@ -67,20 +45,19 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
       decode_check(p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, "bgtq_decode_step");
   if (v != BGTQ_OK) return v;
   const int n = batch * p.desc.n_kv_heads;
-  const int64_t blocks = (int64_t)n * 3;
+  const int64_t blocks = (int64_t)n * 2;
   if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, "bgtq_decode_step: grid too large");
   const int64_t tiles_cap = (capacity + kTile - 1) / kTile;
   const uint8_t *c = (const uint8_t *)dev_consts;
   const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, tiles_cap, false);
   const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, tiles_cap, true);
-  const PrepArgs pa = prep_args(p, dev_consts, q, workspace, batch, max_seq_len, softmax_scale);
   hipStream_t st = (hipStream_t)stream;
-  pick_step(p.hdr.group)<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pa, pos, capacity, n);
-  const bgtq_status ls = launch_status("bgtq_decode_step (append and prep)");
+  step_append_kernel<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pos, capacity, n);
+  const bgtq_status ls = launch_status("bgtq_decode_step (append)");
   if (ls != BGTQ_OK) return ls;
   DecodeCall dc{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, pos, 1, batch, max_seq_len,
                 softmax_scale, out, workspace, stream};
-  return decode_launch(p, dc, false);
+  return decode_launch(p, dc);
 }
 
 }  // extern "C"
