@@ -86,11 +86,12 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 //   [rinv, ..)       per head: 1 / the power-of-two scale of its k-step operands
 //   [vlut, ..)       value table
 //   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
+//   [kw, ..)         per wave: the tile's key words [WK + 2][64] (the last two rows zero)
 // The query preparation uses [scr, ..) (from pt on) as scratch before the tile
 // loop; after it the area from 0 is reused for the wave merge.  Past `total`:
 // 16 spare bytes that take the stores of the table copy falling outside the
 // tables.
-template <int G, int VB>
+template <int G, int VB, int WK = kMaxWK>
 struct StreamLds {
   static constexpr int c4 = kDtabC4, t2 = kDtabT2, t1 = kDtabT1, t3 = kDtabT3;
   static constexpr int q4 = kDtabBytes;
@@ -98,7 +99,9 @@ struct StreamLds {
   static constexpr int rinv = q4 + PrepOut<G>::rinv;
   static constexpr int vlut = q4 + PrepOut<G>::bytes;
   static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
-  static constexpr int end = pt + kStreamWaves * G * kTile * 2;
+  static constexpr int kw = pt + kStreamWaves * G * kTile * 2;
+  static constexpr int kw_rows = WK + 2;  // key words of the tile, then two zero rows
+  static constexpr int end = kw + kStreamWaves * kw_rows * kTile * 4;
   static constexpr int scr = pt;
   static constexpr int scr_end = scr + PrepScratch<G>::bytes;
   static constexpr int merge = kStreamWaves * G * kPartStride * 4;
@@ -106,7 +109,7 @@ struct StreamLds {
   static constexpr int total = m1 > merge ? m1 : merge;
   static constexpr int spare = total, alloc = total + 16;
   static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0, "table bases above the index bits");
-  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && scr % 16 == 0, "16-byte aligned areas");
+  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && scr % 16 == 0 && kw % 16 == 0, "16-byte aligned areas");
 };
 
 template <int VB, int WK>
@@ -161,10 +164,10 @@ __device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *_
 }
 
 struct StreamState {
-  uint32_t dv0;       // lane c: descriptor of k-step c
-  uint32_t av;        // lane jj: first k-step anchored at key word jj-1
-  uint32_t laneoff;   // (lane & 3) * 8: this lane's query row inside a k-step operand
-  uint32_t cgrp, jrng;  // k-step boundaries and word-slot ranges of the width-3, 2, 1 groups
+  uint32_t kwl;       // LDS byte address of this lane's word 0 in this wave's key-word rows
+  uint32_t qrl;       // LDS byte address of this lane's row in k-step 0's query operand
+  uint32_t cgrp;      // first k-step of the width-3, 2, 1 groups (bytes 0..2), k-step count (byte 3)
+  uint32_t gbit;      // first stream bit of the width-3, 2, 1 groups (10 bits each)
   uint32_t ptw;       // LDS byte offset of this wave's weight rows
   int wk, n4w;
   int64_t seq;
@@ -222,69 +225,80 @@ __device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, in
 // Width-1..3 groups on the matrix cores: per k-step (four positions of one
 // group), v_mfma_f32_4x4x4f16 adds sum_i q[m][i] c[code_i] for every token.
 // Block k is lanes 4k .. 4k + 3 = tokens; its B operand is the token's four
-// fp16 centroids, looked up from the k-step's code bits (funnel-shifted out of
-// the key words hi:lo so that they start at bit kstep_bit(W)), and every block
+// fp16 centroids, looked up from the k-step's 4w code bits, and every block
 // takes the same A operand, head m's four scaled query values, from the LDS
 // operand row of the k-step (lane 4k + m reads row m).
-template <int G, int VB, int W>
-__device__ __forceinline__ h4v kstep_b(uint32_t dsc, uint32_t hi, uint32_t lo) {
-  typedef StreamLds<G, VB> Lds;
-  const uint32_t t = __builtin_amdgcn_alignbit(hi, lo, dsc);
-  if constexpr (W == 3)
-    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(Lds::t3 + (t & 0xFCu)),
-                                         lds_at<uint32_t>(Lds::t3 + ((t >> 6) & 0xFCu))});
-  else if constexpr (W == 2)
-    return lds_at<h4v>(Lds::t2 + (t & 0x7F8u));
+//
+// The key words of the tile are staged in LDS (this wave's rows [word][lane],
+// two zero rows past the last word), so that a group's bits can be re-read
+// from its first word b (a per-head value) and realigned to bit 0:
+// al[i] = bits [32 i, 32 i + 32) of the group = alignbit(W[b + i + 1], W[b + i],
+// shift).  K-step s then sits at the static bits [4 w s, 4 w s + 4 w) of al.
+template <int W>
+struct KStep {
+  static constexpr int bits = 4 * W;
+  // highest aligned register that k-step s touches
+  static constexpr int last_reg(int s) { return (bits * s + bits - 1) / 32; }
+};
+
+template <int W, int S>
+__device__ __forceinline__ uint32_t kstep_bits(const uint32_t (&al)[13]) {
+  constexpr int lo = KStep<W>::bits * S, i = lo / 32, off = lo % 32;
+  if constexpr (off + KStep<W>::bits <= 32)
+    return al[i] >> off;
   else
-    return lds_at<h4v>(Lds::t1 + (t & 0x78u));
+    return __builtin_amdgcn_alignbit(al[i + 1], al[i], off);
 }
 
-template <int G, int VB>
-__device__ __forceinline__ uint32_t kstep_a(uint32_t dsc, uint32_t laneoff) {
-  return (uint32_t)StreamLds<G, VB>::qr + ((dsc >> 5) & 63u) * (VQuads<G>::v * 32) + laneoff;
+template <int G, int VB, int W>
+__device__ __forceinline__ h4v kstep_b(uint32_t t) {
+  typedef StreamLds<G, VB> Lds;
+  if constexpr (W == 3)
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(Lds::t3 + ((t << 2) & 0xFCu)),
+                                         lds_at<uint32_t>(Lds::t3 + ((t >> 4) & 0xFCu))});
+  else if constexpr (W == 2)
+    return lds_at<h4v>(Lds::t2 + ((t & 255u) << 3));
+  else
+    return lds_at<h4v>(Lds::t1 + ((t & 15u) << 3));
 }
 
-// K-steps of one width group (rest group R = width 3 - R), grouped by the key
-// word their window starts in; two k-steps per iteration with all their
-// lookups in flight.
+// K-steps S, S + 1, ... of the group of width W (ns of them), reading aligned
+// register i of the group when the first k-step needs it.
+template <int G, int VB, int W, int S>
+__device__ __forceinline__ void kgroup_steps(uint32_t (&wd)[14], uint32_t (&al)[13], uint32_t wa, uint32_t sh,
+                                             uint32_t qa, int ns, f4v (&acc)[VQuads<G>::v]) {
+  if constexpr (S < 32) {
+    if (S >= ns) return;
+    constexpr int hi = KStep<W>::last_reg(S), lo = S == 0 ? 0 : KStep<W>::last_reg(S - 1) + 1;
+#pragma unroll
+    for (int i = lo; i <= hi; ++i) {
+      wd[i + 1] = lds_at<uint32_t>(wa + 256 * (i + 1));
+      al[i] = __builtin_amdgcn_alignbit(wd[i + 1], wd[i], sh);
+    }
+    const h4v bq = kstep_b<G, VB, W>(kstep_bits<W, S>(al));
+#pragma unroll
+    for (int g = 0; g < VQuads<G>::v; ++g)
+      acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(lds_at<h4v>(qa + (S * VQuads<G>::v + g) * 32), bq, acc[g], 0, 0, 0);
+    kgroup_steps<G, VB, W, S + 1>(wd, al, wa, sh, qa, ns, acc);
+  }
+}
+
+// The k-steps of the width-(3 - R) group.
 template <int G, int VB, int WK, int R>
-__device__ __forceinline__ void key_group(const uint32_t (&w)[WK], const StreamState &st, f4v (&acc)[VQuads<G>::v]) {
-  constexpr int W = 3 - R, NQ = VQuads<G>::v;
+__device__ __forceinline__ void key_group(const StreamState &st, f4v (&acc)[VQuads<G>::v]) {
+  constexpr int W = 3 - R;
   const int cb = (st.cgrp >> (8 * R)) & 255, ce = (st.cgrp >> (8 * R + 8)) & 255;
   if (cb >= ce) return;
-  const int jl = (st.jrng >> (10 * R)) & 31, jh = (st.jrng >> (10 * R + 5)) & 31;
-#pragma unroll
-  for (int jj = 0; jj <= WK; ++jj) {
-    if (jj >= jl && jj <= jh) {
-      const uint32_t lo = jj ? w[jj - 1] : 0u, hi = jj < WK ? w[jj] : 0u;
-      const int a0 = __builtin_amdgcn_readlane((int)st.av, jj);
-      const int a1 = __builtin_amdgcn_readlane((int)st.av, jj + 1);
-      const int c0 = a0 > cb ? a0 : cb, c1 = a1 < ce ? a1 : ce;
-      int c = c0;
-      for (; c + 1 < c1; c += 2) {
-        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c);
-        const uint32_t d1 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c + 1);
-        const h4v b0 = kstep_b<G, VB, W>(d0, hi, lo), b1 = kstep_b<G, VB, W>(d1, hi, lo);
-        const uint32_t r0 = kstep_a<G, VB>(d0, st.laneoff), r1 = kstep_a<G, VB>(d1, st.laneoff);
-        h4v q0[NQ], q1[NQ];
-#pragma unroll
-        for (int g = 0; g < NQ; ++g) q0[g] = lds_at<h4v>(r0 + 32 * g), q1[g] = lds_at<h4v>(r1 + 32 * g);
-#pragma unroll
-        for (int g = 0; g < NQ; ++g) {
-          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(q0[g], b0, acc[g], 0, 0, 0);
-          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(q1[g], b1, acc[g], 0, 0, 0);
-        }
-      }
-      if (c < c1) {
-        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)st.dv0, c);
-        const h4v b0 = kstep_b<G, VB, W>(d0, hi, lo);
-        const uint32_t r0 = kstep_a<G, VB>(d0, st.laneoff);
-#pragma unroll
-        for (int g = 0; g < NQ; ++g)
-          acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(lds_at<h4v>(r0 + 32 * g), b0, acc[g], 0, 0, 0);
-      }
-    }
-  }
+  const uint32_t bit = (st.gbit >> (10 * R)) & 1023u;
+  const uint32_t wa = st.kwl + (bit >> 5) * 256;
+  const uint32_t qa = st.qrl + (uint32_t)cb * (VQuads<G>::v * 32);
+  uint32_t wd[14], al[13];
+  wd[0] = lds_at<uint32_t>(wa);
+  // The k-step count is opaque per tile, so that the compiler evaluates each
+  // k-step's guard where it is used instead of keeping all of them live.
+  int ns = ce - cb;
+  asm volatile("" : "+s"(ns));
+  kgroup_steps<G, VB, W, 0>(wd, al, wa, bit & 31u, qa, ns, acc);
 }
 
 // In-place maximum over the 64 lanes of each v[h] (every lane receives it):
@@ -386,14 +400,18 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
   key4_blocks<G, VB, WK, 0>(r.w, st.n4w, lane, a4);
-  // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w
+  // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w,
+  // from the key words staged in this wave's LDS rows
+#pragma unroll
+  for (int j = 0; j < WK; ++j)
+    *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * j) = r.w[j];
   float lr[G];
   {
     f4v ak[VQuads<G>::v];
 #define BGTQ_KG(R, NORM)                                                              \
   {                                                                                   \
     _Pragma("unroll") for (int g = 0; g < VQuads<G>::v; ++g) ak[g] = (f4v){0.f, 0.f, 0.f, 0.f}; \
-    key_group<G, VB, WK, R>(r.w, st, ak);                                             \
+    key_group<G, VB, WK, R>(st, ak);                                                  \
     const float nw = h2f((uint16_t)(NORM));                                           \
     _Pragma("unroll") for (int h = 0; h < G; ++h) lr[h] = R == 0 ? nw * ak[h >> 2][h & 3] : fmaf(nw, ak[h >> 2][h & 3], lr[h]); \
   }
@@ -458,7 +476,7 @@ struct DecodeArgs {
   const uint16_t *vn;
   const int32_t *seq_lens;
   float *part;  // split partials [batch][hq][n_splits][kPartStride]
-  int64_t tiles_cap, max_seq_len, off_kvh, off_ksd, off_dtab, off_vlut, off_rowk, off_bandk;
+  int64_t tiles_cap, max_seq_len, off_kvh, off_dtab, off_vlut, off_rowk, off_bandk;
   int hkv, hq, wk, tiles_per_split, n_splits;
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
   float kscale;
@@ -473,7 +491,7 @@ void decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
-  typedef StreamLds<G, VB> Lds;
+  typedef StreamLds<G, VB, WK> Lds;
 
   // ---- prologue loads, in this order so that waiting for an earlier group
   // does not wait for a later one (loads complete in order): query-prep
@@ -493,8 +511,6 @@ void decode_kernel(const DecodeArgs a) {
     cr[k] = *(i < n0 ? cs0 + i : cs1 + i);
   }
   StreamState st;
-  st.dv0 = ((const uint32_t *)(consts + a.off_ksd))[kvh * kMaxKSteps + min(lane, kMaxKSteps - 1)];
-  st.av = (uint32_t)kd->anchor[min(lane, kMaxWK + 1)];
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tile request
   // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers.
   // The first is requested now, its range bounded by max_seq_len (in memory).
@@ -521,11 +537,15 @@ void decode_kernel(const DecodeArgs a) {
     int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
     st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
     st.wk = a.wk;
-    st.laneoff = (uint32_t)(lane & 3) * 8;
+    st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
+    st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
     st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
     st.n4w = kd->n4w;
     st.cgrp = kd->cgrp;
-    st.jrng = kd->jrng;
+    st.gbit = kd->gbit;
+    // the two zero rows past the key words
+    *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
+    *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
   }
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
@@ -706,9 +726,16 @@ decode_fn pick_decode(int g, int vb, int wk) {
   }
 }
 
-int decode_smem_bytes(int g, int vb) {
+template <int G, int VB>
+int smem_wk(int wk) {
+  if (wk <= 8) return StreamLds<G, VB, 8>::alloc;
+  if (wk <= 12) return StreamLds<G, VB, 12>::alloc;
+  return StreamLds<G, VB, 16>::alloc;
+}
+
+int decode_smem_bytes(int g, int vb, int wk) {
 #define BGTQ_SM(G_, VB_) \
-  if (g == G_ && vb == VB_) return StreamLds<G_, VB_>::alloc;
+  if (g == G_ && vb == VB_) return smem_wk<G_, VB_>(wk);
   BGTQ_SM(1, 1) BGTQ_SM(1, 2) BGTQ_SM(1, 3) BGTQ_SM(1, 4)
   BGTQ_SM(2, 1) BGTQ_SM(2, 2) BGTQ_SM(2, 3) BGTQ_SM(2, 4)
   BGTQ_SM(4, 1) BGTQ_SM(4, 2) BGTQ_SM(4, 3) BGTQ_SM(4, 4)
@@ -768,7 +795,7 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
 bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   const DecodeLayout lay = decode_layout(p, c.batch, c.max_seq_len);
   const int G = p.hdr.group, vb = p.hdr.v_bits;
-  const int smem = decode_smem_bytes(G, vb);
+  const int smem = decode_smem_bytes(G, vb, p.hdr.wk);
   decode_fn fn = pick_decode(G, vb, p.hdr.wk);
   if (smem < 0 || !decode_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
   if (smem > 65536) {
@@ -803,7 +830,6 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.tiles_cap = (c.capacity + kTile - 1) / kTile;
   a.max_seq_len = c.max_seq_len;
   a.off_kvh = p.hdr.off_kvh;
-  a.off_ksd = p.hdr.off_ksd;
   a.off_dtab = p.hdr.off_dtab;
   a.off_vlut = p.hdr.off_vlut;
   a.off_rowk = p.hdr.off_rowk;

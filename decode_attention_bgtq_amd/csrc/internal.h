@@ -22,11 +22,8 @@ constexpr int kMaxKSteps = 36;      // bound on the width-1..3 k-steps of one he
 // matrix-core step per code).  A k-step is four consecutive positions of one
 // group (a group's last step may hold two; its query operand is zero past the
 // group): its codes are the 4w stream bits that start at its first position's
-// bit, code k at bits [w k, w (k + 1)).
-// ksd (32 bits): [0,5) funnel shift that brings the k-step's first bit to bit
-//   kstep_bit(w) of the shifted word, [5,11) k-step index (row of its query
-//   operand).  K-steps are numbered through the groups of width 3, 2, 1.
-constexpr int kstep_bit(int w) { return w == 3 ? 2 : 3; }  // log2 of the table entry bytes: 4 (two fp16), 8 (four)
+// bit, code k at bits [w k, w (k + 1)).  K-steps are numbered through the
+// groups of width 3, 2, 1.
 
 // Decode tables shared by every head of a plan, copied as one block into LDS:
 // 4-bit centroid pairs of a code byte (float2 [256]); four fp16 centroids of a
@@ -47,16 +44,13 @@ struct KvhDesc {
   int32_t n_groups;
   int32_t d_nz;
   int32_t n_ksteps;            // k-steps of the width-1..3 groups
-  int32_t pad0;
+  uint32_t gbit;               // bits [10r, 10r+10): first stream bit of the width-(3-r) group (0 if absent)
   int32_t d4;                  // coordinates of the 4-bit group (group 0 when present), else 0
   int32_t n4blk;               // 16-code blocks of the 4-bit group, ceil(d4 / 16)
   int32_t n4w;                 // key words holding 4-bit codes, ceil(d4 / 8)
   uint32_t cgrp;               // byte r (r = 0..2): first k-step of the width-(3-r) group; byte 3 = n_ksteps
-  uint32_t jrng;               // bits [10r, 10r+5) / [10r+5, 10r+10): first / last word slot jj of group r's k-steps
   KGroupDesc g[kMaxGroups];
   int16_t coord[kHeadDim];     // original coordinate of each group-order position
-  int16_t pad_[4];
-  int32_t anchor[kMaxWK + 2];  // k-steps whose window starts in word jj-1 are [anchor[jj], anchor[jj+1])
 };
 
 // Device constant image header.  All offsets are bytes from the image start.
@@ -66,7 +60,6 @@ struct ConstHeader {
   int32_t max_ksteps;        // largest k-step count over heads
   int32_t pad0;
   int64_t off_kvh;           // KvhDesc[n_kv_heads]
-  int64_t off_ksd;           // uint32 [n_kv_heads][kMaxKSteps], k-step descriptors (zero past a head's k-steps)
   int64_t off_rot64_k;       // double area (Pi^T per K group)
   int64_t off_rot32_k;       // float [n_kv_heads][128][128]: block-diagonal R, R[pos_g + i][pos_g + k] = Pi_g[i][k]
   int64_t off_rot64_v;       // double [n_kv_heads][128][128], Pi_V^T ([k][i])
@@ -94,7 +87,6 @@ struct Plan {
   bgtq_plan_desc desc{};
   std::vector<int8_t> bits;             // [Hkv][64]
   std::vector<KvhDesc> kvh;
-  std::vector<uint32_t> ksd;            // k-step descriptors [Hkv][kMaxKSteps] (see above)
   std::vector<std::vector<double>> rot_k;  // per (kvh, group) Pi row-major
   std::vector<std::vector<double>> rot_v;  // per kvh Pi_V row-major
   std::vector<uint8_t> image;           // device constant image

@@ -277,36 +277,27 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   }
 
   // decode k-steps of the width-1..3 groups (four positions each)
-  p.ksd.assign((size_t)hkv * kMaxKSteps, 0u);
   std::vector<int> kbase((size_t)hkv * kMaxGroups, 0);  // first k-step of each width-1..3 group
   int max_ksteps = 0;
   for (int h = 0; h < hkv; ++h) {
     KvhDesc &kd = p.kvh[h];
-    std::vector<int> anchors;
     int c = 0;
     kd.d4 = (kd.n_groups > 0 && kd.g[0].w == 4) ? kd.g[0].d : 0;
     kd.n4blk = (kd.d4 + 15) / 16;
     kd.n4w = (kd.d4 + 7) / 8;
+    kd.gbit = 0;
     int cfirst[3] = {-1, -1, -1};  // first k-step of the width-3, 2, 1 groups
-    int jlo[3] = {31, 31, 31}, jhi[3] = {0, 0, 0};
     for (int gi = 0; gi < kd.n_groups; ++gi) {
       const KGroupDesc &g = kd.g[gi];
       if (g.w == 4) continue;  // one matrix-core step per code in the decode
       const int rg = 3 - g.w;  // rest-group index
       cfirst[rg] = c;
       kbase[(size_t)h * kMaxGroups + gi] = c;
-      for (int r0 = 0; r0 < g.d; r0 += 4, ++c) {
-        if (c >= kMaxKSteps) {
-          err = "internal: too many k-steps";
-          return BGTQ_EINVAL;
-        }
-        const int lo = g.bit_off + g.w * r0 - kstep_bit(g.w);  // window start, may be -2 or -3
-        const int anchor = lo >= 0 ? lo / 32 : -1;
-        const uint32_t shift = (uint32_t)(lo - 32 * anchor);
-        p.ksd[(size_t)h * kMaxKSteps + c] = shift | ((uint32_t)c << 5);
-        anchors.push_back(anchor);
-        jlo[rg] = std::min(jlo[rg], anchor + 1);
-        jhi[rg] = std::max(jhi[rg], anchor + 1);
+      kd.gbit |= (uint32_t)g.bit_off << (10 * rg);
+      c += (g.d + 3) / 4;
+      if (c > kMaxKSteps) {
+        err = "internal: too many k-steps";
+        return BGTQ_EINVAL;
       }
     }
     kd.n_ksteps = c;
@@ -316,14 +307,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     bnd[3] = c;
     for (int rg = 2; rg >= 0; --rg) bnd[rg] = cfirst[rg] >= 0 ? cfirst[rg] : bnd[rg + 1];
     kd.cgrp = (uint32_t)bnd[0] | ((uint32_t)bnd[1] << 8) | ((uint32_t)bnd[2] << 16) | ((uint32_t)bnd[3] << 24);
-    kd.jrng = 0;
-    for (int rg = 0; rg < 3; ++rg) kd.jrng |= ((uint32_t)jlo[rg] | ((uint32_t)jhi[rg] << 5)) << (10 * rg);
-    // anchor ranges: k-steps whose window starts in word jj-1 are [anchor[jj], anchor[jj+1])
-    for (int jj = 0; jj <= kMaxWK + 1; ++jj) {
-      int first = 0;
-      while (first < c && anchors[first] < jj - 1) ++first;
-      kd.anchor[jj] = first;
-    }
   }
 
   // constant image
@@ -348,8 +331,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   size_t off = align256(sizeof(ConstHeader));
   hd.off_kvh = off;
   off = align256(off + sizeof(KvhDesc) * hkv);
-  hd.off_ksd = off;
-  off = align256(off + 4 * p.ksd.size());
   hd.off_rot64_k = off;
   off = align256(off + 8 * (size_t)rot64_k);
   hd.off_rot32_k = off;
@@ -377,7 +358,6 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   uint8_t *img = p.image.data();
   std::memcpy(img, &hd, sizeof(hd));
   std::memcpy(img + hd.off_kvh, p.kvh.data(), sizeof(KvhDesc) * hkv);
-  std::memcpy(img + hd.off_ksd, p.ksd.data(), 4 * p.ksd.size());
   double *r64k = (double *)(img + hd.off_rot64_k);
   float *r32k = (float *)(img + hd.off_rot32_k);
   size_t gidx = 0;
