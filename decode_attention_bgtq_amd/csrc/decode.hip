@@ -34,6 +34,7 @@ constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
 constexpr int kPartStride = 132;  // m, l, pad, pad, acc[128]
 constexpr int kMaxSplits = 256;
+constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights within a tile stay below 2^8
 
 
 // LDS access by raw byte offset.  The stream kernel has no static LDS, so its
@@ -421,23 +422,37 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   const bool valid = (int64_t)tile * kTile + lane < st.seq;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
-  // ---- online softmax (log2 domain); P' = p * value norm, fp16, to the wave's
-  // LDS rows [h][token]
-  float l[G], mx[G];
+  // ---- online softmax (log2 domain), rescaled lazily: the running maximum
+  // moves (with the wave maximum, the rescale of the sums and the
+  // accumulators) only when a logit exceeds it by more than kRescaleSlack, so
+  // p = 2^(l - m) stays below 2^kRescaleSlack.  P' = p * value norm, fp16, to
+  // the wave's LDS rows [h][token].
+  float l[G];
+  bool up = false;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     l[h] = valid ? fmaf(n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
-    mx[h] = l[h];
+    up = up || l[h] > mrun[h] + kRescaleSlack;
   }
-  wave_max_heads<G>(mx);
-  float alpha[G];
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) mx[h] = l[h];
+    wave_max_heads<G>(mx);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(mrun[h], mx[h]);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mn);
+      lsum[h] *= alpha;
+      acc0[h >> 2][h & 3] *= alpha;
+      acc1[h >> 2][h & 3] *= alpha;
+      mrun[h] = mn;
+    }
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mn = fmaxf(mrun[h], mx[h]);
-    alpha[h] = __builtin_amdgcn_exp2f(mrun[h] - mn);
-    const float p = __builtin_amdgcn_exp2f(l[h] - mn);
-    lsum[h] = fmaf(lsum[h], alpha[h], p);
-    mrun[h] = mn;
+    const float p = __builtin_amdgcn_exp2f(l[h] - mrun[h]);
+    lsum[h] += p;
     *(__attribute__((address_space(3))) _Float16 *)(size_t)(st.ptw + h * (2 * kTile) + 2 * lane) = (_Float16)(p * nv);
   }
   // A operands: lane 4k + m holds head m's weights of tokens 4k .. 4k + 3 (heads
@@ -447,11 +462,6 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   for (int g = 0; g < VQuads<G>::v; ++g)
     pa[g] = lds_at<h4v>(st.ptw + ((4 * g + (lane & 3)) & (G - 1)) * (2 * kTile) + (lane >> 2) * 8);
   // ---- values: lane = coordinates lane and lane + 64
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    acc0[h >> 2][h & 3] *= alpha[h];
-    acc1[h >> 2][h & 3] *= alpha[h];
-  }
   v_mfma_steps<G, VB, 0>(r.va, r.vb, (uint32_t)StreamLds<G, VB>::vlut, pa, acc0, acc1);
 }
 
