@@ -566,17 +566,13 @@ void decode_kernel(const DecodeArgs a) {
   for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f;
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) acc0[g] = (f4v){0.f, 0.f, 0.f, 0.f}, acc1[g] = acc0[g];
-  if (tile < tile_hi) {
-    for (;;) {
-      load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
-      process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
-      tile += kStreamWaves;
-      if (tile >= tile_hi) break;
-      load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
-      process_tile<G, VB, WK>(rb, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
-      tile += kStreamWaves;
-      if (tile >= tile_hi) break;
-    }
+  // One copy of the tile body (the instruction cache holds the loop): the
+  // next tile's registers are requested before the current one is processed
+  // and moved into place after it.
+  for (; tile < tile_hi; tile += kStreamWaves) {
+    load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
+    process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
+    ra = rb;
   }
 
   // ---- merge the waves of this split into one partial per query head
