@@ -94,7 +94,7 @@ bgtq_status bgtq_allocate(const double *energy, int32_t n_kv_heads, int32_t n_bl
  * (SplitMix64 stream absorbing seed, layer, kvh, tensor (K 0, V 1), width,
  * group size; Box-Muller; Householder QR with the sign of diag(R) taken
  * positive), the group maps, the bit offsets of the key stream and the
- * decode lookup-table descriptors.  Plans are immutable; one plan may be used
+ * decode tables.  Plans are immutable; one plan may be used
  * from several threads and streams at once.
  */
 typedef struct bgtq_plan bgtq_plan;
@@ -175,9 +175,13 @@ bgtq_status bgtq_rotate_queries(const bgtq_plan *plan, const void *dev_consts, c
  *   l_t = softmax_scale * q . k_hat_t,  o = sum_t softmax(l)_t v_hat_t
  * over t < seq_len, where k_hat, v_hat are the TurboQuant-MSE reconstructions
  * (fp16 norm * Pi^T (centroid / sqrt(d_g))).  Computed without
- * materialising k_hat or v_hat: queries rotated once per group, per-group
- * lookup tables of q_rot x centroid in LDS, online softmax, accumulation in
- * the rotated V space, then one un-rotation per head.  fp32 accumulation.
+ * materialising k_hat or v_hat, in two launches: the decode kernel rotates the
+ * queries once per key group, takes the logits in the rotated space from LDS
+ * centroid lookups on the matrix cores (fp32 for the 4-bit group, fp16
+ * operands with fp32 accumulation for widths 1..3), keeps an online softmax
+ * and accumulates the values in the rotated value space, one partial per
+ * split of the sequence; the merge kernel combines the splits and un-rotates
+ * once per head.  fp32 accumulation throughout.
  *   q           device fp16 [batch][n_q_heads][128]
  *   seq_lens    device int32 [batch]; each value is clamped to [0, max_seq_len];
  *               a sequence of length 0 yields a zero output
@@ -203,8 +207,7 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
  * encoded at token pos[b] exactly as bgtq_encode_k / bgtq_encode_v would
  * (sequences with pos[b] outside that range append nothing); then the output
  * is bgtq_decode_attn's with seq_lens[b] = pos[b] + 1 (clamped to
- * [0, max_seq_len]).  The appends and the query preparation share one launch,
- * followed by the cache-streaming and merge launches of the decode.
+ * [0, max_seq_len]).  One append launch, then the two decode launches.
  *   q            device fp16 [batch][n_q_heads][128]
  *   k_new, v_new device fp16 [batch][n_kv_heads][128]
  *   pos          device int32 [batch]
@@ -233,8 +236,8 @@ bgtq_status bgtq_plan_rotation(const bgtq_plan *plan, int32_t kvh, int32_t tenso
 bgtq_status bgtq_plan_bits(const bgtq_plan *plan, int8_t *bits);
 
 /*
- * Kernel timing: when enabled, bgtq_decode_attn brackets its cache-streaming
- * kernel with HIP events on `stream`; bgtq_profile_read waits for the
+ * Kernel timing: when enabled, bgtq_decode_attn and bgtq_decode_step bind HIP
+ * events to every launch of their decode kernel on `stream`; bgtq_profile_read waits for the
  * recorded events, returns the summed duration (ms) and launch count since
  * the last read, and clears them.
  */
