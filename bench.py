@@ -7,7 +7,9 @@ T+1 cached tokens.  The serving step (bgtq_decode_step: the new token's key and
 value appended at position T, then the decode) is timed as well and reported
 under "serving_step".
 Calibration energy, allocation, plan creation and the full 128K prefill
-encode run once before the timed region and are reported as separate fields.
+encode run once before the timed region and are reported as separate fields,
+and so does the fp16 baseline: the same keys and values uncompressed, decoded
+by bgtq_fp16_decode_attn (same split-sequence structure) over the same tokens.
 
 value = algorithmic packed bytes read per step (codes + present fp16 norms)
 / step time.  The packed cache is replicated (>= 1 GiB in total) and steps
@@ -41,7 +43,7 @@ def log(msg: str) -> None:
     print("[bench %s] %s" % (time.strftime("%H:%M:%S"), msg), file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("decode.hip", "prep.h", "device.h", "internal.h")
+KERNEL_SOURCES = ("decode.hip", "prep.h", "merge.h", "device.h", "internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -230,7 +232,6 @@ def main() -> int:
     torch.cuda.synchronize()
     enc_k_s, enc_v_s = e0.elapsed_time(e1) / 1e3, e1.elapsed_time(e2) / 1e3
     token_heads = b * t * hkv
-    del kd, vd
 
     # ---- the appended token and the query (position T)
     cfg1 = dataclasses.replace(cfg, append=1)
@@ -310,6 +311,33 @@ def main() -> int:
         "host enqueue %.4f ms/call" % (step_ms, value, serve_ms, kern_ms, achieved, launches,
                                        host_enqueue_s * 1e3 / n_steps))
 
+    # ---- fp16 baseline: the same keys and values uncompressed, the same split-sequence decode
+    # (bgtq_fp16_decode_attn) over the same t + 1 tokens, replicated against the Infinity Cache
+    del reps
+    kf = torch.zeros((b, cap, hkv, 128), dtype=torch.int16, device=dev)
+    vf = torch.zeros_like(kf)
+    kf[:, :t] = kd
+    vf[:, :t] = vd
+    kf[:, t] = k_new[:, 0]
+    vf[:, t] = v_new[:, 0]
+    del kd, vd
+    fp16_bytes = b * (t + 1) * hkv * 128 * 2 * 2
+    n_rep16 = max(1, math.ceil(args.replica_bytes / fp16_bytes))
+    reps16 = [(kf, vf)] + [(kf.clone(), vf.clone()) for _ in range(n_rep16 - 1)]
+    ws16 = torch.empty(bg.fp16_workspace_size(b, hkv, hq, t + 1), dtype=torch.uint8, device=dev)
+
+    def fp16_attn(i):
+        kk, vv = reps16[i % n_rep16]
+        bg.fp16_decode_attn(q, kk, vv, seq_lens, t + 1, out, ws16)
+
+    for i in range(max(5, args.warmup // 5)):
+        fp16_attn(i)
+    rounds16 = max(1, rounds // 5)
+    fp16_ms = sum(timed_round(fp16_attn, r * per_round, per_round)[0] for r in range(rounds16)) / (rounds16 * per_round)
+    log("fp16 baseline %.4f ms (%.0f GB/s of fp16 K/V); packed decode %.2fx faster" %
+        (fp16_ms, fp16_bytes / (fp16_ms / 1e3) / 1e9, fp16_ms / step_ms))
+    del reps16, kf, vf
+
     # ---- copy probe: practical streaming ceiling (1 GiB read + 1 GiB write)
     src = torch.empty(1 << 28, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
@@ -321,7 +349,7 @@ def main() -> int:
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
-    del src, dst, reps
+    del src, dst
 
     traffic = load_traffic(cfg.cid)
     rec = {
@@ -343,6 +371,13 @@ def main() -> int:
         "encode_token_heads_per_s": {"k_and_v": round(token_heads / (enc_k_s + enc_v_s)),
                                      "k": round(token_heads / enc_k_s), "v": round(token_heads / enc_v_s),
                                      "tokens": b * t},
+        "fp16_baseline": {"what": "bgtq_fp16_decode_attn: the same keys and values uncompressed (fp16), the same "
+                                  "split-sequence decode and merge, over the same t + 1 tokens",
+                          "ms": round(fp16_ms, 5), "bytes_per_step": fp16_bytes,
+                          "GBps": round(fp16_bytes / (fp16_ms / 1e3) / 1e9, 2),
+                          "hbm_peak_frac": round(fp16_bytes / (fp16_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "packed_speedup": round(fp16_ms / step_ms, 3),
+                          "compression": round(fp16_bytes / packed, 3)},
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "one_time": {"energy_us": round(energy_us, 2), "allocate_us": round(alloc_us, 2),
                      "plan_host_ms": round(plan_ms, 2)},

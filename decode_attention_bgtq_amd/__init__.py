@@ -25,6 +25,7 @@ EXPORTED = [
     "bgtq_plan_destroy", "bgtq_plan_sizes", "bgtq_plan_upload", "bgtq_encode_k", "bgtq_encode_v",
     "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
+    "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn",
 ]
 
 
@@ -57,6 +58,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError("libbgtq.so is not built (run __graft_entry__.build())")
+    # torch first: torch ships its own HIP runtime under the same soname as the
+    # system one that libbgtq.so links, and the first one loaded serves the whole
+    # process; the library must use torch's, which owns the memory and streams.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     sig = {
@@ -79,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_plan_bits": (I32, [P, P]),
         "bgtq_profile_enable": (I32, [I32]),
         "bgtq_profile_read": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
+        "bgtq_fp16_decode_workspace_size": (I32, [I32, I32, I32, I64, ctypes.POINTER(SZ)]),
+        "bgtq_fp16_decode_attn": (I32, [P, P, P, I32, I32, I32, I64, P, I64, ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -238,6 +245,24 @@ class Plan:
                                        q.shape[0], max_seq_len, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
                                        _ptr(v_norms), capacity, softmax_scale, _ptr(out), _ptr(workspace),
                                        ws_bytes, _stream(stream)))
+
+
+def fp16_workspace_size(batch: int, n_kv_heads: int, n_q_heads: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().bgtq_fp16_decode_workspace_size(batch, n_kv_heads, n_q_heads, max_seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def fp16_decode_attn(q, k, v, seq_lens, max_seq_len: int, out, workspace, softmax_scale: float | None = None,
+                     stream=None) -> None:
+    """fp16 decode attention over an uncompressed cache k, v [batch][capacity][n_kv_heads][128] (the baseline)."""
+    if softmax_scale is None:
+        softmax_scale = HEAD_DIM ** -0.5
+    b, hq, _ = q.shape
+    _, cap, hkv, _ = k.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().bgtq_fp16_decode_attn(_ptr(q), _ptr(k), _ptr(v), b, hq, hkv, cap, _ptr(seq_lens), max_seq_len,
+                                        softmax_scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def profile_enable(on: bool = True) -> None:

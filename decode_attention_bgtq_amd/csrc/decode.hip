@@ -26,14 +26,13 @@
 
 #include "device.h"
 #include "host.h"
+#include "merge.h"
 #include "prep.h"
 
 namespace bgtq {
 
 constexpr int kStreamWaves = 8;
 constexpr int kStreamThreads = 64 * kStreamWaves;
-constexpr int kPartStride = 132;  // m, l, pad, pad, acc[128]
-constexpr int kMaxSplits = 256;
 constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights within a tile stay below 2^8
 
 
@@ -610,97 +609,6 @@ void decode_kernel(const DecodeArgs a) {
   }
 }
 
-// One workgroup of 512 threads per (query head, sequence).  Every global load
-// is issued first: thread t holds the split accumulators of coordinate t % 128
-// for the splits s = t / 128 (mod 4) (up to kMergeRegs of them in registers),
-// the (m, l) of split t, and a quarter (32 values) of row t / 4 of Pi_V^T.
-// Then: M = max_s m_s, w_s = 2^(m_s - M) / (sum_s 2^(m_s - M) l_s sqrt(128)),
-// y = sum_s w_s acc_s, out[j] = sum_k Pi_V[k][j] y[k] (four threads per j).
-constexpr int kMergeThreads = 512;
-constexpr int kMergeRegs = 16;  // split accumulators per thread loaded before the weights (n_splits <= 64)
-
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ pvt_all,
-                                                              const float *__restrict__ part, int n_splits,
-                                                              int group, int hq, uint16_t *__restrict__ out) {
-  __shared__ float wsm[kMaxSplits];
-  __shared__ __attribute__((aligned(16))) float ys[4 * kHeadDim];
-  __shared__ float red[2 * (kMergeThreads / 64)];
-  const int hqi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kvh = hqi / group;
-  const float *ph = part + ((size_t)b * hq + hqi) * (size_t)n_splits * kPartStride;
-  // rotation quarter: output j = tid / 4, k in [32 (tid % 4), 32 (tid % 4) + 32)
-  const int j = tid >> 2, kq = tid & 3;
-  const float4 *row = (const float4 *)(pvt_all + ((size_t)kvh * kHeadDim + j) * kHeadDim + 32 * kq);
-  float4 pr[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) pr[u] = row[u];
-  float m = -INFINITY, l = 0.f;
-  if (tid < n_splits) {
-    const float2 ml = *(const float2 *)(ph + (size_t)tid * kPartStride);
-    m = ml.x;
-    l = ml.y;
-  }
-  const int i = tid & (kHeadDim - 1), par = tid >> 7;
-  const float *pv = ph + 4 + i;
-  float av[kMergeRegs];
-#pragma unroll
-  for (int u = 0; u < kMergeRegs; ++u) {
-    const int sp = par + 4 * u;
-    av[u] = pv[(size_t)(sp < n_splits ? sp : 0) * kPartStride];
-  }
-  const float wm = wave_max(m);
-  if (lane == 0) red[wave] = wm;
-  __syncthreads();
-  float mx = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) mx = fmaxf(mx, red[w]);
-  const float f = (mx == -INFINITY || m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
-  const float wl = wave_sum(f * l);
-  if (lane == 0) red[kMergeThreads / 64 + wave] = wl;
-  __syncthreads();
-  float lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) lsum += red[kMergeThreads / 64 + w];
-  const float inv = lsum > 0.f ? 1.0f / (lsum * sqrtf((float)kHeadDim)) : 0.f;
-  if (tid < n_splits) wsm[tid] = f * inv;
-  __syncthreads();
-  {
-    float acc = 0.f;
-#pragma unroll
-    for (int u = 0; u < kMergeRegs; ++u) {
-      const int sp = par + 4 * u;
-      if (sp < n_splits) acc = fmaf(wsm[sp], av[u], acc);
-    }
-    // further splits: chunks of kMergeRegs independent loads
-    for (int c0 = par + 4 * kMergeRegs; c0 < n_splits; c0 += 4 * kMergeRegs) {
-      float v[kMergeRegs];
-#pragma unroll
-      for (int u = 0; u < kMergeRegs; ++u) v[u] = pv[(size_t)min(c0 + 4 * u, n_splits - 1) * kPartStride];
-#pragma unroll
-      for (int u = 0; u < kMergeRegs; ++u)
-        if (c0 + 4 * u < n_splits) acc = fmaf(wsm[c0 + 4 * u], v[u], acc);
-    }
-    ys[par * kHeadDim + i] = acc;
-  }
-  __syncthreads();
-  float o = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int k = 32 * kq + 4 * u;
-    const float y0 = ys[k] + ys[kHeadDim + k] + ys[2 * kHeadDim + k] + ys[3 * kHeadDim + k];
-    const float y1 = ys[k + 1] + ys[kHeadDim + k + 1] + ys[2 * kHeadDim + k + 1] + ys[3 * kHeadDim + k + 1];
-    const float y2 = ys[k + 2] + ys[kHeadDim + k + 2] + ys[2 * kHeadDim + k + 2] + ys[3 * kHeadDim + k + 2];
-    const float y3 = ys[k + 3] + ys[kHeadDim + k + 3] + ys[2 * kHeadDim + k + 3] + ys[3 * kHeadDim + k + 3];
-    o = fmaf(pr[u].x, y0, o);
-    o = fmaf(pr[u].y, y1, o);
-    o = fmaf(pr[u].z, y2, o);
-    o = fmaf(pr[u].w, y3, o);
-  }
-  o += __shfl_xor(o, 1);
-  o += __shfl_xor(o, 2);
-  if (kq == 0) out[((size_t)b * hq + hqi) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
-}
-
 // ------------------------------------------------------------------ host
 // ------------------------------------------------------------------ host
 
@@ -861,7 +769,7 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
     pr.pending.emplace_back(e0, e1);
   }
   if (s != BGTQ_OK) return s;
-  merge_kernel<<<dim3(p.desc.n_q_heads, c.batch), kMergeThreads, 0, st>>>(
+  merge_kernel<true><<<dim3(p.desc.n_q_heads, c.batch), kMergeThreads, 0, st>>>(
       (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v), (const float *)ws, lay.n_splits, G,
       p.desc.n_q_heads, c.out);
   return launch_status("decode (merge)");

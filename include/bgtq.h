@@ -222,6 +222,29 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
                              void *workspace, size_t ws_bytes, bgtq_stream stream);
 
 /*
+ * (8) fp16 decode attention over an uncompressed KV cache: the baseline of the
+ * packed path (Abstract: the packed path runs faster than fp16
+ * FlashAttention-2 decode at 128K; README end-to-end decode benchmark).  Per
+ * (sequence, query head h, KV head h / G):
+ *   o = sum_{t < seq_len} softmax(softmax_scale * q . k_t)_t v_t
+ * with fp16 inputs, fp32 products and sums, fp16 output; two launches (split
+ * stream, split merge), the same structure as bgtq_decode_attn.
+ *   q         device fp16 [batch][n_q_heads][128], 16-byte aligned
+ *   k, v      device fp16 [batch][capacity][n_kv_heads][128], 16-byte aligned
+ *   seq_lens  device int32 [batch], clamped to [0, max_seq_len]; length 0 gives 0
+ *   out       device fp16 [batch][n_q_heads][128], written
+ *   workspace bgtq_fp16_decode_workspace_size bytes, 256-byte aligned
+ * Errors: EINVAL (null, shapes, G not 1, 2, 4 or 8, alignment, scale),
+ * ECAPACITY (max_seq_len outside [1, capacity]), EWORKSPACE.
+ */
+bgtq_status bgtq_fp16_decode_workspace_size(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                            int64_t max_seq_len, size_t *bytes);
+bgtq_status bgtq_fp16_decode_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int32_t batch,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int64_t capacity,
+                                  const int32_t *seq_lens, int64_t max_seq_len, float softmax_scale,
+                                  uint16_t *out, void *workspace, size_t ws_bytes, bgtq_stream stream);
+
+/*
  * Host-side inspection (no device work).
  * bgtq_codebook: the b-bit Lloyd-Max quantiser of N(0,1) the library uses:
  * centroids [2^b], interior thresholds [2^b - 1], and D(b).
