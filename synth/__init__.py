@@ -26,7 +26,7 @@ HEAD_DIM = 128
 N_BLOCKS = HEAD_DIM // 2
 
 # stream ids inside one config
-_S_SCALES, _S_K, _S_V, _S_Q, _S_QCAL, _S_KCAL, _S_OUTLIER = 0, 1, 2, 3, 4, 5, 6
+_S_SCALES, _S_K, _S_V, _S_Q, _S_QCAL, _S_KCAL, _S_OUTLIER, _S_QWIN = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -160,6 +160,15 @@ def query(cfg: Config, seq: int = 0, pos: int | None = None) -> np.ndarray:
     return rope_f64(x, np.array([pos]), cfg.theta)[0].astype(np.float16)
 
 
+def queries(cfg: Config, seq: int = 0, start: int = 0, count: int = 1) -> np.ndarray:
+    """Post-RoPE fp16 queries [count, Hq, 128] at positions start..start+count-1, one independent
+    draw per position (drawn like the keys of their KV head), for windowed logit diagnostics."""
+    rng = _rng(cfg, _S_QWIN, seq)
+    sc = np.repeat(block_scales(cfg), cfg.group, axis=0)             # [Hq, 64]
+    x = _draw_blocks(rng, count, sc)
+    return rope_f64(x, np.arange(start, start + count), cfg.theta).astype(np.float16)
+
+
 def calibration(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
     """Calibration activations (post-RoPE fp16) at positions 0..n_cal-1.
 
@@ -190,4 +199,4 @@ def small(cfg_id: int, seq_len: int | None = None, batch: int | None = None,
 
 
 __all__ = ["Config", "CONFIGS", "HEAD_DIM", "N_BLOCKS", "block_scales", "rope_f64", "keys",
-           "values", "query", "calibration", "small"]
+           "values", "query", "queries", "calibration", "small"]
