@@ -506,6 +506,11 @@ void decode_kernel(const DecodeArgs a) {
   // does not wait for a later one (loads complete in order): query-prep
   // inputs, the plan's decode and value tables (16 bytes per thread and
   // round), the k-step descriptors, then the first tile.
+  // (the sequence length and the head's group fields first: the tile loop's
+  // bounds and dispatch depend on them after the query preparation)
+  const int64_t seq_raw = (int64_t)a.seq_lens[b] + a.seq_add;
+  const int n4w = kd->n4w;
+  const uint32_t cgrp = kd->cgrp, gbit = kd->gbit;
   PrepLoads pl;
   prep_load_row<G>(pl, (const uint2 *)(consts + a.off_rowk) + (size_t)kvh * kHeadDim, kd,
                    a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid);
@@ -531,6 +536,9 @@ void decode_kernel(const DecodeArgs a) {
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
   load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), a.wk, wkl, lane);
+  // the rotation bands depend on the row entries loaded above: requested after
+  // the tile, so that waiting for the row entries does not delay the tile
+  __builtin_amdgcn_sched_barrier(0);
   prep_load_band(pl, (const float *)(consts + a.off_bandk), tid);
 #pragma unroll
   for (int k = 0; k < kRounds; ++k) {
@@ -543,15 +551,14 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < G; ++h) rinv[h] = lds_at<float>(Lds::rinv + 4 * h);
   {
-    int64_t s = (int64_t)a.seq_lens[b] + a.seq_add;
-    st.seq = s < 0 ? 0 : (s > a.max_seq_len ? a.max_seq_len : s);
+    st.seq = seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw);
     st.wk = a.wk;
     st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
     st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
     st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
-    st.n4w = kd->n4w;
-    st.cgrp = kd->cgrp;
-    st.gbit = kd->gbit;
+    st.n4w = n4w;
+    st.cgrp = cgrp;
+    st.gbit = gbit;
     // the two zero rows past the key words
     *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
     *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
