@@ -2,17 +2,21 @@
 // packed-cache serving path of "RoPE-Aware Bit Allocation for KV-Cache
 // Quantization", Abstract, and of the Block-GTQ README backend table).
 //
-// Two launches per call.  The decode kernel, one workgroup of 8 waves per
-// (split of the sequence, KV head, sequence):
+// Two launches per call.  The decode kernel, one workgroup of 16 waves (one
+// per CU; 8 waves where four waves per SIMD do not fit) per (split of the
+// sequence, KV head, sequence):
 //  prologue  the plan's decode tables into LDS; the G queries of the KV head
-//            rotated once per key width group (fp32, from the group rotations
-//            stored as bands) into the scaled 4-bit-group queries and the
-//            k-step operands of the width-1..3 groups (prep.h), in LDS.
+//            rotated once per key width group (fp32 MFMA over the head's
+//            block-diagonal rotation) into the scaled 4-bit-group queries and
+//            the k-step operands of the width-1..3 groups (prep.h), in LDS.
+//            The first tile is requested once the small loads of the
+//            preparation have arrived, so that they are not queued behind it.
 //  tiles     per 64-token tile (lane = token): key words read coalesced
 //            (word-major); logits on the matrix cores (the 4-bit group one
 //            fp32 4x4x1 step per code, the width-1..3 groups one fp16 4x4x4
-//            k-step per four codes, both with LDS centroid lookups) times the
-//            group norms, in log2 units; online softmax with wavefront
+//            k-step per four codes, both with LDS centroid lookups, the
+//            lookups of the next batch in flight during the products) times
+//            the group norms, in log2 units; online softmax with wavefront
 //            reductions; the value codes (lane = coordinate) accumulated on the
 //            matrix cores against the fp16 softmax weights in the rotated value
 //            space.  The waves of a workgroup merge into one partial
@@ -31,10 +35,27 @@
 
 namespace bgtq {
 
-constexpr int kStreamWaves = 8;
-constexpr int kStreamThreads = 64 * kStreamWaves;
 constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights within a tile stay below 2^8
 
+
+// Waves per SIMD the register allocation aims at: four (two workgroups per CU,
+// at most 128 VGPRs) up to four query heads per KV head unless the key and
+// value words of two tiles take too many registers; two for eight heads.
+template <int G, int VB, int WK>
+struct StreamOcc {
+  static constexpr bool four = G <= 4 && (WK + 2 * VB <= 18 || (WK == 16 && VB <= 2));
+  static constexpr int v = four ? 4 : (G <= 4 ? 3 : 2);
+};
+
+// Waves per workgroup: one workgroup of 16 waves per CU where four waves per
+// SIMD fit (one query preparation per CU, every wave of the CU the same age),
+// else workgroups of 8 waves.
+template <int G, int VB, int WK>
+struct StreamCfg {
+  static constexpr int waves = StreamOcc<G, VB, WK>::four ? 16 : 8;
+  static constexpr int threads = 64 * waves;
+  static constexpr int per_cu = StreamOcc<G, VB, WK>::v * 4 / waves;  // resident workgroups per CU (by waves)
+};
 
 // LDS access by raw byte offset.  The stream kernel has no static LDS, so its
 // dynamic allocation starts at offset 0 (checked on the host before launch).
@@ -87,9 +108,10 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 //   [vlut, ..)       value table
 //   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
 //   [kw, ..)         per wave: the tile's key words [WK + 2][64] (the last two rows zero)
-// The query preparation uses [scr, ..) (from pt on) as scratch before the tile
-// loop; after it the area from 0 is reused for the wave merge.  Past `total`:
-// 16 spare bytes that take the stores of the table copy falling outside the
+// The decode and value tables are copied from global memory in the prologue,
+// the prepared queries built there (prep_build, with its scratch from pt on);
+// after the tile loop the area from 0 is reused for the wave merge.  Past
+// `total`: 16 spare bytes that take the stores of the copy falling outside the
 // tables.
 template <int G, int VB, int WK = kMaxWK>
 struct StreamLds {
@@ -99,17 +121,17 @@ struct StreamLds {
   static constexpr int rinv = q4 + PrepOut<G>::rinv;
   static constexpr int vlut = q4 + PrepOut<G>::bytes;
   static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
-  static constexpr int kw = pt + kStreamWaves * G * kTile * 2;
+  static constexpr int W = StreamCfg<G, VB, WK>::waves;
+  static constexpr int kw = pt + W * G * kTile * 2;
   static constexpr int kw_rows = WK + 2;  // key words of the tile, then two zero rows
-  static constexpr int end = kw + kStreamWaves * kw_rows * kTile * 4;
-  static constexpr int scr = pt;
-  static constexpr int scr_end = scr + PrepScratch<G>::bytes;
-  static constexpr int merge = kStreamWaves * G * kPartStride * 4;
-  static constexpr int m1 = end > scr_end ? end : scr_end;
-  static constexpr int total = m1 > merge ? m1 : merge;
+  static constexpr int end = kw + W * kw_rows * kTile * 4;
+  static constexpr int merge = W * G * kPartStride * 4;
+  static constexpr int total = end > merge ? end : merge;
   static constexpr int spare = total, alloc = total + 16;
   static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0, "table bases above the index bits");
-  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && scr % 16 == 0 && kw % 16 == 0, "16-byte aligned areas");
+  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && kw % 16 == 0, "16-byte aligned areas");
+  static constexpr int scr = pt;  // query-preparation scratch (before the tile loop)
+  static_assert(scr + PrepScratch<G>::bytes <= total, "preparation scratch inside the allocation");
 };
 
 template <int VB, int WK>
@@ -120,21 +142,17 @@ struct TileRegs {
   uint32_t va[2 * VB], vb[2 * VB];
 };
 
-// All loads unconditional (addresses clamped into valid memory, unused words
-// zeroed afterwards) so that the compiler can count outstanding loads across
-// the software pipeline.  kc / wkl are the key words and their count, or the
-// norm array and 1 for zero-bit keys.  `base` is wave-uniform.
+// The tile's loads: wave-uniform base addresses (scalar registers) plus the
+// lane's offset, so that the compiler keeps one offset register per array.
+// Branch-free: a plan without key words (every block at zero bits) reads the
+// plan's block of zeros for every tile (`kstride` 0).
 template <int VB, int WK>
-__device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *__restrict__ kc,
+__device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *__restrict__ kc, size_t kstride,
                                           const uint16_t *__restrict__ kn, const uint32_t *__restrict__ vc,
-                                          const uint16_t *__restrict__ vn, size_t base, int wk, int wkl,
-                                          int lane) {
-  const uint32_t *kt = kc + base * wkl * kTile;
+                                          const uint16_t *__restrict__ vn, size_t base, int lane) {
+  const uint32_t *kt = kc + base * kstride;
 #pragma unroll
-  for (int j = 0; j < WK; ++j) {
-    const uint32_t v = kt[(size_t)min(j, wkl - 1) * kTile + lane];
-    r.w[j] = j < wk ? v : 0u;
-  }
+  for (int j = 0; j < WK; ++j) r.w[j] = kt[j * kTile + lane];
   r.nr = *(const uint2 *)(kn + base * kTile * 4 + lane * 4);
   r.nv = vn[base * kTile + lane];
   const uint32_t *vt = vc + base * kHeadDim * (2 * VB);
@@ -180,22 +198,28 @@ struct VQuads {
   static constexpr int v = (G + 3) / 4;  // matrix-core registers of 4 query heads
 };
 
-// 4-bit group on the matrix cores, one v_mfma_f32_4x4x1f32 per code r (16 blocks
-// of 4 x 4 x 1): block k is lanes 4k .. 4k + 3 = tokens 4k .. 4k + 3, its B operand
-// the token's centroid c4[code_r] (centroid pairs at LDS byte 8 x code byte) and
-// its output row m head m, so the token's lane keeps a4[h] in register h.  The A
-// operand, head m's query value of code r, is broadcast from block r % 16 of a
-// register whose lane 4k + m holds code 16 (r / 16) + k (CBSZ 4, ABID r % 16).
-// Key word J holds codes 8 J .. 8 J + 7, two per byte (low nibble first).
-template <int G, int WK, int J>
-__device__ __forceinline__ void key4_word(const uint32_t (&w)[WK], const float (&qa)[VQuads<G>::v],
-                                          f4v (&a4)[VQuads<G>::v]) {
+// Key word J holds codes 8 J .. 8 J + 7, two per byte (low nibble first).  The
+// words are pipelined: the four lookups of word J + 1 (and the query operand of
+// its block of 16 codes) are issued before the products of word J.
+template <int WK, int J>
+__device__ __forceinline__ void key4_lookups(const uint32_t (&w)[WK], uint32_t c4l, float2 (&cp)[4]) {
   const uint32_t word = w[J];
-  constexpr int S0 = 8 * (J & 1);
-  float2 cp[4];  // all four lookups in flight before the first product
 #pragma unroll
-  for (int by = 0; by < 4; ++by) cp[by] = lds_at<float2>(((word >> (8 * by)) & 255u) << 3);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int by = 0; by < 4; ++by) cp[by] = lds_at<float2>(c4l + (((word >> (8 * by)) & 255u) << 3));
+}
+
+template <int G, int VB, int BLK>
+__device__ __forceinline__ void key4_query(int lane, float (&qa)[VQuads<G>::v]) {
+#pragma unroll
+  for (int g = 0; g < VQuads<G>::v; ++g)
+    qa[g] = lds_at<float>(StreamLds<G, VB>::q4 +
+                          (uint32_t)(((4 * g + (lane & 3)) & (G - 1)) * kHeadDim + 16 * BLK + (lane >> 2)) * 4);
+}
+
+template <int G, int J>
+__device__ __forceinline__ void key4_products(const float2 (&cp)[4], const float (&qa)[VQuads<G>::v],
+                                              f4v (&a4)[VQuads<G>::v]) {
+  constexpr int S0 = 8 * (J & 1);
 #define BGTQ_K4(BY)                                                                          \
   _Pragma("unroll") for (int g = 0; g < VQuads<G>::v; ++g) {                                 \
     a4[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(qa[g], cp[BY].x, a4[g], 4, S0 + 2 * BY, 0);     \
@@ -205,20 +229,45 @@ __device__ __forceinline__ void key4_word(const uint32_t (&w)[WK], const float (
 #undef BGTQ_K4
 }
 
-// Blocks of 16 codes (two key words); only the words that hold 4-bit codes are read.
-template <int G, int VB, int WK, int BLK>
-__device__ __forceinline__ void key4_blocks(const uint32_t (&w)[WK], int n4w, int lane, f4v (&a4)[VQuads<G>::v]) {
-  if constexpr (2 * BLK < WK) {
-    if (2 * BLK < n4w) {
-      float qa[VQuads<G>::v];
-#pragma unroll
-      for (int g = 0; g < VQuads<G>::v; ++g)
-        qa[g] = lds_at<float>(StreamLds<G, VB>::q4 +
-                              (uint32_t)(((4 * g + (lane & 3)) & (G - 1)) * kHeadDim + 16 * BLK + (lane >> 2)) * 4);
-      key4_word<G, WK, 2 * BLK>(w, qa, a4);
-      if (2 * BLK + 1 < n4w) key4_word<G, WK, 2 * BLK + 1>(w, qa, a4);
-      key4_blocks<G, VB, WK, BLK + 1>(w, n4w, lane, a4);
+// Word J (< n4w) with its lookups in cx and the query operand of its block in qx;
+// word J + 1's go to cy / qy (the query operand only at a block boundary).
+template <int G, int VB, int WK, int J>
+__device__ __forceinline__ void key4_words(const uint32_t (&w)[WK], int n4w, int lane, uint32_t c4l, float2 (&cx)[4],
+                                           float2 (&cy)[4], float (&qx)[VQuads<G>::v], float (&qy)[VQuads<G>::v],
+                                           f4v (&a4)[VQuads<G>::v]) {
+  if constexpr (J < WK) {
+    if (J < n4w) {
+      if constexpr (J + 1 < WK) {
+        key4_lookups<WK, J + 1>(w, c4l, cy);
+        if constexpr ((J & 1) == 1) key4_query<G, VB, (J + 1) / 2>(lane, qy);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      key4_products<G, J>(cx, qx, a4);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr ((J & 1) == 1)
+        key4_words<G, VB, WK, J + 1>(w, n4w, lane, c4l, cy, cx, qy, qx, a4);
+      else
+        key4_words<G, VB, WK, J + 1>(w, n4w, lane, c4l, cy, cx, qx, qy, a4);
     }
+  }
+}
+
+// 4-bit group on the matrix cores, one v_mfma_f32_4x4x1f32 per code r (16 blocks
+// of 4 x 4 x 1): block k is lanes 4k .. 4k + 3 = tokens 4k .. 4k + 3, its B operand
+// the token's centroid c4[code_r] (centroid pairs at LDS byte 8 x code byte) and
+// its output row m head m, so the token's lane keeps
+// a4[h] in register h.  The A operand, head m's query value of code r, is
+// broadcast from block r % 16 of a register whose lane 4k + m holds code
+// 16 (r / 16) + k (CBSZ 4, ABID r % 16).
+template <int G, int VB, int WK>
+__device__ __forceinline__ void key4_group(const uint32_t (&w)[WK], int n4w, int lane, uint32_t c4l,
+                                           f4v (&a4)[VQuads<G>::v]) {
+  if (n4w > 0) {
+    float2 cx[4], cy[4];
+    float qx[VQuads<G>::v], qy[VQuads<G>::v];
+    key4_lookups<WK, 0>(w, c4l, cx);
+    key4_query<G, VB, 0>(lane, qx);
+    key4_words<G, VB, WK, 0>(w, n4w, lane, c4l, cx, cy, qx, qy, a4);
   }
 }
 
@@ -374,20 +423,47 @@ __device__ __forceinline__ h4v v_operand(const uint32_t (&c)[2 * VB], uint32_t v
   }
 }
 
-template <int G, int VB, int S>
-__device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
-                                             const h4v (&pa)[VQuads<G>::v], f4v (&acc0)[VQuads<G>::v],
-                                             f4v (&acc1)[VQuads<G>::v]) {
-  if constexpr (S < kTile / 4) {
-    const h4v b0 = v_operand<VB, S>(va, vlut), b1 = v_operand<VB, S>(vb, vlut);
+// The 16 steps in batches of kVBatch: the lookups of batch k + 1 are issued
+// before the products of batch k, so that the wave keeps 2 kVBatch lookups in
+// flight instead of waiting for each one.
+constexpr int kVBatch = 4;
+
+template <int VB, int S, int N>
+__device__ __forceinline__ void v_lookups(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+                                          h4v (&b0)[kVBatch], h4v (&b1)[kVBatch]) {
+  if constexpr (N < kVBatch) {
+    b0[N] = v_operand<VB, S + N>(va, vlut);
+    b1[N] = v_operand<VB, S + N>(vb, vlut);
+    v_lookups<VB, S, N + 1>(va, vb, vlut, b0, b1);
+  }
+}
+
+template <int G, int S, int N>
+__device__ __forceinline__ void v_products(const h4v (&b0)[kVBatch], const h4v (&b1)[kVBatch],
+                                           const h4v (&pa)[VQuads<G>::v], f4v (&acc0)[VQuads<G>::v],
+                                           f4v (&acc1)[VQuads<G>::v]) {
+  if constexpr (N < kVBatch) {
 #pragma unroll
     for (int g = 0; g < VQuads<G>::v; ++g) {
-      acc0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b0, acc0[g], 4, S, 0);
-      acc1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b1, acc1[g], 4, S, 0);
+      acc0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b0[N], acc0[g], 4, S + N, 0);
+      acc1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[g], b1[N], acc1[g], 4, S + N, 0);
     }
-    constexpr int kBatch = VB <= 2 ? 4 : 2;  // steps whose lookups may be in flight together
-    if constexpr (S % kBatch == kBatch - 1) __builtin_amdgcn_sched_barrier(0);
-    v_mfma_steps<G, VB, S + 1>(va, vb, vlut, pa, acc0, acc1);
+    v_products<G, S, N + 1>(b0, b1, pa, acc0, acc1);
+  }
+}
+
+// Batch starting at step S, whose lookups are in (x0, x1); the next batch's go to (y0, y1).
+template <int G, int VB, int S>
+__device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+                                             const h4v (&pa)[VQuads<G>::v], h4v (&x0)[kVBatch],
+                                             h4v (&x1)[kVBatch], h4v (&y0)[kVBatch], h4v (&y1)[kVBatch],
+                                             f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v]) {
+  if constexpr (S < kTile / 4) {
+    if constexpr (S + kVBatch < kTile / 4) v_lookups<VB, S + kVBatch, 0>(va, vb, vlut, y0, y1);
+    __builtin_amdgcn_sched_barrier(0);
+    v_products<G, S, 0>(x0, x1, pa, acc0, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    v_mfma_steps<G, VB, S + kVBatch>(va, vb, vlut, pa, y0, y1, x0, x1, acc0, acc1);
   }
 }
 
@@ -399,7 +475,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   f4v a4[VQuads<G>::v];
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
-  key4_blocks<G, VB, WK, 0>(r.w, st.n4w, lane, a4);
+  key4_group<G, VB, WK>(r.w, st.n4w, lane, (uint32_t)StreamLds<G, VB, WK>::c4, a4);
   // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w,
   // from the key words staged in this wave's LDS rows
 #pragma unroll
@@ -461,16 +537,13 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   for (int g = 0; g < VQuads<G>::v; ++g)
     pa[g] = lds_at<h4v>(st.ptw + ((4 * g + (lane & 3)) & (G - 1)) * (2 * kTile) + (lane >> 2) * 8);
   // ---- values: lane = coordinates lane and lane + 64
-  v_mfma_steps<G, VB, 0>(r.va, r.vb, (uint32_t)StreamLds<G, VB>::vlut, pa, acc0, acc1);
+  typedef StreamLds<G, VB, WK> L;
+  const uint32_t vlut = (uint32_t)L::vlut;
+  h4v x0[kVBatch], x1[kVBatch], y0[kVBatch], y1[kVBatch];
+  v_lookups<VB, 0, 0>(r.va, r.vb, vlut, x0, x1);
+  v_mfma_steps<G, VB, 0>(r.va, r.vb, vlut, pa, x0, x1, y0, y1, acc0, acc1);
 }
 
-// Waves per SIMD the register allocation aims at: four (two workgroups per CU,
-// at most 128 VGPRs) for up to four query heads per KV head and up to eight key
-// words per token; fewer for the larger register sets.
-template <int G, int WK>
-struct StreamOcc {
-  static constexpr int v = G <= 4 ? (WK <= 8 ? 4 : 3) : 2;
-};
 
 // ------------------------------------------------------------------ decode kernel
 
@@ -485,14 +558,15 @@ struct DecodeArgs {
   const uint16_t *vn;
   const int32_t *seq_lens;
   float *part;  // split partials [batch][hq][n_splits][kPartStride]
-  int64_t tiles_cap, max_seq_len, off_kvh, off_dtab, off_vlut, off_rowk, off_bandk;
-  int hkv, hq, wk, tiles_per_split, n_splits;
+  int64_t tiles_cap, max_seq_len, off_kvh, off_dtab, off_vlut, off_zero;
+  int hkv, hq, wk, tiles_base, tiles_extra, n_splits;  // split s: tiles_base + (s < tiles_extra) tiles
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
-  float kscale;
+  float kscale;  // softmax scale in log2 units
 };
 
 template <int G, int VB, int WK>
-__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(StreamOcc<G, WK>::v)))
+__global__ __attribute__((amdgpu_flat_work_group_size(1, StreamCfg<G, VB, WK>::threads)))
+__attribute__((amdgpu_waves_per_eu(StreamOcc<G, VB, WK>::v)))
 void decode_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint8_t *consts = a.consts;
@@ -501,68 +575,71 @@ void decode_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const KvhDesc *kd = (const KvhDesc *)(consts + a.off_kvh) + kvh;
   typedef StreamLds<G, VB, WK> Lds;
+  constexpr int kStreamWaves = StreamCfg<G, VB, WK>::waves, kStreamThreads = StreamCfg<G, VB, WK>::threads;
 
   // ---- prologue loads, in this order so that waiting for an earlier group
-  // does not wait for a later one (loads complete in order): query-prep
-  // inputs, the plan's decode and value tables (16 bytes per thread and
-  // round), the k-step descriptors, then the first tile.
-  // (the sequence length and the head's group fields first: the tile loop's
-  // bounds and dispatch depend on them after the query preparation)
+  // does not wait for a later one (loads complete in order): the sequence
+  // length and the head's group fields, the query preparation's inputs, the
+  // plan's decode and value tables (16 bytes per thread and round), then the
+  // first tile.
   const int64_t seq_raw = (int64_t)a.seq_lens[b] + a.seq_add;
   const int n4w = kd->n4w;
   const uint32_t cgrp = kd->cgrp, gbit = kd->gbit;
-  PrepLoads pl;
-  prep_load_row<G>(pl, (const uint2 *)(consts + a.off_rowk) + (size_t)kvh * kHeadDim, kd,
-                   a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid);
+  PrepIn<G, kStreamWaves> pin;
+  prep_issue<G, kStreamWaves>(pin, consts, kvh, a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid, wave,
+                              lane);
   constexpr int n0 = kDtabBytes >> 4;
   constexpr int n1 = n0 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
   constexpr int kRounds = (n1 + kStreamThreads - 1) / kStreamThreads;
   const uint4 *cs0 = (const uint4 *)(consts + a.off_dtab), *cs1 = (const uint4 *)(consts + a.off_vlut) - n0;
-  uint4 cr[kRounds];
-#pragma unroll
-  for (int k = 0; k < kRounds; ++k) {
-    const int i = min(tid + k * kStreamThreads, n1 - 1);
-    cr[k] = *(i < n0 ? cs0 + i : cs1 + i);
-  }
+  static_assert(kRounds <= 2 && n0 <= kStreamThreads, "at most two rounds of the table copy");
+  const int i0 = min(tid, n1 - 1), i1 = min(tid + kStreamThreads, n1 - 1);
+  const uint4 cr0 = *(i0 < n0 ? cs0 + i0 : cs1 + i0);
+  uint4 cr1 = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (kRounds == 2) cr1 = *(cs1 + i1);
+  prep_issue_rot<G, kStreamWaves>(pin, consts, kvh, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  // the tables, descriptor and queries into LDS before the first tile is
+  // requested (waiting for these loads only), so that they are not queued
+  // behind the grid's tile requests
+  const auto tab_at = [](int i) { return i < n0 ? 16 * i : i < n1 ? Lds::vlut + 16 * (i - n0) : Lds::spare; };
+  *(uint4 *)(smem + tab_at(tid)) = cr0;
+  if constexpr (kRounds == 2) *(uint4 *)(smem + tab_at(tid + kStreamThreads)) = cr1;
+  prep_stage<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, tid);
   StreamState st;
-  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tile request
-  // ---- tiles of this wave: tile_lo + wave, + 8, ...; double-buffered registers.
-  // The first is requested now, its range bounded by max_seq_len (in memory).
-  const int tile_lo = split * a.tiles_per_split;
-  const int tile_end = min(tile_lo + a.tiles_per_split, (int)((a.max_seq_len + kTile - 1) / kTile));
+  __builtin_amdgcn_sched_barrier(0);  // keep the staging ahead of the tile request
+  // ---- tiles of this wave: tile_lo + wave, + W, ... (W waves); double-buffered
+  // registers.  The first is requested now, before the query preparation, its
+  // range bounded by max_seq_len (in memory).
+  const int tile_lo = split * a.tiles_base + min(split, a.tiles_extra);
+  const int tile_end =
+      min(tile_lo + a.tiles_base + (split < a.tiles_extra ? 1 : 0), (int)((a.max_seq_len + kTile - 1) / kTile));
   const size_t head_base = ((size_t)b * a.hkv + kvh) * (size_t)a.tiles_cap;
-  const uint32_t *ksrc = a.wk ? a.kc : (const uint32_t *)a.kn;
-  const int wkl = a.wk ? a.wk : 1;
+  const bool kzero = a.wk == 0;
+  // (zero-key plans run the 4-word kernel: the plan's zero block is one such tile)
+  static_assert(4 * kTile * 4 == kZeroBytes, "zero block of one 4-word tile");
+  const uint32_t *kcodes = kzero ? (const uint32_t *)(consts + a.off_zero) : a.kc;
+  const size_t kstride = kzero ? 0 : (size_t)WK * kTile;
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
-  load_tile(ra, ksrc, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), a.wk, wkl, lane);
-  // the rotation bands depend on the row entries loaded above: requested after
-  // the tile, so that waiting for the row entries does not delay the tile
+  load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), lane);
   __builtin_amdgcn_sched_barrier(0);
-  prep_load_band(pl, (const float *)(consts + a.off_bandk), tid);
-#pragma unroll
-  for (int k = 0; k < kRounds; ++k) {
-    const int i = tid + k * kStreamThreads;
-    *(uint4 *)(smem + (i < n0 ? 16 * i : i < n1 ? Lds::vlut + 16 * (i - n0) : Lds::spare)) = cr[k];
-  }
   // the queries of this (sequence, KV head), rotated and scaled (ends with a barrier)
-  prep_build_rows<G>(pl, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
+  prep_build<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
+  st.seq = seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw);
+  st.wk = a.wk;
+  st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
+  st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
+  st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
+  st.n4w = n4w;
+  st.cgrp = cgrp;
+  st.gbit = gbit;
+  // the two zero rows past the key words (this lane's column, read by this lane only)
+  *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
+  *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
   float rinv[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) rinv[h] = lds_at<float>(Lds::rinv + 4 * h);
-  {
-    st.seq = seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw);
-    st.wk = a.wk;
-    st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
-    st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
-    st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
-    st.n4w = n4w;
-    st.cgrp = cgrp;
-    st.gbit = gbit;
-    // the two zero rows past the key words
-    *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
-    *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
-  }
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
@@ -576,7 +653,7 @@ void decode_kernel(const DecodeArgs a) {
   // next tile's registers are requested before the current one is processed
   // and moved into place after it.
   for (; tile < tile_hi; tile += kStreamWaves) {
-    load_tile(rb, ksrc, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), a.wk, wkl, lane);
+    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), lane);
     process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
     ra = rb;
   }
@@ -621,15 +698,30 @@ void decode_kernel(const DecodeArgs a) {
 
 typedef void (*decode_fn)(const DecodeArgs);
 
+// The decode kernel of a plan shape with its launch parameters.
+struct DecodeKernel {
+  decode_fn fn;
+  int smem, waves, per_cu;
+};
+
+template <int G, int VB, int WK>
+DecodeKernel kernel_of() {
+  return {decode_kernel<G, VB, WK>, StreamLds<G, VB, WK>::alloc, StreamCfg<G, VB, WK>::waves,
+          StreamCfg<G, VB, WK>::per_cu};
+}
+
+// Key words per token: 4 avg_bits exactly (zero-bit plans run the 4-word kernel
+// with the key words zero).
 template <int G, int VB>
-decode_fn pick_wk(int wk) {
-  if (wk <= 8) return decode_kernel<G, VB, 8>;
-  if (wk <= 12) return decode_kernel<G, VB, 12>;
-  return decode_kernel<G, VB, 16>;
+DecodeKernel pick_wk(int wk) {
+  if (wk <= 4) return kernel_of<G, VB, 4>();
+  if (wk <= 8) return kernel_of<G, VB, 8>();
+  if (wk <= 12) return kernel_of<G, VB, 12>();
+  return kernel_of<G, VB, 16>();
 }
 
 template <int G>
-decode_fn pick_vb(int vb, int wk) {
+DecodeKernel pick_vb(int vb, int wk) {
   switch (vb) {
     case 1: return pick_wk<G, 1>(wk);
     case 2: return pick_wk<G, 2>(wk);
@@ -638,7 +730,7 @@ decode_fn pick_vb(int vb, int wk) {
   }
 }
 
-decode_fn pick_decode(int g, int vb, int wk) {
+DecodeKernel pick_decode(int g, int vb, int wk) {
   switch (g) {
     case 1: return pick_vb<1>(vb, wk);
     case 2: return pick_vb<2>(vb, wk);
@@ -647,40 +739,27 @@ decode_fn pick_decode(int g, int vb, int wk) {
   }
 }
 
-template <int G, int VB>
-int smem_wk(int wk) {
-  if (wk <= 8) return StreamLds<G, VB, 8>::alloc;
-  if (wk <= 12) return StreamLds<G, VB, 12>::alloc;
-  return StreamLds<G, VB, 16>::alloc;
-}
-
-int decode_smem_bytes(int g, int vb, int wk) {
-#define BGTQ_SM(G_, VB_) \
-  if (g == G_ && vb == VB_) return smem_wk<G_, VB_>(wk);
-  BGTQ_SM(1, 1) BGTQ_SM(1, 2) BGTQ_SM(1, 3) BGTQ_SM(1, 4)
-  BGTQ_SM(2, 1) BGTQ_SM(2, 2) BGTQ_SM(2, 3) BGTQ_SM(2, 4)
-  BGTQ_SM(4, 1) BGTQ_SM(4, 2) BGTQ_SM(4, 3) BGTQ_SM(4, 4)
-  BGTQ_SM(8, 1) BGTQ_SM(8, 2) BGTQ_SM(8, 3) BGTQ_SM(8, 4)
-#undef BGTQ_SM
-  return -1;
-}
-
 // Workspace: the split partials [batch][hq][n_splits][kPartStride] f32.
 struct DecodeLayout {
-  int n_splits, tiles_per_split;
+  int n_splits, tiles_base, tiles_extra;  // split s covers tiles_base + (s < tiles_extra) tiles
   size_t total;
 };
+
 
 DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   DecodeLayout d{};
   const int tiles = (int)((max_seq_len + kTile - 1) / kTile);
   const int hkv = p.desc.n_kv_heads, hq = p.desc.n_q_heads;
-  const int target = 2 * device_cus();
+  const DecodeKernel k = pick_decode(p.hdr.group, p.hdr.v_bits, p.hdr.wk);
+  const int target = std::max(1, k.per_cu) * device_cus();  // one round of resident workgroups
   int s = (target + batch * hkv - 1) / (batch * hkv);
-  s = std::max(1, std::min({s, (tiles + 2 * kStreamWaves - 1) / (2 * kStreamWaves), kMaxSplits}));
-  const int tps = (tiles + s - 1) / s;
-  d.n_splits = (tiles + tps - 1) / tps;
-  d.tiles_per_split = tps;
+  s = std::max(1, std::min({s, (tiles + 2 * k.waves - 1) / (2 * k.waves), kMaxSplits}));
+  // tiles dealt out evenly: the first tiles % s splits take one tile more, so
+  // that (with a multiple of the wave count per split) no wave but those of
+  // the first splits has a tile more than the others
+  d.n_splits = s;
+  d.tiles_base = tiles / s;
+  d.tiles_extra = tiles % s;
   d.total = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
   return d;
 }
@@ -716,9 +795,10 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
 bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   const DecodeLayout lay = decode_layout(p, c.batch, c.max_seq_len);
   const int G = p.hdr.group, vb = p.hdr.v_bits;
-  const int smem = decode_smem_bytes(G, vb, p.hdr.wk);
-  decode_fn fn = pick_decode(G, vb, p.hdr.wk);
-  if (smem < 0 || !decode_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
+  const DecodeKernel k = pick_decode(G, vb, p.hdr.wk);
+  const int smem = k.smem;
+  decode_fn fn = k.fn;
+  if (!decode_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: LDS request above the limit");
@@ -753,12 +833,12 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.off_kvh = p.hdr.off_kvh;
   a.off_dtab = p.hdr.off_dtab;
   a.off_vlut = p.hdr.off_vlut;
-  a.off_rowk = p.hdr.off_rowk;
-  a.off_bandk = p.hdr.off_bandk;
+  a.off_zero = p.hdr.off_zero;
   a.hkv = p.desc.n_kv_heads;
   a.hq = p.desc.n_q_heads;
   a.wk = p.hdr.wk;
-  a.tiles_per_split = lay.tiles_per_split;
+  a.tiles_base = lay.tiles_base;
+  a.tiles_extra = lay.tiles_extra;
   a.n_splits = lay.n_splits;
   a.seq_add = c.seq_add;
   a.kscale = kscale_of(c.softmax_scale);
@@ -766,9 +846,9 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   // With profiling on, the events are bound to the launch itself, so their elapsed time is the
   // kernel's own start-to-end time (no queue packets of their own around the kernel).
   if (e0)
-    hipExtLaunchKernelGGL(fn, grid, dim3(kStreamThreads), (uint32_t)smem, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(fn, grid, dim3(64 * k.waves), (uint32_t)smem, st, e0, e1, 0, a);
   else
-    fn<<<grid, kStreamThreads, smem, st>>>(a);
+    fn<<<grid, 64 * k.waves, smem, st>>>(a);
   const bgtq_status s = launch_status("decode");
   if (e1) {
     Prof &pr = prof();

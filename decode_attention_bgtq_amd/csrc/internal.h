@@ -17,6 +17,7 @@ constexpr int kTile = 64;
 constexpr int kMaxGroups = 4;
 constexpr int kMaxWK = 16;          // key words per token at 4 bits per coordinate
 constexpr int kMaxKSteps = 36;      // bound on the width-1..3 k-steps of one head (at most 33)
+constexpr int kZeroBytes = 4 * 64 * 4;  // one tile of four key words
 
 // Decode k-steps of the key groups of width 1..3 (the 4-bit group takes one
 // matrix-core step per code).  A k-step is four consecutive positions of one
@@ -67,10 +68,10 @@ struct ConstHeader {
   int64_t off_dtab;          // decode tables, kDtabBytes (layout above)
   int64_t off_vlut;          // value-width table: fp16 centroid pairs of the tokens of one code chunk
   int64_t vlut_bytes;
-  int64_t off_rowk;          // uint2 [n_kv_heads][128]: per group-order row p of the key rotation, x = float
-                             // offset of its band in the band area, y = d_g | pos_g << 8 | w << 16 | kbase << 19
+  int64_t off_rowk;          // uint2 [n_kv_heads][128]: per group-order row p of the key rotation, x = row
+                             // within its group, y = d_g | pos_g << 8 | w << 16 | kbase << 19
                              // (kbase: first k-step of a width-1..3 group); y = 0 past d_nz
-  int64_t off_bandk;         // float: per KV head and group, Pi_g row-major (d_g x d_g), groups in order
+  int64_t off_zero;          // kZeroBytes of zeros: the key words of every tile for a plan without key bits
   int64_t total_bytes;
   double thr[4][16];         // interior thresholds of the b-bit quantiser, row b-1
   double cent[4][16];        // centroids, row b-1

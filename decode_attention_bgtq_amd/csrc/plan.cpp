@@ -347,11 +347,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   off = align256(off + 4 * vlut.size());
   hd.off_rowk = off;
   off = align256(off + 8 * (size_t)hkv * kHeadDim);
-  hd.off_bandk = off;
-  int64_t band_floats = 0;
-  for (int h = 0; h < hkv; ++h)
-    for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) band_floats += (int64_t)p.kvh[h].g[gi].d * p.kvh[h].g[gi].d;
-  off = align256(off + 4 * (size_t)std::max<int64_t>(band_floats, 4));
+  hd.off_zero = off;
+  off = align256(off + kZeroBytes);
   hd.total_bytes = off;
 
   p.image.assign(off, 0);
@@ -372,23 +369,17 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
         }
     }
   {
-    // key rotation bands for the decode's query preparation
+    // per group-order row of the key rotation: its group's size, position, width and first k-step
     uint32_t *rowk = (uint32_t *)(img + hd.off_rowk);
-    float *band = (float *)(img + hd.off_bandk);
-    size_t gi_all = 0;
-    int64_t boff = 0;
     for (int h = 0; h < hkv; ++h)
-      for (int gi = 0; gi < p.kvh[h].n_groups; ++gi, ++gi_all) {
+      for (int gi = 0; gi < p.kvh[h].n_groups; ++gi) {
         const KGroupDesc &g = p.kvh[h].g[gi];
-        const std::vector<double> &pi = p.rot_k[gi_all];
         const uint32_t kb = g.w < 4 ? (uint32_t)kbase[(size_t)h * kMaxGroups + gi] : 0u;
         for (int i = 0; i < g.d; ++i) {
           const size_t r = (size_t)h * kHeadDim + g.pos + i;
-          rowk[2 * r] = (uint32_t)(boff + (int64_t)i * g.d);
+          rowk[2 * r] = (uint32_t)i;
           rowk[2 * r + 1] = (uint32_t)g.d | ((uint32_t)g.pos << 8) | ((uint32_t)g.w << 16) | (kb << 19);
-          for (int k = 0; k < g.d; ++k) band[boff + (int64_t)i * g.d + k] = (float)pi[(size_t)i * g.d + k];
         }
-        boff += (int64_t)g.d * g.d;
       }
   }
   {
