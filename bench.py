@@ -121,7 +121,7 @@ def traffic_from(fetch_dir: str, write_dir: str, cid: int, packed: int | None, o
             dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             if "copyBuffer" in r["Kernel_Name"]:
                 copy.append((dur, float(r["Counter_Value"])))
-            elif STREAM_KERNEL in r["Kernel_Name"]:
+            elif ("bgtq::%s<" % STREAM_KERNEL) in r["Kernel_Name"]:  # not the fp16 baseline's kernel
                 stream.append(float(r["Counter_Value"]))
         top = max(d for d, _ in copy)
         big = [v for d, v in copy if d >= top / 2]  # the 1 GiB copies
