@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libbgtq.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
 TILE = 64
 HEAD_DIM = 128
+ROPE_PAIRINGS = {"half": 0, "interleaved": 1}  # half-split (j, j+64), interleaved (2j, 2j+1)
 
 EXPORTED = [
     "bgtq_abi_version", "bgtq_last_error", "bgtq_energy", "bgtq_allocate", "bgtq_plan_create",
@@ -39,7 +40,7 @@ class _PlanDesc(ctypes.Structure):
     _fields_ = [("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("k_avg_bits", ctypes.c_int32),
                 ("v_bits", ctypes.c_int32), ("k_bits", ctypes.POINTER(ctypes.c_int8)),
-                ("seed", ctypes.c_uint64), ("layer", ctypes.c_int32)]
+                ("seed", ctypes.c_uint64), ("layer", ctypes.c_int32), ("rope_pairing", ctypes.c_int32)]
 
 
 class _Sizes(ctypes.Structure):
@@ -67,7 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "bgtq_abi_version": (I32, []),
         "bgtq_last_error": (ctypes.c_char_p, []),
-        "bgtq_energy": (I32, [P, P, I64, I32, I32, I32, P, P]),
+        "bgtq_energy": (I32, [P, P, I64, I32, I32, I32, I32, P, P]),
         "bgtq_allocate": (I32, [P, I32, I32, I32, P, P]),
         "bgtq_plan_create": (I32, [ctypes.POINTER(_PlanDesc), ctypes.POINTER(P)]),
         "bgtq_plan_destroy": (None, [P]),
@@ -129,9 +130,16 @@ def codebook(bits: int):
     return c, t, d.value
 
 
-def energy(q_cal, k_cal, n_kv_heads: int, out, stream=None) -> None:
+def _pairing(p) -> int:
+    if p not in ROPE_PAIRINGS:
+        raise ValueError("rope pairing must be one of %s" % (list(ROPE_PAIRINGS),))
+    return ROPE_PAIRINGS[p]
+
+
+def energy(q_cal, k_cal, n_kv_heads: int, out, stream=None, pairing: str = "half") -> None:
     n, hq, d = q_cal.shape
-    _check(load().bgtq_energy(_ptr(q_cal), _ptr(k_cal), n, hq, n_kv_heads, d, _ptr(out), _stream(stream)))
+    _check(load().bgtq_energy(_ptr(q_cal), _ptr(k_cal), n, hq, n_kv_heads, d, _pairing(pairing), _ptr(out),
+                              _stream(stream)))
 
 
 def allocate(energy_t, avg_bits: int, out, stream=None) -> None:
@@ -152,7 +160,7 @@ class Plan:
     """Host plan for one layer (widths, V width, seed, layer id)."""
 
     def __init__(self, k_bits: np.ndarray, k_avg_bits: int, v_bits: int, n_q_heads: int,
-                 seed: int = 0, layer: int = 0):
+                 seed: int = 0, layer: int = 0, pairing: str = "half"):
         lib = load()
         kb = np.ascontiguousarray(np.asarray(k_bits, dtype=np.int8))
         self.n_kv_heads = kb.shape[0]
@@ -161,8 +169,9 @@ class Plan:
         self.v_bits = v_bits
         self.seed = seed
         self.layer = layer
+        self.pairing = pairing
         desc = _PlanDesc(self.n_kv_heads, n_q_heads, HEAD_DIM, k_avg_bits, v_bits,
-                         kb.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), seed, layer)
+                         kb.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), seed, layer, _pairing(pairing))
         h = ctypes.c_void_p()
         _check(lib.bgtq_plan_create(ctypes.byref(desc), ctypes.byref(h)))
         self._h = h

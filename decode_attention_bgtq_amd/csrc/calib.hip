@@ -7,10 +7,12 @@
 
 namespace bgtq {
 
-// One workgroup per KV head: exact integer sums of squares per coordinate.
+// One workgroup per KV head: exact integer sums of squares per coordinate,
+// then per block over its two coordinates (j, j+64) half-split or (2j, 2j+1)
+// interleaved.
 __global__ __launch_bounds__(256) void energy_kernel(const uint16_t *__restrict__ q,
                                                      const uint16_t *__restrict__ k, int64_t n,
-                                                     int hq, int hkv, double *__restrict__ energy) {
+                                                     int hq, int hkv, int inter, double *__restrict__ energy) {
   __shared__ u128 sq[256], sk[256];
   const int kvh = blockIdx.x, tid = threadIdx.x, c = tid & 127, half = tid >> 7;
   const int G = hq / hkv;
@@ -27,9 +29,9 @@ __global__ __launch_bounds__(256) void energy_kernel(const uint16_t *__restrict_
   sk[tid] = ak;
   __syncthreads();
   if (tid < kBlocks) {
-    const int j = tid;
-    const u128 tq = sq[j] + sq[j + 64] + sq[128 + j] + sq[128 + j + 64];
-    const u128 tk = sk[j] + sk[j + 64] + sk[128 + j] + sk[128 + j + 64];
+    const int j = tid, a = inter ? 2 * j : j, b = inter ? 2 * j + 1 : j + kBlocks;
+    const u128 tq = sq[a] + sq[b] + sq[128 + a] + sq[128 + b];
+    const u128 tk = sk[a] + sk[b] + sk[128 + a] + sk[128 + b];
     const double eq = ldexp(u128_to_f64(tq), -48) / (double)(n * G);
     const double ek = ldexp(u128_to_f64(tk), -48) / (double)n;
     energy[(size_t)kvh * kBlocks + j] = eq * ek;
@@ -69,14 +71,17 @@ using namespace bgtq;
 extern "C" {
 
 bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_cal, int32_t n_q_heads,
-                        int32_t n_kv_heads, int32_t head_dim, double *energy, bgtq_stream stream) {
+                        int32_t n_kv_heads, int32_t head_dim, int32_t rope_pairing, double *energy,
+                        bgtq_stream stream) {
   if (!q_cal || !k_cal || !energy) return fail(BGTQ_EINVAL, "bgtq_energy: null pointer");
   if (n_cal < 1 || n_cal > (1 << 22)) return fail(BGTQ_EINVAL, "bgtq_energy: n_cal must be 1..2^22");
   if (head_dim != kHeadDim) return fail(BGTQ_EINVAL, "bgtq_energy: head_dim must be 128");
   if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads)
     return fail(BGTQ_EINVAL, "bgtq_energy: n_q_heads must be a positive multiple of n_kv_heads");
+  if (rope_pairing != BGTQ_ROPE_HALF && rope_pairing != BGTQ_ROPE_INTERLEAVED)
+    return fail(BGTQ_EINVAL, "bgtq_energy: rope_pairing must be BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED");
   energy_kernel<<<n_kv_heads, 256, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
-                                                              energy);
+                                                              rope_pairing, energy);
   return launch_status("bgtq_energy");
 }
 

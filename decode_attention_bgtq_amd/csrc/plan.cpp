@@ -218,6 +218,10 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     err = "k_bits is NULL";
     return BGTQ_EINVAL;
   }
+  if (d.rope_pairing != BGTQ_ROPE_HALF && d.rope_pairing != BGTQ_ROPE_INTERLEAVED) {
+    err = "rope_pairing must be BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED";
+    return BGTQ_EINVAL;
+  }
   if (d.k_avg_bits < 0 || d.k_avg_bits > 4 || d.v_bits < 1 || d.v_bits > 4) {
     err = "k_avg_bits must be 0..4 and v_bits 1..4";
     return BGTQ_EBUDGET;
@@ -242,7 +246,9 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
   }
   const int wk = 4 * d.k_avg_bits;
 
-  // groups, coordinates, bit offsets, rotations
+  // groups, coordinates, bit offsets, rotations; block j holds coordinates (j, j+64) half-split
+  // or (2j, 2j+1) interleaved, next to each other in its group
+  const bool inter = d.rope_pairing == BGTQ_ROPE_INTERLEAVED;
   p.kvh.assign(hkv, KvhDesc{});
   p.rot_k.clear();
   p.rot_v.clear();
@@ -255,8 +261,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
       int dg = 0;
       for (int j = 0; j < kBlocks; ++j)
         if (p.bits[(size_t)h * kBlocks + j] == w) {
-          kd.coord[pos + dg++] = (int16_t)j;
-          kd.coord[pos + dg++] = (int16_t)(j + kBlocks);
+          kd.coord[pos + dg++] = (int16_t)(inter ? 2 * j : j);
+          kd.coord[pos + dg++] = (int16_t)(inter ? 2 * j + 1 : j + kBlocks);
         }
       if (!dg) continue;
       KGroupDesc &g = kd.g[kd.n_groups++];

@@ -45,8 +45,14 @@ enum {
   BGTQ_EWORKSPACE = -5  /* workspace smaller than the size query */
 };
 
-#define BGTQ_ABI_VERSION 1
+#define BGTQ_ABI_VERSION 2
 #define BGTQ_TILE 64 /* cache tokens per tile */
+
+/* RoPE pairing of the 128 head coordinates into 64 2-D frequency blocks (the
+ * pages name none; both conventions in use): half-split ("rotate-half"),
+ * block j = coordinates (j, j+64); interleaved, block j = (2j, 2j+1). */
+#define BGTQ_ROPE_HALF 0
+#define BGTQ_ROPE_INTERLEAVED 1
 
 typedef void *bgtq_stream; /* hipStream_t */
 
@@ -56,21 +62,24 @@ const char *bgtq_last_error(void);
 /*
  * (1) Label-free block energy (Abstract: "computes a label-free energy score
  * for each RoPE block"; README calibration paragraph: Q/K activations of one
- * forward pass).  Block j of a 128-wide head is the coordinate pair (j, j+64).
+ * forward pass).  Block j of a 128-wide head is the coordinate pair (a_j, b_j)
+ * = (j, j+64) for rope_pairing BGTQ_ROPE_HALF, (2j, 2j+1) for
+ * BGTQ_ROPE_INTERLEAVED.
  *   E[h][j] = Eq[h][j] * Ek[h][j]
- *   Eq[h][j] = sum over t < n_cal and h' in {hG..hG+G-1} of q[t][h'][j]^2 + q[t][h'][j+64]^2, / (n_cal G)
- *   Ek[h][j] = sum over t < n_cal of k[t][h][j]^2 + k[t][h][j+64]^2, / n_cal
+ *   Eq[h][j] = sum over t < n_cal and h' in {hG..hG+G-1} of q[t][h'][a_j]^2 + q[t][h'][b_j]^2, / (n_cal G)
+ *   Ek[h][j] = sum over t < n_cal of k[t][h][a_j]^2 + k[t][h][b_j]^2, / n_cal
  * Each sum is exact and rounded once to double; the division and the product
  * round once each, so the result is deterministic to the last bit.
  *   q_cal   device fp16 [n_cal][n_q_heads][head_dim], post-RoPE, d fastest
  *   k_cal   device fp16 [n_cal][n_kv_heads][head_dim]
  *   energy  device double [n_kv_heads][head_dim/2], written
+ *   rope_pairing  BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED
  * Errors: EINVAL on null pointers, n_cal < 1 or n_cal > 2^22, head_dim != 128,
- * n_q_heads not a positive multiple of n_kv_heads.
+ * n_q_heads not a positive multiple of n_kv_heads, an unknown rope_pairing.
  */
 bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_cal,
                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                        double *energy, bgtq_stream stream);
+                        int32_t rope_pairing, double *energy, bgtq_stream stream);
 
 /*
  * (2) Greedy integer bit allocation by marginal gain (Abstract: "greedily
@@ -108,6 +117,8 @@ typedef struct {
   const int8_t *k_bits; /* host int8 [n_kv_heads][64], values 0..4 */
   uint64_t seed;
   int32_t layer;
+  int32_t rope_pairing; /* BGTQ_ROPE_HALF (0) or BGTQ_ROPE_INTERLEAVED: the two coordinates that block j
+                           contributes to its key group */
 } bgtq_plan_desc;
 
 typedef struct {
@@ -118,7 +129,7 @@ typedef struct {
   uint64_t v_norms; /* fp16 [batch][Hkv][tiles][64] */
 } bgtq_sizes;
 
-/* Errors: EINVAL (null, shape), EBUDGET (a row of k_bits does not sum to
+/* Errors: EINVAL (null, shape, unknown rope_pairing), EBUDGET (a row of k_bits does not sum to
  * k_avg_bits * 64 or holds a width outside 0..4, v_bits outside 1..4). */
 bgtq_status bgtq_plan_create(const bgtq_plan_desc *desc, bgtq_plan **out);
 void bgtq_plan_destroy(bgtq_plan *plan);

@@ -31,7 +31,7 @@ from .quant import (groups_for, encode_groups, encode_k, encode_v, f16_bits, f16
                     dequant_k, dequant_v)
 from .layout import (k_words_per_token, pack_k, unpack_k, pack_v, unpack_v, k_bit_offsets)
 from .attention import decode_attention, softmax_attention
-from .rope import rope_blocks, block_logits
+from .rope import rope_blocks, block_logits, block_pairs
 from .diagnostics import logit_mae
 
 __all__ = [
@@ -42,5 +42,5 @@ __all__ = [
     "dequant_k", "dequant_v",
     "k_words_per_token", "pack_k", "unpack_k", "pack_v", "unpack_v", "k_bit_offsets",
     "decode_attention", "softmax_attention",
-    "rope_blocks", "block_logits", "logit_mae",
+    "rope_blocks", "block_logits", "block_pairs", "logit_mae",
 ]

@@ -9,10 +9,12 @@ bits shift toward high-energy blocks under a fixed average budget.
 
 Readings taken where the pages are silent:
 
-* Energy of block j of KV head h (2-D block = coordinates (j, j+64)):
+* Energy of block j of KV head h, whose coordinates are (a_j, b_j) =
+  (j, j+64) under the half-split pairing or (2j, 2j+1) under the interleaved
+  one (oracle.rope.block_pairs):
     E_{h,j} = Eq_{h,j} * Ek_{h,j},
-    Eq_{h,j} = sum_{t, h' in grp(h)} (q_{t,h',j}^2 + q_{t,h',j+64}^2) / (n_cal * G),
-    Ek_{h,j} = sum_t (k_{t,h,j}^2 + k_{t,h,j+64}^2) / n_cal,
+    Eq_{h,j} = sum_{t, h' in grp(h)} (q_{t,h',a_j}^2 + q_{t,h',b_j}^2) / (n_cal * G),
+    Ek_{h,j} = sum_t (k_{t,h,a_j}^2 + k_{t,h,b_j}^2) / n_cal,
   with grp(h) = {hG, ..., hG+G-1}.  The logit term of block j is bounded by
   |q_j| |k_j| and RoPE preserves block norms, so this is position-free.
   Each sum is the exact sum of the fp16 squares rounded once to float64;
@@ -25,6 +27,8 @@ Readings taken where the pages are silent:
 from __future__ import annotations
 
 import numpy as np
+
+from .rope import block_pairs
 
 
 def exact_sum_squares_f16(x16: np.ndarray, axis: int = -1) -> np.ndarray:
@@ -46,7 +50,7 @@ def exact_sum_squares_f16(x16: np.ndarray, axis: int = -1) -> np.ndarray:
     return np.asarray(tot, dtype=object).astype(np.float64) * (2.0 ** -48)
 
 
-def energy(q_cal: np.ndarray, k_cal: np.ndarray, n_kv_heads: int) -> np.ndarray:
+def energy(q_cal: np.ndarray, k_cal: np.ndarray, n_kv_heads: int, pairing: str = "half") -> np.ndarray:
     """Block energies E [Hkv, head_dim/2] (float64) from fp16 calibration Q [n, Hq, d] and K [n, Hkv, d]."""
     q_cal = np.asarray(q_cal, dtype=np.float16)
     k_cal = np.asarray(k_cal, dtype=np.float16)
@@ -54,11 +58,12 @@ def energy(q_cal: np.ndarray, k_cal: np.ndarray, n_kv_heads: int) -> np.ndarray:
     assert k_cal.shape == (n, n_kv_heads, d) and d % 2 == 0 and hq % n_kv_heads == 0
     g = hq // n_kv_heads
     nb = d // 2
+    a, b = block_pairs(d, pairing)
     out = np.empty((n_kv_heads, nb), dtype=np.float64)
     for h in range(n_kv_heads):
         qh = q_cal[:, h * g:(h + 1) * g, :]                          # [n, G, d]
-        q_pairs = np.concatenate([qh[..., :nb], qh[..., nb:]], axis=1)  # [n, 2G, nb]
-        k_pairs = np.stack([k_cal[:, h, :nb], k_cal[:, h, nb:]], axis=1)  # [n, 2, nb]
+        q_pairs = np.concatenate([qh[..., a], qh[..., b]], axis=1)    # [n, 2G, nb]
+        k_pairs = np.stack([k_cal[:, h, a], k_cal[:, h, b]], axis=1)  # [n, 2, nb]
         sq = exact_sum_squares_f16(q_pairs.transpose(2, 0, 1).reshape(nb, -1))
         sk = exact_sum_squares_f16(k_pairs.transpose(2, 0, 1).reshape(nb, -1))
         eq = sq / float(n * g)

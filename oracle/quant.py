@@ -7,8 +7,9 @@ do not spell out the encoder; the readings taken are:
 
 * Groups (keys): one group per width w present in the allocation, in the
   order w = 4, 3, 2, 1.  Group w holds the blocks j with b_j = w in
-  ascending j, each block contributing its two coordinates (j, j+64) next to
-  each other.  Zero-width blocks are not stored and decode to 0.
+  ascending j, each block contributing its two coordinates next to each
+  other: (j, j+64) under the half-split RoPE pairing, (2j, 2j+1) under the
+  interleaved one.  Zero-width blocks are not stored and decode to 0.
 * Values: one group of all 128 coordinates in natural order at width b_V.
 * Per token and group: n = ||x_g|| in float64 (exact sum of the fp16 squares
   rounded once, then a correctly rounded sqrt); y = Pi x_g / n (y = 0 when
@@ -25,6 +26,7 @@ import numpy as np
 
 from .alloc import exact_sum_squares_f16
 from .codebook import lloyd_max
+from .rope import block_pairs
 from .rotation import rotation_for
 
 HEAD_DIM = 128
@@ -41,14 +43,15 @@ def f16_value(bits) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
-def groups_for(bits_row) -> list[tuple[int, np.ndarray]]:
+def groups_for(bits_row, pairing: str = "half") -> list[tuple[int, np.ndarray]]:
     """[(width, coordinate indices)] for widths 4, 3, 2, 1 that are present."""
     bits_row = np.asarray(bits_row)
+    first, second = block_pairs(HEAD_DIM, pairing)
     out = []
     for w in (4, 3, 2, 1):
         blocks = np.nonzero(bits_row == w)[0]
         if blocks.size:
-            coords = np.stack([blocks, blocks + N_BLOCKS], axis=1).reshape(-1)
+            coords = np.stack([first[blocks], second[blocks]], axis=1).reshape(-1)
             out.append((w, coords))
     return out
 
@@ -88,12 +91,12 @@ def v_rotation(v_bits: int, seed: int, layer: int, kvh: int):
     return rotation_for(seed, layer, kvh, V_TENSOR, v_bits, HEAD_DIM)
 
 
-def encode_k(k16: np.ndarray, bits_row, seed: int, layer: int, kvh: int, rots=None):
+def encode_k(k16: np.ndarray, bits_row, seed: int, layer: int, kvh: int, rots=None, pairing: str = "half"):
     """Keys of one KV head, fp16 [N, 128] -> (codes [N, d_nz] uint8, norm bits [N, 4] uint16).
 
     Norm slot 4 - w holds the fp16 norm of the width-w group; absent slots are 0.
     """
-    groups = groups_for(bits_row)
+    groups = groups_for(bits_row, pairing)
     if rots is None:
         rots = k_rotations(bits_row, seed, layer, kvh)
     codes, norms = encode_groups(k16, groups, rots)
@@ -112,9 +115,10 @@ def encode_v(v16: np.ndarray, v_bits: int, seed: int, layer: int, kvh: int, rot=
     return codes, f16_bits(norms[:, 0])
 
 
-def dequant_k(codes, norm_bits, bits_row, seed: int, layer: int, kvh: int, rots=None) -> np.ndarray:
+def dequant_k(codes, norm_bits, bits_row, seed: int, layer: int, kvh: int, rots=None,
+              pairing: str = "half") -> np.ndarray:
     """Reconstructed keys [N, 128] float64 from codes [N, d_nz] and norm slots [N, 4]."""
-    groups = groups_for(bits_row)
+    groups = groups_for(bits_row, pairing)
     if rots is None:
         rots = k_rotations(bits_row, seed, layer, kvh)
     n_rows = codes.shape[0]

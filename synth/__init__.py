@@ -7,13 +7,16 @@ oracle and the HIP library both consume what it returns.
 Shapes and distributions follow the five workloads of the packed-cache path
 (post-RoPE fp16 keys, queries and calibration activations, fp16 values):
 
-* RoPE uses the half-split ("rotate-half") pairing: 2-D block j of a
-  128-wide head is the coordinate pair (j, j+64), rotated at position p by
-  the angle p * theta**(-2j/128).  RoPE is applied in float64 and the result
+* RoPE pairs the coordinates of a 128-wide head into 2-D blocks either
+  half-split ("rotate-half", the default: block j is the pair (j, j+64)) or
+  interleaved (block j is (2j, 2j+1)), as ``Config.pairing`` says; block j
+  is rotated at position p by the angle p * theta**(-2j/128).  RoPE is applied in float64 and the result
   is rounded to fp16 (round-to-nearest-even) in one step.
 * Pre-RoPE keys (and queries, drawn the same way from the KV head they
   share) have both coordinates of block j ~ N(0, s_{h,j}^2); values are
-  iid N(0, 1).
+  iid N(0, 1).  An interleaved config draws exactly the numbers of its
+  half-split twin, with coordinate (j, j+64) of every key, query and
+  calibration row moved to (2j, 2j+1).
 * Random streams are ``numpy.random.Generator(PCG64(SeedSequence(seed,
   spawn_key=(config, stream, seq))))`` with one stream per tensor kind.
 """
@@ -48,6 +51,7 @@ class Config:
     n_cal: int               # calibration tokens
     append: int = 0          # tokens appended after the prefill cache
     seed: int = 0
+    pairing: str = "half"    # RoPE block pairing: "half" (j, j+64) or "interleaved" (2j, 2j+1)
 
     @property
     def group(self) -> int:
@@ -88,21 +92,40 @@ def block_scales(cfg: Config) -> np.ndarray:
     return s
 
 
-def rope_f64(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
-    """Half-split RoPE on float64 ``x[..., tokens, heads, 128]`` at positions ``pos``.
+def to_pairing(x: np.ndarray, pairing: str) -> np.ndarray:
+    """Move half-split coordinates (j, j+64) of ``x[..., 128]`` to the slots of ``pairing``."""
+    if pairing == "half":
+        return x
+    if pairing != "interleaved":
+        raise ValueError("pairing must be 'half' or 'interleaved'")
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., :N_BLOCKS]
+    out[..., 1::2] = x[..., N_BLOCKS:]
+    return out
+
+
+def rope_f64(x: np.ndarray, pos: np.ndarray, theta: float, pairing: str = "half") -> np.ndarray:
+    """RoPE on float64 ``x[..., tokens, heads, 128]`` at positions ``pos``.
 
     ``pos`` has one entry per token (axis -3 of ``x``).
     """
+    if pairing == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+    elif pairing == "half":
+        a, b = x[..., :N_BLOCKS], x[..., N_BLOCKS:]
+    else:
+        raise ValueError("pairing must be 'half' or 'interleaved'")
     j = np.arange(N_BLOCKS, dtype=np.float64)
     omega = theta ** (-2.0 * j / HEAD_DIM)
     ang = pos.astype(np.float64)[:, None] * omega[None, :]          # [T, 64]
     c = np.cos(ang)[:, None, :]
     s = np.sin(ang)[:, None, :]
-    a = x[..., :N_BLOCKS]
-    b = x[..., N_BLOCKS:]
+    ra, rb = a * c - b * s, a * s + b * c
     out = np.empty_like(x)
-    out[..., :N_BLOCKS] = a * c - b * s
-    out[..., N_BLOCKS:] = a * s + b * c
+    if pairing == "interleaved":
+        out[..., 0::2], out[..., 1::2] = ra, rb
+    else:
+        out[..., :N_BLOCKS], out[..., N_BLOCKS:] = ra, rb
     return out
 
 
@@ -144,7 +167,7 @@ def _token_tensor(cfg, stream, seq, start, count, chunk, rope):
         rng = _rng(cfg, stream, seq * 4096 + c)
         x = _draw_blocks(rng, hi - lo, scales)
         if rope:
-            x = rope_f64(x, np.arange(lo, hi), cfg.theta)
+            x = rope_f64(to_pairing(x, cfg.pairing), np.arange(lo, hi), cfg.theta, cfg.pairing)
         a, b = max(lo, start), min(hi, start + count)
         out[a - start:b - start] = x[a - lo:b - lo].astype(np.float16)
     return out
@@ -156,8 +179,8 @@ def query(cfg: Config, seq: int = 0, pos: int | None = None) -> np.ndarray:
         pos = cfg.seq_len
     rng = _rng(cfg, _S_Q, seq)
     sc = np.repeat(block_scales(cfg), cfg.group, axis=0)             # [Hq, 64]
-    x = _draw_blocks(rng, 1, sc)
-    return rope_f64(x, np.array([pos]), cfg.theta)[0].astype(np.float16)
+    x = to_pairing(_draw_blocks(rng, 1, sc), cfg.pairing)
+    return rope_f64(x, np.array([pos]), cfg.theta, cfg.pairing)[0].astype(np.float16)
 
 
 def queries(cfg: Config, seq: int = 0, start: int = 0, count: int = 1) -> np.ndarray:
@@ -165,8 +188,8 @@ def queries(cfg: Config, seq: int = 0, start: int = 0, count: int = 1) -> np.nda
     draw per position (drawn like the keys of their KV head), for windowed logit diagnostics."""
     rng = _rng(cfg, _S_QWIN, seq)
     sc = np.repeat(block_scales(cfg), cfg.group, axis=0)             # [Hq, 64]
-    x = _draw_blocks(rng, count, sc)
-    return rope_f64(x, np.arange(start, start + count), cfg.theta).astype(np.float16)
+    x = to_pairing(_draw_blocks(rng, count, sc), cfg.pairing)
+    return rope_f64(x, np.arange(start, start + count), cfg.theta, cfg.pairing).astype(np.float16)
 
 
 def calibration(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
@@ -178,8 +201,8 @@ def calibration(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
     sk = block_scales(cfg)
     sq = np.repeat(sk, cfg.group, axis=0)
     pos = np.arange(n)
-    q = rope_f64(_draw_blocks(_rng(cfg, _S_QCAL), n, sq), pos, cfg.theta)
-    k = rope_f64(_draw_blocks(_rng(cfg, _S_KCAL), n, sk), pos, cfg.theta)
+    q = rope_f64(to_pairing(_draw_blocks(_rng(cfg, _S_QCAL), n, sq), cfg.pairing), pos, cfg.theta, cfg.pairing)
+    k = rope_f64(to_pairing(_draw_blocks(_rng(cfg, _S_KCAL), n, sk), cfg.pairing), pos, cfg.theta, cfg.pairing)
     return q.astype(np.float16), k.astype(np.float16)
 
 
@@ -198,5 +221,5 @@ def small(cfg_id: int, seq_len: int | None = None, batch: int | None = None,
     return dataclasses.replace(c, **rep)
 
 
-__all__ = ["Config", "CONFIGS", "HEAD_DIM", "N_BLOCKS", "block_scales", "rope_f64", "keys",
+__all__ = ["Config", "CONFIGS", "HEAD_DIM", "N_BLOCKS", "block_scales", "rope_f64", "to_pairing", "keys",
            "values", "query", "queries", "calibration", "small"]

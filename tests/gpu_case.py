@@ -31,8 +31,8 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(a).to(dev())
 
 
-def ref_bits(q_cal, k_cal, n_kv, avg):
-    e = oracle.energy(q_cal, k_cal, n_kv)
+def ref_bits(q_cal, k_cal, n_kv, avg, pairing="half"):
+    e = oracle.energy(q_cal, k_cal, n_kv, pairing)
     dist = oracle.distortion_table()
     return e, np.stack([oracle.greedy_allocate(e[h], avg, dist) for h in range(n_kv)])
 
@@ -40,10 +40,11 @@ def ref_bits(q_cal, k_cal, n_kv, avg):
 class OracleHead:
     """Oracle encode of one (sequence, KV head) over tokens [0, t)."""
 
-    def __init__(self, k16, v16, bits_row, v_bits, seed, layer, kvh):
+    def __init__(self, k16, v16, bits_row, v_bits, seed, layer, kvh, pairing="half"):
         self.bits_row = bits_row
         self.v_bits = v_bits
-        self.kc, self.kn = oracle.encode_k(k16, bits_row, seed, layer, kvh)
+        self.pairing = pairing
+        self.kc, self.kn = oracle.encode_k(k16, bits_row, seed, layer, kvh, pairing=pairing)
         self.vc, self.vn = oracle.encode_v(v16, v_bits, seed, layer, kvh)
         self.seed, self.layer, self.kvh = seed, layer, kvh
 
@@ -53,7 +54,8 @@ class OracleHead:
         return karr, knrm, varr, vnrm
 
     def k_hat(self):
-        return oracle.dequant_k(self.kc, self.kn, self.bits_row, self.seed, self.layer, self.kvh)
+        return oracle.dequant_k(self.kc, self.kn, self.bits_row, self.seed, self.layer, self.kvh,
+                                pairing=self.pairing)
 
     def v_hat(self):
         return oracle.dequant_v(self.vc, self.vn, self.v_bits, self.seed, self.layer, self.kvh)

@@ -28,10 +28,10 @@ def bg():
     return m
 
 
-def _energy_alloc(bg, q_cal, k_cal, n_kv, avg):
+def _energy_alloc(bg, q_cal, k_cal, n_kv, avg, pairing="half"):
     import torch
     e = torch.empty((n_kv, 64), dtype=torch.float64, device="cuda")
-    bg.energy(to_dev(q_cal), to_dev(k_cal), n_kv, e)
+    bg.energy(to_dev(q_cal), to_dev(k_cal), n_kv, e, pairing=pairing)
     bits = torch.empty((n_kv, 64), dtype=torch.int8, device="cuda")
     bg.allocate(e, avg, bits)
     torch.cuda.synchronize()
@@ -48,6 +48,21 @@ def test_energy_and_allocation_bitexact(bg, cid):
     assert np.array_equal(e_gpu, e_ref)
     assert np.array_equal(b_gpu, b_ref)
     assert np.all(b_gpu.sum(1) == 64 * cfg.k_bits)
+
+
+@pytest.mark.parametrize("cid", [1, 3])
+def test_energy_and_allocation_bitexact_interleaved(bg, cid):
+    cfg = synth.small(cid, pairing="interleaved")
+    log("config %d interleaved: calibration %d tokens" % (cid, cfg.n_cal))
+    q_cal, k_cal = synth.calibration(cfg)
+    e_gpu, b_gpu = _energy_alloc(bg, q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits, "interleaved")
+    e_ref, b_ref = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits, "interleaved")
+    assert np.array_equal(e_gpu, e_ref)
+    assert np.array_equal(b_gpu, b_ref)
+    # the interleaved twin of a half-split config sees the same blocks
+    qh, kh = synth.calibration(synth.CONFIGS[cid])
+    e_half, _ = _energy_alloc(bg, qh, kh, cfg.n_kv_heads, cfg.k_bits)
+    assert np.array_equal(e_gpu, e_half)
 
 
 def test_allocation_budgets_and_uniform(bg):
@@ -75,8 +90,8 @@ def _encode_case(bg, cfg, seq_len, batch=1, capacity=None, bits=None, chunks=Non
     capacity = capacity or seq_len
     if bits is None:
         q_cal, k_cal = synth.calibration(cfg)
-        _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
-    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed, layer=0)
+        _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits, cfg.pairing)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed, layer=0, pairing=cfg.pairing)
     cache = bg.Cache(plan, batch, capacity, device="cuda")
     ks = np.stack([synth.keys(cfg, seq=s, count=seq_len) for s in range(batch)])
     vs = np.stack([synth.values(cfg, seq=s, count=seq_len) for s in range(batch)])
@@ -87,7 +102,7 @@ def _encode_case(bg, cfg, seq_len, batch=1, capacity=None, bits=None, chunks=Non
     heads = {}
     for s in range(batch):
         for h in range(cfg.n_kv_heads):
-            ref = OracleHead(ks[s, :, h], vs[s, :, h], bits[h], cfg.v_bits, cfg.seed, 0, h)
+            ref = OracleHead(ks[s, :, h], vs[s, :, h], bits[h], cfg.v_bits, cfg.seed, 0, h, cfg.pairing)
             got = gpu_arrays(cache, s, h)
             exp = ref.packed(cache.tiles)
             for name, g, e in zip(("k_codes", "k_norms", "v_codes", "v_norms"), got, exp):
@@ -177,6 +192,14 @@ def _decode_check(bg, cfg, seq_len, batch=1, seq_lens=None, capacity=None):
 def test_decode_matches_oracle(bg, cid, seq_len):
     log("decode config %d T=%d" % (cid, seq_len))
     _decode_check(bg, synth.small(cid, seq_len=seq_len), seq_len)
+
+
+@pytest.mark.parametrize("cid,seq_len", [(1, 1000), (3, 3000), (4, 777)])
+def test_decode_interleaved_pairing(bg, cid, seq_len):
+    """Interleaved RoPE pairing end to end: the plan's key groups take coordinates (2j, 2j+1)."""
+    log("decode config %d interleaved T=%d" % (cid, seq_len))
+    _decode_check(bg, synth.small(cid, seq_len=seq_len, batch=2 if cid == 4 else None,
+                                  pairing="interleaved"), seq_len, batch=2 if cid == 4 else 1)
 
 
 def test_decode_ragged_batch_and_empty(bg):

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(bg):
 
 
 def test_abi_version(bg):
-    assert bg.abi_version() == 1
+    assert bg.abi_version() == 2
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
@@ -108,11 +108,23 @@ def test_plan_validation(bg):
     assert "k_bits" in bg.load().bgtq_last_error().decode() or True
 
 
+def test_plan_rejects_unknown_pairing(bg):
+    bits = np.ascontiguousarray(_bits(3, 2).astype(np.int8))
+    desc = bg._PlanDesc(3, 6, 128, 2, 2, bits.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), 0, 0, 2)
+    h = ctypes.c_void_p()
+    assert bg.load().bgtq_plan_create(ctypes.byref(desc), ctypes.byref(h)) == bg.EINVAL
+    assert "rope_pairing" in bg.load().bgtq_last_error().decode()
+    with pytest.raises(ValueError):
+        bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6, pairing="other")
+    bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6, pairing="interleaved").close()
+
+
 def test_device_calls_reject_bad_arguments_before_launch(bg):
     lib = bg.load()
-    assert lib.bgtq_energy(None, None, 10, 8, 2, 128, None, None) == bg.EINVAL
-    assert lib.bgtq_energy(1, 1, 10, 8, 3, 128, 1, None) == bg.EINVAL      # 8 % 3
-    assert lib.bgtq_energy(1, 1, 10, 8, 2, 64, 1, None) == bg.EINVAL       # head_dim
+    assert lib.bgtq_energy(None, None, 10, 8, 2, 128, 0, None, None) == bg.EINVAL
+    assert lib.bgtq_energy(1, 1, 10, 8, 3, 128, 0, 1, None) == bg.EINVAL      # 8 % 3
+    assert lib.bgtq_energy(1, 1, 10, 8, 2, 64, 0, 1, None) == bg.EINVAL       # head_dim
+    assert lib.bgtq_energy(1, 1, 10, 8, 2, 128, 2, 1, None) == bg.EINVAL      # pairing
     assert lib.bgtq_allocate(1, 2, 64, 5, 1, None) == bg.EBUDGET
     assert lib.bgtq_allocate(1, 2, 32, 2, 1, None) == bg.EINVAL
     plan = bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6)

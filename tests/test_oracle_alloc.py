@@ -131,3 +131,45 @@ def test_energy_is_rope_invariant():
     e_post = oracle.energy(synth.rope_f64(q, pos, 1e4).astype(np.float16),
                            synth.rope_f64(k, pos, 1e4).astype(np.float16), 1)
     np.testing.assert_allclose(e_post, e_pre, rtol=2e-3)
+
+
+def test_energy_interleaved_pairing_on_constructed_inputs():
+    """Interleaved pairing: block j is coordinates (2j, 2j+1); mass at 10 and 11 lands in block 5."""
+    n = 2
+    q = np.zeros((n, 1, 128), np.float16)
+    k = np.zeros((n, 1, 128), np.float16)
+    q[:, 0, 10] = 1.0
+    q[:, 0, 11] = 2.0
+    k[:, 0, 11] = 3.0
+    k[:, 0, 69] = 7.0          # block 34 (coordinates 68, 69); no query mass there
+    e = oracle.energy(q, k, 1, pairing="interleaved")
+    assert e[0, 5] == (2 * 1 + 2 * 4) / 2 * (2 * 9) / 2
+    e[0, 5] = 0.0
+    assert np.all(e == 0.0)
+    # the same inputs read half-split put coordinate 10 in block 10 and 69 in block 5
+    eh = oracle.energy(q, k, 1)
+    assert eh[0, 10] == 0.0 and eh[0, 5] == 0.0 and eh[0, 11] == 4.0 * 9.0
+
+
+def test_energy_interleaved_matches_fraction_arithmetic():
+    cfg = synth.small(2, n_cal=16, pairing="interleaved")
+    q, k = synth.calibration(cfg)
+    e = oracle.energy(q, k, cfg.n_kv_heads, pairing="interleaved")
+    g = cfg.group
+    for h, j in [(0, 0), (1, 17), (0, 63)]:
+        sq = sum(Fraction(float(q[t, hh, c])) ** 2 for t in range(16)
+                 for hh in range(h * g, (h + 1) * g) for c in (2 * j, 2 * j + 1))
+        sk = sum(Fraction(float(k[t, h, c])) ** 2 for t in range(16) for c in (2 * j, 2 * j + 1))
+        assert e[h, j] == (float(sq) / float(16 * g)) * (float(sk) / 16.0)
+
+
+def test_interleaved_config_is_a_coordinate_move_of_its_half_split_twin():
+    """Both pairings see the same blocks: energies of the twin configs are identical."""
+    half = synth.small(2, n_cal=64)
+    inter = synth.small(2, n_cal=64, pairing="interleaved")
+    qh, kh = synth.calibration(half)
+    qi, ki = synth.calibration(inter)
+    np.testing.assert_array_equal(qi[..., 0::2], qh[..., :64])
+    np.testing.assert_array_equal(qi[..., 1::2], qh[..., 64:])
+    np.testing.assert_array_equal(ki[..., 0::2], kh[..., :64])
+    np.testing.assert_array_equal(oracle.energy(qi, ki, 2, pairing="interleaved"), oracle.energy(qh, kh, 2))

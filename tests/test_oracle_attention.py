@@ -28,6 +28,26 @@ def test_rope_block_decomposition_identity():
         assert abs(blocks.sum() - full) <= tol * scale
 
 
+def test_interleaved_rope_is_complex_multiplication():
+    """Interleaved RoPE multiplies z_j = x[2j] + i x[2j+1] by exp(i p omega_j); the sum of the
+    interleaved block logits equals the dot product of the rotated vectors."""
+    rng = np.random.default_rng(2)
+    for trial in range(40):
+        x = rng.normal(0, 2, 128)
+        p = float(rng.integers(0, 5000))
+        theta = float(rng.choice([1e4, 5e5]))
+        z = (x[0::2] + 1j * x[1::2]) * np.exp(1j * p * theta ** (-np.arange(64) / 64.0))
+        got = oracle.rope_blocks(x, p, theta, "interleaved")
+        np.testing.assert_allclose(got[0::2], z.real, atol=1e-11)
+        np.testing.assert_allclose(got[1::2], z.imag, atol=1e-11)
+        q, k = rng.normal(0, 3, 128), rng.normal(0, 3, 128)
+        m, n = rng.integers(0, 4096, 2)
+        blocks = oracle.block_logits(q, k, float(m), float(n), theta, "interleaved")
+        full = oracle.rope_blocks(q, float(m), theta, "interleaved") @ oracle.rope_blocks(k, float(n), theta,
+                                                                                          "interleaved")
+        assert abs(blocks.sum() - full) <= 1e-12 * max(1.0, np.linalg.norm(q) * np.linalg.norm(k))
+
+
 def test_generator_rope_matches_oracle_rope():
     rng = np.random.default_rng(1)
     x = rng.normal(0, 1, (5, 1, 128))
@@ -35,6 +55,10 @@ def test_generator_rope_matches_oracle_rope():
     got = synth.rope_f64(x, pos, 5e5)
     for i, p in enumerate(pos):
         np.testing.assert_allclose(got[i, 0], oracle.rope_blocks(x[i, 0], float(p), 5e5), atol=1e-12)
+    got = synth.rope_f64(x, pos, 5e5, "interleaved")
+    for i, p in enumerate(pos):
+        np.testing.assert_allclose(got[i, 0], oracle.rope_blocks(x[i, 0], float(p), 5e5, "interleaved"),
+                                   atol=1e-12)
 
 
 def test_single_token_returns_its_value():

@@ -35,6 +35,39 @@ def test_groups_order_and_pairing():
     np.testing.assert_array_equal(g[2][1], [0, 64])
 
 
+def test_groups_interleaved_pairing():
+    bits = np.zeros(64, np.int8)
+    bits[[3, 10]] = 4
+    bits[[0]] = 1
+    bits[[5, 6, 7]] = 2
+    g = oracle.groups_for(bits, "interleaved")
+    assert [w for w, _ in g] == [4, 2, 1]
+    np.testing.assert_array_equal(g[0][1], [6, 7, 20, 21])
+    np.testing.assert_array_equal(g[1][1], [10, 11, 12, 13, 14, 15])
+    np.testing.assert_array_equal(g[2][1], [0, 1])
+    with pytest.raises(ValueError):
+        oracle.groups_for(bits, "other")
+
+
+def test_interleaved_encode_equals_half_split_on_moved_coordinates():
+    """A key with its (j, j+64) pairs moved to (2j, 2j+1) encodes to the same codes and norms
+    under the interleaved pairing, and decodes to the moved reconstruction."""
+    rng = np.random.default_rng(3)
+    bits = np.zeros(64, np.int8)
+    bits[rng.permutation(64)[:48]] = rng.integers(1, 5, 48)
+    x = (rng.normal(0, 1, (50, 128)) * np.exp(rng.normal(0, 1, 128))).astype(np.float16)
+    xi = np.empty_like(x)
+    xi[:, 0::2], xi[:, 1::2] = x[:, :64], x[:, 64:]
+    c_h, n_h = oracle.encode_k(x, bits, 7, 2, 1)
+    c_i, n_i = oracle.encode_k(xi, bits, 7, 2, 1, pairing="interleaved")
+    np.testing.assert_array_equal(c_i, c_h)
+    np.testing.assert_array_equal(n_i, n_h)
+    r_h = oracle.dequant_k(c_h, n_h, bits, 7, 2, 1)
+    r_i = oracle.dequant_k(c_i, n_i, bits, 7, 2, 1, pairing="interleaved")
+    np.testing.assert_array_equal(r_i[:, 0::2], r_h[:, :64])
+    np.testing.assert_array_equal(r_i[:, 1::2], r_h[:, 64:])
+
+
 def test_hand_worked_two_dim_group():
     """x = (3, 4), identity rotation, 2 bits: n = 5, z = sqrt(2) * (0.6, 0.8) -> codes (2, 3)."""
     x = np.array([[3.0, 4.0]], np.float16)
