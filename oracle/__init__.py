@@ -30,7 +30,7 @@ from .alloc import energy, greedy_allocate, exact_sum_squares_f16
 from .quant import (groups_for, encode_groups, encode_k, encode_v, f16_bits, f16_value,
                     dequant_k, dequant_v)
 from .layout import (k_words_per_token, pack_k, unpack_k, pack_v, unpack_v, k_bit_offsets)
-from .attention import decode_attention, softmax_attention
+from .attention import decode_attention, softmax_attention, decode_attention_buffered, buffered_positions
 from .rope import rope_blocks, block_logits, block_pairs
 from .diagnostics import logit_mae
 
@@ -41,6 +41,6 @@ __all__ = [
     "groups_for", "encode_groups", "encode_k", "encode_v", "f16_bits", "f16_value",
     "dequant_k", "dequant_v",
     "k_words_per_token", "pack_k", "unpack_k", "pack_v", "unpack_v", "k_bit_offsets",
-    "decode_attention", "softmax_attention",
+    "decode_attention", "softmax_attention", "decode_attention_buffered", "buffered_positions",
     "rope_blocks", "block_logits", "block_pairs", "logit_mae",
 ]

@@ -47,3 +47,27 @@ def decode_attention(q16: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, seq_
         kv = h // g
         out[h] = softmax_attention(q[h], k_hat[:seq_len, kv], v_hat[:seq_len, kv], scale)
     return out
+
+
+def buffered_positions(seq_len: int, n_sink: int, n_recent: int) -> np.ndarray:
+    """Boolean mask [seq_len]: True where a token is kept in fp16 (the first ``n_sink`` tokens and the
+    last ``n_recent``), False where the packed cache serves it."""
+    t = np.arange(seq_len)
+    return (t < n_sink) | (t >= seq_len - n_recent)
+
+
+def decode_attention_buffered(q16: np.ndarray, k16: np.ndarray, v16: np.ndarray, k_hat: np.ndarray,
+                              v_hat: np.ndarray, seq_len: int, n_sink: int, n_recent: int,
+                              scale: float | None = None) -> np.ndarray:
+    """Decode attention with an fp16 sink and recent window (the Block-GTQ README's "withbuffer"
+    setting of its AIME runs: 4 attention-sink tokens and a 128-token recent window in fp16).
+
+    Reading: token t of a sequence of length T attends with its original fp16 key and value
+    (taken exactly as float64) when t < n_sink or t >= T - n_recent, and with the dequantised
+    k_hat_t, v_hat_t otherwise; the softmax and the weighted sum are those of decode_attention.
+    q16 [Hq, d]; k16, v16 fp16 and k_hat, v_hat float64, all [T', Hkv, d] with T' >= seq_len.
+    """
+    keep = buffered_positions(seq_len, n_sink, n_recent)[:, None, None]
+    k = np.where(keep, np.asarray(k16[:seq_len], np.float16).astype(np.float64), k_hat[:seq_len])
+    v = np.where(keep, np.asarray(v16[:seq_len], np.float16).astype(np.float64), v_hat[:seq_len])
+    return decode_attention(q16, k, v, seq_len, scale)

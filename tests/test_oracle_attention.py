@@ -99,3 +99,59 @@ def test_decode_attention_head_mapping_and_empty():
     np.testing.assert_allclose(o[3], oracle.softmax_attention(q[3], kh[:, 1], vh[:, 1], 1 / math.sqrt(128)))
     np.testing.assert_allclose(o[1], oracle.softmax_attention(q[1], kh[:, 0], vh[:, 0], 1 / math.sqrt(128)))
     assert np.all(oracle.decode_attention(q16, kh, vh, 0) == 0.0)
+
+
+def test_buffered_positions_mask():
+    np.testing.assert_array_equal(oracle.buffered_positions(10, 2, 3),
+                                  [1, 1, 0, 0, 0, 0, 0, 1, 1, 1])
+    assert oracle.buffered_positions(5, 4, 128).all()          # window covers everything
+    assert not oracle.buffered_positions(6, 0, 0).any()
+    np.testing.assert_array_equal(oracle.buffered_positions(6, 0, 2), [0, 0, 0, 0, 1, 1])
+    assert oracle.buffered_positions(0, 4, 128).size == 0
+
+
+def test_buffered_attention_brute_force():
+    """Tiny case by explicit loops: fp16 key/value for sink and window tokens, dequantised otherwise."""
+    rng = np.random.default_rng(11)
+    t_len, hkv, g, d = 10, 2, 2, 128
+    k16 = rng.normal(0, 1, (t_len, hkv, d)).astype(np.float16)
+    v16 = rng.normal(0, 1, (t_len, hkv, d)).astype(np.float16)
+    kh = k16.astype(np.float64) + rng.normal(0, 0.3, k16.shape)
+    vh = v16.astype(np.float64) + rng.normal(0, 0.3, v16.shape)
+    q = rng.normal(0, 1, (hkv * g, d)).astype(np.float16)
+    got = oracle.decode_attention_buffered(q, k16, v16, kh, vh, 9, 2, 3)
+    for h in range(hkv * g):
+        kv = h // g
+        w, acc = [], np.zeros(d)
+        for t in range(9):
+            exact = t < 2 or t >= 6
+            kt = [float(x) for x in k16[t, kv]] if exact else list(kh[t, kv])
+            w.append(sum(float(a) * b for a, b in zip(q[h], kt)) / math.sqrt(d))
+        mx = max(w)
+        e = [math.exp(x - mx) for x in w]
+        for t in range(9):
+            vt = v16[t, kv].astype(np.float64) if (t < 2 or t >= 6) else vh[t, kv]
+            acc += e[t] * vt
+        np.testing.assert_allclose(got[h], acc / sum(e), rtol=1e-12, atol=1e-13)
+
+
+def test_buffered_attention_special_cases():
+    rng = np.random.default_rng(12)
+    t_len, hkv, d = 40, 1, 128
+    k16 = rng.normal(0, 1, (t_len, hkv, d)).astype(np.float16)
+    v16 = rng.normal(0, 1, (t_len, hkv, d)).astype(np.float16)
+    kh = rng.normal(0, 1, k16.shape)
+    vh = rng.normal(0, 1, v16.shape)
+    q = rng.normal(0, 1, (2, d)).astype(np.float16)
+    # no buffer: the packed-cache result
+    np.testing.assert_array_equal(oracle.decode_attention_buffered(q, k16, v16, kh, vh, 40, 0, 0),
+                                  oracle.decode_attention(q, kh, vh, 40))
+    # buffer covering the whole sequence: plain fp16 attention
+    np.testing.assert_array_equal(oracle.decode_attention_buffered(q, k16, v16, kh, vh, 30, 4, 128),
+                                  oracle.decode_attention(q, k16.astype(np.float64), v16.astype(np.float64), 30))
+    # a lossless cache makes the buffer irrelevant
+    np.testing.assert_allclose(
+        oracle.decode_attention_buffered(q, k16, v16, k16.astype(np.float64), v16.astype(np.float64), 40, 4, 8),
+        oracle.decode_attention(q, k16.astype(np.float64), v16.astype(np.float64), 40), rtol=0, atol=0)
+    # empty sequence
+    assert np.all(oracle.decode_attention_buffered(q, k16, v16, kh, vh, 0, 4, 128) == 0.0)
