@@ -311,6 +311,21 @@ def main() -> int:
         "host enqueue %.4f ms/call" % (step_ms, value, serve_ms, kern_ms, achieved, launches,
                                        host_enqueue_s * 1e3 / n_steps))
 
+    # ---- the fp16 sink + recent-window variant (4 + 128 tokens in fp16, the rest packed)
+    buf = bg.Buffer(b, hkv, 4, 128, device=dev)
+    buf.append(kd, vd, 0)
+    buf.append(k_new, v_new, t)
+
+    def attn_buf(i):
+        kc_, kn_, vc_, vn_ = reps[i % n_rep]
+        plan.decode_attn_buffered(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, buf, out, ws)
+
+    for i in range(max(5, args.warmup // 5)):
+        attn_buf(i)
+    buf_ms = sum(timed_round(attn_buf, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
+    log("buffered decode (4 sink + 128 recent fp16 tokens) %.4f ms" % buf_ms)
+    del buf
+
     # ---- fp16 baseline: the same keys and values uncompressed, the same split-sequence decode
     # (bgtq_fp16_decode_attn) over the same t + 1 tokens, replicated against the Infinity Cache
     del reps
@@ -365,6 +380,9 @@ def main() -> int:
                                  "decode attention over T + 1 tokens", "ms": round(serve_ms, 5),
                          "GBps": round(packed / (serve_ms / 1e3) / 1e9, 2)},
         "packed_bytes_per_step": packed,
+        "buffered_decode": {"what": "bgtq_decode_attn_buffered: 4 sink and 128 recent tokens from fp16 buffers, "
+                                    "the rest from the packed cache, over the same t + 1 tokens",
+                            "ms": round(buf_ms, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": STREAM_KERNEL, "kernel_ms": round(kern_ms, 5)},

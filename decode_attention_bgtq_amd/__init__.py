@@ -26,7 +26,8 @@ EXPORTED = [
     "bgtq_plan_destroy", "bgtq_plan_sizes", "bgtq_plan_upload", "bgtq_encode_k", "bgtq_encode_v",
     "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
-    "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn",
+    "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
+    "bgtq_buffer_append",
 ]
 
 
@@ -87,6 +88,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_profile_read": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
         "bgtq_fp16_decode_workspace_size": (I32, [I32, I32, I32, I64, ctypes.POINTER(SZ)]),
         "bgtq_fp16_decode_attn": (I32, [P, P, P, I32, I32, I32, I64, P, I64, ctypes.c_float, P, P, SZ, P]),
+        "bgtq_decode_attn_buffered": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float,
+                                            P, P, I32, P, P, I32, P, P, SZ, P]),
+        "bgtq_buffer_append": (I32, [P, P, I32, I64, I64, I32, P, P, I32, P, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -244,6 +248,19 @@ class Plan:
                                        max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
 
+    def decode_attn_buffered(self, consts, q, k_codes, k_norms, v_codes, v_norms, capacity: int, seq_lens,
+                             max_seq_len: int, buf: "Buffer", out, workspace, softmax_scale: float | None = None,
+                             stream=None) -> None:
+        """decode_attn with the fp16 sink and recent-window tokens of ``buf`` taken from fp16."""
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_attn_buffered(
+            self._h, _ptr(consts), _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), capacity,
+            _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale, _ptr(buf.k_sink), _ptr(buf.v_sink),
+            buf.n_sink, _ptr(buf.k_recent), _ptr(buf.v_recent), buf.n_recent, _ptr(out), _ptr(workspace),
+            ws_bytes, _stream(stream)))
+
     def decode_step(self, consts, q, k_new, v_new, pos, max_seq_len: int, k_codes, k_norms, v_codes, v_norms,
                     capacity: int, out, workspace, softmax_scale: float | None = None, stream=None) -> None:
         """Append k_new / v_new at token pos[b] of each sequence, then attend q over pos[b] + 1 tokens."""
@@ -272,6 +289,27 @@ def fp16_decode_attn(q, k, v, seq_lens, max_seq_len: int, out, workspace, softma
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().bgtq_fp16_decode_attn(_ptr(q), _ptr(k), _ptr(v), b, hq, hkv, cap, _ptr(seq_lens), max_seq_len,
                                         softmax_scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+class Buffer:
+    """fp16 sink and recent-window buffers of one layer (caller-owned torch tensors):
+    k_sink / v_sink [batch][Hkv][n_sink][128], k_recent / v_recent [batch][Hkv][n_recent][128]
+    (token t in row t % n_recent)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, n_sink: int = 4, n_recent: int = 128, device="cuda"):
+        import torch
+        self.batch, self.n_kv_heads, self.n_sink, self.n_recent = batch, n_kv_heads, n_sink, n_recent
+        mk = lambda n: (torch.zeros((batch, n_kv_heads, n, HEAD_DIM), dtype=torch.int16, device=device)
+                        if n else None)
+        self.k_sink, self.v_sink = mk(n_sink), mk(n_sink)
+        self.k_recent, self.v_recent = mk(n_recent), mk(n_recent)
+
+    def append(self, k, v, t0: int, stream=None) -> None:
+        """Copy new fp16 tokens k, v [batch][n_new][Hkv][128] (positions t0 ..) into the buffers."""
+        b, n_new, hkv, _ = k.shape
+        _check(load().bgtq_buffer_append(_ptr(k), _ptr(v), b, n_new, t0, hkv, _ptr(self.k_sink),
+                                         _ptr(self.v_sink), self.n_sink, _ptr(self.k_recent),
+                                         _ptr(self.v_recent), self.n_recent, _stream(stream)))
 
 
 def profile_enable(on: bool = True) -> None:

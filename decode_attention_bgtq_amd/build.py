@@ -19,7 +19,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Wno-pass-failed"]
-SOURCES = ["abi.cpp", "calib.hip", "decode.hip", "encode.hip", "fp16.hip", "plan.cpp", "step.hip"]
+SOURCES = ["abi.cpp", "buffer.hip", "calib.hip", "decode.hip", "encode.hip", "fp16.hip", "plan.cpp", "step.hip"]
 
 
 def _hipcc() -> str:

@@ -188,7 +188,8 @@ struct StreamState {
   uint32_t gbit;      // first stream bit of the width-3, 2, 1 groups (10 bits each)
   uint32_t ptw;       // LDS byte offset of this wave's weight rows
   int wk, n4w;
-  int64_t seq;
+  int lo;       // first token of the packed range
+  int64_t seq;  // end of the packed range (may be below lo: an empty range)
 };
 
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
@@ -494,7 +495,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
     BGTQ_KG(0, r.nr.x >> 16) BGTQ_KG(1, r.nr.y & 0xFFFFu) BGTQ_KG(2, r.nr.y >> 16)
 #undef BGTQ_KG
   }
-  const bool valid = (int64_t)tile * kTile + lane < st.seq;
+  const int64_t tok = (int64_t)tile * kTile + lane;
+  const bool valid = tok < st.seq && tok >= st.lo;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
   // ---- online softmax (log2 domain), rescaled lazily: the running maximum
@@ -561,6 +563,7 @@ struct DecodeArgs {
   int64_t tiles_cap, max_seq_len, off_kvh, off_dtab, off_vlut, off_zero;
   int hkv, hq, wk, tiles_base, tiles_extra, n_splits;  // split s: tiles_base + (s < tiles_extra) tiles
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
+  int n_sink, n_recent;  // tokens [0, n_sink) and [T - n_recent, T) are served from fp16 buffers, not here
   float kscale;  // softmax scale in log2 units
 };
 
@@ -626,7 +629,8 @@ void decode_kernel(const DecodeArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   // the queries of this (sequence, KV head), rotated and scaled (ends with a barrier)
   prep_build<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
-  st.seq = seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw);
+  st.seq = (seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw)) - a.n_recent;
+  st.lo = a.n_sink;
   st.wk = a.wk;
   st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
   st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
@@ -646,7 +650,10 @@ void decode_kernel(const DecodeArgs a) {
   float mrun[G], lsum[G];
   f4v acc0[VQuads<G>::v], acc1[VQuads<G>::v];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mrun[h] = -INFINITY, lsum[h] = 0.f;
+  // The running maximum starts finite, far below any logit, so that a tile
+  // without a valid token (all logits -inf; possible below the packed range's
+  // first token) gives p = 2^(-inf) = 0 rather than 2^(-inf + inf).
+  for (int h = 0; h < G; ++h) mrun[h] = -0x1p100f, lsum[h] = 0.f;
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) acc0[g] = (f4v){0.f, 0.f, 0.f, 0.f}, acc1[g] = acc0[g];
   // One copy of the tile body (the instruction cache holds the loop): the
@@ -841,6 +848,8 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.tiles_extra = lay.tiles_extra;
   a.n_splits = lay.n_splits;
   a.seq_add = c.seq_add;
+  a.n_sink = c.n_sink;
+  a.n_recent = c.n_recent;
   a.kscale = kscale_of(c.softmax_scale);
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
   // With profiling on, the events are bound to the launch itself, so their elapsed time is the
@@ -856,9 +865,17 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
     pr.pending.emplace_back(e0, e1);
   }
   if (s != BGTQ_OK) return s;
-  merge_kernel<true><<<dim3(p.desc.n_q_heads, c.batch), kMergeThreads, 0, st>>>(
-      (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v), (const float *)ws, lay.n_splits, G,
-      p.desc.n_q_heads, c.out);
+  const float *pvt = (const float *)((const uint8_t *)c.dev_consts + p.hdr.off_rot32_v);
+  const dim3 mgrid(p.desc.n_q_heads, c.batch);
+  if (c.n_sink || c.n_recent) {
+    const MergeBuf bf{c.q,        c.k_sink,      c.v_sink,    c.k_recent, c.v_recent, c.seq_lens,
+                      c.max_seq_len, c.n_sink, c.n_recent, p.desc.n_kv_heads, c.seq_add, a.kscale};
+    merge_kernel<true, true><<<mgrid, kMergeThreads, 0, st>>>(pvt, (const float *)ws, lay.n_splits, G,
+                                                               p.desc.n_q_heads, c.out, bf);
+  } else {
+    merge_kernel<true><<<mgrid, kMergeThreads, 0, st>>>(pvt, (const float *)ws, lay.n_splits, G, p.desc.n_q_heads,
+                                                        c.out, MergeBuf{});
+  }
   return launch_status("decode (merge)");
 }
 
@@ -897,6 +914,36 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
   if (v != BGTQ_OK) return v;
   DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
                softmax_scale, out, workspace, stream};
+  return decode_launch(plan->p, c);
+}
+
+bgtq_status bgtq_decode_attn_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                      const uint32_t *k_codes, const uint16_t *k_norms, const uint32_t *v_codes,
+                                      const uint16_t *v_norms, int64_t capacity, const int32_t *seq_lens,
+                                      int32_t batch, int64_t max_seq_len, float softmax_scale,
+                                      const uint16_t *k_sink, const uint16_t *v_sink, int32_t n_sink,
+                                      const uint16_t *k_recent, const uint16_t *v_recent, int32_t n_recent,
+                                      uint16_t *out, void *workspace, size_t ws_bytes, bgtq_stream stream) {
+  const char *nm = "bgtq_decode_attn_buffered";
+  if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace ||
+      (!k_codes && plan->p.hdr.wk > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  if (n_sink < 0 || n_sink > kMaxSink || n_recent < 0 || n_recent > kMaxRecent)
+    return fail(BGTQ_EINVAL, std::string(nm) + ": n_sink must be 0..64 and n_recent 0..65536");
+  if ((n_sink && (!k_sink || !v_sink)) || (n_recent && (!k_recent || !v_recent)))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null buffer with a non-zero count");
+  if (((uintptr_t)k_sink | (uintptr_t)v_sink | (uintptr_t)k_recent | (uintptr_t)v_recent | (uintptr_t)q) & 15)
+    return fail(BGTQ_EINVAL, std::string(nm) + ": q and the buffers must be 16-byte aligned");
+  const bgtq_status v = decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
+  if (v != BGTQ_OK) return v;
+  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
+               softmax_scale, out, workspace, stream};
+  c.k_sink = k_sink;
+  c.v_sink = v_sink;
+  c.k_recent = k_recent;
+  c.v_recent = v_recent;
+  c.n_sink = n_sink;
+  c.n_recent = n_recent;
   return decode_launch(plan->p, c);
 }
 

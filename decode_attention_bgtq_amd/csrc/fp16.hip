@@ -259,7 +259,8 @@ bgtq_status bgtq_fp16_decode_attn(const uint16_t *q, const uint16_t *k, const ui
   const bgtq_status s = launch_status("bgtq_fp16_decode_attn");
   if (s != BGTQ_OK) return s;
   merge_kernel<false><<<dim3(n_q_heads, batch), kMergeThreads, 0, st>>>(nullptr, (const float *)workspace,
-                                                                       lay.n_splits, G, n_q_heads, out);
+                                                                       lay.n_splits, G, n_q_heads, out,
+                                                                       MergeBuf{});
   return launch_status("bgtq_fp16_decode_attn (merge)");
 }
 

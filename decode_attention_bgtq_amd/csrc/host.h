@@ -41,6 +41,9 @@ struct DecodeCall {
   uint16_t *out;
   void *workspace;
   bgtq_stream stream;
+  // fp16 sink and recent window (counts 0: none)
+  const uint16_t *k_sink = nullptr, *v_sink = nullptr, *k_recent = nullptr, *v_recent = nullptr;
+  int n_sink = 0, n_recent = 0;
 };
 bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
                          const void *workspace, size_t ws_bytes, const char *nm);

@@ -11,6 +11,7 @@ namespace bgtq {
 
 constexpr int kPartStride = 132;  // m, l, pad, pad, acc[128]
 constexpr int kMaxSplits = 256;
+constexpr int kMaxSink = 64, kMaxRecent = 65536;  // fp16 buffer bounds (sink, recent window)
 
 // One workgroup of 512 threads (8 waves) per (query head, sequence).  Every
 // global load is issued first: each wave loads the (m, l) of every split (lane
@@ -23,16 +24,111 @@ constexpr int kMaxSplits = 256;
 // of k and a cross-lane sum.  After one barrier, out[j] = sum_k Pi_V[k][j] y[k]
 // (ROT: the packed path, c = sqrt(128) for the centroid scale; four threads per
 // j) or out[k] = y[k] (c = 1).
+//
+// With BUF (the fp16 sink and recent window), the merge also attends to the
+// buffered fp16 tokens of its head: thread t takes token rows t / 8 (+ 64 per
+// round) and the 16 coordinates 16 (t % 8) .. of the key and value; the
+// logit is the sum over the 8 threads of a row; each thread keeps a running
+// (max, sum, 16 value sums), combined over the rows of a wave by cross-lane
+// steps and over the waves in LDS.  The packed result y (normalised by its own
+// sum) and the buffer's are then mixed by their shares of the total softmax
+// mass.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeRegs = 16;  // split accumulators per lane loaded before the weights (n_splits <= 64)
 
-template <bool ROT>
+struct MergeBuf {
+  const uint16_t *q;                    // [batch][hq][128]
+  const uint16_t *k_sink, *v_sink;      // [batch][hkv][n_sink][128]
+  const uint16_t *k_recent, *v_recent;  // [batch][hkv][n_recent][128], token t in row t % n_recent
+  const int32_t *seq_lens;
+  int64_t max_seq_len;
+  int n_sink, n_recent, hkv, seq_add;
+  float kscale;  // softmax scale in log2 units
+};
+
+// Running softmax state of one thread over its buffered tokens: maximum logit
+// (log2 units), sum of 2^(l - m) and the 16 value sums.
+struct BufState {
+  float m, l, a[16];
+};
+
+__device__ __forceinline__ void buf_combine(BufState &s, float om, float ol, const float *oa) {
+  const float mn = fmaxf(s.m, om);
+  if (mn == -INFINITY) return;
+  const float f0 = __builtin_amdgcn_exp2f(s.m - mn), f1 = __builtin_amdgcn_exp2f(om - mn);
+  s.l = s.l * f0 + ol * f1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s.a[i] = s.a[i] * f0 + oa[i] * f1;
+  s.m = mn;
+}
+
+// The buffered tokens of sequence b for the query head of this workgroup:
+// sink rows [0, min(n_sink, T)), then the window tokens [max(n_sink, T - n_recent), T).
+__device__ __forceinline__ void buf_rows(const MergeBuf &bf, int b, int kvh, int tid, BufState &st,
+                                         const float *qv) {
+  const int64_t sr = (int64_t)bf.seq_lens[b] + bf.seq_add;
+  const int64_t seq = sr < 0 ? 0 : (sr > bf.max_seq_len ? bf.max_seq_len : sr);
+  const int64_t n_s = seq < bf.n_sink ? seq : bf.n_sink;
+  const int64_t r0 = seq - bf.n_recent > bf.n_sink ? seq - bf.n_recent : bf.n_sink;
+  const int64_t n_f = n_s + (seq > r0 ? seq - r0 : 0);
+  const int row = tid >> 3, part = tid & 7;
+  const size_t hb = (size_t)b * bf.hkv + kvh;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.a[i] = 0.f;
+  for (int64_t c0 = 0; c0 < n_f; c0 += kMergeThreads / 8) {
+    const int64_t f = c0 + row, fc = f < n_f ? f : n_f - 1;  // rows past the end re-read the last one
+    const uint16_t *kp, *vp;
+    if (fc < n_s) {
+      kp = bf.k_sink + (hb * bf.n_sink + fc) * kHeadDim;
+      vp = bf.v_sink + (hb * bf.n_sink + fc) * kHeadDim;
+    } else {
+      const int64_t slot = (r0 + (fc - n_s)) % bf.n_recent;
+      kp = bf.k_recent + (hb * bf.n_recent + slot) * kHeadDim;
+      vp = bf.v_recent + (hb * bf.n_recent + slot) * kHeadDim;
+    }
+    const uint4 k0 = ((const uint4 *)kp)[2 * part], k1 = ((const uint4 *)kp)[2 * part + 1];
+    const uint4 v0 = ((const uint4 *)vp)[2 * part], v1 = ((const uint4 *)vp)[2 * part + 1];
+    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s = fmaf(qv[2 * i], h2f((uint16_t)(kw[i] & 0xFFFFu)), s);
+      s = fmaf(qv[2 * i + 1], h2f((uint16_t)(kw[i] >> 16)), s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (f < n_f) {
+      float va[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) va[2 * i] = h2f((uint16_t)(vw[i] & 0xFFFFu)), va[2 * i + 1] = h2f((uint16_t)(vw[i] >> 16));
+      buf_combine(st, s, 1.f, va);  // one token: (logit, 1, its value)
+    }
+  }
+  // rows of the wave (lane bits 3..5)
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    const float om = __shfl_xor(st.m, off), ol = __shfl_xor(st.l, off);
+    float oa[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oa[i] = __shfl_xor(st.a[i], off);
+    buf_combine(st, om, ol, oa);
+  }
+}
+
+template <bool ROT, bool BUF = false>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ pvt_all,
                                                               const float *__restrict__ part, int n_splits,
-                                                              int group, int hq, uint16_t *__restrict__ out) {
+                                                              int group, int hq, uint16_t *__restrict__ out,
+                                                              const MergeBuf bf) {
   constexpr int kWaves = kMergeThreads / 64;
+  static_assert(!BUF || ROT, "the buffered merge is the packed path's");
   __shared__ float wsm[kWaves][kMaxSplits];
   __shared__ __attribute__((aligned(16))) float ys[kHeadDim];
+  __shared__ float bsm[BUF ? kWaves : 1][8][18];  // per wave and coordinate block: m, l, 16 value sums
   const int hqi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvh = hqi / group;
   const float *ph = part + ((size_t)b * hq + hqi) * (size_t)n_splits * kPartStride;
@@ -57,6 +153,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
   for (int u = 0; u < kMergeRegs; ++u) {
     const int sp = sg + 4 * u;
     av[u] = pv[(size_t)(sp < n_splits ? sp : 0) * kPartStride];
+  }
+  if constexpr (BUF) {
+    // this thread's 16 query coordinates, in log2 units
+    const uint4 *qp = (const uint4 *)(bf.q + ((size_t)b * hq + hqi) * kHeadDim) + 2 * (tid & 7);
+    const uint4 q0 = qp[0], q1 = qp[1];
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    float qv[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      qv[2 * i] = h2f((uint16_t)(qw[i] & 0xFFFFu)) * bf.kscale, qv[2 * i + 1] = h2f((uint16_t)(qw[i] >> 16)) * bf.kscale;
+    BufState bs;
+    buf_rows(bf, b, kvh, tid, bs, qv);
+    if (lane < 8) {
+      bsm[wave][lane][0] = bs.m;
+      bsm[wave][lane][1] = bs.l;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bsm[wave][lane][2 + i] = bs.a[i];
+    }
   }
   // ---- weights, per wave
   float m = -INFINITY;
@@ -107,6 +221,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
   }
   o += __shfl_xor(o, 1);
   o += __shfl_xor(o, 2);
+  if constexpr (BUF) {
+    // the buffer's (max, sum, value sum of coordinate j) over the waves, then
+    // the two results mixed by their shares of the softmax mass
+    const int jb = j >> 4, ji = j & 15;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) bm = fmaxf(bm, bsm[w][jb][0]);
+    float bl = 0.f, ba = 0.f;
+    if (bm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(bsm[w][jb][0] - bm);
+        bl = fmaf(f, bsm[w][jb][1], bl);
+        ba = fmaf(f, bsm[w][jb][2 + ji], ba);
+      }
+    }
+    const float mm = fmaxf(mx, bm);
+    const float ep = lsum > 0.f ? __builtin_amdgcn_exp2f(mx - mm) * lsum : 0.f;
+    const float eb = bl > 0.f ? __builtin_amdgcn_exp2f(bm - mm) * bl : 0.f;
+    const float tot = ep + eb;
+    o = tot > 0.f ? (ep * o + (bl > 0.f ? eb * (ba / bl) : 0.f)) / tot : 0.f;
+  }
   if (kq == 0) out[((size_t)b * hq + hqi) * kHeadDim + j] = __builtin_bit_cast(uint16_t, (_Float16)o);
 }
 

@@ -212,6 +212,50 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
                              bgtq_stream stream);
 
 /*
+ * (6b) Decode attention with an fp16 sink and recent window: the Block-GTQ
+ * README runs its AIME evaluation in two settings, without and with an fp16
+ * buffer of 4 attention-sink tokens and a 128-token recent window.  Reading
+ * taken: for a sequence of length T, token t attends with its original fp16
+ * key and value when t < n_sink or t >= T - n_recent, and through the packed
+ * cache otherwise; the softmax runs over all T tokens.  The packed cache
+ * still holds every token (so a token leaving the window needs no
+ * re-encoding); the decode kernel skips the buffered ones and the merge
+ * kernel takes the fp16 tokens itself, in parallel with the split partials.
+ *   k_sink, v_sink      device fp16 [batch][n_kv_heads][n_sink][128], token t < n_sink in row t
+ *   k_recent, v_recent  device fp16 [batch][n_kv_heads][n_recent][128], token t in row t % n_recent
+ *                       (a ring: it must hold tokens [max(0, T - n_recent), T))
+ *   n_sink              0..64;  n_recent 0..65536
+ *   everything else     as bgtq_decode_attn (the same workspace size)
+ * Null buffer pointers are allowed for a zero count.  n_sink = n_recent = 0 is
+ * bgtq_decode_attn.
+ * Errors: as bgtq_decode_attn; EINVAL for counts out of range or a null
+ * buffer with a non-zero count.
+ */
+bgtq_status bgtq_decode_attn_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                      const uint32_t *k_codes, const uint16_t *k_norms,
+                                      const uint32_t *v_codes, const uint16_t *v_norms, int64_t capacity,
+                                      const int32_t *seq_lens, int32_t batch, int64_t max_seq_len,
+                                      float softmax_scale, const uint16_t *k_sink, const uint16_t *v_sink,
+                                      int32_t n_sink, const uint16_t *k_recent, const uint16_t *v_recent,
+                                      int32_t n_recent, uint16_t *out, void *workspace, size_t ws_bytes,
+                                      bgtq_stream stream);
+
+/*
+ * (6c) Buffer append: copies new fp16 keys and values into the sink and
+ * recent-window buffers of (6b).  Token t = t0 + i (i < n_new) goes to sink
+ * row t when t < n_sink and to ring row t % n_recent when
+ * t >= t0 + n_new - n_recent (earlier new tokens would be overwritten by later
+ * ones of the same call).  Call it with the same k/v as bgtq_encode_k/v.
+ *   k, v     device fp16 [batch][n_new][n_kv_heads][128]
+ *   buffers  as (6b), written
+ * Errors: EINVAL on null pointers with non-zero counts, counts out of range,
+ * t0 < 0 or n_new < 0.
+ */
+bgtq_status bgtq_buffer_append(const uint16_t *k, const uint16_t *v, int32_t batch, int64_t n_new, int64_t t0,
+                               int32_t n_kv_heads, uint16_t *k_sink, uint16_t *v_sink, int32_t n_sink,
+                               uint16_t *k_recent, uint16_t *v_recent, int32_t n_recent, bgtq_stream stream);
+
+/*
  * (7) Decode step: appends one new key and value per sequence to the packed
  * cache and attends the new query over the cache including that token.  For
  * each sequence b with 0 <= pos[b] < capacity, k_new[b] and v_new[b] are

@@ -75,14 +75,18 @@ def rel_l2(got, ref):
     return np.where(den > 0, num / np.maximum(den, 1e-300), num)
 
 
-def decode_gpu(plan, cache, q16_batch, seq_lens, max_seq_len, scale=None):
+def decode_gpu(plan, cache, q16_batch, seq_lens, max_seq_len, scale=None, buf=None):
+    """The packed decode through the C ABI (with ``buf``: the fp16 sink / recent-window variant)."""
     import torch
     b = q16_batch.shape[0]
     out = torch.empty((b, plan.n_q_heads, 128), dtype=torch.int16, device=dev())
     ws = torch.empty(plan.workspace_size(b, max_seq_len), dtype=torch.uint8, device=dev())
-    plan.decode_attn(cache.consts, to_dev(q16_batch), cache.k_codes, cache.k_norms, cache.v_codes,
-                     cache.v_norms, cache.capacity, to_dev(np.asarray(seq_lens, np.int32)), max_seq_len,
-                     out, ws, softmax_scale=scale)
+    args = (cache.consts, to_dev(q16_batch), cache.k_codes, cache.k_norms, cache.v_codes, cache.v_norms,
+            cache.capacity, to_dev(np.asarray(seq_lens, np.int32)), max_seq_len)
+    if buf is None:
+        plan.decode_attn(*args, out, ws, softmax_scale=scale)
+    else:
+        plan.decode_attn_buffered(*args, buf, out, ws, softmax_scale=scale)
     torch.cuda.synchronize()
     return out.cpu().numpy().view(np.float16).astype(np.float64)
 

@@ -260,6 +260,10 @@ def test_full_size_128k_sampled(bg):
     cache.encode(to_dev(k[None]), to_dev(v[None]), 0)
     q = synth.query(cfg)[None]
     got = decode_gpu(plan, cache, q, [t], t)
+    log("128K: buffered decode (4 sink + 128 recent fp16 tokens)")
+    buf = bg.Buffer(1, cfg.n_kv_heads, 4, 128)
+    buf.append(to_dev(k[None]), to_dev(v[None]), 0)
+    got_buf = decode_gpu(plan, cache, q, [t], t, buf=buf)
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
     for h in range(cfg.n_kv_heads):
@@ -284,3 +288,9 @@ def test_full_size_128k_sampled(bg):
             r = rel_l2(got[0, h * cfg.group:(h + 1) * cfg.group], o)
             log("128K: head %d rel-L2 max %.3e" % (h, r.max()))
             assert r.max() <= TOL
+            ob = oracle.decode_attention_buffered(q[0, h * cfg.group:(h + 1) * cfg.group], k[:, h:h + 1],
+                                                  v[:, h:h + 1], ref.k_hat()[:, None], ref.v_hat()[:, None],
+                                                  t, 4, 128)
+            rb = rel_l2(got_buf[0, h * cfg.group:(h + 1) * cfg.group], ob)
+            log("128K: head %d buffered rel-L2 max %.3e" % (h, rb.max()))
+            assert rb.max() <= TOL
