@@ -326,6 +326,29 @@ def main() -> int:
     log("buffered decode (4 sink + 128 recent fp16 tokens) %.4f ms" % buf_ms)
     del buf
 
+    # ---- the paged layout: each replica read as a pool of pages [Hkv][tiles] through a shuffled
+    # block table (one sequence), the same bytes per call
+    paged_ms = None
+    if b == 1:
+        table = torch.from_numpy(np.random.default_rng(0).permutation(cache.tiles).astype(np.int32)[None]).to(dev)
+
+        class _Pool:
+            def __init__(self, arrs):
+                self.k_codes, self.k_norms, self.v_codes, self.v_norms = arrs
+
+            def desc(self):
+                return bg._Pages(table.data_ptr(), cache.tiles, cache.tiles)
+
+        pools = [_Pool(r) for r in reps]
+
+        def attn_paged(i):
+            plan.decode_attn_paged(cache.consts, q, pools[i % n_rep], seq_lens, t + 1, out, ws)
+
+        for i in range(max(5, args.warmup // 5)):
+            attn_paged(i)
+        paged_ms = sum(timed_round(attn_paged, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
+        log("paged decode (shuffled block table) %.4f ms" % paged_ms)
+
     # ---- fp16 baseline: the same keys and values uncompressed, the same split-sequence decode
     # (bgtq_fp16_decode_attn) over the same t + 1 tokens, replicated against the Infinity Cache
     del reps
@@ -380,6 +403,8 @@ def main() -> int:
                                  "decode attention over T + 1 tokens", "ms": round(serve_ms, 5),
                          "GBps": round(packed / (serve_ms / 1e3) / 1e9, 2)},
         "packed_bytes_per_step": packed,
+        "paged_decode": {"what": "bgtq_decode_attn_paged: the same cache read as 64-token pages through a "
+                                 "shuffled block table", "ms": None if paged_ms is None else round(paged_ms, 5)},
         "buffered_decode": {"what": "bgtq_decode_attn_buffered: 4 sink and 128 recent tokens from fp16 buffers, "
                                     "the rest from the packed cache, over the same t + 1 tokens",
                             "ms": round(buf_ms, 5)},

@@ -27,7 +27,7 @@ EXPORTED = [
     "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
-    "bgtq_buffer_append",
+    "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
 ]
 
 
@@ -42,6 +42,10 @@ class _PlanDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("k_avg_bits", ctypes.c_int32),
                 ("v_bits", ctypes.c_int32), ("k_bits", ctypes.POINTER(ctypes.c_int8)),
                 ("seed", ctypes.c_uint64), ("layer", ctypes.c_int32), ("rope_pairing", ctypes.c_int32)]
+
+
+class _Pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class _Sizes(ctypes.Structure):
@@ -91,6 +95,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_decode_attn_buffered": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float,
                                             P, P, I32, P, P, I32, P, P, SZ, P]),
         "bgtq_buffer_append": (I32, [P, P, I32, I64, I64, I32, P, P, I32, P, P, I32, P]),
+        "bgtq_encode_k_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
+        "bgtq_encode_v_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
+        "bgtq_decode_attn_paged": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
+                                         ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -248,6 +256,27 @@ class Plan:
                                        max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
 
+    def encode_k_paged(self, consts, k, pages: "PagedCache", t0: int, stream=None) -> None:
+        pg = pages.desc()
+        _check(load().bgtq_encode_k_paged(self._h, _ptr(consts), _ptr(k), k.shape[0], ctypes.byref(pg), t0,
+                                          k.shape[1], _ptr(pages.k_codes), _ptr(pages.k_norms), _stream(stream)))
+
+    def encode_v_paged(self, consts, v, pages: "PagedCache", t0: int, stream=None) -> None:
+        pg = pages.desc()
+        _check(load().bgtq_encode_v_paged(self._h, _ptr(consts), _ptr(v), v.shape[0], ctypes.byref(pg), t0,
+                                          v.shape[1], _ptr(pages.v_codes), _ptr(pages.v_norms), _stream(stream)))
+
+    def decode_attn_paged(self, consts, q, pages: "PagedCache", seq_lens, max_seq_len: int, out, workspace,
+                          softmax_scale: float | None = None, stream=None) -> None:
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        pg = pages.desc()
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_attn_paged(
+            self._h, _ptr(consts), _ptr(q), _ptr(pages.k_codes), _ptr(pages.k_norms), _ptr(pages.v_codes),
+            _ptr(pages.v_norms), ctypes.byref(pg), _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale,
+            _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
     def decode_attn_buffered(self, consts, q, k_codes, k_norms, v_codes, v_norms, capacity: int, seq_lens,
                              max_seq_len: int, buf: "Buffer", out, workspace, softmax_scale: float | None = None,
                              stream=None) -> None:
@@ -289,6 +318,38 @@ def fp16_decode_attn(q, k, v, seq_lens, max_seq_len: int, out, workspace, softma
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().bgtq_fp16_decode_attn(_ptr(q), _ptr(k), _ptr(v), b, hq, hkv, cap, _ptr(seq_lens), max_seq_len,
                                         softmax_scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+class PagedCache:
+    """A paged pool of one layer's packed cache (caller-owned torch tensors, zero-filled): pages of one
+    64-token tile per KV head, k_codes [Hkv][n_pages][4 k_avg_bits][64] and so on, plus a device block
+    table [batch][max_pages] of int32 page ids (logical tile j of sequence b is page table[b][j])."""
+
+    def __init__(self, plan: "Plan", n_pages: int, block_table, device="cuda"):
+        import torch
+        hkv = plan.n_kv_heads
+        self.plan, self.n_pages = plan, n_pages
+        self.block_table = torch.as_tensor(np.ascontiguousarray(block_table, dtype=np.int32)).to(device)
+        self.batch, self.max_pages = self.block_table.shape
+        s = plan.sizes(1, n_pages * TILE)
+        self.consts = torch.zeros(s.consts // 4 + 64, dtype=torch.int32, device=device)
+        self.k_codes = torch.zeros((hkv, n_pages, 4 * plan.k_avg_bits, TILE), dtype=torch.int32, device=device)
+        self.k_norms = torch.zeros((hkv, n_pages, TILE, 4), dtype=torch.int16, device=device)
+        self.v_codes = torch.zeros((hkv, n_pages, HEAD_DIM, 2 * plan.v_bits), dtype=torch.int32, device=device)
+        self.v_norms = torch.zeros((hkv, n_pages, TILE), dtype=torch.int16, device=device)
+        assert self.k_codes.numel() * 4 == s.k_codes and self.v_codes.numel() * 4 == s.v_codes
+        plan.upload(self.consts)
+
+    @property
+    def capacity(self) -> int:
+        return self.max_pages * TILE
+
+    def desc(self) -> _Pages:
+        return _Pages(self.block_table.data_ptr(), self.max_pages, self.n_pages)
+
+    def encode(self, k, v, t0: int, stream=None) -> None:
+        self.plan.encode_k_paged(self.consts, k, self, t0, stream)
+        self.plan.encode_v_paged(self.consts, v, self, t0, stream)
 
 
 class Buffer:

@@ -16,7 +16,8 @@ struct AppendArgs {
   const uint16_t *x;  // [rows][n_kv_heads][128] fp16
   uint32_t *codes;
   uint16_t *norms;
-  int64_t tiles_cap, off_kvh, off_rot64;  // off_rot64: K group area or Pi_V^T area
+  TileMap map;                  // tile addresses (contiguous or paged)
+  int64_t off_kvh, off_rot64;  // off_rot64: K group area or Pi_V^T area
   int hkv, wk, v_bits;
 };
 
@@ -50,7 +51,9 @@ __device__ __forceinline__ void append_role(const AppendArgs &a, int64_t tile, i
   const ConstHeader *hd = hdr_of(a.consts);
   const int hkv = a.hkv, tid = threadIdx.x, lane = tid & 63;
   const int p = tid & (kHeadDim - 1), qtr = tid >> 7;
-  const size_t base = ((size_t)b * hkv + kvh) * (size_t)a.tiles_cap + (size_t)tile;
+  const int64_t tix = tile_at(a.map, b, kvh, tile);
+  if (tix < 0) return;  // a paged table entry outside the pool: nothing is written (uniform per workgroup)
+  const size_t base = (size_t)tix;
   // ---- descriptor, thresholds and the first token into LDS
   if (!IS_V) {
     const uint32_t *src = (const uint32_t *)((const KvhDesc *)(a.consts + a.off_kvh) + kvh);

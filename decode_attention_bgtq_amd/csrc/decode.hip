@@ -560,7 +560,10 @@ struct DecodeArgs {
   const uint16_t *vn;
   const int32_t *seq_lens;
   float *part;  // split partials [batch][hq][n_splits][kPartStride]
-  int64_t tiles_cap, max_seq_len, off_kvh, off_dtab, off_vlut, off_zero;
+  const int32_t *table;  // paged pools: block table [batch][max_pages], else null
+  int64_t head_stride, seq_stride;  // tile index = kvh * head_stride + b * seq_stride + page
+  int max_pages, n_pages;
+  int64_t max_seq_len, off_kvh, off_dtab, off_vlut, off_zero;
   int hkv, hq, wk, tiles_base, tiles_extra, n_splits;  // split s: tiles_base + (s < tiles_extra) tiles
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
   int n_sink, n_recent;  // tokens [0, n_sink) and [T - n_recent, T) are served from fp16 buffers, not here
@@ -617,7 +620,14 @@ void decode_kernel(const DecodeArgs a) {
   const int tile_lo = split * a.tiles_base + min(split, a.tiles_extra);
   const int tile_end =
       min(tile_lo + a.tiles_base + (split < a.tiles_extra ? 1 : 0), (int)((a.max_seq_len + kTile - 1) / kTile));
-  const size_t head_base = ((size_t)b * a.hkv + kvh) * (size_t)a.tiles_cap;
+  // tile index = head_base + page; page = tile (contiguous) or the block
+  // table's entry (paged; clamped into the pool, read one tile ahead)
+  const size_t head_base = (size_t)kvh * a.head_stride + (size_t)b * a.seq_stride;
+  const bool paged = a.table != nullptr;
+  const int32_t *btab = paged ? a.table + (size_t)b * a.max_pages : nullptr;
+  const auto page_of = [&](int t) -> size_t {
+    return (size_t)min((uint32_t)__builtin_amdgcn_readfirstlane(btab[t]), (uint32_t)(a.n_pages - 1));
+  };
   const bool kzero = a.wk == 0;
   // (zero-key plans run the 4-word kernel: the plan's zero block is one such tile)
   static_assert(4 * kTile * 4 == kZeroBytes, "zero block of one 4-word tile");
@@ -625,7 +635,13 @@ void decode_kernel(const DecodeArgs a) {
   const size_t kstride = kzero ? 0 : (size_t)WK * kTile;
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
-  load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), lane);
+  size_t pn = 0;  // paged: page of the wave's next tile
+  if (paged) {
+    load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + page_of(min(tile, tile_end - 1)), lane);
+    pn = page_of(min(tile + kStreamWaves, tile_end - 1));
+  } else {
+    load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // the queries of this (sequence, KV head), rotated and scaled (ends with a barrier)
   prep_build<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
@@ -660,7 +676,13 @@ void decode_kernel(const DecodeArgs a) {
   // next tile's registers are requested before the current one is processed
   // and moved into place after it.
   for (; tile < tile_hi; tile += kStreamWaves) {
-    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile + kStreamWaves, tile_hi - 1), lane);
+    const int tn = min(tile + kStreamWaves, tile_hi - 1);
+    size_t bn = head_base + tn;
+    if (paged) {  // (the prefetched page belongs to tn except on the last pass, whose load is not used)
+      bn = head_base + pn;
+      pn = page_of(min(tile + 2 * kStreamWaves, tile_hi - 1));
+    }
+    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
     process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
     ra = rb;
   }
@@ -835,7 +857,12 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.vn = c.v_norms;
   a.seq_lens = c.seq_lens;
   a.part = (float *)ws;
-  a.tiles_cap = (c.capacity + kTile - 1) / kTile;
+  const TileMap map = c.pages ? paged_map(p, c.pages) : contiguous_map(p.desc.n_kv_heads, c.capacity);
+  a.table = map.table;
+  a.head_stride = map.head_stride;
+  a.seq_stride = map.seq_stride;
+  a.max_pages = map.max_pages;
+  a.n_pages = map.n_pages;
   a.max_seq_len = c.max_seq_len;
   a.off_kvh = p.hdr.off_kvh;
   a.off_dtab = p.hdr.off_dtab;
@@ -914,6 +941,26 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
   if (v != BGTQ_OK) return v;
   DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
                softmax_scale, out, workspace, stream};
+  return decode_launch(plan->p, c);
+}
+
+bgtq_status bgtq_decode_attn_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                   const uint32_t *k_codes, const uint16_t *k_norms, const uint32_t *v_codes,
+                                   const uint16_t *v_norms, const bgtq_pages *pages, const int32_t *seq_lens,
+                                   int32_t batch, int64_t max_seq_len, float softmax_scale, uint16_t *out,
+                                   void *workspace, size_t ws_bytes, bgtq_stream stream) {
+  const char *nm = "bgtq_decode_attn_paged";
+  if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace ||
+      (!k_codes && plan->p.hdr.wk > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  const bgtq_status ps = pages_check(pages, nm);
+  if (ps != BGTQ_OK) return ps;
+  const int64_t capacity = (int64_t)kTile * pages->max_pages;
+  const bgtq_status v = decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
+  if (v != BGTQ_OK) return v;
+  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
+               softmax_scale, out, workspace, stream};
+  c.pages = pages;
   return decode_launch(plan->p, c);
 }
 

@@ -116,6 +116,18 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Tile index of logical tile j of (sequence b, KV head kvh), or -1 when a
+// paged table entry is outside the pool (writers skip such tiles).
+__device__ __forceinline__ int64_t tile_at(const TileMap &m, int b, int kvh, int64_t j) {
+  int64_t page = j;
+  if (m.table) {
+    const int32_t e = m.table[(size_t)b * m.max_pages + j];
+    if (e < 0 || e >= m.n_pages) return -1;
+    page = e;
+  }
+  return (int64_t)kvh * m.head_stride + (int64_t)b * m.seq_stride + page;
+}
+
 __device__ __forceinline__ const ConstHeader *hdr_of(const uint8_t *c) {
   return (const ConstHeader *)c;
 }

@@ -14,7 +14,7 @@ namespace bgtq {
 // tokens).
 template <bool IS_V>
 __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__ consts,
-                                                     const uint16_t *__restrict__ x, int64_t tiles_cap,
+                                                     const uint16_t *__restrict__ x, const TileMap map,
                                                      int64_t t0, int64_t n_new,
                                                      uint32_t *__restrict__ codes,
                                                      uint16_t *__restrict__ norms) {
@@ -30,6 +30,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   const int lo = (int)(std::max(t0, tok0) - tok0);
   const int hi = (int)(std::min(t0 + n_new, tok0 + kTile) - tok0);
   const KvhDesc *kd = (const KvhDesc *)(consts + hd->off_kvh) + kvh;
+  const int64_t tix = tile_at(map, b, kvh, tile);
+  if (tix < 0) return;  // a paged table entry outside the pool: nothing is written (uniform per workgroup)
 
   for (int idx = tid; idx < kTile * kHeadDim; idx += 256) {
     const int t = idx >> 7, c = idx & 127;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
     __syncthreads();
   }
 
-  const size_t base = ((size_t)b * hkv + kvh) * (size_t)tiles_cap + (size_t)tile;
+  const size_t base = (size_t)tix;
   if (!IS_V) {
     const int wk = hd->wk;
     if (tid >= lo && tid < hi) {
@@ -172,13 +174,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const AppendArgs
 }
 
 AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,
-                       int64_t tiles_cap, bool is_v) {
+                       const TileMap &map, bool is_v) {
   AppendArgs a;
   a.consts = consts;
   a.x = x;
   a.codes = codes;
   a.norms = norms;
-  a.tiles_cap = tiles_cap;
+  a.map = map;
   a.off_kvh = p.hdr.off_kvh;
   a.off_rot64 = is_v ? p.hdr.off_rot64_v : p.hdr.off_rot64_k;
   a.hkv = p.desc.n_kv_heads;
@@ -195,15 +197,20 @@ namespace {
 
 bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_consts, const uint16_t *x,
                           int32_t batch, int64_t capacity, int64_t t0, int64_t n_new, uint32_t *codes,
-                          uint16_t *norms, bgtq_stream stream) {
-  const char *nm = is_v ? "bgtq_encode_v" : "bgtq_encode_k";
+                          uint16_t *norms, bgtq_stream stream, const bgtq_pages *pages = nullptr) {
+  const char *nm = pages ? (is_v ? "bgtq_encode_v_paged" : "bgtq_encode_k_paged") : (is_v ? "bgtq_encode_v" : "bgtq_encode_k");
+  if (pages) {
+    const bgtq_status ps = pages_check(pages, nm);
+    if (ps != BGTQ_OK) return ps;
+    capacity = (int64_t)kTile * pages->max_pages;
+  }
   const bool no_codes = !is_v && plan && plan->p.hdr.wk == 0;  // zero-bit keys store no code words
   if (!plan || !dev_consts || (!codes && !no_codes) || !norms || (!x && n_new > 0))
     return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
   if (batch < 1 || n_new < 0 || capacity < 0) return fail(BGTQ_EINVAL, std::string(nm) + ": bad batch or count");
   if (t0 < 0 || t0 + n_new > capacity) return fail(BGTQ_ECAPACITY, std::string(nm) + ": tokens beyond capacity");
   if (n_new == 0 || no_codes) return BGTQ_OK;  // zero-bit keys: the caller's zero norms stand
-  const int64_t tiles_cap = (capacity + kTile - 1) / kTile;
+  const TileMap map = pages ? paged_map(plan->p, pages) : contiguous_map(plan->p.desc.n_kv_heads, capacity);
   const int64_t first = t0 / kTile, last = (t0 + n_new - 1) / kTile;
   if (last - first + 1 > 0x7FFFFFFF || batch > 65535 || plan->p.desc.n_kv_heads > 65535)
     return fail(BGTQ_EINVAL, std::string(nm) + ": grid too large");
@@ -212,11 +219,11 @@ bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_cons
   hipStream_t st = (hipStream_t)stream;
   const bool small = n_new <= 8;  // a few tokens per tile: dot-product path
   if (is_v) {
-    if (small) append_kernel<true><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, tiles_cap, true), t0, n_new);
-    else encode_kernel<true><<<grid, 256, 0, st>>>(c, x, tiles_cap, t0, n_new, codes, norms);
+    if (small) append_kernel<true><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, map, true), t0, n_new);
+    else encode_kernel<true><<<grid, 256, 0, st>>>(c, x, map, t0, n_new, codes, norms);
   } else {
-    if (small) append_kernel<false><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, tiles_cap, false), t0, n_new);
-    else encode_kernel<false><<<grid, 256, 0, st>>>(c, x, tiles_cap, t0, n_new, codes, norms);
+    if (small) append_kernel<false><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, map, false), t0, n_new);
+    else encode_kernel<false><<<grid, 256, 0, st>>>(c, x, map, t0, n_new, codes, norms);
   }
   return launch_status(nm);
 }
@@ -235,6 +242,20 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
                           int64_t capacity, int64_t t0, int64_t n_new, uint32_t *v_codes, uint16_t *v_norms,
                           bgtq_stream stream) {
   return encode_common(true, plan, dev_consts, v, batch, capacity, t0, n_new, v_codes, v_norms, stream);
+}
+
+bgtq_status bgtq_encode_k_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, int32_t batch,
+                                const bgtq_pages *pages, int64_t t0, int64_t n_new, uint32_t *k_codes,
+                                uint16_t *k_norms, bgtq_stream stream) {
+  if (!pages) return fail(BGTQ_EINVAL, "bgtq_encode_k_paged: null pages");
+  return encode_common(false, plan, dev_consts, k, batch, 0, t0, n_new, k_codes, k_norms, stream, pages);
+}
+
+bgtq_status bgtq_encode_v_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *v, int32_t batch,
+                                const bgtq_pages *pages, int64_t t0, int64_t n_new, uint32_t *v_codes,
+                                uint16_t *v_norms, bgtq_stream stream) {
+  if (!pages) return fail(BGTQ_EINVAL, "bgtq_encode_v_paged: null pages");
+  return encode_common(true, plan, dev_consts, v, batch, 0, t0, n_new, v_codes, v_norms, stream, pages);
 }
 
 }  // extern "C"

@@ -41,6 +41,8 @@ struct DecodeCall {
   uint16_t *out;
   void *workspace;
   bgtq_stream stream;
+  // paged pool (null: the contiguous layout)
+  const bgtq_pages *pages = nullptr;
   // fp16 sink and recent window (counts 0: none)
   const uint16_t *k_sink = nullptr, *v_sink = nullptr, *k_recent = nullptr, *v_recent = nullptr;
   int n_sink = 0, n_recent = 0;
@@ -51,6 +53,18 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c);  // the fused dec
 
 struct AppendArgs;
 AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,
-                       int64_t tiles_cap, bool is_v);
+                       const TileMap &map, bool is_v);
+
+// Paged pools: argument checks and the tile map of a pool.
+inline bgtq_status pages_check(const bgtq_pages *pg, const char *nm) {
+  if (!pg || !pg->block_table) return fail(BGTQ_EINVAL, std::string(nm) + ": null pages or block table");
+  if (pg->max_pages < 1 || pg->n_pages < 1 || (int64_t)pg->max_pages * kTile > ((int64_t)1 << 40))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": max_pages and n_pages must be >= 1");
+  return BGTQ_OK;
+}
+
+inline TileMap paged_map(const Plan &, const bgtq_pages *pg) {
+  return TileMap{pg->block_table, pg->n_pages, 0, pg->max_pages, pg->n_pages};
+}
 
 }  // namespace bgtq

@@ -54,6 +54,22 @@ struct KvhDesc {
   int16_t coord[kHeadDim];     // original coordinate of each group-order position
 };
 
+// Where logical tile j of (sequence b, KV head h) lives in a cache array of
+// tiles: contiguous caches [batch][n_kv_heads][tiles_cap] (no table; page = j,
+// head_stride = tiles_cap, seq_stride = n_kv_heads * tiles_cap) or paged pools
+// [n_kv_heads][n_pages] (page = table[b][j], head_stride = n_pages,
+// seq_stride = 0).  Tile index = h * head_stride + b * seq_stride + page.
+struct TileMap {
+  const int32_t *table;  // device int32 [batch][max_pages], or null
+  int64_t head_stride, seq_stride;
+  int32_t max_pages, n_pages;
+};
+
+inline TileMap contiguous_map(int n_kv_heads, int64_t capacity) {
+  const int64_t tiles = (capacity + kTile - 1) / kTile;
+  return TileMap{nullptr, tiles, (int64_t)n_kv_heads * tiles, 0, 0};
+}
+
 // Device constant image header.  All offsets are bytes from the image start.
 struct ConstHeader {
   int32_t n_kv_heads, n_q_heads, group, head_dim;

@@ -47,10 +47,10 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
   const int n = batch * p.desc.n_kv_heads;
   const int64_t blocks = (int64_t)n * 2;
   if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, "bgtq_decode_step: grid too large");
-  const int64_t tiles_cap = (capacity + kTile - 1) / kTile;
+  const TileMap map = contiguous_map(p.desc.n_kv_heads, capacity);
   const uint8_t *c = (const uint8_t *)dev_consts;
-  const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, tiles_cap, false);
-  const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, tiles_cap, true);
+  const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, map, false);
+  const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, map, true);
   hipStream_t st = (hipStream_t)stream;
   step_append_kernel<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pos, capacity, n);
   const bgtq_status ls = launch_status("bgtq_decode_step (append)");

@@ -256,6 +256,50 @@ bgtq_status bgtq_buffer_append(const uint16_t *k, const uint16_t *v, int32_t bat
                                uint16_t *k_recent, uint16_t *v_recent, int32_t n_recent, bgtq_stream stream);
 
 /*
+ * (6d) Paged packed cache (the paged-KV serving layout: the cache as a pool of
+ * fixed-size pages and a per-sequence block table, so that sequences grow
+ * without reallocation and share one pool).  A page is one 64-token tile of
+ * one KV head; the pool arrays are the per-tile blocks of (4) with the pages
+ * in place of the tiles:
+ *   k_codes  u32  [n_kv_heads][n_pages][4*k_avg_bits][64]
+ *   k_norms  fp16 [n_kv_heads][n_pages][64][4]
+ *   v_codes  u32  [n_kv_heads][n_pages][128][2*v_bits]
+ *   v_norms  fp16 [n_kv_heads][n_pages][64]
+ * (bgtq_plan_sizes(plan, 1, 64 * n_pages) gives their sizes).  Token t of
+ * sequence b lives in page block_table[b][t / 64], row t % 64, for every KV
+ * head.  The table is read on the device; entries must lie in [0, n_pages)
+ * for every tile a call writes or attends to (an entry outside the pool makes
+ * the writers skip that tile; reads are clamped to the pool, so a bad entry
+ * gives wrong results, never an access outside the pool).  Decoding a paged
+ * pool gives the same results, bit for bit, as the contiguous cache holding
+ * the same tokens.
+ */
+typedef struct {
+  const int32_t *block_table; /* device int32 [batch][max_pages] */
+  int32_t max_pages;          /* table entries per sequence: capacity 64 * max_pages tokens */
+  int32_t n_pages;            /* pages in the pool */
+} bgtq_pages;
+
+/* (4) on a paged pool: tokens t0 .. t0 + n_new - 1 of every sequence, k / v as
+ * in (4).  Errors: as (4), with capacity = 64 * max_pages; EINVAL for null
+ * pages or table, max_pages < 1 or n_pages < 1. */
+bgtq_status bgtq_encode_k_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k,
+                                int32_t batch, const bgtq_pages *pages, int64_t t0, int64_t n_new,
+                                uint32_t *k_codes, uint16_t *k_norms, bgtq_stream stream);
+bgtq_status bgtq_encode_v_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *v,
+                                int32_t batch, const bgtq_pages *pages, int64_t t0, int64_t n_new,
+                                uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
+
+/* (6) on a paged pool: everything as bgtq_decode_attn, capacity 64 * max_pages
+ * (the same workspace size).  Errors: as (6); EINVAL for bad pages. */
+bgtq_status bgtq_decode_attn_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                   const uint32_t *k_codes, const uint16_t *k_norms,
+                                   const uint32_t *v_codes, const uint16_t *v_norms,
+                                   const bgtq_pages *pages, const int32_t *seq_lens, int32_t batch,
+                                   int64_t max_seq_len, float softmax_scale, uint16_t *out,
+                                   void *workspace, size_t ws_bytes, bgtq_stream stream);
+
+/*
  * (7) Decode step: appends one new key and value per sequence to the packed
  * cache and attends the new query over the cache including that token.  For
  * each sequence b with 0 <= pos[b] < capacity, k_new[b] and v_new[b] are

@@ -119,6 +119,25 @@ def test_plan_rejects_unknown_pairing(bg):
     bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6, pairing="interleaved").close()
 
 
+def test_paged_calls_reject_bad_arguments_before_launch(bg):
+    lib = bg.load()
+    plan = bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6)
+    h = plan.handle
+    pg = bg._Pages(256, 4, 10)
+    bad = [bg._Pages(None, 4, 10), bg._Pages(256, 0, 10), bg._Pages(256, 4, 0)]
+    assert lib.bgtq_encode_k_paged(h, 256, 256, 1, None, 0, 10, 256, 256, None) == bg.EINVAL
+    for b in bad:
+        assert lib.bgtq_encode_k_paged(h, 256, 256, 1, ctypes.byref(b), 0, 10, 256, 256, None) == bg.EINVAL
+        assert lib.bgtq_encode_v_paged(h, 256, 256, 1, ctypes.byref(b), 0, 10, 256, 256, None) == bg.EINVAL
+    assert lib.bgtq_encode_k_paged(h, 256, 256, 1, ctypes.byref(pg), 250, 10, 256, 256, None) == bg.ECAPACITY
+    args = [h, 256, 256, 256, 256, 256, 256]
+    assert lib.bgtq_decode_attn_paged(*args, None, 256, 1, 100, 0.1, 256, 256, 1 << 30, None) == bg.EINVAL
+    assert lib.bgtq_decode_attn_paged(*args, ctypes.byref(pg), 256, 1, 257, 0.1, 256, 256, 1 << 30,
+                                      None) == bg.ECAPACITY
+    assert lib.bgtq_decode_attn_paged(*args, ctypes.byref(bad[1]), 256, 1, 100, 0.1, 256, 256, 1 << 30,
+                                      None) == bg.EINVAL
+
+
 def test_device_calls_reject_bad_arguments_before_launch(bg):
     lib = bg.load()
     assert lib.bgtq_energy(None, None, 10, 8, 2, 128, 0, None, None) == bg.EINVAL
