@@ -80,9 +80,12 @@ def cpu_baseline(cfg, bits, n_heads: int):
     t = cfg.seq_len
     q = synth.query(cfg)
     total_s, total_bytes = 0.0, 0
+    n_heads = min(n_heads, cfg.n_kv_heads)
+    k_all = synth.keys(cfg, count=t)
+    v_all = synth.values(cfg, count=t)
     for h in range(n_heads):
-        k = synth.keys(cfg, count=t)[:, h]
-        v = synth.values(cfg, count=t)[:, h]
+        k = k_all[:, h]
+        v = v_all[:, h]
         kc, kn = oracle.encode_k(k, bits[h], cfg.seed, 0, h)
         vc, vn = oracle.encode_v(v, cfg.v_bits, cfg.seed, 0, h)
         n_groups = len([w for w in (1, 2, 3, 4) if np.any(bits[h] == w)])
@@ -153,7 +156,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--replica-bytes", type=float, default=1.1e9)
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/decode_kernel_traffic.json from two rocprofv3 --pmc runs and exit")

@@ -35,6 +35,7 @@
 
 namespace bgtq {
 
+constexpr int64_t kMaxSeqLen = 0x7FFFFFFFLL - kTile;  // token positions of the decode fit 32 bits
 constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights within a tile stay below 2^8
 
 
@@ -189,6 +190,7 @@ struct StreamState {
   uint32_t ptw;       // LDS byte offset of this wave's weight rows
   int wk, n4w;
   int lo;       // first token of the packed range
+  uint32_t nv;  // tokens in the packed range [lo, lo + nv)
   int64_t seq;  // end of the packed range (may be below lo: an empty range)
 };
 
@@ -470,8 +472,9 @@ __device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const
 
 template <int G, int VB, int WK>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
-                                             const float (&rinv)[G], float (&mrun)[G], float (&lsum)[G],
-                                             f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v], int lane) {
+                                             const float (&rinv)[G], float (&mrun)[G], float (&mth)[G],
+                                             float (&lsum)[G], f4v (&acc0)[VQuads<G>::v],
+                                             f4v (&acc1)[VQuads<G>::v], int lane) {
   // ---- keys, lane = token.  4-bit group: one fp32 step per code.
   f4v a4[VQuads<G>::v];
 #pragma unroll
@@ -495,8 +498,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
     BGTQ_KG(0, r.nr.x >> 16) BGTQ_KG(1, r.nr.y & 0xFFFFu) BGTQ_KG(2, r.nr.y >> 16)
 #undef BGTQ_KG
   }
-  const int64_t tok = (int64_t)tile * kTile + lane;
-  const bool valid = tok < st.seq && tok >= st.lo;
+  // token positions fit 32 bits (max_seq_len < 2^31 - 64); below lo wraps to a large unsigned value
+  const bool valid = (uint32_t)(tile * kTile + lane - st.lo) < st.nv;
   const float n4 = h2f((uint16_t)(r.nr.x & 0xFFFF));  // norm slot 0: the 4-bit group
   const float nv = h2f((uint16_t)r.nv);
   // ---- online softmax (log2 domain), rescaled lazily: the running maximum
@@ -509,7 +512,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     l[h] = valid ? fmaf(n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
-    up = up || l[h] > mrun[h] + kRescaleSlack;
+    up = up || l[h] > mth[h];
   }
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
     float mx[G];
@@ -523,7 +526,9 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
       lsum[h] *= alpha;
       acc0[h >> 2][h & 3] *= alpha;
       acc1[h >> 2][h & 3] *= alpha;
-      mrun[h] = mn;
+      // wave-uniform: kept in scalar registers
+      mrun[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));
+      mth[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn + kRescaleSlack)));
     }
   }
 #pragma unroll
@@ -647,6 +652,7 @@ void decode_kernel(const DecodeArgs a) {
   prep_build<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
   st.seq = (seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw)) - a.n_recent;
   st.lo = a.n_sink;
+  st.nv = (uint32_t)(st.seq > st.lo ? st.seq - st.lo : 0);
   st.wk = a.wk;
   st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
   st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
@@ -663,18 +669,19 @@ void decode_kernel(const DecodeArgs a) {
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
-  float mrun[G], lsum[G];
+  float mrun[G], mth[G], lsum[G];  // running maximum, rescale threshold mrun + kRescaleSlack, sum
   f4v acc0[VQuads<G>::v], acc1[VQuads<G>::v];
 #pragma unroll
   // The running maximum starts finite, far below any logit, so that a tile
   // without a valid token (all logits -inf; possible below the packed range's
   // first token) gives p = 2^(-inf) = 0 rather than 2^(-inf + inf).
-  for (int h = 0; h < G; ++h) mrun[h] = -0x1p100f, lsum[h] = 0.f;
+  for (int h = 0; h < G; ++h) mrun[h] = -0x1p100f, mth[h] = -0x1p100f, lsum[h] = 0.f;
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) acc0[g] = (f4v){0.f, 0.f, 0.f, 0.f}, acc1[g] = acc0[g];
   // One copy of the tile body (the instruction cache holds the loop): the
   // next tile's registers are requested before the current one is processed
-  // and moved into place after it.
+  // and moved into place after it.  (Two copies with alternating register
+  // sets raise the register count past the occupancy limit.)
   for (; tile < tile_hi; tile += kStreamWaves) {
     const int tn = min(tile + kStreamWaves, tile_hi - 1);
     size_t bn = head_base + tn;
@@ -683,7 +690,7 @@ void decode_kernel(const DecodeArgs a) {
       pn = page_of(min(tile + 2 * kStreamWaves, tile_hi - 1));
     }
     load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
-    process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, lsum, acc0, acc1, lane);
+    process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, mth, lsum, acc0, acc1, lane);
     ra = rb;
   }
 
@@ -813,6 +820,7 @@ bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t
   if (batch < 1 || batch > 65535) return fail(BGTQ_EINVAL, std::string(nm) + ": batch must be 1..65535");
   if (max_seq_len < 1 || max_seq_len > capacity)
     return fail(BGTQ_ECAPACITY, std::string(nm) + ": max_seq_len must be in [1, capacity]");
+  if (max_seq_len > kMaxSeqLen) return fail(BGTQ_EINVAL, std::string(nm) + ": max_seq_len must be below 2^31 - 64");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(BGTQ_EINVAL, std::string(nm) + ": softmax_scale must be positive and finite");
   if ((uintptr_t)workspace & 255) return fail(BGTQ_EINVAL, std::string(nm) + ": workspace must be 256-byte aligned");

@@ -27,13 +27,16 @@ constexpr int kMaxSink = 64, kMaxRecent = 65536;  // fp16 buffer bounds (sink, r
 //
 // With BUF (the fp16 sink and recent window), the merge also attends to the
 // buffered fp16 tokens of its head: thread t takes token rows t / 8 (+ 64 per
-// round) and the 16 coordinates 16 (t % 8) .. of the key and value; the
+// round, the loads of three rounds issued together) and the 16 coordinates
+// 16 (t % 8) .. of the key and value; the
 // logit is the sum over the 8 threads of a row; each thread keeps a running
 // (max, sum, 16 value sums), combined over the rows of a wave by cross-lane
 // steps and over the waves in LDS.  The packed result y (normalised by its own
 // sum) and the buffer's are then mixed by their shares of the total softmax
 // mass.
 constexpr int kMergeThreads = 512;
+constexpr int kBufRows = kMergeThreads / 8;  // buffered token rows per round
+constexpr int kBufRounds = 3;                // rounds whose loads are issued together (192 tokens)
 constexpr int kMergeRegs = 16;  // split accumulators per lane loaded before the weights (n_splits <= 64)
 
 struct MergeBuf {
@@ -77,35 +80,44 @@ __device__ __forceinline__ void buf_rows(const MergeBuf &bf, int b, int kvh, int
   st.l = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) st.a[i] = 0.f;
-  for (int64_t c0 = 0; c0 < n_f; c0 += kMergeThreads / 8) {
-    const int64_t f = c0 + row, fc = f < n_f ? f : n_f - 1;  // rows past the end re-read the last one
-    const uint16_t *kp, *vp;
-    if (fc < n_s) {
-      kp = bf.k_sink + (hb * bf.n_sink + fc) * kHeadDim;
-      vp = bf.v_sink + (hb * bf.n_sink + fc) * kHeadDim;
-    } else {
-      const int64_t slot = (r0 + (fc - n_s)) % bf.n_recent;
-      kp = bf.k_recent + (hb * bf.n_recent + slot) * kHeadDim;
-      vp = bf.v_recent + (hb * bf.n_recent + slot) * kHeadDim;
-    }
-    const uint4 k0 = ((const uint4 *)kp)[2 * part], k1 = ((const uint4 *)kp)[2 * part + 1];
-    const uint4 v0 = ((const uint4 *)vp)[2 * part], v1 = ((const uint4 *)vp)[2 * part + 1];
-    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float s = 0.f;
+  // ring row of the first window token (the window's tokens are consecutive, fewer than n_recent)
+  const int64_t slot0 = n_f > n_s ? r0 % bf.n_recent : 0;
+  for (int64_t c0 = 0; c0 < n_f; c0 += kBufRows * kBufRounds) {
+    // every load of the pass first (rows past the end re-read the last one), then the rows
+    uint4 kx[kBufRounds][2], vx[kBufRounds][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s = fmaf(qv[2 * i], h2f((uint16_t)(kw[i] & 0xFFFFu)), s);
-      s = fmaf(qv[2 * i + 1], h2f((uint16_t)(kw[i] >> 16)), s);
+    for (int u = 0; u < kBufRounds; ++u) {
+      const int64_t f = c0 + u * kBufRows + row, fc = f < n_f ? f : n_f - 1;
+      int64_t slot = slot0 + (fc - n_s);
+      slot = slot >= bf.n_recent ? slot - bf.n_recent : slot;
+      const bool sink = fc < n_s;
+      const size_t off = (hb * (sink ? bf.n_sink : bf.n_recent) + (sink ? fc : slot)) * kHeadDim;
+      const uint4 *kp = (const uint4 *)((sink ? bf.k_sink : bf.k_recent) + off) + 2 * part;
+      const uint4 *vp = (const uint4 *)((sink ? bf.v_sink : bf.v_recent) + off) + 2 * part;
+      kx[u][0] = kp[0], kx[u][1] = kp[1], vx[u][0] = vp[0], vx[u][1] = vp[1];
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (f < n_f) {
-      float va[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) va[2 * i] = h2f((uint16_t)(vw[i] & 0xFFFFu)), va[2 * i + 1] = h2f((uint16_t)(vw[i] >> 16));
-      buf_combine(st, s, 1.f, va);  // one token: (logit, 1, its value)
+    for (int u = 0; u < kBufRounds; ++u) {
+      const uint32_t kw[8] = {kx[u][0].x, kx[u][0].y, kx[u][0].z, kx[u][0].w,
+                              kx[u][1].x, kx[u][1].y, kx[u][1].z, kx[u][1].w};
+      const uint32_t vw[8] = {vx[u][0].x, vx[u][0].y, vx[u][0].z, vx[u][0].w,
+                              vx[u][1].x, vx[u][1].y, vx[u][1].z, vx[u][1].w};
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s = fmaf(qv[2 * i], h2f((uint16_t)(kw[i] & 0xFFFFu)), s);
+        s = fmaf(qv[2 * i + 1], h2f((uint16_t)(kw[i] >> 16)), s);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if (c0 + u * kBufRows + row < n_f) {
+        float va[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          va[2 * i] = h2f((uint16_t)(vw[i] & 0xFFFFu)), va[2 * i + 1] = h2f((uint16_t)(vw[i] >> 16));
+        buf_combine(st, s, 1.f, va);  // one token: (logit, 1, its value)
+      }
     }
   }
   // rows of the wave (lane bits 3..5)
