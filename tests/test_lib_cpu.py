@@ -154,6 +154,7 @@ def test_device_calls_reject_bad_arguments_before_launch(bg):
     args = [h, 256, 256, 256, 256, 256, 256]
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 101, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 0, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
+    assert lib.bgtq_decode_attn(*args, 1 << 32, 256, 1, 1 << 31, 0.1, 256, 256, 1 << 30, None) == bg.EINVAL
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 50, 0.1, 256, 256, 16, None) == bg.EWORKSPACE
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 50, -1.0, 256, 256, 1 << 30, None) == bg.EINVAL
     assert lib.bgtq_decode_attn(h, 256, None, 256, 256, 256, 256, 100, 256, 1, 50, 0.1, 256, 256, 1 << 30,
