@@ -28,6 +28,7 @@ EXPORTED = [
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
+    "bgtq_decode_step_paged",
 ]
 
 
@@ -98,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_encode_k_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
         "bgtq_encode_v_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
         "bgtq_decode_attn_paged": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
+                                         ctypes.c_float, P, P, SZ, P]),
+        "bgtq_decode_step_paged": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, ctypes.POINTER(_Pages),
                                          ctypes.c_float, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -276,6 +279,18 @@ class Plan:
             self._h, _ptr(consts), _ptr(q), _ptr(pages.k_codes), _ptr(pages.k_norms), _ptr(pages.v_codes),
             _ptr(pages.v_norms), ctypes.byref(pg), _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale,
             _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+    def decode_step_paged(self, consts, q, k_new, v_new, pos, max_seq_len: int, pages: "PagedCache", out,
+                          workspace, softmax_scale: float | None = None, stream=None) -> None:
+        """decode_step on a paged pool: k_new / v_new appended at token pos[b], then attention over pos[b] + 1."""
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        pg = pages.desc()
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_step_paged(
+            self._h, _ptr(consts), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), q.shape[0], max_seq_len,
+            _ptr(pages.k_codes), _ptr(pages.k_norms), _ptr(pages.v_codes), _ptr(pages.v_norms), ctypes.byref(pg),
+            softmax_scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
     def decode_attn_buffered(self, consts, q, k_codes, k_norms, v_codes, v_norms, capacity: int, seq_lens,
                              max_seq_len: int, buf: "Buffer", out, workspace, softmax_scale: float | None = None,

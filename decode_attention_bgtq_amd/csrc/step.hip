@@ -30,6 +30,38 @@ __global__ __launch_bounds__(kAppendThreads) void step_append_kernel(const Appen
 }  // namespace bgtq
 using namespace bgtq;
 
+namespace {
+
+bgtq_status step_common(const char *nm, const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                        const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, int32_t batch,
+                        int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms, uint32_t *v_codes,
+                        uint16_t *v_norms, int64_t capacity, const bgtq_pages *pages, float softmax_scale,
+                        uint16_t *out, void *workspace, size_t ws_bytes, bgtq_stream stream) {
+  if (!plan || !dev_consts || !q || !k_new || !v_new || !pos || !k_norms || !v_codes || !v_norms || !out ||
+      !workspace || (!k_codes && plan->p.hdr.wk > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  const Plan &p = plan->p;
+  const bgtq_status v = decode_check(p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
+  if (v != BGTQ_OK) return v;
+  const int n = batch * p.desc.n_kv_heads;
+  const int64_t blocks = (int64_t)n * 2;
+  if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, std::string(nm) + ": grid too large");
+  const TileMap map = pages ? paged_map(p, pages) : contiguous_map(p.desc.n_kv_heads, capacity);
+  const uint8_t *c = (const uint8_t *)dev_consts;
+  const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, map, false);
+  const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, map, true);
+  hipStream_t st = (hipStream_t)stream;
+  step_append_kernel<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pos, capacity, n);
+  const bgtq_status ls = launch_status((std::string(nm) + " (append)").c_str());
+  if (ls != BGTQ_OK) return ls;
+  DecodeCall dc{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, pos, 1, batch, max_seq_len,
+                softmax_scale, out, workspace, stream};
+  dc.pages = pages;
+  return decode_launch(p, dc);
+}
+
+}  // namespace
+
 extern "C" {
 
 bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
@@ -37,27 +69,21 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
                              int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms, uint32_t *v_codes,
                              uint16_t *v_norms, int64_t capacity, float softmax_scale, uint16_t *out,
                              void *workspace, size_t ws_bytes, bgtq_stream stream) {
-  if (!plan || !dev_consts || !q || !k_new || !v_new || !pos || !k_norms || !v_codes || !v_norms || !out ||
-      !workspace || (!k_codes && plan->p.hdr.wk > 0))
-    return fail(BGTQ_EINVAL, "bgtq_decode_step: null pointer");
-  const Plan &p = plan->p;
-  const bgtq_status v =
-      decode_check(p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, "bgtq_decode_step");
-  if (v != BGTQ_OK) return v;
-  const int n = batch * p.desc.n_kv_heads;
-  const int64_t blocks = (int64_t)n * 2;
-  if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, "bgtq_decode_step: grid too large");
-  const TileMap map = contiguous_map(p.desc.n_kv_heads, capacity);
-  const uint8_t *c = (const uint8_t *)dev_consts;
-  const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, map, false);
-  const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, map, true);
-  hipStream_t st = (hipStream_t)stream;
-  step_append_kernel<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pos, capacity, n);
-  const bgtq_status ls = launch_status("bgtq_decode_step (append)");
-  if (ls != BGTQ_OK) return ls;
-  DecodeCall dc{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, pos, 1, batch, max_seq_len,
-                softmax_scale, out, workspace, stream};
-  return decode_launch(p, dc);
+  return step_common("bgtq_decode_step", plan, dev_consts, q, k_new, v_new, pos, batch, max_seq_len, k_codes,
+                     k_norms, v_codes, v_norms, capacity, nullptr, softmax_scale, out, workspace, ws_bytes, stream);
+}
+
+bgtq_status bgtq_decode_step_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                   const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                   int32_t batch, int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms,
+                                   uint32_t *v_codes, uint16_t *v_norms, const bgtq_pages *pages,
+                                   float softmax_scale, uint16_t *out, void *workspace, size_t ws_bytes,
+                                   bgtq_stream stream) {
+  const bgtq_status ps = pages_check(pages, "bgtq_decode_step_paged");
+  if (ps != BGTQ_OK) return ps;
+  return step_common("bgtq_decode_step_paged", plan, dev_consts, q, k_new, v_new, pos, batch, max_seq_len,
+                     k_codes, k_norms, v_codes, v_norms, (int64_t)kTile * pages->max_pages, pages, softmax_scale,
+                     out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

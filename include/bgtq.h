@@ -320,6 +320,17 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
                              uint16_t *v_norms, int64_t capacity, float softmax_scale, uint16_t *out,
                              void *workspace, size_t ws_bytes, bgtq_stream stream);
 
+/* (7) on a paged pool (6d): the new token of sequence b goes to page
+ * block_table[b][pos[b] / 64] (sequences with pos[b] outside
+ * [0, 64 * max_pages) append nothing), then bgtq_decode_attn_paged over
+ * pos[b] + 1 tokens.  Errors: as bgtq_decode_attn_paged. */
+bgtq_status bgtq_decode_step_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                   const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                   int32_t batch, int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms,
+                                   uint32_t *v_codes, uint16_t *v_norms, const bgtq_pages *pages,
+                                   float softmax_scale, uint16_t *out, void *workspace, size_t ws_bytes,
+                                   bgtq_stream stream);
+
 /*
  * (8) fp16 decode attention over an uncompressed KV cache: the baseline of the
  * packed path (Abstract: the packed path runs faster than fp16

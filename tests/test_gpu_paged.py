@@ -93,3 +93,36 @@ def test_paged_writer_skips_entries_outside_the_pool(bg):
         arr = getattr(pool, name).cpu().numpy()
         assert np.any(arr[:, 1] != 0), name                # page 1 written
         assert np.all(arr[:, [0, 2, 3]] == 0), name        # nothing else touched
+
+
+def test_paged_decode_step_equals_contiguous(bg):
+    """The fused step on a pool: the appended pages and the output equal the contiguous step's."""
+    import torch
+    cfg = synth.small(4, seq_len=300, batch=3, append=1)
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    max_pages, n_pages = 6, 20
+    table = np.random.default_rng(5).permutation(n_pages)[:3 * max_pages].reshape(3, max_pages).astype(np.int32)
+    pool = bg.PagedCache(plan, n_pages, table)
+    cont = bg.Cache(plan, 3, 64 * max_pages)
+    ks = np.stack([synth.keys(cfg, seq=s, count=301) for s in range(3)])
+    vs = np.stack([synth.values(cfg, seq=s, count=301) for s in range(3)])
+    pool.encode(to_dev(ks[:, :300]), to_dev(vs[:, :300]), 0)
+    cont.encode(to_dev(ks[:, :300]), to_dev(vs[:, :300]), 0)
+    pos = np.array([300, 130, 5], np.int32)
+    k_new = np.stack([ks[s, pos[s]] for s in range(3)])
+    v_new = np.stack([vs[s, pos[s]] for s in range(3)])
+    q = np.stack([synth.query(cfg, seq=s) for s in range(3)])
+    out_p = torch.empty((3, cfg.n_q_heads, 128), dtype=torch.int16, device=dev())
+    out_c = torch.empty_like(out_p)
+    ws = torch.empty(plan.workspace_size(3, 301), dtype=torch.uint8, device=dev())
+    plan.decode_step_paged(pool.consts, to_dev(q), to_dev(k_new), to_dev(v_new), to_dev(pos), 301, pool, out_p, ws)
+    cont.step(to_dev(q), to_dev(k_new), to_dev(v_new), to_dev(pos), 301, out_c, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_p.cpu().numpy(), out_c.cpu().numpy())
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        pa, ca = getattr(pool, name).cpu().numpy(), getattr(cont, name).cpu().numpy()
+        for s in range(3):
+            for j in range(5):
+                assert np.array_equal(pa[:, table[s, j]], ca[s, :, j]), (name, s, j)
