@@ -599,13 +599,15 @@ void decode_kernel(const DecodeArgs a) {
 
   // ---- prologue loads, in this order so that waiting for an earlier group
   // does not wait for a later one (loads complete in order): the sequence
-  // length and the head's group fields, the query preparation's inputs, the
-  // plan's decode and value tables (16 bytes per thread and round), then the
-  // first tile.
+  // length and the head's group fields, the row-table entries of the
+  // rotation rows, the query preparation's inputs, the plan's decode and
+  // value tables (16 bytes per thread and round), the nonzero part of the
+  // rotation (addressed from the row-table entries), then the first tile.
   const int64_t seq_raw = (int64_t)a.seq_lens[b] + a.seq_add;
   const int n4w = kd->n4w;
   const uint32_t cgrp = kd->cgrp, gbit = kd->gbit;
   PrepIn<G, kStreamWaves> pin;
+  prep_issue_keys<G, kStreamWaves>(pin, consts, kvh, wave, lane);
   prep_issue<G, kStreamWaves>(pin, consts, kvh, a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid, wave,
                               lane);
   constexpr int n0 = kDtabBytes >> 4;
@@ -617,7 +619,7 @@ void decode_kernel(const DecodeArgs a) {
   const uint4 cr0 = *(i0 < n0 ? cs0 + i0 : cs1 + i0);
   uint4 cr1 = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (kRounds == 2) cr1 = *(cs1 + i1);
-  prep_issue_rot<G, kStreamWaves>(pin, consts, kvh, wave, lane);
+  prep_issue_rot<G, kStreamWaves>(pin, consts, a.off_zero, kvh, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   // the tables, descriptor and queries into LDS before the first tile is
   // requested (waiting for these loads only), so that they are not queued

@@ -46,6 +46,44 @@ __device__ __forceinline__ void rot_rows(const float *R, int wave, int lane, Rot
   }
 }
 
+// The decode prologue fetches only the nonzero part of R: the row-table
+// entries of the lane's rows first (rot_keys; y = d_g | pos_g << 8 | ..., 0
+// past d_nz), then (rot_rows_sparse) the lane's four columns of each step
+// from R when they meet its row's group [pos_g, pos_g + d_g), else from the
+// plan's zero block (one line for every lane), so that the zero blocks of R
+// are not read.  For the 128K workload's plans that is under a third of R.
+template <int WAVES>
+struct RotKeys {
+  uint32_t y[RotRows<WAVES>::nt];
+};
+
+template <int WAVES>
+__device__ __forceinline__ void rot_keys(const uint2 *rowk, int wave, int lane, RotKeys<WAVES> &rk) {
+  const int n = lane & 15;
+  const bool idle = WAVES > 8 && wave >= 8;
+#pragma unroll
+  for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) rk.y[t2] = rowk[idle ? 0 : 16 * (wave + t2 * WAVES) + n].y;
+}
+
+template <int WAVES>
+__device__ __forceinline__ void rot_rows_sparse(const float *R, const float *zero, const RotKeys<WAVES> &rk, int wave,
+                                                int lane, RotRows<WAVES> &rr) {
+  const int n = lane & 15, kq = lane >> 4;
+  const bool idle = WAVES > 8 && wave >= 8;
+#pragma unroll
+  for (int t2 = 0; t2 < RotRows<WAVES>::nt; ++t2) {
+    const int t = wave + t2 * WAVES;
+    const int dg = (int)(rk.y[t2] & 255u), pg = (int)((rk.y[t2] >> 8) & 255u);
+    const float *row = R + (16 * t + n) * kHeadDim + 4 * kq;
+#pragma unroll
+    for (int u = 0; u < kHeadDim / 16; ++u) {
+      const int c = 16 * u + 4 * kq;
+      const bool need = !idle && c < pg + dg && c + 4 > pg;
+      rr.a[t2][u] = *(const float4 *)(need ? row + 16 * u : zero);
+    }
+  }
+}
+
 template <int WAVES>
 __device__ __forceinline__ void rot_tiles(const RotRows<WAVES> &rr, int G, const float *qg, float *qs, int wave,
                                           int lane) {
@@ -131,6 +169,7 @@ struct PrepIn {
   uint32_t dw;                                             // one word of the KvhDesc
   uint16_t qv[nq];
   uint2 row;  // row table entry of p: y = d_g | pos_g << 8 | w << 16 | first k-step << 19
+  RotKeys<WAVES> rk;
   RotRows<WAVES> rr;
 };
 
@@ -148,11 +187,20 @@ __device__ __forceinline__ void prep_issue(PrepIn<G, WAVES> &in, const uint8_t *
   in.row = ((const uint2 *)(consts + hd->off_rowk))[(size_t)kvh * kHeadDim + (tid & (kHeadDim - 1))];
 }
 
+// The row-table entries of the lane's rotation rows: the first loads of the prologue.
 template <int G, int WAVES>
-__device__ __forceinline__ void prep_issue_rot(PrepIn<G, WAVES> &in, const uint8_t *consts, int kvh, int wave,
-                                               int lane) {
+__device__ __forceinline__ void prep_issue_keys(PrepIn<G, WAVES> &in, const uint8_t *consts, int kvh, int wave,
+                                                int lane) {
   const ConstHeader *hd = hdr_of(consts);
-  rot_rows<WAVES>((const float *)(consts + hd->off_rot32_k) + (size_t)kvh * kHeadDim * kHeadDim, wave, lane, in.rr);
+  rot_keys<WAVES>((const uint2 *)(consts + hd->off_rowk) + (size_t)kvh * kHeadDim, wave, lane, in.rk);
+}
+
+template <int G, int WAVES>
+__device__ __forceinline__ void prep_issue_rot(PrepIn<G, WAVES> &in, const uint8_t *consts, int64_t off_zero, int kvh,
+                                               int wave, int lane) {
+  const ConstHeader *hd = hdr_of(consts);
+  rot_rows_sparse<WAVES>((const float *)(consts + hd->off_rot32_k) + (size_t)kvh * kHeadDim * kHeadDim,
+                         (const float *)(consts + off_zero), in.rk, wave, lane, in.rr);
 }
 
 // `out` and `scr`: LDS (PrepOut and PrepScratch layouts).
