@@ -799,8 +799,10 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   const int hkv = p.desc.n_kv_heads, hq = p.desc.n_q_heads;
   const DecodeKernel k = pick_decode(p.hdr.group, p.hdr.v_bits, p.hdr.wk);
   const int target = std::max(1, k.per_cu) * device_cus();  // one round of resident workgroups
+  // (short sequences: at least one tile per wave, the latency-bound case
+  // measured faster than two tiles per wave)
   int s = (target + batch * hkv - 1) / (batch * hkv);
-  s = std::max(1, std::min({s, (tiles + 2 * k.waves - 1) / (2 * k.waves), kMaxSplits}));
+  s = std::max(1, std::min({s, (tiles + k.waves - 1) / k.waves, kMaxSplits}));
   // tiles dealt out evenly: the first tiles % s splits take one tile more, so
   // that (with a multiple of the wave count per split) no wave but those of
   // the first splits has a tile more than the others
