@@ -294,3 +294,23 @@ def test_full_size_128k_sampled(bg):
             rb = rel_l2(got_buf[0, h * cfg.group:(h + 1) * cfg.group], ob)
             log("128K: head %d buffered rel-L2 max %.3e" % (h, rb.max()))
             assert rb.max() <= TOL
+
+
+def test_decode_invariant_to_split_count(bg):
+    """The same cache and query decoded with different max_seq_len bounds (so different split
+    counts, visible as different workspace sizes) agree to fp16 output rounding."""
+    cfg = synth.small(2, seq_len=3000)
+    plan, cache, bits, ks, vs, heads = _encode_case(bg, cfg, 3000, capacity=65536)
+    q = synth.query(cfg)[None]
+    outs, sizes = [], []
+    for msl in (3000, 9000, 65536):
+        sizes.append(plan.workspace_size(1, msl))
+        outs.append(decode_gpu(plan, cache, q, [3000], msl))
+    assert len(set(sizes)) == 3
+    for o in outs[1:]:
+        r = rel_l2(o[0], outs[0][0])
+        assert r.max() <= 1e-3, r.max()      # one fp16 ulp is ~1e-3 relative
+    ref = oracle.decode_attention(q[0], np.stack([heads[(0, h)].k_hat() for h in range(2)], axis=1),
+                                  np.stack([heads[(0, h)].v_hat() for h in range(2)], axis=1), 3000)
+    for o in outs:
+        assert rel_l2(o[0], ref).max() <= TOL
