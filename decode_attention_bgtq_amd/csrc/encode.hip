@@ -33,14 +33,27 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   const int64_t tix = tile_at(map, b, kvh, tile);
   if (tix < 0) return;  // a paged table entry outside the pool: nothing is written (uniform per workgroup)
 
-  for (int idx = tid; idx < kTile * kHeadDim; idx += 256) {
-    const int t = idx >> 7, c = idx & 127;
-    float v = 0.f;
-    if (t >= lo && t < hi) {
-      const int64_t row = (int64_t)b * n_new + (tok0 + t - t0);
-      v = h2f(x[((size_t)row * hkv + kvh) * kHeadDim + c]);
+  // the tile's rows into LDS as floats (zero outside [lo, hi)): 16-byte loads,
+  // all issued before the first use (rows outside the range re-read row lo)
+  constexpr int kChunks = kTile * kHeadDim / 8 / 256;  // 16-byte chunks per thread
+  uint4 xv[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int idx = tid + 256 * j, t = idx >> 4, c8 = idx & 15;
+    const int tt = (t >= lo && t < hi) ? t : lo;
+    const int64_t row = (int64_t)b * n_new + (tok0 + tt - t0);
+    xv[j] = *(const uint4 *)(x + ((size_t)row * hkv + kvh) * kHeadDim + 8 * c8);
+  }
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int idx = tid + 256 * j, t = idx >> 4, c8 = idx & 15;
+    const bool in = t >= lo && t < hi;
+    const uint32_t w4[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xs[t][8 * c8 + 2 * e] = in ? h2f((uint16_t)(w4[e] & 0xFFFFu)) : 0.f;
+      xs[t][8 * c8 + 2 * e + 1] = in ? h2f((uint16_t)(w4[e] >> 16)) : 0.f;
     }
-    xs[t][c] = v;
   }
   if (tid < kTile * 4) nrm16[tid >> 2][tid & 3] = 0;
   __syncthreads();
@@ -209,6 +222,7 @@ bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_cons
     return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
   if (batch < 1 || n_new < 0 || capacity < 0) return fail(BGTQ_EINVAL, std::string(nm) + ": bad batch or count");
   if (t0 < 0 || t0 + n_new > capacity) return fail(BGTQ_ECAPACITY, std::string(nm) + ": tokens beyond capacity");
+  if ((uintptr_t)x & 15) return fail(BGTQ_EINVAL, std::string(nm) + ": k / v must be 16-byte aligned");
   if (n_new == 0 || no_codes) return BGTQ_OK;  // zero-bit keys: the caller's zero norms stand
   const TileMap map = pages ? paged_map(plan->p, pages) : contiguous_map(plan->p.desc.n_kv_heads, capacity);
   const int64_t first = t0 / kTile, last = (t0 + n_new - 1) / kTile;

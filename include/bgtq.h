@@ -151,14 +151,16 @@ bgtq_status bgtq_plan_upload(const bgtq_plan *plan, void *dev_consts, bgtq_strea
  * correctly rounded sqrt), y = Pi x_g / n (0 if n = 0), z = sqrt(d_g) y,
  * code_i = #{Lloyd-Max thresholds < z_i}; the norm is stored as fp16 with one
  * round-to-nearest-even step.  Keys use the plan's widths (groups in width
- * order 4,3,2,1, each block's coordinates j, j+64 adjacent, blocks
- * ascending); values one group of all 128 coordinates at v_bits.
- *   k / v      device fp16 [batch][n_new][n_kv_heads][128], post-RoPE keys
+ * order 4,3,2,1, each block's two coordinates adjacent (j, j+64 or 2j, 2j+1
+ * by the plan's rope_pairing), blocks ascending); values one group of all 128
+ * coordinates at v_bits.
+ *   k / v      device fp16 [batch][n_new][n_kv_heads][128], post-RoPE keys,
+ *              16-byte aligned
  *   capacity   tokens per sequence the cache arrays were sized for
  *   k_codes... device arrays laid out as in bgtq_sizes
  * Tokens outside [t0, t0+n_new) are left unchanged.
- * Errors: EINVAL (null, batch < 1, n_new < 0), ECAPACITY (t0 < 0 or
- * t0 + n_new > capacity).
+ * Errors: EINVAL (null, batch < 1, n_new < 0, k / v not 16-byte aligned),
+ * ECAPACITY (t0 < 0 or t0 + n_new > capacity).
  */
 bgtq_status bgtq_encode_k(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k,
                           int32_t batch, int64_t capacity, int64_t t0, int64_t n_new,
