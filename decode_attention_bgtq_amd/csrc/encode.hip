@@ -10,8 +10,9 @@
 namespace bgtq {
 
 // Prefill path: one workgroup per (tile, KV head, sequence), every token of the
-// tile at once.  fp64 rotation with a 4 x 8 register tile per thread (rows x
-// tokens).
+// tile and every group at once: exact group norms (four threads per token),
+// then the fp64 rotation and the quantiser with a 4 x 8 register tile per work
+// item (rows x tokens), the work items of all groups spread over the threads.
 template <bool IS_V>
 __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__ consts,
                                                      const uint16_t *__restrict__ x, const TileMap map,
@@ -20,8 +21,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
                                                      uint16_t *__restrict__ norms) {
   __shared__ float xs[kTile][kHeadDim + 1];
   __shared__ uint8_t cs[kTile][kHeadDim];
-  __shared__ double nrm[kTile];
+  __shared__ double nrm[kMaxGroups][kTile];
   __shared__ uint16_t nrm16[kTile][4];
+  __shared__ int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
   const ConstHeader *hd = hdr_of(consts);
   const int hkv = hd->n_kv_heads;
   const int64_t tile = t0 / kTile + blockIdx.x;
@@ -56,67 +58,111 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
     }
   }
   if (tid < kTile * 4) nrm16[tid >> 2][tid & 3] = 0;
+  if (!IS_V && tid < kHeadDim) cds[tid] = kd->coord[tid];
   __syncthreads();
 
+  // ---- the groups (keys: up to four, in width order; values: one of 128)
   const int n_groups = IS_V ? 1 : kd->n_groups;
-  for (int gi = 0; gi < n_groups; ++gi) {
-    const int w = IS_V ? hd->v_bits : kd->g[gi].w;
-    const int d = IS_V ? kHeadDim : kd->g[gi].d;
-    const int pos = IS_V ? 0 : kd->g[gi].pos;
-    const double *pt = IS_V ? (const double *)(consts + hd->off_rot64_v) + (size_t)kvh * kHeadDim * kHeadDim
-                            : (const double *)(consts + hd->off_rot64_k) + kd->g[gi].rot64;
-    if (tid < kTile) {
-      u128 s = 0;
-      for (int k = 0; k < d; ++k) {
-        const int c = IS_V ? k : kd->coord[pos + k];
-        const double a = fabs((double)xs[tid][c]) * 16777216.0;
-        const uint64_t u = (uint64_t)a;
-        s += (u128)u * u;
+  int gw[kMaxGroups], gd[kMaxGroups], gpos[kMaxGroups], gpre[kMaxGroups];
+  const double *gpt[kMaxGroups];
+  int total_rb = 0;  // row blocks of four over every group
+#pragma unroll
+  for (int gi = 0; gi < kMaxGroups; ++gi) {
+    const bool on = gi < n_groups;
+    gw[gi] = !on ? 1 : IS_V ? hd->v_bits : kd->g[gi].w;
+    gd[gi] = !on ? 0 : IS_V ? kHeadDim : kd->g[gi].d;
+    gpos[gi] = !on ? 0 : IS_V ? 0 : kd->g[gi].pos;
+    gpt[gi] = IS_V ? (const double *)(consts + hd->off_rot64_v) + (size_t)kvh * kHeadDim * kHeadDim
+                   : (const double *)(consts + hd->off_rot64_k) + (on ? kd->g[gi].rot64 : 0);
+    gpre[gi] = total_rb;
+    total_rb += (gd[gi] + 3) / 4;
+  }
+
+  // ---- group norms, exact: |x| 2^24 = h 2^20 + l with h, l < 2^20 integers
+  // (h = floor(|x| 16), l = its fraction times 2^20, both exact in fp32), so
+  // x^2 2^48 = h^2 2^40 + 2 h l 2^20 + l^2; the three sums are 64-bit
+  // integers.  Four threads per token, each every fourth coordinate, then the
+  // total rounded once to double.
+  {
+    const int t = tid >> 2, q = tid & 3;
+#pragma unroll
+    for (int gi = 0; gi < kMaxGroups; ++gi) {
+      if (gi >= n_groups) break;
+      unsigned long long A = 0, B = 0, C = 0;
+      for (int k = q; k < gd[gi]; k += 4) {
+        const int c = IS_V ? k : cds[gpos[gi] + k];
+        const float f = fabsf(xs[t][c]) * 16.f;
+        const uint32_t h = (uint32_t)f;
+        const uint32_t l = (uint32_t)((f - (float)h) * 1048576.f);
+        A += (unsigned long long)h * h;
+        B += (unsigned long long)h * l;
+        C += (unsigned long long)l * l;
       }
-      const double nn = sqrt(ldexp(u128_to_f64(s), -48));
-      nrm[tid] = nn;
-      nrm16[tid][IS_V ? 0 : 4 - w] = f64_to_f16(nn);
+      A += __shfl_xor(A, 1);
+      B += __shfl_xor(B, 1);
+      C += __shfl_xor(C, 1);
+      A += __shfl_xor(A, 2);
+      B += __shfl_xor(B, 2);
+      C += __shfl_xor(C, 2);
+      if (q == 0) {
+        const u128 ss = ((u128)A << 40) + ((u128)B << 21) + (u128)C;
+        const double nn = sqrt(ldexp(u128_to_f64(ss), -48));
+        nrm[gi][t] = nn;
+        nrm16[t][IS_V ? 0 : 4 - gw[gi]] = f64_to_f16(nn);
+      }
     }
-    __syncthreads();
-    const int rb = tid & 31, tb = tid >> 5;
-    const int i0 = rb * 4, u0 = tb * 8;
-    if (i0 < d) {
-      double acc[4][8];
+  }
+  __syncthreads();
+
+  // ---- rotation and quantiser, every group at once: work item = (row block of
+  // four rows of a group, block of eight tokens), a 4 x 8 register tile each
+  const auto sel = [](const int (&a)[kMaxGroups], int gi) {
+    return gi == 0 ? a[0] : gi == 1 ? a[1] : gi == 2 ? a[2] : a[3];
+  };
+  for (int item = tid; item < total_rb * 8; item += 256) {
+    const int grb = item >> 3, tb = item & 7;
+    int gi = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int jg = 1; jg < kMaxGroups; ++jg) gi += (jg < n_groups && grb >= gpre[jg]) ? 1 : 0;
+    const int w = sel(gw, gi), d = sel(gd, gi), pos = sel(gpos, gi);
+    const double *pt = gi == 0 ? gpt[0] : gi == 1 ? gpt[1] : gi == 2 ? gpt[2] : gpt[3];
+    const int i0 = 4 * (grb - sel(gpre, gi)), u0 = 8 * tb;
+    double acc[4][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[r][u] = 0.0;
-      for (int k = 0; k < d; ++k) {
-        const int c = IS_V ? k : kd->coord[pos + k];
-        double p[4];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = (i0 + r < d) ? pt[(size_t)k * d + i0 + r] : 0.0;
+      for (int u = 0; u < 8; ++u) acc[r][u] = 0.0;
+#pragma unroll 4
+    for (int k = 0; k < d; ++k) {
+      const int c = IS_V ? k : cds[pos + k];
+      double pr[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const double xv = (double)xs[u0 + u][c];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r][u] = fma(p[r], xv, acc[r][u]);
-        }
-      }
-      const int nthr = (1 << w) - 1;
-      const double *thr = hd->thr[w - 1];
-      const double sd = sqrt((double)d);
+      for (int r = 0; r < 4; ++r) pr[r] = (i0 + r < d) ? pt[(size_t)k * d + i0 + r] : 0.0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const double nn = nrm[u0 + u];
+        const double xv = (double)xs[u0 + u][c];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (i0 + r >= d) continue;
-          const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
-          const double z = sd * y;
-          int code = 0;
-          for (int kk = 0; kk < nthr; ++kk) code += thr[kk] < z ? 1 : 0;
-          cs[u0 + u][pos + i0 + r] = (uint8_t)code;
-        }
+        for (int r = 0; r < 4; ++r) acc[r][u] = fma(pr[r], xv, acc[r][u]);
       }
     }
-    __syncthreads();
+    const int nthr = (1 << w) - 1;
+    const double *thr = hd->thr[w - 1];
+    const double sd = sqrt((double)d);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double nn = nrm[gi][u0 + u];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (i0 + r >= d) continue;
+        const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
+        const double z = sd * y;
+        int code = 0;
+        for (int kk = 0; kk < nthr; ++kk) code += thr[kk] < z ? 1 : 0;
+        cs[u0 + u][pos + i0 + r] = (uint8_t)code;
+      }
+    }
   }
+  __syncthreads();
 
   const size_t base = (size_t)tix;
   if (!IS_V) {
