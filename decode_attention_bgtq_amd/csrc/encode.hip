@@ -166,27 +166,33 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
 
   const size_t base = (size_t)tix;
   if (!IS_V) {
+    // key words: work item (token t, word wi), lanes = tokens; word wi holds the
+    // stream bits [32 wi, 32 wi + 32): the codes of every group that overlap them
     const int wk = hd->wk;
-    if (tid >= lo && tid < hi) {
-      uint64_t accb = 0;
-      int nb = 0, word = 0;
-      for (int gi = 0; gi < kd->n_groups; ++gi) {
-        const int w = kd->g[gi].w, d = kd->g[gi].d, pos = kd->g[gi].pos;
-        for (int i = 0; i < d; ++i) {
-          accb |= (uint64_t)cs[tid][pos + i] << nb;
-          nb += w;
-          if (nb >= 32) {
-            codes[(base * wk + word) * kTile + tid] = (uint32_t)accb;
-            ++word;
-            accb >>= 32;
-            nb -= 32;
-          }
+    int gbo[kMaxGroups];
+#pragma unroll
+    for (int gi = 0; gi < kMaxGroups; ++gi) gbo[gi] = gi < n_groups ? kd->g[gi].bit_off : 0;
+    for (int item = tid; item < kTile * wk; item += 256) {
+      const int t = item & (kTile - 1), wi = item >> 6;
+      if (t < lo || t >= hi) continue;
+      const int b0 = 32 * wi;
+      uint64_t val = 0;
+#pragma unroll
+      for (int gi = 0; gi < kMaxGroups; ++gi) {
+        if (gi >= n_groups) break;
+        const int w = gw[gi], bo = gbo[gi], e = bo + gd[gi] * w;
+        if (e <= b0 || bo >= b0 + 32) continue;
+        const int k0 = bo >= b0 ? 0 : (b0 - bo) / w;
+        const int k1 = min(gd[gi], (b0 + 32 - bo + w - 1) / w);
+        for (int k = k0; k < k1; ++k) {
+          const int off = bo + k * w - b0;  // may be negative for a code straddling the word start
+          const uint64_t cv = cs[t][gpos[gi] + k];
+          val |= off >= 0 ? cv << off : cv >> (-off);
         }
       }
-      for (; word < wk; ++word) {  // only reached for an empty stream tail
-        codes[(base * wk + word) * kTile + tid] = (uint32_t)accb;
-        accb = 0;
-      }
+      codes[(base * wk + wi) * kTile + t] = (uint32_t)val;
+    }
+    if (tid >= lo && tid < hi) {
       uint2 nv;
       nv.x = (uint32_t)nrm16[tid][0] | ((uint32_t)nrm16[tid][1] << 16);
       nv.y = (uint32_t)nrm16[tid][2] | ((uint32_t)nrm16[tid][3] << 16);
