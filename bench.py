@@ -226,7 +226,7 @@ def main() -> int:
     plan_ms = (time.perf_counter() - tp) * 1e3
 
     # ---- prefill encode of the whole context (timed once more after a warm-up)
-    cap = t + 64
+    cap = t + max(64, cfg.append)
     cache = bg.Cache(plan, b, cap, device=dev)
     log("generating %d x %d tokens" % (b, t))
     ks = [synth.keys(cfg, seq=s, count=t) for s in range(b)]
@@ -245,6 +245,28 @@ def main() -> int:
     torch.cuda.synchronize()
     enc_k_s, enc_v_s = e0.elapsed_time(e1) / 1e3, e1.elapsed_time(e2) / 1e3
     token_heads = b * t * hkv
+    # ---- the workload's append (new tokens at positions T ..), encoded into the same cache
+    append_rec = None
+    if cfg.append > 0:
+        ka = to_dev(np.stack([synth.keys(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
+        va = to_dev(np.stack([synth.values(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
+        plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
+        plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
+        torch.cuda.synchronize()
+        a0, a1, a2 = ev(), ev(), ev()
+        a0.record()
+        plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
+        a1.record()
+        plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
+        a2.record()
+        torch.cuda.synchronize()
+        ak, av = a0.elapsed_time(a1) / 1e3, a1.elapsed_time(a2) / 1e3
+        ath = b * cfg.append * hkv
+        append_rec = {"tokens": cfg.append, "at": t, "k_and_v": round(ath / (ak + av)), "k": round(ath / ak),
+                      "v": round(ath / av), "us": round((ak + av) * 1e6, 2)}
+        log("append of %d tokens at %d: %.1f us (%.0f M token-heads/s)" % (cfg.append, t, (ak + av) * 1e6,
+                                                                           ath / (ak + av) / 1e6))
+        del ka, va
 
     # ---- the appended token and the query (position T)
     cfg1 = dataclasses.replace(cfg, append=1)
@@ -424,6 +446,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": STREAM_KERNEL, "kernel_ms": round(kern_ms, 5)},
+        "append_token_heads_per_s": append_rec,
         "encode_token_heads_per_s": {"k_and_v": round(token_heads / (enc_k_s + enc_v_s)),
                                      "k": round(token_heads / enc_k_s), "v": round(token_heads / enc_v_s),
                                      "tokens": b * t},

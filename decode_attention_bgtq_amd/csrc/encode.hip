@@ -135,9 +135,14 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
 #pragma unroll 4
     for (int k = 0; k < d; ++k) {
       const int c = IS_V ? k : cds[pos + k];
+      // unconditional loads (rows past d re-read row d - 1 and are zeroed), so
+      // that the loads of the unrolled iterations are issued together
       double pr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = (i0 + r < d) ? pt[(size_t)k * d + i0 + r] : 0.0;
+      for (int r = 0; r < 4; ++r) {
+        const double pv = pt[(size_t)k * d + min(i0 + r, d - 1)];
+        pr[r] = i0 + r < d ? pv : 0.0;
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const double xv = (double)xs[u0 + u][c];
