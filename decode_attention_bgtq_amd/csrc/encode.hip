@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   __shared__ double nrm[kMaxGroups][kTile];
   __shared__ uint16_t nrm16[kTile][4];
   __shared__ int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
+  __shared__ double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
   const ConstHeader *hd = hdr_of(consts);
   const int hkv = hd->n_kv_heads;
   const int64_t tile = t0 / kTile + blockIdx.x;
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   }
   if (tid < kTile * 4) nrm16[tid >> 2][tid & 3] = 0;
   if (!IS_V && tid < kHeadDim) cds[tid] = kd->coord[tid];
+  if (!IS_V && tid < 64) thr_s[tid >> 4][tid & 15] = hd->thr[tid >> 4][tid & 15];
   __syncthreads();
 
   // ---- the groups (keys: up to four, in width order; values: one of 128)
@@ -150,8 +152,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
         for (int r = 0; r < 4; ++r) acc[r][u] = fma(pr[r], xv, acc[r][u]);
       }
     }
-    const int nthr = (1 << w) - 1;
-    const double *thr = hd->thr[w - 1];
+    // keys: a wave mixes groups of different widths, so the thresholds come from
+    // LDS by bisection; values: one width, the thresholds read through the
+    // scalar cache and counted
+    const double *thr = IS_V ? hd->thr[w - 1] : thr_s[w - 1];
     const double sd = sqrt((double)d);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -161,8 +165,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
         if (i0 + r >= d) continue;
         const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
         const double z = sd * y;
+        // code = #{k : thr[k] < z} over the ascending thresholds
         int code = 0;
-        for (int kk = 0; kk < nthr; ++kk) code += thr[kk] < z ? 1 : 0;
+        if constexpr (IS_V) {
+          for (int kk = 0; kk < (1 << w) - 1; ++kk) code += thr[kk] < z ? 1 : 0;
+        } else {
+          for (int step = 1 << (w - 1); step > 0; step >>= 1) code += thr[code + step - 1] < z ? step : 0;
+        }
         cs[u0 + u][pos + i0 + r] = (uint8_t)code;
       }
     }

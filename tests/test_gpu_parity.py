@@ -314,3 +314,26 @@ def test_decode_invariant_to_split_count(bg):
                                   np.stack([heads[(0, h)].v_hat() for h in range(2)], axis=1), 3000)
     for o in outs:
         assert rel_l2(o[0], ref).max() <= TOL
+
+
+def test_decode_on_two_streams_shares_the_plan(bg):
+    """One plan and constant image used by decode calls on two streams at once (separate
+    workspaces and outputs) gives the same outputs as the calls one after the other."""
+    import torch
+    cfg = synth.small(3, seq_len=2000)
+    plan, cache, bits, ks, vs, heads = _encode_case(bg, cfg, 2000)
+    q = to_dev(synth.query(cfg)[None])
+    lens = to_dev(np.array([2000], np.int32))
+    serial = decode_gpu(plan, cache, synth.query(cfg)[None], [2000], 2000)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty((1, cfg.n_q_heads, 128), dtype=torch.int16, device="cuda") for _ in streams]
+    wss = [torch.empty(plan.workspace_size(1, 2000), dtype=torch.uint8, device="cuda") for _ in streams]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for st, o, ws in zip(streams, outs, wss):
+            with torch.cuda.stream(st):
+                plan.decode_attn(cache.consts, q, cache.k_codes, cache.k_norms, cache.v_codes, cache.v_norms,
+                                 cache.capacity, lens, 2000, o, ws, stream=st)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.float16).astype(np.float64), serial)
