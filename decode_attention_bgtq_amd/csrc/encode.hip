@@ -116,63 +116,111 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   }
   __syncthreads();
 
-  // ---- rotation and quantiser, every group at once: work item = (row block of
-  // four rows of a group, block of eight tokens), a 4 x 8 register tile each
+  // ---- rotation and quantiser.  Keys, every group at once: work item = (row
+  // block of four rows of a group, block of eight tokens), a 4 x 8 register tile
+  // each.
   const auto sel = [](const int (&a)[kMaxGroups], int gi) {
     return gi == 0 ? a[0] : gi == 1 ? a[1] : gi == 2 ? a[2] : a[3];
   };
-  for (int item = tid; item < total_rb * 8; item += 256) {
-    const int grb = item >> 3, tb = item & 7;
-    int gi = 0;
+  if constexpr (IS_V) {
+    // values: Y = Pi X^T on the matrix cores (v_mfma_f64_16x16x4f64: A = 16
+    // rows x 4 columns of Pi in lane r + 16 k, B = 4 coordinates x 16 tokens in
+    // lane t + 16 k, D = rows lane / 16 + 4 e of token lane % 16, checked on the
+    // device); wave w takes row tiles 2w and 2w + 1 and the four token tiles
+    const double *pt = gpt[0];  // Pi^T [k][i]
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = lane >> 4;
+    typedef double d4v __attribute__((ext_vector_type(4)));
+    d4v acc[2][4];
 #pragma unroll
-    for (int jg = 1; jg < kMaxGroups; ++jg) gi += (jg < n_groups && grb >= gpre[jg]) ? 1 : 0;
-    const int w = sel(gw, gi), d = sel(gd, gi), pos = sel(gpos, gi);
-    const double *pt = gi == 0 ? gpt[0] : gi == 1 ? gpt[1] : gi == 2 ? gpt[2] : gpt[3];
-    const int i0 = 4 * (grb - sel(gpre, gi)), u0 = 8 * tb;
-    double acc[4][8];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int bt = 0; bt < 4; ++bt) acc[a][bt] = (d4v){0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int k0 = 0; k0 < kHeadDim; k0 += 4) {
+      const int k = k0 + lk;
+      double av[2], bv[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[r][u] = 0.0;
-#pragma unroll 4
-    for (int k = 0; k < d; ++k) {
-      const int c = IS_V ? k : cds[pos + k];
-      // unconditional loads (rows past d re-read row d - 1 and are zeroed), so
-      // that the loads of the unrolled iterations are issued together
-      double pr[4];
+      for (int a = 0; a < 2; ++a) av[a] = pt[(size_t)k * kHeadDim + 16 * (2 * wave + a) + lr];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const double pv = pt[(size_t)k * d + min(i0 + r, d - 1)];
-        pr[r] = i0 + r < d ? pv : 0.0;
-      }
+      for (int bt = 0; bt < 4; ++bt) bv[bt] = (double)xs[16 * bt + lr][k];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const double xv = (double)xs[u0 + u][c];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r][u] = fma(pr[r], xv, acc[r][u]);
-      }
+        for (int bt = 0; bt < 4; ++bt) acc[a][bt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[bt], acc[a][bt], 0, 0, 0);
     }
-    // keys: a wave mixes groups of different widths, so the thresholds come from
-    // LDS by bisection; values: one width, the thresholds read through the
-    // scalar cache and counted
-    const double *thr = IS_V ? hd->thr[w - 1] : thr_s[w - 1];
-    const double sd = sqrt((double)d);
+    const int w = gw[0];
+    const double *thr = hd->thr[w - 1];
+    const double sd = sqrt((double)kHeadDim);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const double nn = nrm[gi][u0 + u];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (i0 + r >= d) continue;
-        const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
-        const double z = sd * y;
-        // code = #{k : thr[k] < z} over the ascending thresholds
-        int code = 0;
-        if constexpr (IS_V) {
+      for (int bt = 0; bt < 4; ++bt) {
+        const int t = 16 * bt + lr;
+        const double nn = nrm[0][t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * (2 * wave + a) + lk + 4 * e;
+          const double y = nn > 0.0 ? acc[a][bt][e] / nn : 0.0;
+          const double z = sd * y;
+          int code = 0;
           for (int kk = 0; kk < (1 << w) - 1; ++kk) code += thr[kk] < z ? 1 : 0;
-        } else {
-          for (int step = 1 << (w - 1); step > 0; step >>= 1) code += thr[code + step - 1] < z ? step : 0;
+          cs[t][i] = (uint8_t)code;
         }
-        cs[u0 + u][pos + i0 + r] = (uint8_t)code;
+      }
+  } else {
+    for (int item = tid; item < total_rb * 8; item += 256) {
+      const int grb = item >> 3, tb = item & 7;
+      int gi = 0;
+  #pragma unroll
+      for (int jg = 1; jg < kMaxGroups; ++jg) gi += (jg < n_groups && grb >= gpre[jg]) ? 1 : 0;
+      const int w = sel(gw, gi), d = sel(gd, gi), pos = sel(gpos, gi);
+      const double *pt = gi == 0 ? gpt[0] : gi == 1 ? gpt[1] : gi == 2 ? gpt[2] : gpt[3];
+      const int i0 = 4 * (grb - sel(gpre, gi)), u0 = 8 * tb;
+      double acc[4][8];
+  #pragma unroll
+      for (int r = 0; r < 4; ++r)
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) acc[r][u] = 0.0;
+  #pragma unroll 4
+      for (int k = 0; k < d; ++k) {
+        const int c = IS_V ? k : cds[pos + k];
+        // unconditional loads (rows past d re-read row d - 1 and are zeroed), so
+        // that the loads of the unrolled iterations are issued together
+        double pr[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double pv = pt[(size_t)k * d + min(i0 + r, d - 1)];
+          pr[r] = i0 + r < d ? pv : 0.0;
+        }
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double xv = (double)xs[u0 + u][c];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r][u] = fma(pr[r], xv, acc[r][u]);
+        }
+      }
+      // keys: a wave mixes groups of different widths, so the thresholds come from
+      // LDS by bisection; values: one width, the thresholds read through the
+      // scalar cache and counted
+      const double *thr = IS_V ? hd->thr[w - 1] : thr_s[w - 1];
+      const double sd = sqrt((double)d);
+  #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double nn = nrm[gi][u0 + u];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (i0 + r >= d) continue;
+          const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
+          const double z = sd * y;
+          // code = #{k : thr[k] < z} over the ascending thresholds
+          int code = 0;
+          if constexpr (IS_V) {
+            for (int kk = 0; kk < (1 << w) - 1; ++kk) code += thr[kk] < z ? 1 : 0;
+          } else {
+            for (int step = 1 << (w - 1); step > 0; step >>= 1) code += thr[code + step - 1] < z ? step : 0;
+          }
+          cs[u0 + u][pos + i0 + r] = (uint8_t)code;
+        }
       }
     }
   }
