@@ -7,31 +7,59 @@
 
 namespace bgtq {
 
-// One workgroup per KV head: exact integer sums of squares per coordinate,
-// then per block over its two coordinates (j, j+64) half-split or (2j, 2j+1)
-// interleaved.
-__global__ __launch_bounds__(256) void energy_kernel(const uint16_t *__restrict__ q,
-                                                     const uint16_t *__restrict__ k, int64_t n,
-                                                     int hq, int hkv, int inter, double *__restrict__ energy) {
-  __shared__ u128 sq[256], sk[256];
-  const int kvh = blockIdx.x, tid = threadIdx.x, c = tid & 127, half = tid >> 7;
+// One workgroup of 1024 threads per KV head: thread (phase, coordinate) takes
+// the tokens t = phase (mod 8).  Sums of squares are exact: |x| 2^24 = u =
+// h 2^20 + l (h, l < 2^20), u^2 = h^2 2^40 + 2 h l 2^20 + l^2, the three sums in
+// 64-bit integers folded into 128-bit totals every kFold tokens; then per block
+// over its two coordinates (j, j+64) half-split or (2j, 2j+1) interleaved.
+constexpr int kEnergyThreads = 1024, kEnergyPhases = kEnergyThreads / kHeadDim, kFold = 4096;
+
+__device__ __forceinline__ void sq_split(uint64_t u, uint64_t &a, uint64_t &b, uint64_t &c) {
+  const uint64_t h = u >> 20, l = u & 0xFFFFFu;
+  a += h * h;
+  b += h * l;
+  c += l * l;
+}
+
+__device__ __forceinline__ u128 sq_fold(uint64_t &a, uint64_t &b, uint64_t &c) {
+  const u128 s = ((u128)a << 40) + ((u128)b << 21) + (u128)c;
+  a = b = c = 0;
+  return s;
+}
+
+__global__ __launch_bounds__(kEnergyThreads) void energy_kernel(const uint16_t *__restrict__ q,
+                                                                const uint16_t *__restrict__ k, int64_t n,
+                                                                int hq, int hkv, int inter,
+                                                                double *__restrict__ energy) {
+  __shared__ u128 sq[kEnergyThreads], sk[kEnergyThreads];
+  const int kvh = blockIdx.x, tid = threadIdx.x, c = tid & 127, ph = tid >> 7;
   const int G = hq / hkv;
   u128 aq = 0, ak = 0;
-  for (int64_t t = half; t < n; t += 2) {
-    for (int hh = 0; hh < G; ++hh) {
-      const uint64_t u = f16_mag_units(q[((size_t)t * hq + (size_t)kvh * G + hh) * kHeadDim + c]);
-      aq += (u128)u * u;
+  uint64_t qa = 0, qb = 0, qc = 0, ka = 0, kb = 0, kc = 0;
+  int cnt = 0;
+  for (int64_t t = ph; t < n; t += kEnergyPhases) {
+    const uint16_t *qt = q + ((size_t)t * hq + (size_t)kvh * G) * kHeadDim + c;
+    for (int hh = 0; hh < G; ++hh) sq_split(f16_mag_units(qt[(size_t)hh * kHeadDim]), qa, qb, qc);
+    sq_split(f16_mag_units(k[((size_t)t * hkv + kvh) * kHeadDim + c]), ka, kb, kc);
+    if (++cnt == kFold) {  // (at most kFold * G terms below 2^40 in each 64-bit sum)
+      aq += sq_fold(qa, qb, qc);
+      ak += sq_fold(ka, kb, kc);
+      cnt = 0;
     }
-    const uint64_t u = f16_mag_units(k[((size_t)t * hkv + kvh) * kHeadDim + c]);
-    ak += (u128)u * u;
   }
+  aq += sq_fold(qa, qb, qc);
+  ak += sq_fold(ka, kb, kc);
   sq[tid] = aq;
   sk[tid] = ak;
   __syncthreads();
   if (tid < kBlocks) {
     const int j = tid, a = inter ? 2 * j : j, b = inter ? 2 * j + 1 : j + kBlocks;
-    const u128 tq = sq[a] + sq[b] + sq[128 + a] + sq[128 + b];
-    const u128 tk = sk[a] + sk[b] + sk[128 + a] + sk[128 + b];
+    u128 tq = 0, tk = 0;
+#pragma unroll
+    for (int p = 0; p < kEnergyPhases; ++p) {
+      tq += sq[p * kHeadDim + a] + sq[p * kHeadDim + b];
+      tk += sk[p * kHeadDim + a] + sk[p * kHeadDim + b];
+    }
     const double eq = ldexp(u128_to_f64(tq), -48) / (double)(n * G);
     const double ek = ldexp(u128_to_f64(tk), -48) / (double)n;
     energy[(size_t)kvh * kBlocks + j] = eq * ek;
@@ -80,8 +108,10 @@ bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_
     return fail(BGTQ_EINVAL, "bgtq_energy: n_q_heads must be a positive multiple of n_kv_heads");
   if (rope_pairing != BGTQ_ROPE_HALF && rope_pairing != BGTQ_ROPE_INTERLEAVED)
     return fail(BGTQ_EINVAL, "bgtq_energy: rope_pairing must be BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED");
-  energy_kernel<<<n_kv_heads, 256, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
-                                                              rope_pairing, energy);
+  if (n_q_heads / n_kv_heads > 1024)
+    return fail(BGTQ_EINVAL, "bgtq_energy: at most 1024 query heads per KV head");
+  energy_kernel<<<n_kv_heads, kEnergyThreads, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
+                                                                         rope_pairing, energy);
   return launch_status("bgtq_energy");
 }
 
