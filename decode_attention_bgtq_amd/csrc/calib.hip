@@ -68,28 +68,35 @@ __global__ __launch_bounds__(kEnergyThreads) void energy_kernel(const uint16_t *
 
 // ============================================================ (2) allocation
 
-// One wave per KV head; lane j owns block j.
+// One wave per KV head; lane j owns block j.  The greedy's result is the top
+// avg * 64 of the marginal gains g[j][b] = E_j (D(b) - D(b + 1)), b < 4, in the
+// order (gain descending, block ascending, width ascending): each block's gains
+// are non-increasing in b, so the greedy takes them in that order, and a tie
+// between blocks goes to the lower block as in the greedy.  Each candidate's
+// rank in that order is counted against all 256; block j gets one bit per
+// candidate of rank < avg * 64.
 __global__ __launch_bounds__(64) void allocate_kernel(const double *__restrict__ energy, int avg,
-                                                      int8_t *__restrict__ bits, double dd0,
-                                                      double dd1, double dd2, double dd3) {
+                                                      int8_t *__restrict__ bits, double dd0, double dd1,
+                                                      double dd2, double dd3) {
+  __shared__ double gs[kBlocks * 4];
   const int kvh = blockIdx.x, lane = threadIdx.x;
   const double e = energy[(size_t)kvh * kBlocks + lane];
-  int b = 0;
-  for (int step = 0; step < avg * kBlocks; ++step) {
-    const double dd = b == 0 ? dd0 : b == 1 ? dd1 : b == 2 ? dd2 : dd3;
-    double bg = b < 4 ? e * dd : -1.0;
-    int bj = lane;
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double og = __shfl_xor(bg, off);
-      const int oj = __shfl_xor(bj, off);
-      if (og > bg || (og == bg && oj < bj)) {
-        bg = og;
-        bj = oj;
-      }
-    }
-    if (bj == lane) ++b;
+  const double g[4] = {e * dd0, e * dd1, e * dd2, e * dd3};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) gs[lane * 4 + b] = g[b];
+  __syncthreads();
+  int rank[4] = {0, 0, 0, 0};
+  for (int i = 0; i < kBlocks * 4; ++i) {
+    const double o = gs[i];
+    const int j2 = i >> 2, b2 = i & 3;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      rank[b] += (o > g[b] || (o == g[b] && (j2 < lane || (j2 == lane && b2 < b)))) ? 1 : 0;
   }
-  bits[(size_t)kvh * kBlocks + lane] = (int8_t)b;
+  int nb = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) nb += rank[b] < avg * kBlocks ? 1 : 0;
+  bits[(size_t)kvh * kBlocks + lane] = (int8_t)nb;
 }
 
 }  // namespace bgtq
