@@ -337,3 +337,87 @@ def test_decode_on_two_streams_shares_the_plan(bg):
     torch.cuda.synchronize()
     for o in outs:
         assert np.array_equal(o.cpu().numpy().view(np.float16).astype(np.float64), serial)
+
+
+def test_full_size_512k_with_append_sampled(bg):
+    """The 512K Qwen2.5-3B-shaped layer at full size, then its 4096-token append at position
+    524,288: sampled tiles (the appended ones included) bit-exact, and the decode over all
+    528,384 tokens of KV head 0's query heads within tolerance of the oracle."""
+    import torch
+    cfg = synth.CONFIGS[5]
+    t, app = cfg.seq_len, cfg.append
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = _energy_alloc(bg, q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    cache = bg.Cache(plan, 1, t + app, device="cuda")
+    log("512K: generate + encode + append")
+    k = synth.keys(cfg, count=t + app)
+    v = synth.values(cfg, count=t + app)
+    cache.encode(to_dev(k[None, :t]), to_dev(v[None, :t]), 0)
+    cache.encode(to_dev(k[None, t:]), to_dev(v[None, t:]), t)
+    q = synth.query(cfg, pos=t + app)[None]
+    got = decode_gpu(plan, cache, q, [t + app], t + app)
+    torch.cuda.synchronize()
+    from oracle import layout
+    rng = np.random.default_rng(1)
+    for h in range(cfg.n_kv_heads):
+        full = h == 0
+        if full:
+            idx = np.arange(t + app)
+        else:
+            tiles = np.concatenate([rng.choice(t // 64, 6, replace=False), [t // 64, (t + app) // 64 - 1]])
+            idx = (tiles[:, None] * 64 + np.arange(64)[None]).reshape(-1)
+        log("512K: oracle head %d (%s)" % (h, "full" if full else "8 tiles"))
+        ref = OracleHead(k[idx, h], v[idx, h], bits[h], cfg.v_bits, cfg.seed, 0, h)
+        kc, kn, vc, vn = gpu_arrays(cache, 0, h)
+        gk_codes, gk_norms = layout.unpack_k(kc, kn, bits[h], t + app)
+        gv_codes, gv_norms = layout.unpack_v(vc, vn, cfg.v_bits, t + app)
+        assert np.array_equal(gk_codes[idx], ref.kc) and np.array_equal(gk_norms[idx], ref.kn)
+        assert np.array_equal(gv_codes[idx], ref.vc) and np.array_equal(gv_norms[idx], ref.vn)
+        if full:
+            o = np.stack([oracle.softmax_attention(q[0, hh].astype(np.float64), ref.k_hat(), ref.v_hat(),
+                                                   1 / math.sqrt(128))
+                          for hh in range(cfg.group)])
+            r = rel_l2(got[0, :cfg.group], o)
+            log("512K: head 0 rel-L2 max %.3e" % r.max())
+            assert r.max() <= TOL
+
+
+def test_full_size_16x32k_sampled(bg):
+    """The batched 16 x 32K Llama-3.1-8B-shaped layer at full size: sampled tiles of every
+    sequence bit-exact, and the decode of sequences 0 and 15 (query heads of KV head 3) within
+    tolerance of the oracle over all 32,768 tokens."""
+    import torch
+    cfg = synth.CONFIGS[4]
+    t, nb = cfg.seq_len, cfg.batch
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = _energy_alloc(bg, q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    cache = bg.Cache(plan, nb, t, device="cuda")
+    log("16x32K: generate + encode")
+    ks = np.stack([synth.keys(cfg, seq=s, count=t) for s in range(nb)])
+    vs = np.stack([synth.values(cfg, seq=s, count=t) for s in range(nb)])
+    cache.encode(to_dev(ks), to_dev(vs), 0)
+    q = np.stack([synth.query(cfg, seq=s) for s in range(nb)])
+    got = decode_gpu(plan, cache, q, [t] * nb, t)
+    torch.cuda.synchronize()
+    from oracle import layout
+    rng = np.random.default_rng(2)
+    h = 3
+    for s in range(nb):
+        full = s in (0, nb - 1)
+        idx = np.arange(t) if full else (rng.choice(t // 64, 2, replace=False)[:, None] * 64
+                                         + np.arange(64)[None]).reshape(-1)
+        ref = OracleHead(ks[s, idx, h], vs[s, idx, h], bits[h], cfg.v_bits, cfg.seed, 0, h)
+        kc, kn, vc, vn = gpu_arrays(cache, s, h)
+        gk_codes, gk_norms = layout.unpack_k(kc, kn, bits[h], t)
+        gv_codes, gv_norms = layout.unpack_v(vc, vn, cfg.v_bits, t)
+        assert np.array_equal(gk_codes[idx], ref.kc) and np.array_equal(gk_norms[idx], ref.kn)
+        assert np.array_equal(gv_codes[idx], ref.vc) and np.array_equal(gv_norms[idx], ref.vn)
+        if full:
+            o = np.stack([oracle.softmax_attention(q[s, hh].astype(np.float64), ref.k_hat(), ref.v_hat(),
+                                                   1 / math.sqrt(128))
+                          for hh in range(h * cfg.group, (h + 1) * cfg.group)])
+            r = rel_l2(got[s, h * cfg.group:(h + 1) * cfg.group], o)
+            log("16x32K: sequence %d rel-L2 max %.3e" % (s, r.max()))
+            assert r.max() <= TOL
