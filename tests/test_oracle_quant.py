@@ -170,3 +170,99 @@ def test_v_layout_token_lane_bits():
     varr, _ = layout.pack_v(codes, np.zeros(64, np.uint16), 2, 1)
     assert varr[0, 5, 0] == 3 << 20
     assert varr[0, 127, 3] == 2 << 30
+
+
+@pytest.mark.parametrize("widths", [(4, 2), (3, 1)])
+def test_dequant_k_roundtrip_per_group_distortion(widths):
+    """dequant_k(encode_k(x)) over a two-group allocation (d_g = 64 each): every group's relative
+    error is within 5% of the codebook's D(b).  Each group's coordinates carry their own scale
+    (x 1 and x 1000), so a wrong norm slot, a wrong scatter of the group coordinates or an
+    un-rotation by Pi instead of Pi^T moves the error far outside the bound."""
+    rng = np.random.default_rng(6 + widths[0])
+    bits = np.zeros(64, np.int8)
+    perm = rng.permutation(64)
+    bits[perm[:32]], bits[perm[32:]] = widths
+    n = 40000
+    x = rng.normal(0, 1, (n, 128))
+    groups = oracle.groups_for(bits)
+    x[:, groups[1][1]] *= 1000.0
+    x16 = x.astype(np.float16)
+    codes, slots = oracle.encode_k(x16, bits, 3, 1, 2)
+    xh = oracle.dequant_k(codes, slots, bits, 3, 1, 2)
+    xf = x16.astype(np.float64)
+    dist = oracle.distortion_table()
+    for w, coords in groups:
+        e = np.mean(np.sum((xf[:, coords] - xh[:, coords]) ** 2, 1) / np.sum(xf[:, coords] ** 2, 1))
+        assert abs(e - dist[w]) / dist[w] < 0.05, (w, e, dist[w])
+    zero = np.setdiff1d(np.arange(128), np.concatenate([c for _, c in groups]))
+    assert zero.size == 0 or np.all(xh[:, zero] == 0.0)
+
+
+def test_dequant_k_four_groups_at_32():
+    """Four groups of 16 blocks (d_g = 32): each group's error is within 8% of D(b) (the N(0, 1/d)
+    codebook sits a few per cent off the exact marginal at d = 32), and the norms of the four
+    slots, scaled apart by powers of ten, each reconstruct their own group."""
+    rng = np.random.default_rng(5)
+    bits = np.zeros(64, np.int8)
+    perm = rng.permutation(64)
+    for i, w in enumerate((4, 3, 2, 1)):
+        bits[perm[16 * i:16 * (i + 1)]] = w
+    x = rng.normal(0, 1, (20000, 128))
+    groups = oracle.groups_for(bits)
+    for w, coords in groups:
+        x[:, coords] *= 10.0 ** (w - 1)
+    x16 = x.astype(np.float16)
+    codes, slots = oracle.encode_k(x16, bits, 0, 4, 1)
+    xh = oracle.dequant_k(codes, slots, bits, 0, 4, 1)
+    xf = x16.astype(np.float64)
+    dist = oracle.distortion_table()
+    for w, coords in groups:
+        e = np.mean(np.sum((xf[:, coords] - xh[:, coords]) ** 2, 1) / np.sum(xf[:, coords] ** 2, 1))
+        assert abs(e - dist[w]) / dist[w] < 0.08, (w, e, dist[w])
+
+
+def test_dequant_k_hand_worked_two_groups():
+    """Block 0 at 4 bits (coordinates 0, 64), blocks 1 and 2 at 2 bits (1, 65, 2, 66), the rest 0.
+    Rotations given explicitly: a 2 x 2 rotation Pi = [[0.6, -0.8], [0.8, 0.6]] for the 4-bit
+    group (x_hat = n Pi^T y_hat, not n Pi y_hat) and the identity for the 2-bit group.  Norm slots
+    4 - w: slot 0 = 2, slot 2 = 0.5; slots 1 and 3 hold 7 and 9 and must not be read."""
+    bits = np.zeros(64, np.int8)
+    bits[0] = 4
+    bits[[1, 2]] = 2
+    pi4 = np.array([[0.6, -0.8], [0.8, 0.6]])
+    rots = [pi4, np.eye(4)]
+    codes = np.array([[3, 12, 0, 3, 1, 2]], np.uint8)
+    slots = oracle.f16_bits(np.array([[2.0, 7.0, 0.5, 9.0]]))
+    got = oracle.dequant_k(codes, slots, bits, 0, 0, 0, rots=rots)
+    c4, c2 = oracle.lloyd_max(4)[0], oracle.lloyd_max(2)[0]
+    a, b = c4[3] / math.sqrt(2), c4[12] / math.sqrt(2)
+    want = np.zeros(128)
+    want[0], want[64] = 2.0 * (0.6 * a + 0.8 * b), 2.0 * (-0.8 * a + 0.6 * b)
+    want[[1, 65, 2, 66]] = 0.5 * c2[[0, 3, 1, 2]] / 2.0
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-15)
+    # the centroids used, against the printed 4-bit Lloyd-Max values (+-1.2562 for codes 3 and 12,
+    # +-0.4528 and +-1.5104 for the 2-bit codes)
+    assert abs(c4[3] + 1.2562) < 5e-4 and abs(c4[12] - 1.2562) < 5e-4
+    assert abs(c2[0] + 1.5104) < 5e-4 and abs(c2[1] + 0.4528) < 5e-4
+
+
+def test_k_layout_word_major_hand_placed():
+    """Key array [tile][word][lane]: token t's stream word k sits at [t // 64, k, t % 64]; its
+    norm slots at [t // 64, t % 64, slot].  Token 70 (tile 1, lane 6) with the 4-bit code 0xB at
+    stream position 0 (bits 0..3 of word 0) and the 2-bit code 2 at position 8, the first code after
+    the 32 bits of the 4-bit group (bits 0..1 of word 1); everything else 0."""
+    bits = np.full(64, 2, np.int8)
+    bits[:4] = 4
+    bits[4:8] = 0                           # 8 coordinates of 4 bits, 112 of 2 bits: 256 bits
+    assert oracle.k_words_per_token(bits) == 8
+    codes = np.zeros((100, 120), np.uint8)
+    codes[70, 0], codes[70, 8] = 0xB, 0x2
+    slots = np.zeros((100, 4), np.uint16)
+    slots[70] = [0x3C00, 0, 0x4000, 0]
+    karr, knrm = layout.pack_k(codes, slots, bits, 2)
+    assert karr[1, 0, 6] == 0xB and karr[1, 1, 6] == 0x2
+    karr[1, 0, 6] = karr[1, 1, 6] = 0
+    assert not karr.any()
+    np.testing.assert_array_equal(knrm[1, 6], [0x3C00, 0, 0x4000, 0])
+    knrm[1, 6] = 0
+    assert not knrm.any()

@@ -67,3 +67,21 @@ def test_haar_first_moment():
     d, n = 4, 1500
     vals = [oracle.rotation_for(s, 0, 0, 0, 1, d)[0, 0] ** 2 for s in range(n)]
     assert abs(np.mean(vals) - 1.0 / d) < 4 * np.std(vals) / math.sqrt(n)
+
+
+def test_box_muller_order_from_reference_outputs(golden_dir):
+    """The Gaussian fill, computed by hand from the published SplitMix64 outputs: pair k takes
+    u1 = out[2k] >> 11 * 2^-53 and u2 = out[2k+1] >> 11 * 2^-53, z0 = r cos(2 pi u2) goes to
+    element 2k and z1 = r sin(2 pi u2) to element 2k + 1 of the row-major matrix, with
+    r = sqrt(-2 ln(1 - u1)).  A swapped cos / sin, swapped u1 / u2 or a column-major fill fails."""
+    with open(os.path.join(golden_dir, "splitmix64.json")) as f:
+        g = json.load(f)
+    outs = [int(v) for v in g["outputs"]]
+    u = [(o >> 11) * 2.0 ** -53 for o in outs[:4]]
+    want = []
+    for k in range(2):
+        r = math.sqrt(-2.0 * math.log(1.0 - u[2 * k]))
+        want += [r * math.cos(2.0 * math.pi * u[2 * k + 1]), r * math.sin(2.0 * math.pi * u[2 * k + 1])]
+    z = gaussian_matrix(oracle.SplitMix64(g["state"]), 2)
+    np.testing.assert_allclose(z, np.array(want).reshape(2, 2), rtol=0, atol=1e-15)
+    assert z[0, 1] == want[1] and z[1, 0] == want[2]
