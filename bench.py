@@ -207,7 +207,7 @@ def main() -> int:
     e_dev = torch.empty((hkv, 64), dtype=torch.float64, device=dev)
     bits_dev = torch.empty((hkv, 64), dtype=torch.int8, device=dev)
     bg.energy(qc, kc, hkv, e_dev)
-    bg.allocate(e_dev, cfg.k_bits, bits_dev)
+    bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
     torch.cuda.synchronize()
     e0, e1, e2 = ev(), ev(), ev()
     e0.record()
@@ -215,12 +215,17 @@ def main() -> int:
         bg.energy(qc, kc, hkv, e_dev)
     e1.record()
     for _ in range(10):
-        bg.allocate(e_dev, cfg.k_bits, bits_dev)
+        bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
     e2.record()
     torch.cuda.synchronize()
     energy_us = e0.elapsed_time(e1) * 100.0
     alloc_us = e1.elapsed_time(e2) * 100.0
     bits = bits_dev.cpu().numpy()
+    e_host = e_dev.cpu().numpy()
+    th = time.perf_counter()
+    bits_host = bg.allocate(e_host, cfg.k_bits)
+    alloc_host_us = (time.perf_counter() - th) * 1e6
+    assert np.array_equal(bits_host, bits), "host and device allocations differ"
     tp = time.perf_counter()
     plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, hq, seed=cfg.seed, layer=0)
     plan_ms = (time.perf_counter() - tp) * 1e3
@@ -458,7 +463,8 @@ def main() -> int:
                           "packed_speedup": round(fp16_ms / step_ms, 3),
                           "compression": round(fp16_bytes / packed, 3)},
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "one_time": {"energy_us": round(energy_us, 2), "allocate_us": round(alloc_us, 2),
+        "one_time": {"energy_us": round(energy_us, 2), "allocate_device_us": round(alloc_us, 2),
+                     "allocate_host_us": round(alloc_host_us, 2),
                      "plan_host_ms": round(plan_ms, 2)},
     }
     if not args.no_cpu_baseline:

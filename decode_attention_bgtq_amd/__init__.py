@@ -22,7 +22,8 @@ HEAD_DIM = 128
 ROPE_PAIRINGS = {"half": 0, "interleaved": 1}  # half-split (j, j+64), interleaved (2j, 2j+1)
 
 EXPORTED = [
-    "bgtq_abi_version", "bgtq_last_error", "bgtq_energy", "bgtq_allocate", "bgtq_plan_create",
+    "bgtq_abi_version", "bgtq_last_error", "bgtq_energy", "bgtq_allocate", "bgtq_allocate_device",
+    "bgtq_plan_create",
     "bgtq_plan_destroy", "bgtq_plan_sizes", "bgtq_plan_upload", "bgtq_encode_k", "bgtq_encode_v",
     "bgtq_rotate_queries", "bgtq_decode_workspace_size", "bgtq_decode_attn", "bgtq_codebook",
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
@@ -75,7 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_abi_version": (I32, []),
         "bgtq_last_error": (ctypes.c_char_p, []),
         "bgtq_energy": (I32, [P, P, I64, I32, I32, I32, I32, P, P]),
-        "bgtq_allocate": (I32, [P, I32, I32, I32, P, P]),
+        "bgtq_allocate": (I32, [P, I32, I32, I32, P]),
+        "bgtq_allocate_device": (I32, [P, I32, I32, I32, P, P]),
         "bgtq_plan_create": (I32, [ctypes.POINTER(_PlanDesc), ctypes.POINTER(P)]),
         "bgtq_plan_destroy": (None, [P]),
         "bgtq_plan_sizes": (I32, [P, I32, I64, ctypes.POINTER(_Sizes)]),
@@ -116,6 +118,34 @@ def _check(status: int) -> None:
         raise BgtqError(status, load().bgtq_last_error().decode())
 
 
+def _need(t, name: str, *, elem: int | None = None, dtype=None, shape=None, device: bool = False) -> None:
+    """Check a tensor argument before its address crosses the ABI (the C side cannot tell a
+    strided view, a wrong element type or a host tensor from a valid device buffer).
+    ``shape`` is a tuple whose None entries match any size."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s (got %s)" % (name, dtype, t.dtype))
+    if elem is not None and t.element_size() != elem:
+        raise ValueError("%s must have %d-byte elements (got %d)" % (name, elem, t.element_size()))
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+            raise ValueError("%s must have shape %s (got %s)" % (
+                name, tuple("*" if s is None else s for s in shape), tuple(t.shape)))
+    if device and not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+
+
+def _gpu(**tensors) -> None:
+    """Every named tensor must be in GPU memory (checked after the layout checks)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be on the GPU" % name)
+
+
 def _ptr(t) -> int | None:
     """Device (or host numpy) address of a tensor/array; None passes NULL."""
     if t is None:
@@ -152,14 +182,35 @@ def _pairing(p) -> int:
 
 
 def energy(q_cal, k_cal, n_kv_heads: int, out, stream=None, pairing: str = "half") -> None:
+    import torch
+    _need(q_cal, "q_cal", elem=2, shape=(None, None, HEAD_DIM))
     n, hq, d = q_cal.shape
+    _need(k_cal, "k_cal", elem=2, shape=(n, n_kv_heads, HEAD_DIM))
+    _need(out, "energy", dtype=torch.float64, shape=(n_kv_heads, 64))
+    _gpu(q_cal=q_cal, k_cal=k_cal, energy=out)
     _check(load().bgtq_energy(_ptr(q_cal), _ptr(k_cal), n, hq, n_kv_heads, d, _pairing(pairing), _ptr(out),
                               _stream(stream)))
 
 
-def allocate(energy_t, avg_bits: int, out, stream=None) -> None:
+def allocate(energy_arr, avg_bits: int) -> np.ndarray:
+    """Host greedy allocation: float64 energies [Hkv, 64] (numpy or a CPU tensor) -> int8 widths."""
+    e = np.ascontiguousarray(np.asarray(energy_arr.cpu() if hasattr(energy_arr, "cpu") else energy_arr,
+                                        dtype=np.float64))
+    if e.ndim != 2:
+        raise ValueError("energies must be [n_kv_heads, 64]")
+    out = np.zeros(e.shape, np.int8)
+    _check(load().bgtq_allocate(e.ctypes.data, e.shape[0], e.shape[1], avg_bits, out.ctypes.data))
+    return out
+
+
+def allocate_device(energy_t, avg_bits: int, out, stream=None) -> None:
+    """Device allocation: energies already in device memory -> int8 widths in ``out``."""
+    import torch
+    _need(energy_t, "energy", dtype=torch.float64, shape=(None, 64))
     hkv, nb = energy_t.shape
-    _check(load().bgtq_allocate(_ptr(energy_t), hkv, nb, avg_bits, _ptr(out), _stream(stream)))
+    _need(out, "bits", elem=1, shape=(hkv, nb))
+    _gpu(energy=energy_t, bits=out)
+    _check(load().bgtq_allocate_device(_ptr(energy_t), hkv, nb, avg_bits, _ptr(out), _stream(stream)))
 
 
 @dataclasses.dataclass
@@ -229,17 +280,53 @@ class Plan:
         _check(load().bgtq_plan_bits(self._h, out.ctypes.data))
         return out
 
+    def _check_tokens(self, x, name: str) -> None:
+        _need(x, name, elem=2, shape=(None, None, self.n_kv_heads, HEAD_DIM))
+
+    def _check_cache(self, k_codes, k_norms, v_codes, v_norms) -> None:
+        if k_codes is not None:
+            _need(k_codes, "k_codes", elem=4)
+        _need(k_norms, "k_norms", elem=2)
+        _need(v_codes, "v_codes", elem=4)
+        _need(v_norms, "v_norms", elem=2)
+
+    def _check_decode(self, q, seq_lens, out, workspace, lens_name: str = "seq_lens") -> None:
+        import torch
+        _need(q, "q", elem=2, shape=(None, self.n_q_heads, HEAD_DIM))
+        _need(out, "out", elem=2, shape=tuple(q.shape))
+        _need(seq_lens, lens_name, dtype=torch.int32, shape=(q.shape[0],))
+        _need(workspace, "workspace")
+
+    def _check_new(self, q, k_new, v_new) -> None:
+        """The new token's key and value: [batch, Hkv, 128] or [batch, 1, Hkv, 128] (the same memory)."""
+        shape = (q.shape[0], 1, self.n_kv_heads, HEAD_DIM) if k_new.dim() == 4 else \
+            (q.shape[0], self.n_kv_heads, HEAD_DIM)
+        _need(k_new, "k_new", elem=2, shape=shape)
+        _need(v_new, "v_new", elem=2, shape=shape)
+
     def encode_k(self, consts, k, capacity: int, t0: int, k_codes, k_norms, stream=None) -> None:
+        self._check_tokens(k, "k")
+        _need(k_codes, "k_codes", elem=4)
+        _need(k_norms, "k_norms", elem=2)
+        _gpu(k=k, k_codes=k_codes, k_norms=k_norms)
         b, n = k.shape[0], k.shape[1]
         _check(load().bgtq_encode_k(self._h, _ptr(consts), _ptr(k), b, capacity, t0, n,
                                     _ptr(k_codes), _ptr(k_norms), _stream(stream)))
 
     def encode_v(self, consts, v, capacity: int, t0: int, v_codes, v_norms, stream=None) -> None:
+        self._check_tokens(v, "v")
+        _need(v_codes, "v_codes", elem=4)
+        _need(v_norms, "v_norms", elem=2)
+        _gpu(v=v, v_codes=v_codes, v_norms=v_norms)
         b, n = v.shape[0], v.shape[1]
         _check(load().bgtq_encode_v(self._h, _ptr(consts), _ptr(v), b, capacity, t0, n,
                                     _ptr(v_codes), _ptr(v_norms), _stream(stream)))
 
     def rotate_queries(self, consts, q, q_rot, stream=None) -> None:
+        import torch
+        _need(q, "q", elem=2, shape=(None, self.n_q_heads, HEAD_DIM))
+        _need(q_rot, "q_rot", dtype=torch.float32, shape=tuple(q.shape))
+        _gpu(q=q, q_rot=q_rot)
         _check(load().bgtq_rotate_queries(self._h, _ptr(consts), _ptr(q), q.shape[0], _ptr(q_rot),
                                           _stream(stream)))
 
@@ -253,6 +340,10 @@ class Plan:
                     stream=None) -> None:
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, seq_lens, out, workspace)
+        self._check_cache(k_codes, k_norms, v_codes, v_norms)
+        _gpu(q=q, seq_lens=seq_lens, out=out, workspace=workspace, k_codes=k_codes, k_norms=k_norms,
+             v_codes=v_codes, v_norms=v_norms)
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(load().bgtq_decode_attn(self._h, _ptr(consts), _ptr(q), _ptr(k_codes), _ptr(k_norms),
                                        _ptr(v_codes), _ptr(v_norms), capacity, _ptr(seq_lens), q.shape[0],
@@ -260,11 +351,15 @@ class Plan:
                                        _stream(stream)))
 
     def encode_k_paged(self, consts, k, pages: "PagedCache", t0: int, stream=None) -> None:
+        self._check_tokens(k, "k")
+        _gpu(k=k)
         pg = pages.desc()
         _check(load().bgtq_encode_k_paged(self._h, _ptr(consts), _ptr(k), k.shape[0], ctypes.byref(pg), t0,
                                           k.shape[1], _ptr(pages.k_codes), _ptr(pages.k_norms), _stream(stream)))
 
     def encode_v_paged(self, consts, v, pages: "PagedCache", t0: int, stream=None) -> None:
+        self._check_tokens(v, "v")
+        _gpu(v=v)
         pg = pages.desc()
         _check(load().bgtq_encode_v_paged(self._h, _ptr(consts), _ptr(v), v.shape[0], ctypes.byref(pg), t0,
                                           v.shape[1], _ptr(pages.v_codes), _ptr(pages.v_norms), _stream(stream)))
@@ -273,6 +368,8 @@ class Plan:
                           softmax_scale: float | None = None, stream=None) -> None:
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, seq_lens, out, workspace)
+        _gpu(q=q, seq_lens=seq_lens, out=out, workspace=workspace)
         pg = pages.desc()
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(load().bgtq_decode_attn_paged(
@@ -285,6 +382,9 @@ class Plan:
         """decode_step on a paged pool: k_new / v_new appended at token pos[b], then attention over pos[b] + 1."""
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, pos, out, workspace, "pos")
+        self._check_new(q, k_new, v_new)
+        _gpu(q=q, pos=pos, out=out, workspace=workspace, k_new=k_new, v_new=v_new)
         pg = pages.desc()
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(load().bgtq_decode_step_paged(
@@ -298,6 +398,10 @@ class Plan:
         """decode_attn with the fp16 sink and recent-window tokens of ``buf`` taken from fp16."""
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, seq_lens, out, workspace)
+        self._check_cache(k_codes, k_norms, v_codes, v_norms)
+        _gpu(q=q, seq_lens=seq_lens, out=out, workspace=workspace, k_codes=k_codes, k_norms=k_norms,
+             v_codes=v_codes, v_norms=v_norms)
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(load().bgtq_decode_attn_buffered(
             self._h, _ptr(consts), _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), capacity,
@@ -310,6 +414,11 @@ class Plan:
         """Append k_new / v_new at token pos[b] of each sequence, then attend q over pos[b] + 1 tokens."""
         if softmax_scale is None:
             softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, pos, out, workspace, "pos")
+        self._check_cache(k_codes, k_norms, v_codes, v_norms)
+        self._check_new(q, k_new, v_new)
+        _gpu(q=q, pos=pos, out=out, workspace=workspace, k_codes=k_codes, k_norms=k_norms, v_codes=v_codes,
+             v_norms=v_norms, k_new=k_new, v_new=v_new)
         ws_bytes = workspace.numel() * workspace.element_size()
         _check(load().bgtq_decode_step(self._h, _ptr(consts), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos),
                                        q.shape[0], max_seq_len, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
@@ -328,8 +437,16 @@ def fp16_decode_attn(q, k, v, seq_lens, max_seq_len: int, out, workspace, softma
     """fp16 decode attention over an uncompressed cache k, v [batch][capacity][n_kv_heads][128] (the baseline)."""
     if softmax_scale is None:
         softmax_scale = HEAD_DIM ** -0.5
+    import torch
+    _need(q, "q", elem=2, shape=(None, None, HEAD_DIM))
     b, hq, _ = q.shape
+    _need(k, "k", elem=2, shape=(b, None, None, HEAD_DIM))
     _, cap, hkv, _ = k.shape
+    _need(v, "v", elem=2, shape=tuple(k.shape))
+    _need(out, "out", elem=2, shape=tuple(q.shape))
+    _need(seq_lens, "seq_lens", dtype=torch.int32, shape=(b,))
+    _need(workspace, "workspace")
+    _gpu(q=q, k=k, v=v, out=out, seq_lens=seq_lens, workspace=workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().bgtq_fp16_decode_attn(_ptr(q), _ptr(k), _ptr(v), b, hq, hkv, cap, _ptr(seq_lens), max_seq_len,
                                         softmax_scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -382,6 +499,9 @@ class Buffer:
 
     def append(self, k, v, t0: int, stream=None) -> None:
         """Copy new fp16 tokens k, v [batch][n_new][Hkv][128] (positions t0 ..) into the buffers."""
+        _need(k, "k", elem=2, shape=(self.batch, None, self.n_kv_heads, HEAD_DIM))
+        _need(v, "v", elem=2, shape=tuple(k.shape))
+        _gpu(k=k, v=v)
         b, n_new, hkv, _ = k.shape
         _check(load().bgtq_buffer_append(_ptr(k), _ptr(v), b, n_new, t0, hkv, _ptr(self.k_sink),
                                          _ptr(self.v_sink), self.n_sink, _ptr(self.k_recent),

@@ -2,6 +2,9 @@
 // energy and the greedy integer bit allocation ("RoPE-Aware Bit Allocation for
 // KV-Cache Quantization", Abstract; Block-GTQ README, introduction and
 // calibration paragraph).  Definitions: include/bgtq.h.
+#include <cmath>
+#include <cstring>
+
 #include "device.h"
 #include "host.h"
 
@@ -122,17 +125,53 @@ bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_
   return launch_status("bgtq_energy");
 }
 
+// The distortion drops D(b) - D(b + 1), b = 0..3, of the library's codebooks.
+static void distortion_drops(double dd[4]) {
+  double dist[5] = {1.0, 0, 0, 0, 0};
+  for (int b = 1; b <= 4; ++b) dist[b] = codebook(b).d;
+  for (int b = 0; b < 4; ++b) dd[b] = dist[b] - dist[b + 1];
+}
+
 bgtq_status bgtq_allocate(const double *energy, int32_t n_kv_heads, int32_t n_blocks, int32_t avg_bits,
-                          int8_t *bits, bgtq_stream stream) {
+                          int8_t *bits) {
   if (!energy || !bits) return fail(BGTQ_EINVAL, "bgtq_allocate: null pointer");
   if (n_blocks != kBlocks || n_kv_heads < 1) return fail(BGTQ_EINVAL, "bgtq_allocate: n_blocks must be 64");
   if (avg_bits < 0 || avg_bits > 4) return fail(BGTQ_EBUDGET, "bgtq_allocate: avg_bits must be 0..4");
-  double dist[5] = {1.0, 0, 0, 0, 0};
-  for (int b = 1; b <= 4; ++b) dist[b] = codebook(b).d;
-  allocate_kernel<<<n_kv_heads, 64, 0, (hipStream_t)stream>>>(energy, avg_bits, bits, dist[0] - dist[1],
-                                                               dist[1] - dist[2], dist[2] - dist[3],
-                                                               dist[3] - dist[4]);
-  return launch_status("bgtq_allocate");
+  for (int64_t i = 0; i < (int64_t)n_kv_heads * kBlocks; ++i)
+    if (!(energy[i] >= 0.0) || !std::isfinite(energy[i]))
+      return fail(BGTQ_EINVAL, "bgtq_allocate: energies must be finite and non-negative");
+  double dd[4];
+  distortion_drops(dd);
+  // The greedy as stated: from all zeros, avg_bits * 64 times one more bit to
+  // the block of largest gain E_j (D(b_j) - D(b_j + 1)) among blocks below 4
+  // bits, the lowest j on a tie.
+  for (int h = 0; h < n_kv_heads; ++h) {
+    const double *e = energy + (size_t)h * kBlocks;
+    int8_t b[kBlocks] = {};
+    for (int step = 0; step < avg_bits * kBlocks; ++step) {
+      int best = -1;
+      double gbest = 0.0;
+      for (int j = 0; j < kBlocks; ++j) {
+        if (b[j] >= 4) continue;
+        const double g = e[j] * dd[b[j]];
+        if (best < 0 || g > gbest) best = j, gbest = g;
+      }
+      ++b[best];
+    }
+    std::memcpy(bits + (size_t)h * kBlocks, b, kBlocks);
+  }
+  return BGTQ_OK;
+}
+
+bgtq_status bgtq_allocate_device(const double *energy, int32_t n_kv_heads, int32_t n_blocks, int32_t avg_bits,
+                                 int8_t *bits, bgtq_stream stream) {
+  if (!energy || !bits) return fail(BGTQ_EINVAL, "bgtq_allocate_device: null pointer");
+  if (n_blocks != kBlocks || n_kv_heads < 1) return fail(BGTQ_EINVAL, "bgtq_allocate_device: n_blocks must be 64");
+  if (avg_bits < 0 || avg_bits > 4) return fail(BGTQ_EBUDGET, "bgtq_allocate_device: avg_bits must be 0..4");
+  double dd[4];
+  distortion_drops(dd);
+  allocate_kernel<<<n_kv_heads, 64, 0, (hipStream_t)stream>>>(energy, avg_bits, bits, dd[0], dd[1], dd[2], dd[3]);
+  return launch_status("bgtq_allocate_device");
 }
 
 }  // extern "C"

@@ -36,7 +36,8 @@
 namespace bgtq {
 
 constexpr int64_t kMaxSeqLen = 0x7FFFFFFFLL - kTile;  // token positions of the decode fit 32 bits
-constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights within a tile stay below 2^8
+constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights between rescales stay below 2^8
+                                      // (less for value norms of 128 and above)
 
 
 // Waves per SIMD the register allocation aims at: four (two workgroups per CU,
@@ -513,15 +514,20 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   const float nv = h2f((uint16_t)r.nv);
   // ---- online softmax (log2 domain), rescaled lazily: the running maximum
   // moves (with the wave maximum, the rescale of the sums and the
-  // accumulators) only when a logit exceeds it by more than kRescaleSlack, so
-  // p = 2^(l - m) stays below 2^kRescaleSlack.  P' = p * value norm, fp16, to
-  // the wave's LDS rows [h][token].
+  // accumulators) only when a logit exceeds it by more than the token's
+  // slack, kRescaleSlack less dv = clamp(E - 21, 0, 8) for the exponent field
+  // E of the token's fp16 value norm.  Without a rescale p = 2^(l - m) stays
+  // below 2^(8 - dv), so P' = p * value norm stays below 2^15 (the norm is
+  // below 2^(E - 14)); after one, p <= 1 and P' <= the norm.  So the fp16
+  // operand P' is finite for every finite norm.  P' goes to the wave's LDS
+  // rows [h][token].
+  const float dv = (float)min(max((int)((r.nv >> 10) & 31u) - 21, 0), 8);
   float l[G];
   bool up = false;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     l[h] = valid ? fmaf(n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
-    up = up || l[h] > mth[h];
+    up = up || l[h] + dv > mth[h];
   }
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
     float mx[G];

@@ -45,7 +45,7 @@ enum {
   BGTQ_EWORKSPACE = -5  /* workspace smaller than the size query */
 };
 
-#define BGTQ_ABI_VERSION 2
+#define BGTQ_ABI_VERSION 3
 #define BGTQ_TILE 64 /* cache tokens per tile */
 
 /* RoPE pairing of the 128 head coordinates into 64 2-D frequency blocks (the
@@ -89,18 +89,39 @@ bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_
  * Widths start at 0; avg_bits * n_blocks times, the block with the largest
  * gain E[j] * (D(b_j) - D(b_j + 1)) among blocks with b_j < 4 gets one more
  * bit (ties: lowest j).  D(b) is the b-bit Lloyd-Max MSE of N(0,1), D(0) = 1.
- *   energy  device double [n_kv_heads][n_blocks]
- *   bits    device int8 [n_kv_heads][n_blocks], written (values 0..4)
- * Errors: EINVAL on null pointers or n_blocks != 64; EBUDGET unless
- * 0 <= avg_bits <= 4.
+ * Host call, synchronous and deterministic: the greedy itself, run on the
+ * caller's thread.
+ *   energy  host double [n_kv_heads][n_blocks], finite and >= 0
+ *   bits    host int8 [n_kv_heads][n_blocks], written (values 0..4)
+ * Errors: EINVAL on null pointers, n_blocks != 64, n_kv_heads < 1 or an
+ * energy that is negative or not finite; EBUDGET unless 0 <= avg_bits <= 4.
+ * Nothing is written on an error.
  */
 bgtq_status bgtq_allocate(const double *energy, int32_t n_kv_heads, int32_t n_blocks,
-                          int32_t avg_bits, int8_t *bits, bgtq_stream stream);
+                          int32_t avg_bits, int8_t *bits);
 
 /*
- * (3) Plan: everything the encoder and decoder need for one layer, fixed by
- * (widths, V width, seed, layer): Lloyd-Max codebooks b = 1..4 in double, one
- * seeded Haar rotation per (KV head, K width group) and per KV head for V
+ * (2b) The same allocation on the device, for energies that are already in
+ * device memory (the output of bgtq_energy): one wave per KV head takes the
+ * avg_bits * 64 largest marginal gains in the order (gain descending, block
+ * ascending, width ascending), which is the greedy's sequence of choices
+ * because each block's gains do not increase with its width.  The result is
+ * identical to bgtq_allocate's.
+ *   energy  device double [n_kv_heads][n_blocks], finite and >= 0 (not checked)
+ *   bits    device int8 [n_kv_heads][n_blocks], written
+ * Errors: as bgtq_allocate except the energy check (the host cannot read it).
+ */
+bgtq_status bgtq_allocate_device(const double *energy, int32_t n_kv_heads, int32_t n_blocks,
+                                 int32_t avg_bits, int8_t *bits, bgtq_stream stream);
+
+/*
+ * (3) Plan: everything the encoder and decoder need for one layer (Abstract:
+ * Block-GTQ sits on top of TurboQuant-MSE, with integer widths per RoPE block
+ * and KxVy budgets; README introduction: a per-(layer, KV head) allocation).
+ * The pages fix neither TurboQuant-MSE's rotation nor its codebook; the plan
+ * holds the readings taken.  Fixed by (widths, V width, seed, layer):
+ * Lloyd-Max codebooks b = 1..4 in double, one seeded Haar rotation per
+ * (KV head, K width group) and per KV head for V
  * (SplitMix64 stream absorbing seed, layer, kvh, tensor (K 0, V 1), width,
  * group size; Box-Muller; Householder QR with the sign of diag(R) taken
  * positive), the group maps, the bit offsets of the key stream and the
@@ -147,7 +168,11 @@ bgtq_status bgtq_plan_upload(const bgtq_plan *plan, void *dev_consts, bgtq_strea
 
 /*
  * (4) TurboQuant-MSE encode of n_new tokens at positions t0 .. t0+n_new-1 of
- * every sequence (prefill: t0 = 0; append: t0 = current length).  Per token,
+ * every sequence (prefill: t0 = 0; append: t0 = current length).  Abstract:
+ * keys are quantised block group by block group at the allocated widths on a
+ * TurboQuant-MSE encoder, values at a uniform width (the "V" of KxVy); the
+ * pages leave the encoder's steps open, and the ones below are the readings
+ * taken.  Per token,
  * KV head and width group: n = ||x_g|| (exact sum of squares, rounded once,
  * correctly rounded sqrt), y = Pi x_g / n (0 if n = 0), z = sqrt(d_g) y,
  * code_i = #{Lloyd-Max thresholds < z_i}; the norm is stored as fp16 with one
@@ -171,7 +196,10 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
                           uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
 
 /*
- * (5) Query rotation: for every query head h and present key width group g,
+ * (5) Query rotation (the fused decode's query side; Abstract: logits are
+ * sums over RoPE frequency blocks, and a TurboQuant-MSE code lives in its
+ * group's rotated space, so q is rotated once per key group instead of
+ * un-rotating every key): for every query head h and present key width group g,
  * q_rot[b][h][o_g + i] = sum_k Pi_g[i][k] q[b][h][coord_g[k]] (fp32, matrix
  * cores), o_g = sum of the sizes of the groups before g; entries past the
  * last group are 0.  This is the "rotate q once per group" step of the fused
@@ -195,7 +223,11 @@ bgtq_status bgtq_rotate_queries(const bgtq_plan *plan, const void *dev_consts, c
  * operands with fp32 accumulation for widths 1..3), keeps an online softmax
  * and accumulates the values in the rotated value space, one partial per
  * split of the sequence; the merge kernel combines the splits and un-rotates
- * once per head.  fp32 accumulation throughout.
+ * once per head.  fp32 accumulation throughout.  The value operand (softmax
+ * weight x fp16 value norm) is kept finite for every finite value norm (the
+ * running maximum is raised early for tokens whose norm is 128 or more); a
+ * value whose norm overflowed fp16 at encode (+inf) makes the output NaN, as
+ * its reconstruction is infinite.
  *   q           device fp16 [batch][n_q_heads][128]
  *   seq_lens    device int32 [batch]; each value is clamped to [0, max_seq_len];
  *               a sequence of length 0 yields a zero output
@@ -261,7 +293,9 @@ bgtq_status bgtq_buffer_append(const uint16_t *k, const uint16_t *v, int32_t bat
 /*
  * (6d) Paged packed cache (the paged-KV serving layout: the cache as a pool of
  * fixed-size pages and a per-sequence block table, so that sequences grow
- * without reallocation and share one pool).  A page is one 64-token tile of
+ * without reallocation and share one pool).  The pages name a packed-cache
+ * serving path (Abstract; README backend table) but no cache organisation;
+ * the paged form is the one serving engines use.  A page is one 64-token tile of
  * one KV head; the pool arrays are the per-tile blocks of (4) with the pages
  * in place of the tiles:
  *   k_codes  u32  [n_kv_heads][n_pages][4*k_avg_bits][64]
@@ -304,7 +338,10 @@ bgtq_status bgtq_decode_attn_paged(const bgtq_plan *plan, const void *dev_consts
 
 /*
  * (7) Decode step: appends one new key and value per sequence to the packed
- * cache and attends the new query over the cache including that token.  For
+ * cache and attends the new query over the cache including that token (the
+ * serving step of the packed-cache path, Abstract and README backend table:
+ * each generated token is encoded into the packed cache and the fused kernel
+ * attends over it).  For
  * each sequence b with 0 <= pos[b] < capacity, k_new[b] and v_new[b] are
  * encoded at token pos[b] exactly as bgtq_encode_k / bgtq_encode_v would
  * (sequences with pos[b] outside that range append nothing); then the output

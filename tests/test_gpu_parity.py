@@ -33,9 +33,11 @@ def _energy_alloc(bg, q_cal, k_cal, n_kv, avg, pairing="half"):
     e = torch.empty((n_kv, 64), dtype=torch.float64, device="cuda")
     bg.energy(to_dev(q_cal), to_dev(k_cal), n_kv, e, pairing=pairing)
     bits = torch.empty((n_kv, 64), dtype=torch.int8, device="cuda")
-    bg.allocate(e, avg, bits)
+    bg.allocate_device(e, avg, bits)
     torch.cuda.synchronize()
-    return e.cpu().numpy(), bits.cpu().numpy()
+    e_host, b_dev = e.cpu().numpy(), bits.cpu().numpy()
+    assert np.array_equal(bg.allocate(e_host, avg), b_dev)      # host greedy = device kernel
+    return e_host, b_dev
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
@@ -75,11 +77,12 @@ def test_allocation_budgets_and_uniform(bg):
     for avg in range(5):
         ed = torch.from_numpy(e).cuda()
         bits = torch.empty((5, 64), dtype=torch.int8, device="cuda")
-        bg.allocate(ed, avg, bits)
+        bg.allocate_device(ed, avg, bits)
         torch.cuda.synchronize()
         got = bits.cpu().numpy()
         ref = np.stack([oracle.greedy_allocate(e[h], avg, dist) for h in range(5)])
         assert np.array_equal(got, ref), avg
+        assert np.array_equal(bg.allocate(e, avg), ref), avg
         assert np.all(got[1] == avg)
 
 
@@ -421,3 +424,37 @@ def test_full_size_16x32k_sampled(bg):
             r = rel_l2(got[s, h * cfg.group:(h + 1) * cfg.group], o)
             log("16x32K: sequence %d rel-L2 max %.3e" % (s, r.max()))
             assert r.max() <= TOL
+
+
+@pytest.mark.parametrize("cid,vscale", [(3, 300.0), (2, 300.0), (3, 1e-3), (1, 3000.0)])
+def test_decode_value_norm_range(bg, cid, vscale):
+    """Value norms far from the synthetic ~11 (x300: ~3.4e3; x3000: ~3.4e4, near the top of fp16;
+    x1e-3: ~0.011) with keys whose scale grows along the sequence, so that the logits keep
+    rising and the running maximum is overtaken again and again.  The softmax-weight x
+    value-norm operand must stay finite and accurate: outputs within tolerance of the oracle."""
+    import torch
+    t = 3000
+    cfg = synth.small(cid, seq_len=t)
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    cache = bg.Cache(plan, 1, t, device="cuda")
+    ramp = np.linspace(0.25, 3.0, t)[:, None, None]
+    k = (synth.keys(cfg, count=t).astype(np.float64) * ramp).astype(np.float16)
+    v = (synth.values(cfg, count=t).astype(np.float64) * vscale).astype(np.float16)
+    assert np.all(np.isfinite(k)) and np.all(np.isfinite(v))
+    log("value norm range: config %d, value scale %g (norms up to %.3g)" %
+        (cid, vscale, float(np.linalg.norm(v.astype(np.float64), axis=-1).max())))
+    cache.encode(to_dev(k[None]), to_dev(v[None]), 0)
+    torch.cuda.synchronize()
+    q = synth.query(cfg)[None]
+    got = decode_gpu(plan, cache, q, [t], t)
+    assert np.all(np.isfinite(got))
+    kh = np.stack([OracleHead(k[:, h], v[:, h], bits[h], cfg.v_bits, cfg.seed, 0, h).k_hat()
+                   for h in range(cfg.n_kv_heads)], axis=1)
+    vh = np.stack([OracleHead(k[:, h], v[:, h], bits[h], cfg.v_bits, cfg.seed, 0, h).v_hat()
+                   for h in range(cfg.n_kv_heads)], axis=1)
+    ref = oracle.decode_attention(q[0], kh, vh, t)
+    r = rel_l2(got[0], ref)
+    log("value norm range: worst rel-L2 %.3e" % r.max())
+    assert r.max() <= TOL

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(bg):
 
 
 def test_abi_version(bg):
-    assert bg.abi_version() == 2
+    assert bg.abi_version() == 3
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
@@ -144,8 +144,8 @@ def test_device_calls_reject_bad_arguments_before_launch(bg):
     assert lib.bgtq_energy(1, 1, 10, 8, 3, 128, 0, 1, None) == bg.EINVAL      # 8 % 3
     assert lib.bgtq_energy(1, 1, 10, 8, 2, 64, 0, 1, None) == bg.EINVAL       # head_dim
     assert lib.bgtq_energy(1, 1, 10, 8, 2, 128, 2, 1, None) == bg.EINVAL      # pairing
-    assert lib.bgtq_allocate(1, 2, 64, 5, 1, None) == bg.EBUDGET
-    assert lib.bgtq_allocate(1, 2, 32, 2, 1, None) == bg.EINVAL
+    assert lib.bgtq_allocate_device(1, 2, 64, 5, 1, None) == bg.EBUDGET
+    assert lib.bgtq_allocate_device(1, 2, 32, 2, 1, None) == bg.EINVAL
     plan = bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6)
     h = plan.handle
     assert lib.bgtq_encode_k(h, 256, 256, 1, 100, 90, 20, 256, 256, None) == bg.ECAPACITY
@@ -161,3 +161,68 @@ def test_device_calls_reject_bad_arguments_before_launch(bg):
                                 None) == bg.EINVAL
     assert lib.bgtq_plan_upload(h, 255, None) == bg.EINVAL                  # misaligned
     assert lib.bgtq_codebook(0, None, None, None) == bg.EINVAL
+
+
+@pytest.mark.parametrize("avg", [0, 1, 2, 3, 4])
+def test_host_allocation_matches_oracle_greedy(bg, avg):
+    """bgtq_allocate (host, synchronous) gives the oracle's greedy widths bit for bit: random
+    log-normal energies, a row of equal energies (uniform widths), a row with zero-energy
+    blocks and a row of pairwise-equal energies (ties to the lowest block)."""
+    rng = np.random.default_rng(100 + avg)
+    e = np.exp(rng.normal(0, 2, (6, 64)))
+    e[1] = 1.0
+    e[2, :20] = 0.0
+    e[3] = np.repeat(np.exp(rng.normal(0, 1, 32)), 2)
+    e[4] = np.exp(rng.normal(0, 8, 64))                 # a wide range of scales
+    got = bg.allocate(e, avg)
+    dist = oracle.distortion_table()
+    ref = np.stack([oracle.greedy_allocate(r, avg, dist) for r in e])
+    np.testing.assert_array_equal(got, ref)
+    assert np.all(got[1] == avg) and np.all(got.sum(1) == 64 * avg)
+
+
+def test_host_allocation_rejects_bad_energies(bg):
+    lib = bg.load()
+    bits = np.full((2, 64), 7, np.int8)
+    for bad in (-1.0, np.nan, np.inf):
+        e = np.ones((2, 64))
+        e[1, 5] = bad
+        assert lib.bgtq_allocate(e.ctypes.data, 2, 64, 2, bits.ctypes.data) == bg.EINVAL
+        assert "finite" in lib.bgtq_last_error().decode()
+    assert np.all(bits == 7)                             # nothing written on an error
+    e = np.ones((2, 64))
+    assert lib.bgtq_allocate(e.ctypes.data, 2, 64, 5, bits.ctypes.data) == bg.EBUDGET
+    assert lib.bgtq_allocate(e.ctypes.data, 2, 32, 2, bits.ctypes.data) == bg.EINVAL
+    assert lib.bgtq_allocate(None, 2, 64, 2, bits.ctypes.data) == bg.EINVAL
+
+
+def test_binding_rejects_bad_tensors_before_the_call(bg):
+    """The binding checks layout, element type, shape and device before an address crosses the
+    ABI: a strided time slice, a wrong head count, a wrong dtype or a host tensor raise."""
+    import torch
+    plan = bg.Plan(_bits(3, 2), 2, 2, n_q_heads=6)
+    k = torch.zeros((2, 40, 3, 128), dtype=torch.float16)
+    codes = torch.zeros(16, dtype=torch.int32)
+    norms = torch.zeros(16, dtype=torch.int16)
+    with pytest.raises(ValueError, match="contiguous"):
+        plan.encode_k(codes, k[:, 5:20], 64, 0, codes, norms)
+    with pytest.raises(ValueError, match="shape"):
+        plan.encode_k(codes, torch.zeros((2, 40, 4, 128), dtype=torch.float16), 64, 0, codes, norms)
+    with pytest.raises(ValueError, match="2-byte"):
+        plan.encode_v(codes, k.float(), 64, 0, codes, norms)
+    with pytest.raises(ValueError, match="GPU"):
+        plan.encode_k(codes, k, 64, 0, codes, norms)
+    q = torch.zeros((2, 6, 128), dtype=torch.float16)
+    out = torch.zeros((2, 6, 128), dtype=torch.float16)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="int32"):
+        plan.decode_attn(codes, q, codes, norms, codes, norms, 64, torch.zeros(2, dtype=torch.int64), 64, out, ws)
+    with pytest.raises(ValueError, match="shape"):
+        plan.decode_attn(codes, q, codes, norms, codes, norms, 64, torch.zeros(3, dtype=torch.int32), 64, out, ws)
+    with pytest.raises(ValueError, match="shape"):
+        plan.decode_attn(codes, torch.zeros((2, 4, 128), dtype=torch.float16), codes, norms, codes, norms, 64,
+                         torch.zeros(2, dtype=torch.int32), 64, out, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        plan.decode_attn(codes, q, codes, norms, codes, norms, 64, torch.zeros(2, dtype=torch.int32), 64, out, ws)
+    with pytest.raises(ValueError, match="shape"):
+        bg.allocate_device(torch.zeros((3, 32), dtype=torch.float64), 2, torch.zeros((3, 32), dtype=torch.int8))
