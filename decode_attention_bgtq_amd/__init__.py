@@ -29,7 +29,7 @@ EXPORTED = [
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
-    "bgtq_decode_step_paged",
+    "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc",
 ]
 
 
@@ -104,6 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.c_float, P, P, SZ, P]),
         "bgtq_decode_step_paged": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, ctypes.POINTER(_Pages),
                                          ctypes.c_float, P, P, SZ, P]),
+        "bgtq_noalloc_scratch_bytes": (SZ, []),
+        "bgtq_decode_attn_noalloc": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -349,6 +351,22 @@ class Plan:
                                        _ptr(v_codes), _ptr(v_norms), capacity, _ptr(seq_lens), q.shape[0],
                                        max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
+
+    def decode_attn_noalloc(self, consts, q, k_codes, k_norms, v_codes, v_norms, capacity: int, seq_lens,
+                            max_seq_len: int, out, softmax_scale: float | None = None, stream=None) -> None:
+        """decode_attn with the split partials in the library's device scratch (no workspace; calls that
+        overlap on one device race)."""
+        import torch
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        _need(q, "q", elem=2, shape=(None, self.n_q_heads, HEAD_DIM))
+        _need(out, "out", elem=2, shape=tuple(q.shape))
+        _need(seq_lens, "seq_lens", dtype=torch.int32, shape=(q.shape[0],))
+        self._check_cache(k_codes, k_norms, v_codes, v_norms)
+        _gpu(q=q, seq_lens=seq_lens, out=out, k_codes=k_codes, k_norms=k_norms, v_codes=v_codes, v_norms=v_norms)
+        _check(load().bgtq_decode_attn_noalloc(self._h, _ptr(consts), _ptr(q), _ptr(k_codes), _ptr(k_norms),
+                                               _ptr(v_codes), _ptr(v_norms), capacity, _ptr(seq_lens), q.shape[0],
+                                               max_seq_len, softmax_scale, _ptr(out), _stream(stream)))
 
     def encode_k_paged(self, consts, k, pages: "PagedCache", t0: int, stream=None) -> None:
         self._check_tokens(k, "k")

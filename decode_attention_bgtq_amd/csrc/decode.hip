@@ -864,7 +864,7 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   {
     Prof &pr = prof();
     std::lock_guard<std::mutex> lk(pr.mu);
-    if (pr.on) {
+    if (pr.on && !(c.no_alloc && pr.pool.empty())) {
       if (!pr.pool.empty()) {
         e0 = pr.pool.back().first;
         e1 = pr.pool.back().second;
@@ -933,11 +933,67 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   return launch_status("decode (merge)");
 }
 
+// ------------------------------------------------------------------ no-allocation entry
+
+// Scratch of bgtq_decode_attn_noalloc: the split partials of the decode, in a
+// file-scope device array (each device that runs the library holds its own
+// copy until the process ends).  In host code `scratch` is a host-side
+// stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device (resolved on the device's
+// first call, with that device current).
+static bgtq_status scratch_address(void **out) {
+  static std::mutex mu;
+  static std::vector<void *> addr;  // by device ordinal
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(BGTQ_EDEVICE, "bgtq_decode_attn_noalloc: no device");
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(BGTQ_EDEVICE, std::string("bgtq_decode_attn_noalloc: scratch address: ") + hipGetErrorString(e));
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return BGTQ_OK;
+}
+
 }  // namespace bgtq
 
 using namespace bgtq;
 
 extern "C" {
+
+size_t bgtq_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+bgtq_status bgtq_decode_attn_noalloc(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                     const uint32_t *k_codes, const uint16_t *k_norms, const uint32_t *v_codes,
+                                     const uint16_t *v_norms, int64_t capacity, const int32_t *seq_lens,
+                                     int32_t batch, int64_t max_seq_len, float softmax_scale, uint16_t *out,
+                                     bgtq_stream stream) {
+  const char *nm = "bgtq_decode_attn_noalloc";
+  if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out ||
+      (!k_codes && plan->p.hdr.wk > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  if (batch < 1 || max_seq_len < 1) return fail(BGTQ_EINVAL, std::string(nm) + ": batch, max_seq_len >= 1");
+  if (decode_layout(plan->p, batch, max_seq_len).total > kNoAllocScratchBytes)
+    return fail(BGTQ_EWORKSPACE, std::string(nm) + ": the split partials exceed the 4 MiB scratch");
+  void *ws = nullptr;
+  const bgtq_status sa = scratch_address(&ws);
+  if (sa != BGTQ_OK) return sa;
+  const bgtq_status v =
+      decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, ws, kNoAllocScratchBytes, nm);
+  if (v != BGTQ_OK) return v;
+  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
+               softmax_scale, out, ws, stream};
+  c.no_alloc = true;
+  return decode_launch(plan->p, c);
+}
 
 bgtq_status bgtq_rotate_queries(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q, int32_t batch,
                                 float *q_rot, bgtq_stream stream) {

@@ -247,6 +247,27 @@ bgtq_status bgtq_decode_attn(const bgtq_plan *plan, const void *dev_consts, cons
                              bgtq_stream stream);
 
 /*
+ * (6n) bgtq_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a scratch array
+ * the library holds in device memory (bgtq_noalloc_scratch_bytes() bytes,
+ * 4 MiB, one per device, kept until the process ends); the call makes no HIP
+ * allocation of any kind.  Every call on a device shares that device's
+ * scratch, which needs no clearing (each call writes the partials it reads):
+ * calls that overlap on one device (other streams, other threads) race and
+ * must not be issued.  Results are identical to bgtq_decode_attn's.
+ * Arguments as bgtq_decode_attn without workspace and ws_bytes.
+ * Errors: as bgtq_decode_attn; EWORKSPACE when the partials
+ * (bgtq_decode_workspace_size) exceed the scratch.
+ */
+size_t bgtq_noalloc_scratch_bytes(void);
+bgtq_status bgtq_decode_attn_noalloc(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                     const uint32_t *k_codes, const uint16_t *k_norms,
+                                     const uint32_t *v_codes, const uint16_t *v_norms, int64_t capacity,
+                                     const int32_t *seq_lens, int32_t batch, int64_t max_seq_len,
+                                     float softmax_scale, uint16_t *out, bgtq_stream stream);
+
+/*
  * (6b) Decode attention with an fp16 sink and recent window: the Block-GTQ
  * README runs its AIME evaluation in two settings, without and with an fp16
  * buffer of 4 attention-sink tokens and a 128-token recent window.  Reading
