@@ -40,12 +40,13 @@ constexpr float kRescaleSlack = 8.f;  // log2 units: softmax weights between res
                                       // (less for value norms of 128 and above)
 
 
-// Waves per SIMD the register allocation aims at: four (two workgroups per CU,
-// at most 128 VGPRs) up to four query heads per KV head unless the key and
-// value words of two tiles take too many registers; two for eight heads.
+// Waves per SIMD the register allocation aims at: four (at most 128 VGPRs) up
+// to four query heads per KV head unless the key and value words of two tiles
+// and the query registers take too many registers; two for eight heads.
 template <int G, int VB, int WK>
 struct StreamOcc {
-  static constexpr bool four = G <= 4 && (WK + 2 * VB <= 18 || (WK == 16 && VB <= 2));
+  static constexpr bool four =
+      G <= 4 && (VB <= 2 ? WK + 2 * VB <= 16 : WK + 2 * VB <= (G <= 2 ? 14 : 10));
   static constexpr int v = four ? 4 : (G <= 4 ? 3 : 2);
 };
 
@@ -101,40 +102,53 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 
 // LDS layout of the decode kernel (bytes, fixed offsets that the compiler
 // folds into the LDS instruction offsets):
-//   [0, kDtabBytes)  decode tables of the plan: 4-bit centroid pairs (c4),
-//                    four fp16 centroids of a width-2 byte (t2) / width-1
-//                    nibble (t1), two of six width-3 bits (t3)
-//   [q4, +G 512)     4-bit group queries: G x 128 fp32, scaled, zero past d4
-//   [qr, ..)         k-step query operands of the width-1..3 groups (PrepOut)
-//   [rinv, ..)       per head: 1 / the power-of-two scale of its k-step operands
-//   [vlut, ..)       value table
+//   [0, 2560)        k-step tables of the plan: four fp16 centroids of a
+//                    width-2 byte (t2) / width-1 nibble (t1), two of six
+//                    width-3 bits (t3)
+//   [rep, +64 KB)    lookup rows: row e (256 bytes) holds, in its first 128
+//                    bytes, the value-table entry of index e once per lane
+//                    slot (16 slots of 8 bytes, or 32 of 4 bytes) and, in its
+//                    last 128 bytes, the 4-bit centroid pair of code byte e
+//                    once per lane slot (16 slots of 8 bytes).  Lane l reads
+//                    slot l mod 16 (32): the 16 (32) lanes that the LDS
+//                    serves together read 16 (32) different bank pairs
+//                    (banks), whatever their indices, so the random lookups
+//                    take no bank conflicts; the row address is the code
+//                    byte moved to bits 8..15 and the slot offset put below
+//                    it, one v_perm_b32.
+//   [vcomp, ..)      one-bit value table (16 bytes per code byte), VB = 1 only
 //   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
 //   [kw, ..)         per wave: the tile's key words [WK + 2][64] (the last two rows zero)
-// The decode and value tables are copied from global memory in the prologue,
-// the prepared queries built there (prep_build, with its scratch from pt on);
-// after the tile loop the area from 0 is reused for the wave merge.  Past
-// `total`: 16 spare bytes that take the stores of the copy falling outside the
-// tables.
+// The tables are copied (and replicated) from the plan's constant image in
+// the prologue; after the tile loop the area from 0 is reused for the wave
+// merge.
 template <int G, int VB, int WK = kMaxWK>
 struct StreamLds {
-  static constexpr int c4 = kDtabC4, t2 = kDtabT2, t1 = kDtabT1, t3 = kDtabT3;
-  static constexpr int q4 = kDtabBytes;
-  static constexpr int qr = q4 + PrepOut<G>::qr;
-  static constexpr int rinv = q4 + PrepOut<G>::rinv;
-  static constexpr int vlut = q4 + PrepOut<G>::bytes;
-  static constexpr int pt = (vlut + VLut<VB>::entries * VLut<VB>::bytes + 15) & ~15;
+  static constexpr int t2 = 0, t1 = 2048, t3 = 2304, kt_bytes = 2560;
+  static constexpr int rep = kt_bytes, rep_bytes = 256 * 256;
+  static constexpr int vslot = VB == 2 ? 8 : 4;                 // bytes per value slot (VB 2..4)
+  static constexpr int vcomp = rep + rep_bytes;
+  static constexpr int pt = vcomp + (VB == 1 ? VLut<1>::entries * VLut<1>::bytes : 0);
   static constexpr int W = StreamCfg<G, VB, WK>::waves;
   static constexpr int kw = pt + W * G * kTile * 2;
   static constexpr int kw_rows = WK + 2;  // key words of the tile, then two zero rows
   static constexpr int end = kw + W * kw_rows * kTile * 4;
   static constexpr int merge = W * G * kPartStride * 4;
   static constexpr int total = end > merge ? end : merge;
-  static constexpr int spare = total, alloc = total + 16;
-  static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0, "table bases above the index bits");
-  static_assert(q4 % 16 == 0 && vlut % 16 == 0 && kw % 16 == 0, "16-byte aligned areas");
-  static constexpr int scr = pt;  // query-preparation scratch (before the tile loop)
-  static_assert(scr + PrepScratch<G>::bytes <= total, "preparation scratch inside the allocation");
+  static constexpr int alloc = total;
+  static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0 && rep % 256 == 0, "table bases above the index bits");
+  static_assert(rep < 65536, "lookup rows addressed by the instruction offset plus a 16-bit row address");
+  static_assert(pt % 16 == 0 && kw % 16 == 0, "16-byte aligned areas");
+  static_assert(alloc <= 160 * 1024, "LDS of one CU");
 };
+
+// Row address of a lookup: code byte K of `word` at bits 8..15, the lane's
+// slot offset `slot` (below 256) in bits 0..7 (v_perm_b32: result byte 0 is
+// byte 0 of `slot`, byte 1 is byte K of `word`, bytes 2 and 3 are zero).
+template <int K>
+__device__ __forceinline__ uint32_t row_addr(uint32_t word, uint32_t slot) {
+  return __builtin_amdgcn_perm(word, slot, 0x0C0C0400u | ((uint32_t)K << 8));
+}
 
 template <int VB, int WK>
 struct TileRegs {
@@ -194,7 +208,8 @@ __device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *_
 
 struct StreamState {
   uint32_t kwl;       // LDS byte address of this lane's word 0 in this wave's key-word rows
-  uint32_t qrl;       // LDS byte address of this lane's row in k-step 0's query operand
+  uint32_t vslot;     // this lane's slot offset in the value half of a lookup row
+  uint32_t c4slot;    // this lane's slot offset in the centroid-pair half of a lookup row
   uint32_t cgrp;      // first k-step of the width-3, 2, 1 groups (bytes 0..2), k-step count (byte 3)
   uint32_t gbit;      // first stream bit of the width-3, 2, 1 groups (10 bits each)
   uint32_t ptw;       // LDS byte offset of this wave's weight rows
@@ -211,22 +226,31 @@ struct VQuads {
   static constexpr int v = (G + 3) / 4;  // matrix-core registers of 4 query heads
 };
 
-// Key word J holds codes 8 J .. 8 J + 7, two per byte (low nibble first).  The
-// words are pipelined: the four lookups of word J + 1 (and the query operand of
-// its block of 16 codes) are issued before the products of word J.
-template <int WK, int J>
-__device__ __forceinline__ void key4_lookups(const uint32_t (&w)[WK], uint32_t c4l, float2 (&cp)[4]) {
-  const uint32_t word = w[J];
-#pragma unroll
-  for (int by = 0; by < 4; ++by) cp[by] = lds_at<float2>(c4l + (((word >> (8 * by)) & 255u) << 3));
-}
+// The prepared queries of the tile loop, held in registers for the whole loop.
+// The matrix-core A operands are broadcast from one block of 4 lanes to all
+// 16 (CBSZ 4, ABID b), so one register holds the operands of 16 steps:
+//  q4[k][g]     lane 4b + m: head 4g + m's scaled query of 4-bit code 16k + b
+//  kq[r][j][g]  lane 4b + m: head 4g + m's four fp16 query values of k-step
+//               16j + b of the width-(3 - r) group
+template <int G>
+struct QueryRegs {
+  static constexpr int VQ = VQuads<G>::v;
+  float q4[8][VQ];
+  h4v kq[3][2][VQ];
+};
 
-template <int G, int VB, int BLK>
-__device__ __forceinline__ void key4_query(int lane, float (&qa)[VQuads<G>::v]) {
-#pragma unroll
-  for (int g = 0; g < VQuads<G>::v; ++g)
-    qa[g] = lds_at<float>(StreamLds<G, VB>::q4 +
-                          (uint32_t)(((4 * g + (lane & 3)) & (G - 1)) * kHeadDim + 16 * BLK + (lane >> 2)) * 4);
+// Key word J holds codes 8 J .. 8 J + 7, two per byte (low nibble first).  The
+// words are pipelined: the four lookups of word J + 1 are issued before the
+// products of word J.  A lookup reads the centroid pair of its code byte from
+// the lane's slot of the byte's lookup row.
+template <int G, int VB, int WK, int J>
+__device__ __forceinline__ void key4_lookups(const uint32_t (&w)[WK], uint32_t c4slot, float2 (&cp)[4]) {
+  typedef StreamLds<G, VB, WK> L;
+  const uint32_t word = w[J];
+  cp[0] = lds_at<float2>(L::rep + row_addr<0>(word, c4slot));
+  cp[1] = lds_at<float2>(L::rep + row_addr<1>(word, c4slot));
+  cp[2] = lds_at<float2>(L::rep + row_addr<2>(word, c4slot));
+  cp[3] = lds_at<float2>(L::rep + row_addr<3>(word, c4slot));
 }
 
 template <int G, int J>
@@ -242,45 +266,33 @@ __device__ __forceinline__ void key4_products(const float2 (&cp)[4], const float
 #undef BGTQ_K4
 }
 
-// Word J (< n4w) with its lookups in cx and the query operand of its block in qx;
-// word J + 1's go to cy / qy (the query operand only at a block boundary).
+// Word J (< n4w) with its lookups in cx; word J + 1's go to cy.
 template <int G, int VB, int WK, int J>
-__device__ __forceinline__ void key4_words(const uint32_t (&w)[WK], int n4w, int lane, uint32_t c4l, float2 (&cx)[4],
-                                           float2 (&cy)[4], float (&qx)[VQuads<G>::v], float (&qy)[VQuads<G>::v],
-                                           f4v (&a4)[VQuads<G>::v]) {
+__device__ __forceinline__ void key4_words(const uint32_t (&w)[WK], int n4w, uint32_t c4slot, float2 (&cx)[4],
+                                           float2 (&cy)[4], const QueryRegs<G> &qr, f4v (&a4)[VQuads<G>::v]) {
   if constexpr (J < WK) {
     if (J < n4w) {
-      if constexpr (J + 1 < WK) {
-        key4_lookups<WK, J + 1>(w, c4l, cy);
-        if constexpr ((J & 1) == 1) key4_query<G, VB, (J + 1) / 2>(lane, qy);
-      }
+      if constexpr (J + 1 < WK) key4_lookups<G, VB, WK, J + 1>(w, c4slot, cy);
       __builtin_amdgcn_sched_barrier(0);
-      key4_products<G, J>(cx, qx, a4);
+      key4_products<G, J>(cx, qr.q4[J >> 1], a4);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr ((J & 1) == 1)
-        key4_words<G, VB, WK, J + 1>(w, n4w, lane, c4l, cy, cx, qy, qx, a4);
-      else
-        key4_words<G, VB, WK, J + 1>(w, n4w, lane, c4l, cy, cx, qx, qy, a4);
+      key4_words<G, VB, WK, J + 1>(w, n4w, c4slot, cy, cx, qr, a4);
     }
   }
 }
 
 // 4-bit group on the matrix cores, one v_mfma_f32_4x4x1f32 per code r (16 blocks
 // of 4 x 4 x 1): block k is lanes 4k .. 4k + 3 = tokens 4k .. 4k + 3, its B operand
-// the token's centroid c4[code_r] (centroid pairs at LDS byte 8 x code byte) and
-// its output row m head m, so the token's lane keeps
-// a4[h] in register h.  The A operand, head m's query value of code r, is
-// broadcast from block r % 16 of a register whose lane 4k + m holds code
-// 16 (r / 16) + k (CBSZ 4, ABID r % 16).
+// the token's centroid c4[code_r] and its output row m head m, so the token's
+// lane keeps a4[h] in register h.  The A operand, head m's query value of
+// code r, is broadcast from block r % 16 of q4[r / 16] (CBSZ 4, ABID r % 16).
 template <int G, int VB, int WK>
-__device__ __forceinline__ void key4_group(const uint32_t (&w)[WK], int n4w, int lane, uint32_t c4l,
+__device__ __forceinline__ void key4_group(const uint32_t (&w)[WK], int n4w, uint32_t c4slot, const QueryRegs<G> &qr,
                                            f4v (&a4)[VQuads<G>::v]) {
   if (n4w > 0) {
     float2 cx[4], cy[4];
-    float qx[VQuads<G>::v], qy[VQuads<G>::v];
-    key4_lookups<WK, 0>(w, c4l, cx);
-    key4_query<G, VB, 0>(lane, qx);
-    key4_words<G, VB, WK, 0>(w, n4w, lane, c4l, cx, cy, qx, qy, a4);
+    key4_lookups<G, VB, WK, 0>(w, c4slot, cx);
+    key4_words<G, VB, WK, 0>(w, n4w, c4slot, cx, cy, qr, a4);
   }
 }
 
@@ -328,7 +340,7 @@ __device__ __forceinline__ h4v kstep_b(uint32_t t) {
 // register i of the group when the first k-step needs it.
 template <int G, int VB, int W, int S>
 __device__ __forceinline__ void kgroup_steps(uint32_t (&wd)[14], uint32_t (&al)[13], uint32_t wa, uint32_t sh,
-                                             uint32_t qa, int ns, f4v (&acc)[VQuads<G>::v]) {
+                                             const h4v (&kq)[2][VQuads<G>::v], int ns, f4v (&acc)[VQuads<G>::v]) {
   if constexpr (S < 32) {
     if (S >= ns) return;
     constexpr int hi = KStep<W>::last_reg(S), lo = S == 0 ? 0 : KStep<W>::last_reg(S - 1) + 1;
@@ -340,27 +352,27 @@ __device__ __forceinline__ void kgroup_steps(uint32_t (&wd)[14], uint32_t (&al)[
     const h4v bq = kstep_b<G, VB, W>(kstep_bits<W, S>(al));
 #pragma unroll
     for (int g = 0; g < VQuads<G>::v; ++g)
-      acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(lds_at<h4v>(qa + (S * VQuads<G>::v + g) * 32), bq, acc[g], 0, 0, 0);
-    kgroup_steps<G, VB, W, S + 1>(wd, al, wa, sh, qa, ns, acc);
+      acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(kq[S >> 4][g], bq, acc[g], 4, S & 15, 0);
+    kgroup_steps<G, VB, W, S + 1>(wd, al, wa, sh, kq, ns, acc);
   }
 }
 
-// The k-steps of the width-(3 - R) group.
+// The k-steps of the width-(3 - R) group; the query operand of k-step S is
+// broadcast from block S % 16 of kq[R][S / 16].
 template <int G, int VB, int WK, int R>
-__device__ __forceinline__ void key_group(const StreamState &st, f4v (&acc)[VQuads<G>::v]) {
+__device__ __forceinline__ void key_group(const StreamState &st, const QueryRegs<G> &qr, f4v (&acc)[VQuads<G>::v]) {
   constexpr int W = 3 - R;
   const int cb = (st.cgrp >> (8 * R)) & 255, ce = (st.cgrp >> (8 * R + 8)) & 255;
   if (cb >= ce) return;
   const uint32_t bit = (st.gbit >> (10 * R)) & 1023u;
   const uint32_t wa = st.kwl + (bit >> 5) * 256;
-  const uint32_t qa = st.qrl + (uint32_t)cb * (VQuads<G>::v * 32);
   uint32_t wd[14], al[13];
   wd[0] = lds_at<uint32_t>(wa);
   // The k-step count is opaque per tile, so that the compiler evaluates each
   // k-step's guard where it is used instead of keeping all of them live.
   int ns = ce - cb;
   asm volatile("" : "+s"(ns));
-  kgroup_steps<G, VB, W, 0>(wd, al, wa, bit & 31u, qa, ns, acc);
+  kgroup_steps<G, VB, W, 0>(wd, al, wa, bit & 31u, qr.kq[R], ns, acc);
 }
 
 // In-place maximum over the 64 lanes of each v[h] (every lane receives it):
@@ -417,22 +429,23 @@ __device__ __forceinline__ uint32_t bits6(const uint32_t (&c)[N]) {
 }
 
 // B operand of step S: the fp16 centroids of tokens 4S .. 4S + 3 (bits 4 VB S ..
-// 4 VB (S + 1) of the coordinate's code stream) from the value table.
-template <int VB, int S>
-__device__ __forceinline__ h4v v_operand(const uint32_t (&c)[2 * VB], uint32_t vlut) {
+// 4 VB (S + 1) of the coordinate's code stream), from the lane's slot of the
+// lookup rows (VB 2..4; `slot` is the lane's slot offset) or from the compact
+// one-bit table.
+template <class L, int VB, int S>
+__device__ __forceinline__ h4v v_operand(const uint32_t (&c)[2 * VB], uint32_t slot) {
   if constexpr (VB == 1) {  // entry = one byte (8 tokens) x 16 bytes
     const uint32_t y = (c[S >> 3] >> (8 * ((S >> 1) & 3))) & 255u;
-    return lds_at<h4v>(vlut + 16 * y + 8 * (S & 1));
-  } else if constexpr (VB == 2) {  // entry = one byte (4 tokens) x 8 bytes
-    const uint32_t y = (c[S >> 2] >> (8 * (S & 3))) & 255u;
-    return lds_at<h4v>(vlut + 8 * y);
-  } else if constexpr (VB == 3) {  // entry = 6 bits (2 tokens) x 4 bytes
+    return lds_at<h4v>(L::vcomp + 16 * y + 8 * (S & 1));
+  } else if constexpr (VB == 2) {  // row = one byte (4 tokens), 8-byte slots
+    return lds_at<h4v>(L::rep + row_addr<S & 3>(c[S >> 2], slot));
+  } else if constexpr (VB == 3) {  // row = 6 bits (2 tokens), 4-byte slots
     const uint32_t y0 = bits6<12 * S>(c), y1 = bits6<12 * S + 6>(c);
-    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(vlut + 4 * y0), lds_at<uint32_t>(vlut + 4 * y1)});
-  } else {  // entry = one byte (2 tokens) x 4 bytes
-    const uint32_t w = c[S >> 1] >> (16 * (S & 1));
-    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(vlut + 4 * (w & 255u)),
-                                         lds_at<uint32_t>(vlut + 4 * ((w >> 8) & 255u))});
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(L::rep + ((y0 << 8) | slot)),
+                                         lds_at<uint32_t>(L::rep + ((y1 << 8) | slot))});
+  } else {  // row = one byte (2 tokens), 4-byte slots
+    return __builtin_bit_cast(h4v, (u2v){lds_at<uint32_t>(L::rep + row_addr<2 * (S & 1)>(c[S >> 1], slot)),
+                                         lds_at<uint32_t>(L::rep + row_addr<2 * (S & 1) + 1>(c[S >> 1], slot))});
   }
 }
 
@@ -441,13 +454,13 @@ __device__ __forceinline__ h4v v_operand(const uint32_t (&c)[2 * VB], uint32_t v
 // flight instead of waiting for each one.
 constexpr int kVBatch = 4;
 
-template <int VB, int S, int N>
-__device__ __forceinline__ void v_lookups(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+template <class L, int VB, int S, int N>
+__device__ __forceinline__ void v_lookups(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t slot,
                                           h4v (&b0)[kVBatch], h4v (&b1)[kVBatch]) {
   if constexpr (N < kVBatch) {
-    b0[N] = v_operand<VB, S + N>(va, vlut);
-    b1[N] = v_operand<VB, S + N>(vb, vlut);
-    v_lookups<VB, S, N + 1>(va, vb, vlut, b0, b1);
+    b0[N] = v_operand<L, VB, S + N>(va, slot);
+    b1[N] = v_operand<L, VB, S + N>(vb, slot);
+    v_lookups<L, VB, S, N + 1>(va, vb, slot, b0, b1);
   }
 }
 
@@ -466,30 +479,30 @@ __device__ __forceinline__ void v_products(const h4v (&b0)[kVBatch], const h4v (
 }
 
 // Batch starting at step S, whose lookups are in (x0, x1); the next batch's go to (y0, y1).
-template <int G, int VB, int S>
-__device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t vlut,
+template <int G, class L, int VB, int S>
+__device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const uint32_t (&vb)[2 * VB], uint32_t slot,
                                              const h4v (&pa)[VQuads<G>::v], h4v (&x0)[kVBatch],
                                              h4v (&x1)[kVBatch], h4v (&y0)[kVBatch], h4v (&y1)[kVBatch],
                                              f4v (&acc0)[VQuads<G>::v], f4v (&acc1)[VQuads<G>::v]) {
   if constexpr (S < kTile / 4) {
-    if constexpr (S + kVBatch < kTile / 4) v_lookups<VB, S + kVBatch, 0>(va, vb, vlut, y0, y1);
+    if constexpr (S + kVBatch < kTile / 4) v_lookups<L, VB, S + kVBatch, 0>(va, vb, slot, y0, y1);
     __builtin_amdgcn_sched_barrier(0);
     v_products<G, S, 0>(x0, x1, pa, acc0, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    v_mfma_steps<G, VB, S + kVBatch>(va, vb, vlut, pa, y0, y1, x0, x1, acc0, acc1);
+    v_mfma_steps<G, L, VB, S + kVBatch>(va, vb, slot, pa, y0, y1, x0, x1, acc0, acc1);
   }
 }
 
 template <int G, int VB, int WK>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
-                                             const float (&rinv)[G], float (&mrun)[G], float (&mth)[G],
-                                             float (&lsum)[G], f4v (&acc0)[VQuads<G>::v],
+                                             const QueryRegs<G> &qr, const float (&rinv)[G], float (&mrun)[G],
+                                             float (&mth)[G], float (&lsum)[G], f4v (&acc0)[VQuads<G>::v],
                                              f4v (&acc1)[VQuads<G>::v], int lane) {
   // ---- keys, lane = token.  4-bit group: one fp32 step per code.
   f4v a4[VQuads<G>::v];
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
-  key4_group<G, VB, WK>(r.w, st.n4w, lane, (uint32_t)StreamLds<G, VB, WK>::c4, a4);
+  key4_group<G, VB, WK>(r.w, st.n4w, st.c4slot, qr, a4);
   // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w,
   // from the key words staged in this wave's LDS rows
 #pragma unroll
@@ -501,7 +514,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
 #define BGTQ_KG(R, NORM)                                                              \
   {                                                                                   \
     _Pragma("unroll") for (int g = 0; g < VQuads<G>::v; ++g) ak[g] = (f4v){0.f, 0.f, 0.f, 0.f}; \
-    key_group<G, VB, WK, R>(st, ak);                                                  \
+    key_group<G, VB, WK, R>(st, qr, ak);                                              \
     const float nw = h2f((uint16_t)(NORM));                                           \
     _Pragma("unroll") for (int h = 0; h < G; ++h) lr[h] = R == 0 ? nw * ak[h >> 2][h & 3] : fmaf(nw, ak[h >> 2][h & 3], lr[h]); \
   }
@@ -560,12 +573,68 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
     pa[g] = lds_at<h4v>(st.ptw + ((4 * g + (lane & 3)) & (G - 1)) * (2 * kTile) + (lane >> 2) * 8);
   // ---- values: lane = coordinates lane and lane + 64
   typedef StreamLds<G, VB, WK> L;
-  const uint32_t vlut = (uint32_t)L::vlut;
   h4v x0[kVBatch], x1[kVBatch], y0[kVBatch], y1[kVBatch];
-  v_lookups<VB, 0, 0>(r.va, r.vb, vlut, x0, x1);
-  v_mfma_steps<G, VB, 0>(r.va, r.vb, vlut, pa, x0, x1, y0, y1, acc0, acc1);
+  v_lookups<L, VB, 0, 0>(r.va, r.vb, st.vslot, x0, x1);
+  v_mfma_steps<G, L, VB, 0>(r.va, r.vb, st.vslot, pa, x0, x1, y0, y1, acc0, acc1);
 }
 
+
+// ------------------------------------------------------------------ query preparation
+
+// The decode kernel's query registers (QueryRegs) of one (sequence, KV head)
+// as the preparation kernel writes them to the workspace: one 64-lane row per
+// register, so that the decode kernel loads each register with one coalesced
+// load whose address does not depend on loaded data.
+template <int G>
+struct QueryImage {
+  static constexpr int VQ = VQuads<G>::v;
+  static constexpr int q4 = 0;                             // float [8][VQ][64]
+  static constexpr int kq = q4 + 8 * VQ * kTile * 4;       // h4v [3][2][VQ][64]
+  static constexpr int rinv = kq + 3 * 2 * VQ * kTile * 8; // float [G], 1 / the k-step operands' scale
+  static constexpr int bytes = rinv + 256;
+  static_assert(bytes % 256 == 0 && G <= 64, "256-byte slots");
+};
+
+constexpr int kPrepWaves = 8;
+
+// One workgroup of 8 waves per (KV head, sequence): the G queries rotated once
+// per key width group and scaled (prep.h, in LDS), then rearranged into the
+// register image of the pair's slot.
+template <int G>
+__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const uint8_t *__restrict__ consts,
+                                                                const uint16_t *__restrict__ q, int hq, int hkv,
+                                                                int64_t off_zero, float kscale,
+                                                                uint8_t *__restrict__ images) {
+  typedef PrepOut<G> PO;
+  typedef QueryImage<G> QI;
+  constexpr int VQ = VQuads<G>::v, T = 64 * kPrepWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t out[PO::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t scr[PrepScratch<G>::bytes];
+  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  PrepIn<G, kPrepWaves> pin;
+  prep_issue_keys<G, kPrepWaves>(pin, consts, kvh, wave, lane);
+  prep_issue<G, kPrepWaves>(pin, consts, kvh, q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim, tid, wave, lane);
+  prep_issue_rot<G, kPrepWaves>(pin, consts, off_zero, kvh, wave, lane);
+  prep_stage<G, kPrepWaves>(pin, out, scr, tid);
+  prep_build<G, kPrepWaves>(pin, out, scr, kscale, tid, wave, lane);  // ends with a barrier
+  const KvhDesc &kds = *(const KvhDesc *)(scr + PrepScratch<G>::kds);
+  uint8_t *img = images + ((size_t)b * hkv + kvh) * QI::bytes;
+  // q4[k][g][l]: head 4g + (l & 3) (repeating a valid head past G), code 16k + l / 4
+  for (int i = tid; i < 8 * VQ * kTile; i += T) {
+    const int l = i & 63, g = (i >> 6) % VQ, k = (i >> 6) / VQ;
+    const int h = (4 * g + (l & 3)) & (G - 1);
+    ((float *)(img + QI::q4))[i] = ((const float *)(out + PO::q4))[h * kHeadDim + 16 * k + (l >> 2)];
+  }
+  // kq[r][j][g][l]: k-step 16j + l / 4 of the width-(3 - r) group, head 4g + (l & 3)
+  for (int i = tid; i < 6 * VQ * kTile; i += T) {
+    const int l = i & 63, g = (i >> 6) % VQ, rj = (i >> 6) / VQ, r = rj >> 1, j = rj & 1;
+    const int cb = (int)((kds.cgrp >> (8 * r)) & 255u);
+    const int k = min(cb + 16 * j + (l >> 2), kMaxKSteps - 1);
+    ((uint2 *)(img + QI::kq))[i] = ((const uint2 *)(out + PO::qr))[(k * VQ + g) * 4 + (l & 3)];
+  }
+  if (tid < G) ((float *)(img + QI::rinv))[tid] = ((const float *)(out + PO::rinv))[tid];
+}
 
 // ------------------------------------------------------------------ decode kernel
 
@@ -580,6 +649,7 @@ struct DecodeArgs {
   const uint16_t *vn;
   const int32_t *seq_lens;
   float *part;  // split partials [batch][hq][n_splits][kPartStride]
+  const uint8_t *qimg;   // prepared query registers [batch][hkv] (QueryImage)
   const int32_t *table;  // paged pools: block table [batch][max_pages], else null
   int64_t head_stride, seq_stride;  // tile index = kvh * head_stride + b * seq_stride + page
   int max_pages, n_pages;
@@ -603,52 +673,74 @@ void decode_kernel(const DecodeArgs a) {
   typedef StreamLds<G, VB, WK> Lds;
   constexpr int kStreamWaves = StreamCfg<G, VB, WK>::waves, kStreamThreads = StreamCfg<G, VB, WK>::threads;
 
-  // ---- prologue loads, in this order so that waiting for an earlier group
-  // does not wait for a later one (loads complete in order): the sequence
-  // length and the head's group fields, the row-table entries of the
-  // rotation rows, the query preparation's inputs, the plan's decode and
-  // value tables (16 bytes per thread and round), the nonzero part of the
-  // rotation (addressed from the row-table entries), then the first tile.
+  // ---- prologue: every load first, none of them addressed from loaded data
+  // (loads complete in order, so waiting for an earlier group does not wait
+  // for a later one): the plan's tables, this (sequence, KV head)'s prepared
+  // query registers, then the wave's first two tiles.  The tables go into LDS
+  // as soon as they arrive; one barrier later the tile loop starts with both
+  // tiles in flight.
   const int64_t seq_raw = (int64_t)a.seq_lens[b] + a.seq_add;
   const int n4w = kd->n4w;
   const uint32_t cgrp = kd->cgrp, gbit = kd->gbit;
-  PrepIn<G, kStreamWaves> pin;
-  prep_issue_keys<G, kStreamWaves>(pin, consts, kvh, wave, lane);
-  prep_issue<G, kStreamWaves>(pin, consts, kvh, a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim, tid, wave,
-                              lane);
-  constexpr int n0 = kDtabBytes >> 4;
-  constexpr int n1 = n0 + ((VLut<VB>::entries * VLut<VB>::bytes) >> 4);
-  constexpr int kRounds = (n1 + kStreamThreads - 1) / kStreamThreads;
-  const uint4 *cs0 = (const uint4 *)(consts + a.off_dtab), *cs1 = (const uint4 *)(consts + a.off_vlut) - n0;
-  static_assert(kRounds <= 2 && n0 <= kStreamThreads, "at most two rounds of the table copy");
-  const int i0 = min(tid, n1 - 1), i1 = min(tid + kStreamThreads, n1 - 1);
-  const uint4 cr0 = *(i0 < n0 ? cs0 + i0 : cs1 + i0);
-  uint4 cr1 = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (kRounds == 2) cr1 = *(cs1 + i1);
-  prep_issue_rot<G, kStreamWaves>(pin, consts, a.off_zero, kvh, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  // the tables, descriptor and queries into LDS before the first tile is
-  // requested (waiting for these loads only), so that they are not queued
-  // behind the grid's tile requests
-  const auto tab_at = [](int i) { return i < n0 ? 16 * i : i < n1 ? Lds::vlut + 16 * (i - n0) : Lds::spare; };
-  *(uint4 *)(smem + tab_at(tid)) = cr0;
-  if constexpr (kRounds == 2) *(uint4 *)(smem + tab_at(tid + kStreamThreads)) = cr1;
-  prep_stage<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, tid);
-  StreamState st;
-  __builtin_amdgcn_sched_barrier(0);  // keep the staging ahead of the tile request
-  // ---- tiles of this wave: tile_lo + wave, + W, ... (W waves); double-buffered
-  // registers.  The first is requested now, before the query preparation, its
-  // range bounded by max_seq_len (in memory).
+  // the plan's tables: the compact k-step tables (bytes 2048 .. 4608 of the
+  // image's decode tables: t2, t1, t3) and, for each lookup row, the entry to
+  // replicate into its slots -- thread (row e, part p): p 0, 1 the value-table
+  // entry e (VB 2..4), p 2, 3 the 4-bit centroid pair of code byte e
+  constexpr int kRowRounds = 256 * 4 / kStreamThreads;
+  static_assert(kRowRounds >= 1 && kRowRounds * kStreamThreads == 1024, "lookup rows over the threads");
+  constexpr int kVEntries = VLut<VB>::entries;
+  const uint8_t *dtab = consts + a.off_dtab, *vtab = consts + a.off_vlut;
+  const uint4 ktab = *((const uint4 *)(dtab + 2048) + min(tid, Lds::kt_bytes / 16 - 1));
+  uint2 rsrc[kRowRounds];
+#pragma unroll
+  for (int rr = 0; rr < kRowRounds; ++rr) {
+    const int e = (tid >> 2) + rr * (kStreamThreads / 4), part = tid & 3;
+    if (part >= 2)
+      rsrc[rr] = *(const uint2 *)(dtab + 8 * e);
+    else if constexpr (VB == 2)
+      rsrc[rr] = *(const uint2 *)(vtab + 8 * e);
+    else if constexpr (VB >= 3)
+      rsrc[rr] = make_uint2(*(const uint32_t *)(vtab + 4 * min(e, kVEntries - 1)), 0u);
+    else
+      rsrc[rr] = make_uint2(0u, 0u);
+  }
+  uint4 vcomp = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (VB == 1) vcomp = *((const uint4 *)vtab + min(tid, kVEntries - 1));
+  // the prepared query registers (QueryRegs), one coalesced row per register
+  constexpr int VQ = VQuads<G>::v;
+  typedef QueryImage<G> QI;
+  const uint8_t *img = a.qimg + ((size_t)b * a.hkv + kvh) * QI::bytes;
+  QueryRegs<G> qr;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int g = 0; g < VQ; ++g) qr.q4[k][g] = ((const float *)(img + QI::q4))[(k * VQ + g) * kTile + lane];
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < VQ; ++g)
+        qr.kq[r][j][g] = __builtin_bit_cast(h4v, ((const uint2 *)(img + QI::kq))[((2 * r + j) * VQ + g) * kTile + lane]);
+  float rinv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(img + QI::rinv))[h];
+  // ---- tiles of this wave: tile_lo + wave, + W, ... (W waves); two in flight
+  // in registers, their range bounded by max_seq_len (in memory)
   const int tile_lo = split * a.tiles_base + min(split, a.tiles_extra);
   const int tile_end =
       min(tile_lo + a.tiles_base + (split < a.tiles_extra ? 1 : 0), (int)((a.max_seq_len + kTile - 1) / kTile));
   // tile index = head_base + page; page = tile (contiguous) or the block
-  // table's entry (paged; clamped into the pool, read one tile ahead)
+  // table's entry (paged; clamped into the pool)
   const size_t head_base = (size_t)kvh * a.head_stride + (size_t)b * a.seq_stride;
   const bool paged = a.table != nullptr;
   const int32_t *btab = paged ? a.table + (size_t)b * a.max_pages : nullptr;
   const auto page_of = [&](int t) -> size_t {
     return (size_t)min((uint32_t)__builtin_amdgcn_readfirstlane(btab[t]), (uint32_t)(a.n_pages - 1));
+  };
+  const auto base_of = [&](int t, int hi) -> size_t {
+    const int tc = min(t, hi - 1);
+    return head_base + (paged ? page_of(tc) : (size_t)tc);
   };
   const bool kzero = a.wk == 0;
   // (zero-key plans run the 4-word kernel: the plan's zero block is one such tile)
@@ -657,22 +749,36 @@ void decode_kernel(const DecodeArgs a) {
   const size_t kstride = kzero ? 0 : (size_t)WK * kTile;
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
-  size_t pn = 0;  // paged: page of the wave's next tile
-  if (paged) {
-    load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + page_of(min(tile, tile_end - 1)), lane);
-    pn = page_of(min(tile + kStreamWaves, tile_end - 1));
-  } else {
-    load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, head_base + min(tile, tile_end - 1), lane);
-  }
+  load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, base_of(tile, tile_end), lane);
+  load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, base_of(tile + kStreamWaves, tile_end), lane);
+  // paged: the page of the tile after next, read one tile ahead of its load
+  size_t pnext = paged ? page_of(min(tile + 2 * kStreamWaves, tile_end - 1)) : 0;
   __builtin_amdgcn_sched_barrier(0);
-  // the queries of this (sequence, KV head), rotated and scaled (ends with a barrier)
-  prep_build<G, kStreamWaves>(pin, smem + Lds::q4, smem + Lds::scr, a.kscale, tid, wave, lane);
+  if (tid < Lds::kt_bytes / 16) *(uint4 *)(smem + 16 * tid) = ktab;
+#pragma unroll
+  for (int rr = 0; rr < kRowRounds; ++rr) {
+    const int e = (tid >> 2) + rr * (kStreamThreads / 4), part = tid & 3;
+    const uint2 v = rsrc[rr];
+    // 64 bytes of row e: slots of 8 bytes (two copies per 16-byte store) or of 4 bytes (four)
+    const uint4 q = (part >= 2 || VB == 2) ? make_uint4(v.x, v.y, v.x, v.y) : make_uint4(v.x, v.x, v.x, v.x);
+    uint4 *dst = (uint4 *)(smem + Lds::rep + 256 * e + 64 * part);
+    if (part >= 2 || VB >= 2) {
+      dst[0] = q;
+      dst[1] = q;
+      dst[2] = q;
+      dst[3] = q;
+    }
+  }
+  if constexpr (VB == 1)
+    if (tid < kVEntries) *(uint4 *)(smem + Lds::vcomp + 16 * tid) = vcomp;
+  StreamState st;
   st.seq = (seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw)) - a.n_recent;
   st.lo = a.n_sink;
   st.nv = (uint32_t)(st.seq > st.lo ? st.seq - st.lo : 0);
   st.wk = a.wk;
   st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
-  st.qrl = (uint32_t)Lds::qr + (uint32_t)(lane & 3) * 8;
+  st.vslot = (uint32_t)(lane & (128 / Lds::vslot - 1)) * Lds::vslot;
+  st.c4slot = 128u + (uint32_t)(lane & 15) * 8u;
   st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
   st.n4w = n4w;
   st.cgrp = cgrp;
@@ -680,9 +786,7 @@ void decode_kernel(const DecodeArgs a) {
   // the two zero rows past the key words (this lane's column, read by this lane only)
   *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
   *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
-  float rinv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) rinv[h] = lds_at<float>(Lds::rinv + 4 * h);
+  __syncthreads();
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
@@ -696,19 +800,16 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) acc0[g] = (f4v){0.f, 0.f, 0.f, 0.f}, acc1[g] = acc0[g];
   // One copy of the tile body (the instruction cache holds the loop): the
-  // next tile's registers are requested before the current one is processed
-  // and moved into place after it.  (Two copies with alternating register
-  // sets raise the register count past the occupancy limit.)
+  // tile after next is requested once the next one has moved into place, so
+  // that one tile is in flight while one is processed.  (Two copies with
+  // alternating register sets raise the register count past the occupancy
+  // limit.)
   for (; tile < tile_hi; tile += kStreamWaves) {
-    const int tn = min(tile + kStreamWaves, tile_hi - 1);
-    size_t bn = head_base + tn;
-    if (paged) {  // (the prefetched page belongs to tn except on the last pass, whose load is not used)
-      bn = head_base + pn;
-      pn = page_of(min(tile + 2 * kStreamWaves, tile_hi - 1));
-    }
-    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
-    process_tile<G, VB, WK>(ra, tile, st, rinv, mrun, mth, lsum, acc0, acc1, lane);
+    process_tile<G, VB, WK>(ra, tile, st, qr, rinv, mrun, mth, lsum, acc0, acc1, lane);
     ra = rb;
+    const size_t bn = head_base + (paged ? pnext : (size_t)min(tile + 2 * kStreamWaves, tile_hi - 1));
+    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
+    if (paged) pnext = page_of(min(tile + 3 * kStreamWaves, tile_hi - 1));
   }
 
   // ---- merge the waves of this split into one partial per query head
@@ -792,11 +893,21 @@ DecodeKernel pick_decode(int g, int vb, int wk) {
   }
 }
 
-// Workspace: the split partials [batch][hq][n_splits][kPartStride] f32.
+// Workspace: the split partials [batch][hq][n_splits][kPartStride] f32, then
+// the prepared query registers [batch][hkv] (QueryImage).
 struct DecodeLayout {
   int n_splits, tiles_base, tiles_extra;  // split s covers tiles_base + (s < tiles_extra) tiles
-  size_t total;
+  size_t img_off, total;
 };
+
+size_t query_image_bytes(int g) {
+  switch (g) {
+    case 1: return QueryImage<1>::bytes;
+    case 2: return QueryImage<2>::bytes;
+    case 4: return QueryImage<4>::bytes;
+    default: return QueryImage<8>::bytes;
+  }
+}
 
 
 DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
@@ -815,7 +926,8 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   d.n_splits = s;
   d.tiles_base = tiles / s;
   d.tiles_extra = tiles % s;
-  d.total = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
+  d.img_off = (((size_t)batch * hq * d.n_splits * kPartStride * 4) + 255) & ~(size_t)255;
+  d.total = d.img_off + (size_t)batch * hkv * query_image_bytes(p.hdr.group);
   return d;
 }
 
@@ -884,6 +996,7 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.vn = c.v_norms;
   a.seq_lens = c.seq_lens;
   a.part = (float *)ws;
+  a.qimg = ws + lay.img_off;
   const TileMap map = c.pages ? paged_map(p, c.pages) : contiguous_map(p.desc.n_kv_heads, c.capacity);
   a.table = map.table;
   a.head_stride = map.head_stride;
@@ -905,6 +1018,20 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.n_sink = c.n_sink;
   a.n_recent = c.n_recent;
   a.kscale = kscale_of(c.softmax_scale);
+  // the queries of every (sequence, KV head), rotated and scaled into the
+  // decode kernel's register image
+  {
+    const dim3 pgrid(p.desc.n_kv_heads, c.batch);
+    uint8_t *img = ws + lay.img_off;
+    switch (G) {
+      case 1: prep_kernel<1><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
+      case 2: prep_kernel<2><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
+      case 4: prep_kernel<4><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
+      default: prep_kernel<8><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
+    }
+    const bgtq_status ps = launch_status("decode (query preparation)");
+    if (ps != BGTQ_OK) return ps;
+  }
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);
   // With profiling on, the events are bound to the launch itself, so their elapsed time is the
   // kernel's own start-to-end time (no queue packets of their own around the kernel).
