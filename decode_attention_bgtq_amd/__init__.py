@@ -29,7 +29,7 @@ EXPORTED = [
     "bgtq_plan_rotation", "bgtq_plan_bits", "bgtq_profile_enable", "bgtq_profile_read", "bgtq_decode_step",
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
-    "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc",
+    "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc", "bgtq_key_logits",
 ]
 
 
@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_encode_k": (I32, [P, P, P, I32, I64, I64, I64, P, P, P]),
         "bgtq_encode_v": (I32, [P, P, P, I32, I64, I64, I64, P, P, P]),
         "bgtq_rotate_queries": (I32, [P, P, P, I32, P, P]),
+        "bgtq_key_logits": (I32, [P, P, P, I32, P, P, I64, I32, I64, I64, P, P]),
         "bgtq_decode_workspace_size": (I32, [P, I32, I64, ctypes.POINTER(SZ)]),
         "bgtq_decode_attn": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float, P, P, SZ, P]),
         "bgtq_decode_step": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, I64, ctypes.c_float, P, P, SZ, P]),
@@ -331,6 +332,22 @@ class Plan:
         _gpu(q=q, q_rot=q_rot)
         _check(load().bgtq_rotate_queries(self._h, _ptr(consts), _ptr(q), q.shape[0], _ptr(q_rot),
                                           _stream(stream)))
+
+    def key_logits(self, consts, q_rot, k_codes, k_norms, capacity: int, t0: int, n_k: int, logits,
+                   stream=None) -> None:
+        """K-only logits q . k_hat of n_q queries per sequence against cache tokens t0 .. t0 + n_k - 1.
+        q_rot: float32 [batch, n_q, n_q_heads, 128] (rotate_queries of the [batch * n_q, n_q_heads, 128]
+        queries); logits: float32 [batch, n_q_heads, n_q, n_k], written."""
+        import torch
+        _need(q_rot, "q_rot", dtype=torch.float32, shape=(None, None, self.n_q_heads, HEAD_DIM))
+        b, nq = q_rot.shape[0], q_rot.shape[1]
+        if k_codes is not None:
+            _need(k_codes, "k_codes", elem=4)
+        _need(k_norms, "k_norms", elem=2)
+        _need(logits, "logits", dtype=torch.float32, shape=(b, self.n_q_heads, nq, n_k))
+        _gpu(q_rot=q_rot, k_codes=k_codes, k_norms=k_norms, logits=logits)
+        _check(load().bgtq_key_logits(self._h, _ptr(consts), _ptr(q_rot), nq, _ptr(k_codes), _ptr(k_norms),
+                                      capacity, b, t0, n_k, _ptr(logits), _stream(stream)))
 
     def workspace_size(self, batch: int, max_seq_len: int) -> int:
         n = ctypes.c_size_t()

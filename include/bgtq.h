@@ -45,7 +45,7 @@ enum {
   BGTQ_EWORKSPACE = -5  /* workspace smaller than the size query */
 };
 
-#define BGTQ_ABI_VERSION 3
+#define BGTQ_ABI_VERSION 4
 #define BGTQ_TILE 64 /* cache tokens per tile */
 
 /* RoPE pairing of the 128 head coordinates into 64 2-D frequency blocks (the
@@ -209,6 +209,29 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
  */
 bgtq_status bgtq_rotate_queries(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
                                 int32_t batch, float *q_rot, bgtq_stream stream);
+
+/*
+ * (5k) Key logits from the packed key cache alone (K-only).  Abstract: the
+ * method is judged by the error of the RoPE query-key logits with only the
+ * keys quantised (2 and 3 bits per coordinate); the README's per-layer
+ * diagnostic takes it over the last positions of a layer.  For every
+ * sequence b, query n < n_q, query head h and token t < n_k,
+ *   logits[b][h][n][t] = q[b][n][h] . k_hat[b][t0 + t][h / G]   (unscaled)
+ * with k_hat the TurboQuant-MSE reconstruction of the cached key, taken in the
+ * rotated space of each key group: sum_g n_g sum_i q_rot_g,i c_w[code_i] /
+ * sqrt(d_g), fp32.
+ *   q_rot   device float [batch][n_q][n_q_heads][128]: bgtq_rotate_queries of
+ *           the fp16 queries [batch][n_q][n_q_heads][128] called with batch x
+ *           n_q sequences
+ *   k_codes, k_norms  the key arrays of a contiguous cache of `capacity`
+ *           tokens (bgtq_sizes); k_codes may be null for a plan without key bits
+ *   logits  device float [batch][n_q_heads][n_q][n_k], written
+ * Errors: EINVAL (null, batch outside 1..65535, n_q < 1), ECAPACITY (t0 < 0,
+ * n_k < 0 or t0 + n_k > capacity).  n_k = 0 writes nothing.
+ */
+bgtq_status bgtq_key_logits(const bgtq_plan *plan, const void *dev_consts, const float *q_rot, int32_t n_q,
+                            const uint32_t *k_codes, const uint16_t *k_norms, int64_t capacity,
+                            int32_t batch, int64_t t0, int64_t n_k, float *logits, bgtq_stream stream);
 
 /*
  * (6) Fused decode attention over the packed cache for one new query per

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(bg):
 
 
 def test_abi_version(bg):
-    assert bg.abi_version() == 3
+    assert bg.abi_version() == 4
 
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4])
