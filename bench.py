@@ -1,20 +1,24 @@
 """Benchmark of the Block-GTQ packed-KV decode path on one MI355X.
 
-One step = one decode-attention call (bgtq_decode_attn: the decode kernel, which
-prepares the queries and streams the packed cache, then the split merge) of the
-128K Llama-3.1-8B-shaped layer (batch 1, 8 KV / 32 query heads, K2V2) over the
-T+1 cached tokens.  The serving step (bgtq_decode_step: the new token's key and
-value appended at position T, then the decode) is timed as well and reported
-under "serving_step".
+One step = one decode-attention call (bgtq_decode_attn: the query preparation
+kernel, the decode kernel that streams the packed cache, then the split merge)
+of the 128K Llama-3.1-8B-shaped layer (batch 1, 8 KV / 32 query heads, K2V2)
+over the T+1 cached tokens.  The serving step (bgtq_decode_step: the new
+token's key and value appended at position T, then the decode) is timed as
+well and reported under "serving_step".
 Calibration energy, allocation, plan creation and the full 128K prefill
 encode run once before the timed region and are reported as separate fields,
 and so does the fp16 baseline: the same keys and values uncompressed, decoded
 by bgtq_fp16_decode_attn (same split-sequence structure) over the same tokens.
+The other four synthetic layers (tiny 4K head, 32K Qwen-shaped, 16 x 32K
+batched, 512K with a 4096-token append) are measured the same way and reported
+under "configs".
 
 value = algorithmic packed bytes read per step (codes + present fp16 norms)
-/ step time.  The packed cache is replicated (>= 1 GiB in total) and steps
-rotate over the replicas so that reads come from HBM, not the 256 MB
-Infinity Cache.
+/ step time.  The packed cache is replicated (>= 1 GiB in total), and so is
+the plan's constant image (one copy per replica, as the layers of a model
+would each have their own); steps rotate over the replicas so that reads come
+from HBM, not the 256 MB Infinity Cache.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -36,7 +40,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-KV decode attn GB/s (% HBM peak), ms/step @128K; encode keys/s"
 HBM_PEAK_GBPS = 8000.0
+FP64_PEAK_TFLOPS = 78.6
 STREAM_KERNEL = "decode_kernel"
+DTYPE = "fp16 and fp32 operands, fp32 accumulate"
 
 
 def log(msg: str) -> None:
@@ -159,6 +165,242 @@ def traffic_from(fetch_dir: str, write_dir: str, cid: int, packed: int | None, o
     return 0
 
 
+class Timer:
+    """Event timing of enqueued calls on torch's current stream (the library's calls go to it)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.spin = getattr(torch.cuda, "_sleep", None)
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def _hold(self):
+        # a short GPU spin, so that the host has queued every call before the GPU reaches them
+        self.torch.cuda.synchronize()
+        if self.spin is not None:
+            self.spin(int(30e6))
+
+    def rounds(self, fn, steps, i0=0):
+        """Mean ms per call over `steps` calls in rounds of at most 100, no events between calls;
+        also the host enqueue time per call."""
+        per_round = min(steps, 100)
+        n_rounds = max(1, steps // per_round)
+        tot_ms, host_s, n = 0.0, 0.0, 0
+        for _ in range(n_rounds):
+            self._hold()
+            s0, s1 = self.ev(), self.ev()
+            s0.record()
+            th = time.perf_counter()
+            for i in range(per_round):
+                fn(i0 + n + i)
+            host_s += time.perf_counter() - th
+            s1.record()
+            self.torch.cuda.synchronize()
+            tot_ms += s0.elapsed_time(s1)
+            n += per_round
+        return tot_ms / n, host_s * 1e3 / n, n
+
+    def per_call(self, fn, steps, i0=0):
+        """Duration of each of `steps` back-to-back calls (an event between consecutive calls)."""
+        out = []
+        per_round = min(steps, 100)
+        done = 0
+        while done < steps:
+            k = min(per_round, steps - done)
+            self._hold()
+            evs = [self.ev() for _ in range(k + 1)]
+            evs[0].record()
+            for i in range(k):
+                fn(i0 + done + i)
+                evs[i + 1].record()
+            self.torch.cuda.synchronize()
+            out += [evs[i].elapsed_time(evs[i + 1]) for i in range(k)]
+            done += k
+        return out
+
+
+def kernel_ms(bg, timer, fn, steps):
+    """Mean duration of the decode kernel: the library's HIP events bound to every decode-kernel
+    launch (hipExtLaunchKernel on the launch stream, so the elapsed time is the kernel's own
+    start-to-end time), in a pass of its own because event timing can slow the dispatch of the
+    launches around it."""
+    bg.profile_enable(True)
+    bg.profile_read()
+    timer.rounds(fn, steps)
+    bg.profile_enable(False)
+    total, launches = bg.profile_read()
+    return total / max(launches, 1), launches
+
+
+def encode_flops(bits) -> tuple[float, float]:
+    """fp64 flops per token-head of the encode's rotations (2 d_g^2 per key group, 2 x 128^2 for the
+    value), averaged over the KV heads; the norms and threshold counts are not counted."""
+    fk = [sum(2.0 * (2 * int((row == w).sum())) ** 2 for w in (1, 2, 3, 4)) for row in bits]
+    return float(np.mean(fk)), 2.0 * 128 * 128
+
+
+class Layer:
+    """One synthetic layer resident in HBM: plan, prefill-encoded packed cache (capacity T plus the
+    workload's append), replicas of the cache and of the constant image, the query and new token."""
+
+    def __init__(self, bg, torch, cfg, dev, replica_bytes, keep_fp16=False):
+        import synth
+        self.cfg = cfg
+        b, t, hkv, hq = cfg.batch, cfg.seq_len, cfg.n_kv_heads, cfg.n_q_heads
+        timer = Timer(torch)
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.float16 else a).to(dev)
+
+        self.to_dev = to_dev
+        # ---- one-time rows: energy, allocation, plan
+        q_cal, k_cal = synth.calibration(cfg)
+        qc, kc = to_dev(q_cal), to_dev(k_cal)
+        e_dev = torch.empty((hkv, 64), dtype=torch.float64, device=dev)
+        bits_dev = torch.empty((hkv, 64), dtype=torch.int8, device=dev)
+        bg.energy(qc, kc, hkv, e_dev)
+        bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
+        torch.cuda.synchronize()
+        e0, e1, e2 = timer.ev(), timer.ev(), timer.ev()
+        e0.record()
+        for _ in range(10):
+            bg.energy(qc, kc, hkv, e_dev)
+        e1.record()
+        for _ in range(10):
+            bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
+        e2.record()
+        torch.cuda.synchronize()
+        self.energy_us = e0.elapsed_time(e1) * 100.0
+        self.energy_bytes = q_cal.size * 2 + k_cal.size * 2
+        self.alloc_us = e1.elapsed_time(e2) * 100.0
+        self.bits = bits_dev.cpu().numpy()
+        th = time.perf_counter()
+        bits_host = bg.allocate(e_dev.cpu().numpy(), cfg.k_bits)
+        self.alloc_host_us = (time.perf_counter() - th) * 1e6
+        assert np.array_equal(bits_host, self.bits), "host and device allocations differ"
+        tp = time.perf_counter()
+        self.plan = plan = bg.Plan(self.bits, cfg.k_bits, cfg.v_bits, hq, seed=cfg.seed, layer=0)
+        self.plan_ms = (time.perf_counter() - tp) * 1e3
+        del qc, kc
+
+        # ---- prefill encode of the whole context (timed once more after a first pass)
+        self.cap = cap = t + max(64, cfg.append)
+        self.cache = cache = bg.Cache(plan, b, cap, device=dev)
+        log("%s: generating %d x %d tokens" % (cfg.name, b, t))
+        kd = to_dev(np.stack([synth.keys(cfg, seq=s, count=t) for s in range(b)]))
+        vd = to_dev(np.stack([synth.values(cfg, seq=s, count=t) for s in range(b)]))
+        cache.encode(kd, vd, 0)
+        torch.cuda.synchronize()
+        e0, e1, e2 = timer.ev(), timer.ev(), timer.ev()
+        e0.record()
+        plan.encode_k(cache.consts, kd, cap, 0, cache.k_codes, cache.k_norms)
+        e1.record()
+        plan.encode_v(cache.consts, vd, cap, 0, cache.v_codes, cache.v_norms)
+        e2.record()
+        torch.cuda.synchronize()
+        self.enc_k_s, self.enc_v_s = e0.elapsed_time(e1) / 1e3, e1.elapsed_time(e2) / 1e3
+        self.token_heads = b * t * hkv
+        self.kd, self.vd = (kd, vd) if keep_fp16 else (None, None)
+        del kd, vd
+        # ---- the workload's append (new tokens at positions T ..), encoded into the same cache
+        self.append = None
+        if cfg.append > 0:
+            ka = to_dev(np.stack([synth.keys(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
+            va = to_dev(np.stack([synth.values(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
+            plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
+            plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
+            torch.cuda.synchronize()
+            a0, a1, a2 = timer.ev(), timer.ev(), timer.ev()
+            a0.record()
+            plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
+            a1.record()
+            plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
+            a2.record()
+            torch.cuda.synchronize()
+            ak, av = a0.elapsed_time(a1) / 1e3, a1.elapsed_time(a2) / 1e3
+            ath = b * cfg.append * hkv
+            fk, fv = encode_flops(self.bits)
+            self.append = {"tokens": cfg.append, "at": t, "k_and_v": round(ath / (ak + av)), "k": round(ath / ak),
+                           "v": round(ath / av), "us": round((ak + av) * 1e6, 2),
+                           "fp64_frac": round(ath * (fk + fv) / (ak + av) / 1e12 / FP64_PEAK_TFLOPS, 4)}
+            log("%s: append of %d tokens at %d: %.1f us (%.0f M token-heads/s)" % (
+                cfg.name, cfg.append, t, (ak + av) * 1e6, ath / (ak + av) / 1e6))
+            del ka, va
+
+        # ---- the appended token and the query (position T), written into every replica
+        cfg1 = dataclasses.replace(cfg, append=1)
+        self.k_new = to_dev(np.stack([synth.keys(cfg1, seq=s, start=t, count=1) for s in range(b)]))
+        self.v_new = to_dev(np.stack([synth.values(cfg1, seq=s, start=t, count=1) for s in range(b)]))
+        self.q = to_dev(np.stack([synth.query(cfg, seq=s, pos=t) for s in range(b)]))
+        self.packed = cache.packed_bytes(t + 1)
+        self.n_rep = n_rep = max(1, math.ceil(replica_bytes / self.packed))
+        log("%s: packed bytes/step %.1f MB; %d replicas" % (cfg.name, self.packed / 1e6, n_rep))
+        self.reps = [(cache.consts, cache.k_codes, cache.k_norms, cache.v_codes, cache.v_norms)]
+        for _ in range(n_rep - 1):
+            self.reps.append(tuple(x.clone() for x in self.reps[0]))
+        self.out = torch.empty((b, hq, 128), dtype=torch.int16, device=dev)
+        self.ws = torch.empty(plan.workspace_size(b, t + 1), dtype=torch.uint8, device=dev)
+        self.pos = torch.full((b,), t, dtype=torch.int32, device=dev)
+        self.seq_lens = torch.full((b,), t + 1, dtype=torch.int32, device=dev)
+        for i in range(n_rep):  # every replica holds token t before the timed decode calls
+            self.serve(i)
+        torch.cuda.synchronize()
+
+    def attn(self, i):  # one decode-attention call over T + 1 tokens
+        c_, kc_, kn_, vc_, vn_ = self.reps[i % self.n_rep]
+        t = self.cfg.seq_len
+        self.plan.decode_attn(c_, self.q, kc_, kn_, vc_, vn_, self.cap, self.seq_lens, t + 1, self.out, self.ws)
+
+    def serve(self, i):  # one serving step: append the new key / value at T, then attend
+        c_, kc_, kn_, vc_, vn_ = self.reps[i % self.n_rep]
+        t = self.cfg.seq_len
+        self.plan.decode_step(c_, self.q, self.k_new, self.v_new, self.pos, t + 1, kc_, kn_, vc_, vn_, self.cap,
+                              self.out, self.ws)
+
+    def record(self, bg, timer, steps, warmup):
+        """Decode timing, kernel roofline, percentiles, serving step, encode and append rates."""
+        for i in range(warmup):
+            self.attn(i)
+            self.serve(i)
+        step_ms, host_ms, n = timer.rounds(self.attn, steps)
+        calls = timer.per_call(self.attn, steps)
+        serve_ms = timer.rounds(self.serve, steps)[0]
+        k_ms, launches = kernel_ms(bg, timer, self.attn, steps)
+        fk, fv = encode_flops(self.bits)
+        th = self.token_heads
+        enc_s = self.enc_k_s + self.enc_v_s
+        cfg = self.cfg
+        rec = {
+            "workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "n_kv_heads": cfg.n_kv_heads,
+            "n_q_heads": cfg.n_q_heads, "k_bits": cfg.k_bits, "v_bits": cfg.v_bits,
+            "packed_bytes_per_step": self.packed, "decode_ms": round(step_ms, 5),
+            "decode_GBps": round(self.packed / (step_ms / 1e3) / 1e9, 2),
+            "decode_hbm_peak_frac": round(self.packed / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(calls, [10, 50, 90])],
+            "kernel_ms": round(k_ms, 5),
+            "kernel_frac": round(self.packed / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "serving_step_ms": round(serve_ms, 5),
+            "encode": {"token_heads_per_s": round(th / enc_s), "k": round(th / self.enc_k_s),
+                       "v": round(th / self.enc_v_s), "tokens": cfg.batch * cfg.seq_len,
+                       "fp64_flops_per_token_head": {"k": round(fk), "v": round(fv)},
+                       "fp64_frac": round(th * (fk + fv) / enc_s / 1e12 / FP64_PEAK_TFLOPS, 4)},
+            "energy": {"us": round(self.energy_us, 2), "bytes": self.energy_bytes,
+                       "hbm_peak_frac": round(self.energy_bytes / (self.energy_us / 1e6) / 1e9 / HBM_PEAK_GBPS, 5)},
+            "append": self.append,
+        }
+        log("%s: decode %.4f ms (%.0f GB/s), kernel %.4f ms (frac %.3f, %d launches), p10/50/90 %s, "
+            "serving step %.4f ms, host enqueue %.4f ms/call" % (
+                cfg.name, step_ms, self.packed / (step_ms / 1e3) / 1e9, k_ms, rec["kernel_frac"], launches,
+                rec["decode_ms_p10_p50_p90"], serve_ms, host_ms))
+        return rec, step_ms, serve_ms, k_ms, calls, n
+
+    def free(self):
+        self.reps = self.kd = self.vd = None
+        self.plan.close()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +410,8 @@ def main() -> int:
     ap.add_argument("--replica-bytes", type=float, default=1.1e9)
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="measure only the main workload (for profiler runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/decode_kernel_traffic.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--packed-bytes", type=int, default=None)
@@ -194,175 +438,26 @@ def main() -> int:
     b, t, hkv, hq = cfg.batch, cfg.seq_len, cfg.n_kv_heads, cfg.n_q_heads
     log("config %d %s: batch %d, T %d, %d/%d heads, K%dV%d" % (cfg.cid, cfg.name, b, t, hkv, hq, cfg.k_bits,
                                                               cfg.v_bits))
-
-    def to_dev(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.float16 else a).to(dev)
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    # ---- one-time rows: energy, allocation, plan
-    q_cal, k_cal = synth.calibration(cfg)
-    qc, kc = to_dev(q_cal), to_dev(k_cal)
-    e_dev = torch.empty((hkv, 64), dtype=torch.float64, device=dev)
-    bits_dev = torch.empty((hkv, 64), dtype=torch.int8, device=dev)
-    bg.energy(qc, kc, hkv, e_dev)
-    bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
-    torch.cuda.synchronize()
-    e0, e1, e2 = ev(), ev(), ev()
-    e0.record()
-    for _ in range(10):
-        bg.energy(qc, kc, hkv, e_dev)
-    e1.record()
-    for _ in range(10):
-        bg.allocate_device(e_dev, cfg.k_bits, bits_dev)
-    e2.record()
-    torch.cuda.synchronize()
-    energy_us = e0.elapsed_time(e1) * 100.0
-    alloc_us = e1.elapsed_time(e2) * 100.0
-    bits = bits_dev.cpu().numpy()
-    e_host = e_dev.cpu().numpy()
-    th = time.perf_counter()
-    bits_host = bg.allocate(e_host, cfg.k_bits)
-    alloc_host_us = (time.perf_counter() - th) * 1e6
-    assert np.array_equal(bits_host, bits), "host and device allocations differ"
-    tp = time.perf_counter()
-    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, hq, seed=cfg.seed, layer=0)
-    plan_ms = (time.perf_counter() - tp) * 1e3
-
-    # ---- prefill encode of the whole context (timed once more after a warm-up)
-    cap = t + max(64, cfg.append)
-    cache = bg.Cache(plan, b, cap, device=dev)
-    log("generating %d x %d tokens" % (b, t))
-    ks = [synth.keys(cfg, seq=s, count=t) for s in range(b)]
-    vs = [synth.values(cfg, seq=s, count=t) for s in range(b)]
-    kd = to_dev(np.stack(ks))
-    vd = to_dev(np.stack(vs))
-    del ks, vs
-    cache.encode(kd, vd, 0)
-    torch.cuda.synchronize()
-    e0, e1, e2 = ev(), ev(), ev()
-    e0.record()
-    plan.encode_k(cache.consts, kd, cap, 0, cache.k_codes, cache.k_norms)
-    e1.record()
-    plan.encode_v(cache.consts, vd, cap, 0, cache.v_codes, cache.v_norms)
-    e2.record()
-    torch.cuda.synchronize()
-    enc_k_s, enc_v_s = e0.elapsed_time(e1) / 1e3, e1.elapsed_time(e2) / 1e3
-    token_heads = b * t * hkv
-    # ---- the workload's append (new tokens at positions T ..), encoded into the same cache
-    append_rec = None
-    if cfg.append > 0:
-        ka = to_dev(np.stack([synth.keys(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
-        va = to_dev(np.stack([synth.values(cfg, seq=s, start=t, count=cfg.append) for s in range(b)]))
-        plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
-        plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
-        torch.cuda.synchronize()
-        a0, a1, a2 = ev(), ev(), ev()
-        a0.record()
-        plan.encode_k(cache.consts, ka, cap, t, cache.k_codes, cache.k_norms)
-        a1.record()
-        plan.encode_v(cache.consts, va, cap, t, cache.v_codes, cache.v_norms)
-        a2.record()
-        torch.cuda.synchronize()
-        ak, av = a0.elapsed_time(a1) / 1e3, a1.elapsed_time(a2) / 1e3
-        ath = b * cfg.append * hkv
-        append_rec = {"tokens": cfg.append, "at": t, "k_and_v": round(ath / (ak + av)), "k": round(ath / ak),
-                      "v": round(ath / av), "us": round((ak + av) * 1e6, 2)}
-        log("append of %d tokens at %d: %.1f us (%.0f M token-heads/s)" % (cfg.append, t, (ak + av) * 1e6,
-                                                                           ath / (ak + av) / 1e6))
-        del ka, va
-
-    # ---- the appended token and the query (position T)
-    cfg1 = dataclasses.replace(cfg, append=1)
-    k_new = to_dev(np.stack([synth.keys(cfg1, seq=s, start=t, count=1) for s in range(b)]))
-    v_new = to_dev(np.stack([synth.values(cfg1, seq=s, start=t, count=1) for s in range(b)]))
-    q = to_dev(np.stack([synth.query(cfg, seq=s, pos=t) for s in range(b)]))
-    packed = cache.packed_bytes(t + 1)
-    n_rep = max(1, math.ceil(args.replica_bytes / packed))
-    log("packed bytes/step %.1f MB; %d replicas" % (packed / 1e6, n_rep))
-    reps = [(cache.k_codes, cache.k_norms, cache.v_codes, cache.v_norms)]
-    for _ in range(n_rep - 1):
-        reps.append(tuple(x.clone() for x in reps[0]))
-    out = torch.empty((b, hq, 128), dtype=torch.int16, device=dev)
-    ws = torch.empty(plan.workspace_size(b, t + 1), dtype=torch.uint8, device=dev)
-
-    pos = torch.full((b,), t, dtype=torch.int32, device=dev)
-    seq_lens = torch.full((b,), t + 1, dtype=torch.int32, device=dev)
-    for i in range(n_rep):  # every replica holds token t before the timed decode calls
-        kc_, kn_, vc_, vn_ = reps[i]
-        plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
-    torch.cuda.synchronize()
-
-    def attn(i):  # one decode-attention call over t + 1 tokens: decode kernel, split merge
-        kc_, kn_, vc_, vn_ = reps[i % n_rep]
-        plan.decode_attn(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, out, ws)
-
-    def serve(i):  # one serving step: append the new key / value at t, then attend (fused entry point)
-        kc_, kn_, vc_, vn_ = reps[i % n_rep]
-        plan.decode_step(cache.consts, q, k_new, v_new, pos, t + 1, kc_, kn_, vc_, vn_, cap, out, ws)
-
-    spin = getattr(torch.cuda, "_sleep", None)
-
-    def timed_round(fn, i0, n):
-        # one round: n calls enqueued behind a short GPU spin so that the host has queued
-        # them all before the GPU reaches them; the events bracket the calls only
-        torch.cuda.synchronize()
-        if spin is not None:
-            spin(int(30e6))
-        s0, s1 = ev(), ev()
-        s0.record()
-        th = time.perf_counter()
-        for i in range(n):
-            fn(i0 + i)
-        th = time.perf_counter() - th
-        s1.record()
-        torch.cuda.synchronize()
-        return s0.elapsed_time(s1), th
-
-    for i in range(args.warmup):
-        attn(i)
-        serve(i)
-    torch.cuda.synchronize()
-    per_round = min(args.steps, 100)
-    rounds = max(1, args.steps // per_round)
-    round_ms, host_enqueue_s, n_steps = [], 0.0, 0
-    for r in range(rounds):
-        ms, th = timed_round(attn, args.warmup + n_steps, per_round)
-        round_ms.append(ms / per_round)
-        host_enqueue_s += th
-        n_steps += per_round
-    step_ms = sum(round_ms) / len(round_ms)
-    serve_ms = sum(timed_round(serve, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
-    # Decode-kernel duration: the same decode calls once more with the library's HIP events
-    # bound to every decode-kernel launch (hipExtLaunchKernel on the launch stream, so the
-    # elapsed time is the kernel's own start-to-end time); a pass of its own because event
-    # timing can slow the dispatch of the launches around it.
-    bg.profile_enable(True)
-    bg.profile_read()
-    for r in range(rounds):
-        timed_round(attn, r * per_round, per_round)
-    bg.profile_enable(False)
-    kern_ms_total, launches = bg.profile_read()
-    kern_ms = kern_ms_total / max(launches, 1)
+    timer = Timer(torch)
+    lay = Layer(bg, torch, cfg, dev, args.replica_bytes, keep_fp16=True)
+    main_rec, step_ms, serve_ms, kern_ms, calls, n_steps = lay.record(bg, timer, args.steps, args.warmup)
+    packed = lay.packed
     value = packed / (step_ms / 1e3) / 1e9
     achieved = packed / (kern_ms / 1e3) / 1e9
-    log("decode %.4f ms (%.0f GB/s); serving step %.4f ms; decode kernel %.4f ms (%.0f GB/s, %d launches); "
-        "host enqueue %.4f ms/call" % (step_ms, value, serve_ms, kern_ms, achieved, launches,
-                                       host_enqueue_s * 1e3 / n_steps))
 
     # ---- the fp16 sink + recent-window variant (4 + 128 tokens in fp16, the rest packed)
     buf = bg.Buffer(b, hkv, 4, 128, device=dev)
-    buf.append(kd, vd, 0)
-    buf.append(k_new, v_new, t)
+    buf.append(lay.kd, lay.vd, 0)
+    buf.append(lay.k_new, lay.v_new, t)
 
     def attn_buf(i):
-        kc_, kn_, vc_, vn_ = reps[i % n_rep]
-        plan.decode_attn_buffered(cache.consts, q, kc_, kn_, vc_, vn_, cap, seq_lens, t + 1, buf, out, ws)
+        c_, kc_, kn_, vc_, vn_ = lay.reps[i % lay.n_rep]
+        lay.plan.decode_attn_buffered(c_, lay.q, kc_, kn_, vc_, vn_, lay.cap, lay.seq_lens, t + 1, buf, lay.out,
+                                      lay.ws)
 
     for i in range(max(5, args.warmup // 5)):
         attn_buf(i)
-    buf_ms = sum(timed_round(attn_buf, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
+    buf_ms = timer.rounds(attn_buf, args.steps)[0]
     log("buffered decode (4 sink + 128 recent fp16 tokens) %.4f ms" % buf_ms)
     del buf
 
@@ -370,35 +465,38 @@ def main() -> int:
     # block table (one sequence), the same bytes per call
     paged_ms = None
     if b == 1:
-        table = torch.from_numpy(np.random.default_rng(0).permutation(cache.tiles).astype(np.int32)[None]).to(dev)
+        table = torch.from_numpy(np.random.default_rng(0).permutation(lay.cache.tiles).astype(np.int32)[None]).to(dev)
 
         class _Pool:
             def __init__(self, arrs):
-                self.k_codes, self.k_norms, self.v_codes, self.v_norms = arrs
+                self.consts, self.k_codes, self.k_norms, self.v_codes, self.v_norms = arrs
 
             def desc(self):
-                return bg._Pages(table.data_ptr(), cache.tiles, cache.tiles)
+                return bg._Pages(table.data_ptr(), lay.cache.tiles, lay.cache.tiles)
 
-        pools = [_Pool(r) for r in reps]
+        pools = [_Pool(r) for r in lay.reps]
 
         def attn_paged(i):
-            plan.decode_attn_paged(cache.consts, q, pools[i % n_rep], seq_lens, t + 1, out, ws)
+            pl = pools[i % lay.n_rep]
+            lay.plan.decode_attn_paged(pl.consts, lay.q, pl, lay.seq_lens, t + 1, lay.out, lay.ws)
 
         for i in range(max(5, args.warmup // 5)):
             attn_paged(i)
-        paged_ms = sum(timed_round(attn_paged, r * per_round, per_round)[0] for r in range(rounds)) / (rounds * per_round)
+        paged_ms = timer.rounds(attn_paged, args.steps)[0]
         log("paged decode (shuffled block table) %.4f ms" % paged_ms)
 
     # ---- fp16 baseline: the same keys and values uncompressed, the same split-sequence decode
     # (bgtq_fp16_decode_attn) over the same t + 1 tokens, replicated against the Infinity Cache
-    del reps
-    kf = torch.zeros((b, cap, hkv, 128), dtype=torch.int16, device=dev)
+    reps_main = lay.reps
+    lay.reps = None
+    del reps_main
+    kf = torch.zeros((b, lay.cap, hkv, 128), dtype=torch.int16, device=dev)
     vf = torch.zeros_like(kf)
-    kf[:, :t] = kd
-    vf[:, :t] = vd
-    kf[:, t] = k_new[:, 0]
-    vf[:, t] = v_new[:, 0]
-    del kd, vd
+    kf[:, :t] = lay.kd
+    vf[:, :t] = lay.vd
+    kf[:, t] = lay.k_new[:, 0]
+    vf[:, t] = lay.v_new[:, 0]
+    lay.kd = lay.vd = None
     fp16_bytes = b * (t + 1) * hkv * 128 * 2 * 2
     n_rep16 = max(1, math.ceil(args.replica_bytes / fp16_bytes))
     reps16 = [(kf, vf)] + [(kf.clone(), vf.clone()) for _ in range(n_rep16 - 1)]
@@ -406,12 +504,11 @@ def main() -> int:
 
     def fp16_attn(i):
         kk, vv = reps16[i % n_rep16]
-        bg.fp16_decode_attn(q, kk, vv, seq_lens, t + 1, out, ws16)
+        bg.fp16_decode_attn(lay.q, kk, vv, lay.seq_lens, t + 1, lay.out, ws16)
 
     for i in range(max(5, args.warmup // 5)):
         fp16_attn(i)
-    rounds16 = max(1, rounds // 5)
-    fp16_ms = sum(timed_round(fp16_attn, r * per_round, per_round)[0] for r in range(rounds16)) / (rounds16 * per_round)
+    fp16_ms = timer.rounds(fp16_attn, max(100, args.steps // 5))[0]
     log("fp16 baseline %.4f ms (%.0f GB/s of fp16 K/V); packed decode %.2fx faster" %
         (fp16_ms, fp16_bytes / (fp16_ms / 1e3) / 1e9, fp16_ms / step_ms))
     del reps16, kf, vf
@@ -420,7 +517,7 @@ def main() -> int:
     src = torch.empty(1 << 28, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
-    c0, c1 = ev(), ev()
+    c0, c1 = timer.ev(), timer.ev()
     c0.record()
     for _ in range(10):
         dst.copy_(src)
@@ -429,12 +526,27 @@ def main() -> int:
     copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
     del src, dst
 
+    # ---- the other synthetic layers, measured the same way (decode, kernel, encode, append)
+    others = {}
+    if not args.no_other_configs:
+        for cid in sorted(synth.CONFIGS):
+            if cid == cfg.cid:
+                continue
+            o = Layer(bg, torch, synth.CONFIGS[cid], dev, args.replica_bytes)
+            others[str(cid)] = o.record(bg, timer, min(args.steps, 200), min(args.warmup, 20))[0]
+            o.free()
+            del o
+            torch.cuda.empty_cache()
+
     traffic = load_traffic(cfg.cid)
+    fk, fv = encode_flops(lay.bits)
+    enc_s = lay.enc_k_s + lay.enc_v_s
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
-        "step_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(round_ms, [10, 50, 90])],
-        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "step_ms_p10_p50_p90": main_rec["decode_ms_p10_p50_p90"],
+        "step_ms_percentiles_from": "per-call event times of %d back-to-back decode calls" % len(calls),
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": b, "seq_len": t, "n_kv_heads": hkv, "n_q_heads": hq,
                    "k_bits": cfg.k_bits, "v_bits": cfg.v_bits, "head_dim": 128, "cache_io": "packed codes + fp16 norms",
                    "query_io": "fp16", "accumulate": "fp32", "parallelism": "single GPU"},
@@ -451,24 +563,29 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": STREAM_KERNEL, "kernel_ms": round(kern_ms, 5)},
-        "append_token_heads_per_s": append_rec,
-        "encode_token_heads_per_s": {"k_and_v": round(token_heads / (enc_k_s + enc_v_s)),
-                                     "k": round(token_heads / enc_k_s), "v": round(token_heads / enc_v_s),
-                                     "tokens": b * t},
+        "append_token_heads_per_s": lay.append,
+        "encode_token_heads_per_s": {"k_and_v": round(lay.token_heads / enc_s),
+                                     "k": round(lay.token_heads / lay.enc_k_s),
+                                     "v": round(lay.token_heads / lay.enc_v_s), "tokens": b * t,
+                                     "roofline": {"bound": "fp64", "peak_TFLOPs": FP64_PEAK_TFLOPS,
+                                                  "flops_per_token_head": round(fk + fv),
+                                                  "frac": main_rec["encode"]["fp64_frac"]}},
         "fp16_baseline": {"what": "bgtq_fp16_decode_attn: the same keys and values uncompressed (fp16), the same "
                                   "split-sequence decode and merge, over the same t + 1 tokens",
                           "ms": round(fp16_ms, 5), "bytes_per_step": fp16_bytes,
                           "GBps": round(fp16_bytes / (fp16_ms / 1e3) / 1e9, 2),
                           "hbm_peak_frac": round(fp16_bytes / (fp16_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "packed_speedup": round(fp16_ms / step_ms, 3),
+                          "packed_speedup_at_copy_ceiling": round(fp16_bytes / (copy_gbps * 1e9) * 1e3 / step_ms, 3),
                           "compression": round(fp16_bytes / packed, 3)},
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "one_time": {"energy_us": round(energy_us, 2), "allocate_device_us": round(alloc_us, 2),
-                     "allocate_host_us": round(alloc_host_us, 2),
-                     "plan_host_ms": round(plan_ms, 2)},
+        "one_time": {"energy_us": round(lay.energy_us, 2), "energy_hbm_peak_frac": main_rec["energy"]["hbm_peak_frac"],
+                     "allocate_device_us": round(lay.alloc_us, 2), "allocate_host_us": round(lay.alloc_host_us, 2),
+                     "plan_host_ms": round(lay.plan_ms, 2)},
+        "configs": others,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, bits, args.cpu_heads)
+        rec["cpu_baseline"] = cpu_baseline(cfg, lay.bits, args.cpu_heads)
     print(json.dumps(rec), flush=True)
     return 0
 

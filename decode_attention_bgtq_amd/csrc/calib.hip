@@ -10,12 +10,15 @@
 
 namespace bgtq {
 
-// One workgroup of 1024 threads per KV head: thread (phase, coordinate) takes
-// the tokens t = phase (mod 8).  Sums of squares are exact: |x| 2^24 = u =
-// h 2^20 + l (h, l < 2^20), u^2 = h^2 2^40 + 2 h l 2^20 + l^2, the three sums in
-// 64-bit integers folded into 128-bit totals every kFold tokens; then per block
-// over its two coordinates (j, j+64) half-split or (2j, 2j+1) interleaved.
-constexpr int kEnergyThreads = 1024, kEnergyPhases = kEnergyThreads / kHeadDim, kFold = 4096;
+// Eight workgroups of 256 threads per KV head: workgroup p owns the sixteen
+// coordinates of blocks 8p .. 8p + 7 (coordinates 8p .. 8p + 7 and 64 + 8p ..
+// 64 + 8p + 7 half-split, 16p .. 16p + 15 interleaved), thread (phase, half)
+// eight of them (one 16-byte load per token and head) over the tokens t = phase
+// (mod 128).  Sums of squares are exact: |x| 2^24 = u = h 2^20 + l (h, l <
+// 2^20), u^2 = h^2 2^40 + 2 h l 2^20 + l^2, the three sums in 64-bit integers
+// folded into 128-bit totals every kFold tokens; integer sums do not depend on
+// their order, so the split over threads and workgroups changes no bit.
+constexpr int kEnergyThreads = 256, kEnergySplit = kBlocks / 8, kEnergyPhases = kEnergyThreads / 2, kFold = 4096;
 
 __device__ __forceinline__ void sq_split(uint64_t u, uint64_t &a, uint64_t &b, uint64_t &c) {
   const uint64_t h = u >> 20, l = u & 0xFFFFFu;
@@ -30,42 +33,62 @@ __device__ __forceinline__ u128 sq_fold(uint64_t &a, uint64_t &b, uint64_t &c) {
   return s;
 }
 
+// The eight fp16 values of a 16-byte load into the sums of their squares.
+__device__ __forceinline__ void sq_split8(const uint4 v, uint64_t (&s)[8][3]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    sq_split(f16_mag_units((uint16_t)(w[i >> 1] >> (16 * (i & 1)))), s[i][0], s[i][1], s[i][2]);
+}
+
 __global__ __launch_bounds__(kEnergyThreads) void energy_kernel(const uint16_t *__restrict__ q,
                                                                 const uint16_t *__restrict__ k, int64_t n,
                                                                 int hq, int hkv, int inter,
                                                                 double *__restrict__ energy) {
-  __shared__ u128 sq[kEnergyThreads], sk[kEnergyThreads];
-  const int kvh = blockIdx.x, tid = threadIdx.x, c = tid & 127, ph = tid >> 7;
+  __shared__ u128 red[kEnergyThreads][8];
+  __shared__ u128 tot[2][16];
+  const int kvh = blockIdx.x, p = blockIdx.y, tid = threadIdx.x, half = tid & 1, ph = tid >> 1;
   const int G = hq / hkv;
-  u128 aq = 0, ak = 0;
-  uint64_t qa = 0, qb = 0, qc = 0, ka = 0, kb = 0, kc = 0;
+  const int off = inter ? 16 * p + 8 * half : (half ? kBlocks + 8 * p : 8 * p);
+  uint64_t sq[8][3] = {}, sk[8][3] = {};
+  u128 aq[8] = {}, ak[8] = {};
   int cnt = 0;
   for (int64_t t = ph; t < n; t += kEnergyPhases) {
-    const uint16_t *qt = q + ((size_t)t * hq + (size_t)kvh * G) * kHeadDim + c;
-    for (int hh = 0; hh < G; ++hh) sq_split(f16_mag_units(qt[(size_t)hh * kHeadDim]), qa, qb, qc);
-    sq_split(f16_mag_units(k[((size_t)t * hkv + kvh) * kHeadDim + c]), ka, kb, kc);
+    const uint16_t *qt = q + ((size_t)t * hq + (size_t)kvh * G) * kHeadDim + off;
+    for (int hh = 0; hh < G; ++hh) sq_split8(*(const uint4 *)(qt + (size_t)hh * kHeadDim), sq);
+    sq_split8(*(const uint4 *)(k + ((size_t)t * hkv + kvh) * kHeadDim + off), sk);
     if (++cnt == kFold) {  // (at most kFold * G terms below 2^40 in each 64-bit sum)
-      aq += sq_fold(qa, qb, qc);
-      ak += sq_fold(ka, kb, kc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        aq[i] += sq_fold(sq[i][0], sq[i][1], sq[i][2]);
+        ak[i] += sq_fold(sk[i][0], sk[i][1], sk[i][2]);
+      }
       cnt = 0;
     }
   }
-  aq += sq_fold(qa, qb, qc);
-  ak += sq_fold(ka, kb, kc);
-  sq[tid] = aq;
-  sk[tid] = ak;
-  __syncthreads();
-  if (tid < kBlocks) {
-    const int j = tid, a = inter ? 2 * j : j, b = inter ? 2 * j + 1 : j + kBlocks;
-    u128 tq = 0, tk = 0;
 #pragma unroll
-    for (int p = 0; p < kEnergyPhases; ++p) {
-      tq += sq[p * kHeadDim + a] + sq[p * kHeadDim + b];
-      tk += sk[p * kHeadDim + a] + sk[p * kHeadDim + b];
+  for (int i = 0; i < 8; ++i) {
+    aq[i] += sq_fold(sq[i][0], sq[i][1], sq[i][2]);
+    ak[i] += sq_fold(sk[i][0], sk[i][1], sk[i][2]);
+  }
+  // per coordinate over the phases: slot h * 8 + i is coordinate i of half h
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tid][i] = r ? ak[i] : aq[i];
+    __syncthreads();
+    if (tid < 16) {
+      u128 s = 0;
+      for (int f = 0; f < kEnergyPhases; ++f) s += red[2 * f + (tid >> 3)][tid & 7];
+      tot[r][tid] = s;
     }
-    const double eq = ldexp(u128_to_f64(tq), -48) / (double)(n * G);
-    const double ek = ldexp(u128_to_f64(tk), -48) / (double)n;
-    energy[(size_t)kvh * kBlocks + j] = eq * ek;
+    __syncthreads();
+  }
+  if (tid < 8) {  // block 8p + tid: its two coordinates' slots
+    const int a = inter ? 2 * tid : tid, b = inter ? 2 * tid + 1 : 8 + tid;
+    const double eq = ldexp(u128_to_f64(tot[0][a] + tot[0][b]), -48) / (double)(n * G);
+    const double ek = ldexp(u128_to_f64(tot[1][a] + tot[1][b]), -48) / (double)n;
+    energy[(size_t)kvh * kBlocks + 8 * p + tid] = eq * ek;
   }
 }
 
@@ -120,8 +143,11 @@ bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_
     return fail(BGTQ_EINVAL, "bgtq_energy: rope_pairing must be BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED");
   if (n_q_heads / n_kv_heads > 1024)
     return fail(BGTQ_EINVAL, "bgtq_energy: at most 1024 query heads per KV head");
-  energy_kernel<<<n_kv_heads, kEnergyThreads, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
-                                                                         rope_pairing, energy);
+  if (((uintptr_t)q_cal | (uintptr_t)k_cal) & 15u)
+    return fail(BGTQ_EINVAL, "bgtq_energy: q_cal and k_cal must be 16-byte aligned");
+  const dim3 grid(n_kv_heads, kEnergySplit);
+  energy_kernel<<<grid, kEnergyThreads, 0, (hipStream_t)stream>>>(q_cal, k_cal, n_cal, n_q_heads, n_kv_heads,
+                                                                   rope_pairing, energy);
   return launch_status("bgtq_energy");
 }
 

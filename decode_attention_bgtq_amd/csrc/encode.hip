@@ -9,14 +9,18 @@
 
 namespace bgtq {
 
-// Prefill path: one workgroup per (tile, KV head, sequence), every token of the
-// tile and every group at once: exact group norms (four threads per token),
-// then the fp64 rotation and the quantiser with a 4 x 8 register tile per work
-// item (rows x tokens), the work items of all groups spread over the threads.
+// Prefill path: one workgroup per (tile, KV head, sequence), or per half tile
+// (split 2: 32 tokens) when whole tiles would leave compute units idle (an
+// append of a few thousand tokens); every token of the (half) tile and every
+// group at once: exact group norms (four threads per token), then the fp64
+// rotation and the quantiser with a 4 x 8 register tile per work item (rows x
+// tokens), the work items of all groups spread over the threads.  A half
+// tile's value codes fill whole words (32 tokens x v_bits bits), so the two
+// halves of a tile never write the same word.
 template <bool IS_V>
 __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__ consts,
                                                      const uint16_t *__restrict__ x, const TileMap map,
-                                                     int64_t t0, int64_t n_new,
+                                                     int64_t t0, int64_t n_new, int split,
                                                      uint32_t *__restrict__ codes,
                                                      uint16_t *__restrict__ norms) {
   __shared__ float xs[kTile][kHeadDim + 1];
@@ -27,11 +31,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
   __shared__ double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
   const ConstHeader *hd = hdr_of(consts);
   const int hkv = hd->n_kv_heads;
-  const int64_t tile = t0 / kTile + blockIdx.x;
+  const int64_t tile = t0 / kTile + blockIdx.x / split;
+  const int part = blockIdx.x % split, span = kTile / split;
   const int kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t tok0 = tile * kTile;
-  const int lo = (int)(std::max(t0, tok0) - tok0);
-  const int hi = (int)(std::min(t0 + n_new, tok0 + kTile) - tok0);
+  const int lo = (int)(std::max(std::max(t0, tok0 + part * span), tok0) - tok0);
+  const int hi = (int)(std::min(t0 + n_new, tok0 + (part + 1) * span) - tok0);
+  if (lo >= hi) return;  // a half tile outside the range (uniform per workgroup)
   const KvhDesc *kd = (const KvhDesc *)(consts + hd->off_kvh) + kvh;
   const int64_t tix = tile_at(map, b, kvh, tile);
   if (tix < 0) return;  // a paged table entry outside the pool: nothing is written (uniform per workgroup)
@@ -146,7 +152,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) acc[a][bt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[bt], acc[a][bt], 0, 0, 0);
+        for (int bt = 0; bt < 4; ++bt)
+          if (16 * bt < hi && 16 * bt + 16 > lo)  // token tiles of the (half) tile only (uniform)
+            acc[a][bt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[bt], acc[a][bt], 0, 0, 0);
     }
     const int w = gw[0];
     const double *thr = hd->thr[w - 1];
@@ -168,8 +176,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint8_t *__restrict__
         }
       }
   } else {
-    for (int item = tid; item < total_rb * 8; item += 256) {
-      const int grb = item >> 3, tb = item & 7;
+    const int tb0 = lo >> 3, ntb = ((hi + 7) >> 3) - tb0;  // token blocks of eight overlapping [lo, hi)
+    for (int item = tid; item < total_rb * ntb; item += 256) {
+      const int grb = item / ntb, tb = tb0 + item % ntb;
       int gi = 0;
   #pragma unroll
       for (int jg = 1; jg < kMaxGroups; ++jg) gi += (jg < n_groups && grb >= gpre[jg]) ? 1 : 0;
@@ -346,12 +355,15 @@ bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_cons
   const uint8_t *c = (const uint8_t *)dev_consts;
   hipStream_t st = (hipStream_t)stream;
   const bool small = n_new <= 8;  // a few tokens per tile: dot-product path
+  // half tiles when whole tiles would fill fewer than two workgroups per compute unit
+  const int split = (small || (int64_t)grid.x * grid.y * grid.z >= 2 * (int64_t)device_cus()) ? 1 : 2;
+  const dim3 egrid(grid.x * split, grid.y, grid.z);
   if (is_v) {
     if (small) append_kernel<true><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, map, true), t0, n_new);
-    else encode_kernel<true><<<grid, 256, 0, st>>>(c, x, map, t0, n_new, codes, norms);
+    else encode_kernel<true><<<egrid, 256, 0, st>>>(c, x, map, t0, n_new, split, codes, norms);
   } else {
     if (small) append_kernel<false><<<grid, kAppendThreads, 0, st>>>(append_args(plan->p, c, x, codes, norms, map, false), t0, n_new);
-    else encode_kernel<false><<<grid, 256, 0, st>>>(c, x, map, t0, n_new, codes, norms);
+    else encode_kernel<false><<<egrid, 256, 0, st>>>(c, x, map, t0, n_new, split, codes, norms);
   }
   return launch_status(nm);
 }

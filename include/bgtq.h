@@ -74,9 +74,11 @@ const char *bgtq_last_error(void);
  *   k_cal   device fp16 [n_cal][n_kv_heads][head_dim]
  *   energy  device double [n_kv_heads][head_dim/2], written
  *   rope_pairing  BGTQ_ROPE_HALF or BGTQ_ROPE_INTERLEAVED
- * Errors: EINVAL on null pointers, n_cal < 1 or n_cal > 2^22, head_dim != 128,
- * n_q_heads not a positive multiple of n_kv_heads (at most 1024 per KV head),
- * an unknown rope_pairing.
+ * Eight workgroups per KV head (eight blocks each); the integer sums make the
+ * result independent of how the tokens are split.
+ * Errors: EINVAL on null pointers, q_cal or k_cal not 16-byte aligned, n_cal < 1
+ * or n_cal > 2^22, head_dim != 128, n_q_heads not a positive multiple of
+ * n_kv_heads (at most 1024 per KV head), an unknown rope_pairing.
  */
 bgtq_status bgtq_energy(const uint16_t *q_cal, const uint16_t *k_cal, int64_t n_cal,
                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
