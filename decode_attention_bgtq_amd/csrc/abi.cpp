@@ -1,4 +1,5 @@
 // Host side of the C ABI: errors, plans, inspection and profiling.
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -21,10 +22,16 @@ bgtq_status launch_status(const char *what) {
   return BGTQ_OK;
 }
 
+// Compute units of the current device, queried once per device (the launch
+// shapes of every call depend on it; the attribute query is not free).
 int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -603,7 +603,7 @@ constexpr int kPrepWaves = 8;
 template <int G>
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const uint8_t *__restrict__ consts,
                                                                 const uint16_t *__restrict__ q, int hq, int hkv,
-                                                                int64_t off_zero, float kscale,
+                                                                int gr, int64_t off_zero, float kscale,
                                                                 uint8_t *__restrict__ images) {
   typedef PrepOut<G> PO;
   typedef QueryImage<G> QI;
@@ -614,7 +614,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const uint8_t *__
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   PrepIn<G, kPrepWaves> pin;
   prep_issue_keys<G, kPrepWaves>(pin, consts, kvh, wave, lane);
-  prep_issue<G, kPrepWaves>(pin, consts, kvh, q + ((size_t)b * hq + (size_t)kvh * G) * kHeadDim, tid, wave, lane);
+  prep_issue<G, kPrepWaves>(pin, consts, kvh, q + ((size_t)b * hq + (size_t)kvh * gr) * kHeadDim, gr, tid, wave,
+                            lane);
   prep_issue_rot<G, kPrepWaves>(pin, consts, off_zero, kvh, wave, lane);
   prep_stage<G, kPrepWaves>(pin, out, scr, tid);
   prep_build<G, kPrepWaves>(pin, out, scr, kscale, tid, wave, lane);  // ends with a barrier
@@ -655,10 +656,27 @@ struct DecodeArgs {
   int max_pages, n_pages;
   int64_t max_seq_len, off_kvh, off_dtab, off_vlut, off_zero;
   int hkv, hq, wk, tiles_base, tiles_extra, n_splits;  // split s: tiles_base + (s < tiles_extra) tiles
+  int group;  // query heads per KV head (at most the kernel's G: the rows past it are not written)
   int seq_add;  // sequence length = seq_lens[b] + seq_add (1 when seq_lens holds the new token's position)
   int n_sink, n_recent;  // tokens [0, n_sink) and [T - n_recent, T) are served from fp16 buffers, not here
   float kscale;  // softmax scale in log2 units
 };
+
+// Issue priority of a wave from the tiles it has left after the current one.
+// The SIMD's arbiter favours older waves, so at equal priority the four waves
+// of a SIMD finish one after another (about 1.6 us apart at the 128K layer)
+// and the last ones run alone, unable to fill the SIMD; a wave that is behind
+// gets the higher priority, so that the waves of a SIMD finish together.
+__device__ __forceinline__ void wave_priority(int rem) {
+  if (rem >= 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (rem == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (rem == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
 
 template <int G, int VB, int WK>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, StreamCfg<G, VB, WK>::threads)))
@@ -676,9 +694,10 @@ void decode_kernel(const DecodeArgs a) {
   // ---- prologue: every load first, none of them addressed from loaded data
   // (loads complete in order, so waiting for an earlier group does not wait
   // for a later one): the plan's tables, this (sequence, KV head)'s prepared
-  // query registers, then the wave's first two tiles.  The tables go into LDS
-  // as soon as they arrive; one barrier later the tile loop starts with both
-  // tiles in flight.
+  // query registers, then the wave's first tile.  The tables go into LDS as
+  // soon as they arrive; after the barrier the second tile is requested.
+  // (Requesting both tiles at once queues every wave's table loads behind
+  // twice the tile traffic: the barrier came 2 us later at the 128K layer.)
   const int64_t seq_raw = (int64_t)a.seq_lens[b] + a.seq_add;
   const int n4w = kd->n4w;
   const uint32_t cgrp = kd->cgrp, gbit = kd->gbit;
@@ -750,7 +769,6 @@ void decode_kernel(const DecodeArgs a) {
   TileRegs<VB, WK> ra, rb;
   int tile = tile_lo + wave;
   load_tile(ra, kcodes, kstride, a.kn, a.vc, a.vn, base_of(tile, tile_end), lane);
-  load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, base_of(tile + kStreamWaves, tile_end), lane);
   // paged: the page of the tile after next, read one tile ahead of its load
   size_t pnext = paged ? page_of(min(tile + 2 * kStreamWaves, tile_end - 1)) : 0;
   __builtin_amdgcn_sched_barrier(0);
@@ -787,6 +805,7 @@ void decode_kernel(const DecodeArgs a) {
   *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * WK) = 0u;
   *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * (WK + 1)) = 0u;
   __syncthreads();
+  load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, base_of(tile + kStreamWaves, tile_end), lane);
 
   const int ntile = (int)((st.seq + kTile - 1) / kTile);
   const int tile_hi = min(tile_end, ntile);
@@ -805,6 +824,7 @@ void decode_kernel(const DecodeArgs a) {
   // alternating register sets raise the register count past the occupancy
   // limit.)
   for (; tile < tile_hi; tile += kStreamWaves) {
+    wave_priority((tile_hi - 1 - tile) / kStreamWaves);
     process_tile<G, VB, WK>(ra, tile, st, qr, rinv, mrun, mth, lsum, acc0, acc1, lane);
     ra = rb;
     const size_t bn = head_base + (paged ? pnext : (size_t)min(tile + 2 * kStreamWaves, tile_hi - 1));
@@ -812,6 +832,7 @@ void decode_kernel(const DecodeArgs a) {
     if (paged) pnext = page_of(min(tile + 3 * kStreamWaves, tile_hi - 1));
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- merge the waves of this split into one partial per query head
 #pragma unroll
   for (int h = 0; h < G; ++h) lsum[h] = wave_sum(lsum[h]);
@@ -825,8 +846,8 @@ void decode_kernel(const DecodeArgs a) {
     rr[4 + 64 + lane] = acc1[h >> 2][h & 3];
   }
   __syncthreads();
-  const size_t head0 = (size_t)b * a.hq + (size_t)kvh * G;  // first query head of this (sequence, KV head)
-  for (int idx = tid; idx < G * kHeadDim; idx += kStreamThreads) {
+  const size_t head0 = (size_t)b * a.hq + (size_t)kvh * a.group;  // first query head of this (sequence, KV head)
+  for (int idx = tid; idx < a.group * kHeadDim; idx += kStreamThreads) {
     const int h = idx / kHeadDim, i = idx % kHeadDim;
     float mx = -INFINITY;
 #pragma unroll
@@ -884,8 +905,11 @@ DecodeKernel pick_vb(int vb, int wk) {
   }
 }
 
+// The kernel instance of a group size: 3 heads run as 4, 5..7 as 8.
+int kernel_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8; }
+
 DecodeKernel pick_decode(int g, int vb, int wk) {
-  switch (g) {
+  switch (kernel_group(g)) {
     case 1: return pick_vb<1>(vb, wk);
     case 2: return pick_vb<2>(vb, wk);
     case 4: return pick_vb<4>(vb, wk);
@@ -901,7 +925,7 @@ struct DecodeLayout {
 };
 
 size_t query_image_bytes(int g) {
-  switch (g) {
+  switch (kernel_group(g)) {
     case 1: return QueryImage<1>::bytes;
     case 2: return QueryImage<2>::bytes;
     case 4: return QueryImage<4>::bytes;
@@ -931,17 +955,25 @@ DecodeLayout decode_layout(const Plan &p, int batch, int64_t max_seq_len) {
   return d;
 }
 
-// The decode kernels address LDS from offset 0: they must have no static LDS.
-bool decode_static_lds_ok(decode_fn fn) {
+// Once per (kernel, device): the decode kernels address LDS from offset 0, so
+// they must have no static LDS; and their dynamic LDS above 64 KB must be
+// allowed.  Later calls find the pair in the list.
+bgtq_status decode_kernel_ready(decode_fn fn, int smem) {
   static std::mutex mu;
-  static std::vector<decode_fn> checked;
+  static std::vector<std::pair<decode_fn, int>> ready;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BGTQ_EDEVICE, "decode: no current device");
   std::lock_guard<std::mutex> lk(mu);
-  for (decode_fn f : checked)
-    if (f == fn) return true;
+  for (const auto &r : ready)
+    if (r.first == fn && r.second == dev) return BGTQ_OK;
   hipFuncAttributes attr{};
-  if (hipFuncGetAttributes(&attr, (const void *)fn) != hipSuccess || attr.sharedSizeBytes != 0) return false;
-  checked.push_back(fn);
-  return true;
+  if (hipFuncGetAttributes(&attr, (const void *)fn) != hipSuccess || attr.sharedSizeBytes != 0)
+    return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
+  if (smem > 65536 &&
+      hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
+    return fail(BGTQ_EDEVICE, "decode: LDS request above the limit");
+  ready.emplace_back(fn, dev);
+  return BGTQ_OK;
 }
 
 float kscale_of(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }  // logits in log2 units
@@ -966,11 +998,8 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   const DecodeKernel k = pick_decode(G, vb, p.hdr.wk);
   const int smem = k.smem;
   decode_fn fn = k.fn;
-  if (!decode_static_lds_ok(fn)) return fail(BGTQ_EDEVICE, "decode: kernel has static LDS");
-  if (smem > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void *)fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return fail(BGTQ_EDEVICE, "decode: LDS request above the limit");
-  }
+  const bgtq_status ks = decode_kernel_ready(fn, smem);
+  if (ks != BGTQ_OK) return ks;
   hipStream_t st = (hipStream_t)c.stream;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   {
@@ -1018,16 +1047,17 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.n_sink = c.n_sink;
   a.n_recent = c.n_recent;
   a.kscale = kscale_of(c.softmax_scale);
+  a.group = G;
   // the queries of every (sequence, KV head), rotated and scaled into the
   // decode kernel's register image
   {
     const dim3 pgrid(p.desc.n_kv_heads, c.batch);
     uint8_t *img = ws + lay.img_off;
-    switch (G) {
-      case 1: prep_kernel<1><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
-      case 2: prep_kernel<2><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
-      case 4: prep_kernel<4><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
-      default: prep_kernel<8><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, a.off_zero, a.kscale, img); break;
+    switch (kernel_group(G)) {
+      case 1: prep_kernel<1><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
+      case 2: prep_kernel<2><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
+      case 4: prep_kernel<4><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
+      default: prep_kernel<8><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
     }
     const bgtq_status ps = launch_status("decode (query preparation)");
     if (ps != BGTQ_OK) return ps;

@@ -206,8 +206,8 @@ bgtq_status build_plan(const bgtq_plan_desc &d, Plan &p, std::string &err) {
     return BGTQ_EINVAL;
   }
   const int G = hq / hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) {
-    err = "query heads per KV head must be 1, 2, 4 or 8";
+  if (G > 8) {
+    err = "at most 8 query heads per KV head";
     return BGTQ_EINVAL;
   }
   if (d.head_dim != kHeadDim) {

@@ -173,9 +173,12 @@ struct PrepIn {
   RotRows<WAVES> rr;
 };
 
+// qb: the KV head's first query head; gr <= G heads are real (a group of 3, 5,
+// 6 or 7 runs as the next power of two): rows h >= gr repeat row gr - 1, so
+// that every row is a valid query and the decode's extra rows are never read.
 template <int G, int WAVES>
 __device__ __forceinline__ void prep_issue(PrepIn<G, WAVES> &in, const uint8_t *consts, int kvh,
-                                           const uint16_t *qb, int tid, int wave, int lane) {
+                                           const uint16_t *qb, int gr, int tid, int wave, int lane) {
   typedef PrepIn<G, WAVES> PI;
   constexpr int kDescWords = (int)(sizeof(KvhDesc) / 4);
   static_assert(kDescWords <= PI::T, "one round of descriptor loads");
@@ -183,7 +186,10 @@ __device__ __forceinline__ void prep_issue(PrepIn<G, WAVES> &in, const uint8_t *
   const KvhDesc *kd = (const KvhDesc *)(consts + hd->off_kvh) + kvh;
   in.dw = ((const uint32_t *)kd)[min(tid, kDescWords - 1)];
 #pragma unroll
-  for (int u = 0; u < PI::nq; ++u) in.qv[u] = qb[min(tid + u * PI::T, G * kHeadDim - 1)];
+  for (int u = 0; u < PI::nq; ++u) {
+    const int i = min(tid + u * PI::T, G * kHeadDim - 1);
+    in.qv[u] = qb[min(i / kHeadDim, gr - 1) * kHeadDim + i % kHeadDim];
+  }
   in.row = ((const uint2 *)(consts + hd->off_rowk))[(size_t)kvh * kHeadDim + (tid & (kHeadDim - 1))];
 }
 

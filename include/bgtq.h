@@ -134,7 +134,8 @@ typedef struct bgtq_plan bgtq_plan;
 
 typedef struct {
   int32_t n_kv_heads;
-  int32_t n_q_heads;    /* multiple of n_kv_heads, query head h reads KV head h / G */
+  int32_t n_q_heads;    /* G = n_q_heads / n_kv_heads query heads per KV head, 1 <= G <= 8;
+                           query head h reads KV head h / G */
   int32_t head_dim;     /* 128 */
   int32_t k_avg_bits;   /* 0..4; each row of k_bits must sum to k_avg_bits * 64 */
   int32_t v_bits;       /* 1..4 */

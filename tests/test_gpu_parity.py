@@ -210,7 +210,8 @@ def test_decode_ragged_batch_and_empty(bg):
     _decode_check(bg, cfg, 1100, batch=5, seq_lens=[0, 1, 64, 700, 1100], capacity=1152)
 
 
-@pytest.mark.parametrize("g,vb", [(1, 1), (2, 2), (4, 3), (8, 4), (8, 1), (4, 4), (2, 3), (1, 2)])
+@pytest.mark.parametrize("g,vb", [(1, 1), (2, 2), (4, 3), (8, 4), (8, 1), (4, 4), (2, 3), (1, 2),
+                                  (3, 2), (5, 3), (6, 1), (7, 2), (7, 4)])  # 3, 5..7: padded kernels
 def test_decode_group_and_value_widths(bg, g, vb):
     cfg = synth.small(2, seq_len=777, n_kv_heads=2, n_q_heads=2 * g, v_bits=vb, k_bits=2)
     _decode_check(bg, cfg, 777)

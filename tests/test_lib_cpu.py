@@ -99,9 +99,11 @@ def test_plan_validation(bg):
     with pytest.raises(bg.BgtqError) as e:
         bg.Plan(bad, 3, 2, n_q_heads=12)
     assert e.value.status == bg.EBUDGET
-    with pytest.raises(bg.BgtqError) as e:
-        bg.Plan(bits, 3, 2, n_q_heads=9)           # G = 3
-    assert e.value.status == bg.EINVAL
+    for hq in (27, 10):                            # G = 9 (above 8); not a multiple of the KV heads
+        with pytest.raises(bg.BgtqError) as e:
+            bg.Plan(bits, 3, 2, n_q_heads=hq)
+        assert e.value.status == bg.EINVAL
+    bg.Plan(bits, 3, 2, n_q_heads=9).close()       # G = 3 runs on the four-head kernels
     with pytest.raises(bg.BgtqError) as e:
         bg.Plan(bits, 3, 5, n_q_heads=12)
     assert e.value.status == bg.EBUDGET
