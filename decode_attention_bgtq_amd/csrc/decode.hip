@@ -28,6 +28,7 @@
 // critical path at the end of the grid.)
 #include <hip/hip_ext.h>
 
+#include "append.h"
 #include "device.h"
 #include "host.h"
 #include "merge.h"
@@ -597,30 +598,37 @@ struct QueryImage {
 
 constexpr int kPrepWaves = 8;
 
-// One workgroup of 8 waves per (KV head, sequence): the G queries rotated once
-// per key width group and scaled (prep.h, in LDS), then rearranged into the
-// register image of the pair's slot.
+struct PrepArgs {
+  const uint8_t *consts;
+  const uint16_t *q;
+  int hq, hkv, gr;  // gr: query heads per KV head (at most G)
+  int64_t off_zero;
+  float kscale;
+  uint8_t *images;
+};
+
+// The G queries of (KV head, sequence) rotated once per key width group and
+// scaled (prep.h, in LDS), then rearranged into the register image of the
+// pair's slot; 8 waves.
 template <int G>
-__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const uint8_t *__restrict__ consts,
-                                                                const uint16_t *__restrict__ q, int hq, int hkv,
-                                                                int gr, int64_t off_zero, float kscale,
-                                                                uint8_t *__restrict__ images) {
+__device__ __forceinline__ void prep_role(const PrepArgs &pa, int kvh, int b) {
   typedef PrepOut<G> PO;
   typedef QueryImage<G> QI;
   constexpr int VQ = VQuads<G>::v, T = 64 * kPrepWaves;
   __shared__ __attribute__((aligned(16))) uint8_t out[PO::bytes];
   __shared__ __attribute__((aligned(16))) uint8_t scr[PrepScratch<G>::bytes];
-  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const uint8_t *consts = pa.consts;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   PrepIn<G, kPrepWaves> pin;
   prep_issue_keys<G, kPrepWaves>(pin, consts, kvh, wave, lane);
-  prep_issue<G, kPrepWaves>(pin, consts, kvh, q + ((size_t)b * hq + (size_t)kvh * gr) * kHeadDim, gr, tid, wave,
-                            lane);
-  prep_issue_rot<G, kPrepWaves>(pin, consts, off_zero, kvh, wave, lane);
+  prep_issue<G, kPrepWaves>(pin, consts, kvh, pa.q + ((size_t)b * pa.hq + (size_t)kvh * pa.gr) * kHeadDim, pa.gr,
+                            tid, wave, lane);
+  prep_issue_rot<G, kPrepWaves>(pin, consts, pa.off_zero, kvh, wave, lane);
   prep_stage<G, kPrepWaves>(pin, out, scr, tid);
-  prep_build<G, kPrepWaves>(pin, out, scr, kscale, tid, wave, lane);  // ends with a barrier
+  prep_build<G, kPrepWaves>(pin, out, scr, pa.kscale, tid, wave, lane);  // ends with a barrier
   const KvhDesc &kds = *(const KvhDesc *)(scr + PrepScratch<G>::kds);
-  uint8_t *img = images + ((size_t)b * hkv + kvh) * QI::bytes;
+  uint8_t *img = pa.images + ((size_t)b * pa.hkv + kvh) * QI::bytes;
   // q4[k][g][l]: head 4g + (l & 3) (repeating a valid head past G), code 16k + l / 4
   for (int i = tid; i < 8 * VQ * kTile; i += T) {
     const int l = i & 63, g = (i >> 6) % VQ, k = (i >> 6) / VQ;
@@ -635,6 +643,41 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const uint8_t *__
     ((uint2 *)(img + QI::kq))[i] = ((const uint2 *)(out + PO::qr))[(k * VQ + g) * 4 + (l & 3)];
   }
   if (tid < G) ((float *)(img + QI::rinv))[tid] = ((const float *)(out + PO::rinv))[tid];
+}
+
+// One workgroup per (KV head, sequence).
+template <int G>
+__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs pa) {
+  prep_role<G>(pa, blockIdx.x, blockIdx.y);
+}
+
+// The front of a serving step in one launch: the new token's key and value
+// appended to the cache and the queries prepared, side by side (the two are
+// independent; the decode kernel after them needs both).  Workgroups [0, n):
+// key append of (sequence, KV head) = (r / hkv, r % hkv); [n, 2n): value
+// append; [2n, 3n): query preparation.  n = batch * hkv.
+static_assert(kAppendThreads == 64 * kPrepWaves, "one workgroup size for both roles");
+template <int G>
+__global__ __launch_bounds__(64 * kPrepWaves) void step_front_kernel(const PrepArgs pa, const AppendArgs ka,
+                                                                     const AppendArgs va,
+                                                                     const int32_t *__restrict__ pos,
+                                                                     int64_t capacity, int n) {
+  const int role = blockIdx.x, hkv = ka.hkv;
+  const int r = role < n ? role : role < 2 * n ? role - n : role - 2 * n;
+  const int kvh = r % hkv, b = r / hkv;
+  if (role >= 2 * n) {
+    prep_role<G>(pa, kvh, b);
+    return;
+  }
+  const int64_t t = pos[b];
+  if (t < 0 || t >= capacity) return;  // uniform per workgroup
+  const int64_t tile = t / kTile;
+  const int lo = (int)(t - tile * kTile);
+  if (role < n) {
+    if (ka.wk > 0) append_role<false>(ka, tile, kvh, b, lo, lo + 1, b);
+  } else {
+    append_role<true>(va, tile, kvh, b, lo, lo + 1, b);
+  }
 }
 
 // ------------------------------------------------------------------ decode kernel
@@ -1049,17 +1092,33 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
   a.kscale = kscale_of(c.softmax_scale);
   a.group = G;
   // the queries of every (sequence, KV head), rotated and scaled into the
-  // decode kernel's register image
+  // decode kernel's register image (in a serving step, side by side with the
+  // new token's append)
   {
-    const dim3 pgrid(p.desc.n_kv_heads, c.batch);
-    uint8_t *img = ws + lay.img_off;
-    switch (kernel_group(G)) {
-      case 1: prep_kernel<1><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
-      case 2: prep_kernel<2><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
-      case 4: prep_kernel<4><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
-      default: prep_kernel<8><<<pgrid, 64 * kPrepWaves, 0, st>>>(a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, img); break;
+    const PrepArgs pa{a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, ws + lay.img_off};
+    if (c.step) {
+      const int n = c.batch * p.desc.n_kv_heads;
+      const unsigned blocks = (unsigned)(3 * n);
+#define BGTQ_FRONT(GK) \
+  step_front_kernel<GK><<<blocks, 64 * kPrepWaves, 0, st>>>(pa, *c.step->ka, *c.step->va, c.step->pos, c.step->capacity, n)
+      switch (kernel_group(G)) {
+        case 1: BGTQ_FRONT(1); break;
+        case 2: BGTQ_FRONT(2); break;
+        case 4: BGTQ_FRONT(4); break;
+        default: BGTQ_FRONT(8); break;
+      }
+#undef BGTQ_FRONT
+    } else {
+      const dim3 pgrid(p.desc.n_kv_heads, c.batch);
+      switch (kernel_group(G)) {
+        case 1: prep_kernel<1><<<pgrid, 64 * kPrepWaves, 0, st>>>(pa); break;
+        case 2: prep_kernel<2><<<pgrid, 64 * kPrepWaves, 0, st>>>(pa); break;
+        case 4: prep_kernel<4><<<pgrid, 64 * kPrepWaves, 0, st>>>(pa); break;
+        default: prep_kernel<8><<<pgrid, 64 * kPrepWaves, 0, st>>>(pa); break;
+      }
     }
-    const bgtq_status ps = launch_status("decode (query preparation)");
+    const bgtq_status ps = launch_status(c.step ? "decode step (append and query preparation)"
+                                                : "decode (query preparation)");
     if (ps != BGTQ_OK) return ps;
   }
   const dim3 grid(lay.n_splits, p.desc.n_kv_heads, c.batch);

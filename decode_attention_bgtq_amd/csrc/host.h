@@ -24,6 +24,16 @@ struct Prof {
 };
 Prof &prof();
 
+struct AppendArgs;
+
+// A serving step's append of the new token (launched with the query
+// preparation): the key and value arguments, each sequence's position.
+struct StepAppend {
+  const AppendArgs *ka, *va;
+  const int32_t *pos;
+  int64_t capacity;
+};
+
 // Decode launches shared by bgtq_decode_attn and bgtq_decode_step.
 struct DecodeCall {
   const void *dev_consts;
@@ -48,12 +58,13 @@ struct DecodeCall {
   int n_sink = 0, n_recent = 0;
   // no HIP allocation of any kind in this call (no profiling events are created)
   bool no_alloc = false;
+  // a serving step: the new token is appended in the launch that prepares the queries
+  const StepAppend *step = nullptr;
 };
 bgtq_status decode_check(const Plan &p, int64_t capacity, int32_t batch, int64_t max_seq_len, float softmax_scale,
                          const void *workspace, size_t ws_bytes, const char *nm);
 bgtq_status decode_launch(const Plan &p, const DecodeCall &c);  // the fused decode kernel
 
-struct AppendArgs;
 AppendArgs append_args(const Plan &p, const uint8_t *consts, const uint16_t *x, uint32_t *codes, uint16_t *norms,
                        const TileMap &map, bool is_v);
 

@@ -1,33 +1,12 @@
 // Fused decode step: the new token's key and value appended to the packed
-// cache in one launch, then the fused decode over the cache including that
-// token ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract:
-// packed-cache serving; Block-GTQ README, backend table).
+// cache, then the fused decode over the cache including that token
+// ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract:
+// packed-cache serving; Block-GTQ README, backend table).  The append runs in
+// the launch that prepares the queries (decode.hip, step_front_kernel).
 #include "append.h"
 #include "device.h"
 #include "host.h"
 
-namespace bgtq {
-
-// Workgroups [0, n): key append of (sequence, KV head) = (r / hkv, r % hkv);
-// [n, 2n): value append.  n = batch * hkv.
-__global__ __launch_bounds__(kAppendThreads) void step_append_kernel(const AppendArgs ka, const AppendArgs va,
-                                                                     const int32_t *__restrict__ pos,
-                                                                     int64_t capacity, int n) {
-  const int role = blockIdx.x, hkv = ka.hkv;
-  const int r = role < n ? role : role - n;
-  const int kvh = r % hkv, b = r / hkv;
-  const int64_t t = pos[b];
-  if (t < 0 || t >= capacity) return;  // uniform per workgroup
-  const int64_t tile = t / kTile;
-  const int lo = (int)(t - tile * kTile);
-  if (role < n) {
-    if (ka.wk > 0) append_role<false>(ka, tile, kvh, b, lo, lo + 1, b);
-  } else {
-    append_role<true>(va, tile, kvh, b, lo, lo + 1, b);
-  }
-}
-
-}  // namespace bgtq
 using namespace bgtq;
 
 namespace {
@@ -44,19 +23,16 @@ bgtq_status step_common(const char *nm, const bgtq_plan *plan, const void *dev_c
   const bgtq_status v = decode_check(p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
   if (v != BGTQ_OK) return v;
   const int n = batch * p.desc.n_kv_heads;
-  const int64_t blocks = (int64_t)n * 2;
-  if (blocks > 0x7FFFFFFF) return fail(BGTQ_EINVAL, std::string(nm) + ": grid too large");
+  if ((int64_t)n * 3 > 0x7FFFFFFF) return fail(BGTQ_EINVAL, std::string(nm) + ": grid too large");
   const TileMap map = pages ? paged_map(p, pages) : contiguous_map(p.desc.n_kv_heads, capacity);
   const uint8_t *c = (const uint8_t *)dev_consts;
   const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, map, false);
   const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, map, true);
-  hipStream_t st = (hipStream_t)stream;
-  step_append_kernel<<<(unsigned)blocks, kAppendThreads, 0, st>>>(ka, va, pos, capacity, n);
-  const bgtq_status ls = launch_status((std::string(nm) + " (append)").c_str());
-  if (ls != BGTQ_OK) return ls;
+  const StepAppend sa{&ka, &va, pos, capacity};
   DecodeCall dc{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, pos, 1, batch, max_seq_len,
                 softmax_scale, out, workspace, stream};
   dc.pages = pages;
+  dc.step = &sa;
   return decode_launch(p, dc);
 }
 
