@@ -40,11 +40,11 @@ def _step(bg, plan, cache, q, k_new, v_new, pos, max_seq_len):
     return out.cpu().numpy().view(np.float16).astype(np.float64)
 
 
-@pytest.mark.parametrize("cid", [4, 2, 1])
-def test_decode_step_ragged_matches_oracle(bg, cid):
+@pytest.mark.parametrize("cid,hq", [(4, None), (2, None), (1, None), (4, 56)])  # 56 / 8: G = 7, padded
+def test_decode_step_ragged_matches_oracle(bg, cid, hq):
     import torch
     prefix, capacity = 200, 320
-    cfg = synth.small(cid, seq_len=prefix, batch=4)
+    cfg = synth.small(cid, seq_len=prefix, batch=4, **({} if hq is None else {"n_q_heads": hq}))
     plan, bits = _plan(bg, cfg)
     cache = bg.Cache(plan, 4, capacity, device="cuda")
     ks = np.stack([synth.keys(cfg, seq=s, count=prefix) for s in range(4)])
@@ -55,7 +55,7 @@ def test_decode_step_ragged_matches_oracle(bg, cid):
     v_new = np.stack([synth.values(cfg, seq=s + 10, count=1)[0] for s in range(4)])
     q = np.stack([synth.query(cfg, seq=s) for s in range(4)])
     max_seq_len = prefix + 1
-    log("decode step config %d pos %s" % (cid, pos))
+    log("decode step config %d (G = %d) pos %s" % (cid, cfg.group, pos))
     got = _step(bg, plan, cache, q, k_new, v_new, pos, max_seq_len)
     for s in range(4):
         n_tok = max(prefix, pos[s] + 1)
