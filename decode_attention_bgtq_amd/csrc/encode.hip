@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const auto xs = [&](int t, int c) -> float { return h2f((uint16_t)(xs2[t][c >> 1] >> (16 * (c & 1)))); };
   __shared__ uint8_t cs_[kTile * kHeadDim];  // values [token][coordinate], keys [coordinate][token]
   const auto cs = [&](int t, int c) -> uint8_t & { return cs_[IS_V ? t * kHeadDim + c : c * kTile + t]; };
-  __shared__ double nrm[kMaxGroups][kTile];
+  __shared__ double ninv[kMaxGroups][kTile];  // sqrt(d_g) / n (0 for a zero group)
   __shared__ uint16_t nrm16[kTile][4];
   __shared__ int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
   __shared__ double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
@@ -92,38 +92,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     total_rb += (gd[gi] + 3) / 4;
   }
 
+  const auto sel = [](const int (&a)[kMaxGroups], int gi) {
+    return gi == 0 ? a[0] : gi == 1 ? a[1] : gi == 2 ? a[2] : a[3];
+  };
   // ---- group norms, exact: |x| 2^24 = h 2^20 + l with h, l < 2^20 integers
   // (h = floor(|x| 16), l = its fraction times 2^20, both exact in fp32), so
-  // x^2 2^48 = h^2 2^40 + 2 h l 2^20 + l^2; the three sums are 64-bit
-  // integers.  Four threads per token, each every fourth coordinate, then the
-  // total rounded once to double.
+  // x^2 2^48 = h^2 2^40 + 2 h l 2^20 + l^2.  The three sums of at most 128
+  // products below 2^40 stay below 2^47, so fp64 fused multiply-adds keep them
+  // exact (cheaper than 64-bit integer multiplies).  Four threads per token,
+  // each every fourth coordinate; after the cross-lane sums, lane q of the
+  // token's four combines group q's sums in 128-bit integers and rounds the
+  // total once to double.  The quantiser's factor sqrt(d_g) / n is taken here,
+  // once per (group, token): a code compares acc * (sqrt(d_g) / n) with the
+  // thresholds, one rounding away from sqrt(d_g) (acc / n), instead of
+  // dividing per code.
   {
     const int t = tid >> 2, q = tid & 3;
+    double A[kMaxGroups], B[kMaxGroups], C[kMaxGroups];
 #pragma unroll
     for (int gi = 0; gi < kMaxGroups; ++gi) {
-      if (gi >= n_groups) break;
-      unsigned long long A = 0, B = 0, C = 0;
-      for (int k = q; k < gd[gi]; k += 4) {
-        const int c = IS_V ? k : cds[gpos[gi] + k];
-        const float f = fabsf(xs(t, c)) * 16.f;
-        const uint32_t h = (uint32_t)f;
-        const uint32_t l = (uint32_t)((f - (float)h) * 1048576.f);
-        A += (unsigned long long)h * h;
-        B += (unsigned long long)h * l;
-        C += (unsigned long long)l * l;
+      A[gi] = 0.0, B[gi] = 0.0, C[gi] = 0.0;
+      if (gi < n_groups) {
+#pragma unroll 4
+        for (int k = q; k < gd[gi]; k += 4) {
+          const int c = IS_V ? k : cds[gpos[gi] + k];
+          const float f = fabsf(xs(t, c)) * 16.f;
+          const float hf = floorf(f);
+          const double h = (double)hf, l = (double)((f - hf) * 1048576.f);
+          A[gi] = fma(h, h, A[gi]);
+          B[gi] = fma(h, l, B[gi]);
+          C[gi] = fma(l, l, C[gi]);
+        }
       }
-      A += __shfl_xor(A, 1);
-      B += __shfl_xor(B, 1);
-      C += __shfl_xor(C, 1);
-      A += __shfl_xor(A, 2);
-      B += __shfl_xor(B, 2);
-      C += __shfl_xor(C, 2);
-      if (q == 0) {
-        const u128 ss = ((u128)A << 40) + ((u128)B << 21) + (u128)C;
-        const double nn = sqrt(ldexp(u128_to_f64(ss), -48));
-        nrm[gi][t] = nn;
-        nrm16[t][IS_V ? 0 : 4 - gw[gi]] = f64_to_f16(nn);
-      }
+      A[gi] += __shfl_xor(A[gi], 1);
+      B[gi] += __shfl_xor(B[gi], 1);
+      C[gi] += __shfl_xor(C[gi], 1);
+      A[gi] += __shfl_xor(A[gi], 2);
+      B[gi] += __shfl_xor(B[gi], 2);
+      C[gi] += __shfl_xor(C[gi], 2);
+    }
+    if (q < n_groups) {
+      const double Aq = q == 0 ? A[0] : q == 1 ? A[1] : q == 2 ? A[2] : A[3];
+      const double Bq = q == 0 ? B[0] : q == 1 ? B[1] : q == 2 ? B[2] : B[3];
+      const double Cq = q == 0 ? C[0] : q == 1 ? C[1] : q == 2 ? C[2] : C[3];
+      const u128 ss = ((u128)(unsigned long long)Aq << 40) + ((u128)(unsigned long long)Bq << 21) +
+                      (u128)(unsigned long long)Cq;
+      const double nn = sqrt(ldexp(u128_to_f64(ss), -48));
+      ninv[q][t] = nn > 0.0 ? sqrt((double)sel(gd, q)) / nn : 0.0;
+      nrm16[t][IS_V ? 0 : 4 - sel(gw, q)] = f64_to_f16(nn);
     }
   }
   __syncthreads();
@@ -131,9 +147,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   // ---- rotation and quantiser.  Keys, every group at once: work item = (row
   // block of four rows of a group, block of eight tokens), a 4 x 8 register tile
   // each.
-  const auto sel = [](const int (&a)[kMaxGroups], int gi) {
-    return gi == 0 ? a[0] : gi == 1 ? a[1] : gi == 2 ? a[2] : a[3];
-  };
   if constexpr (IS_V) {
     // values: Y = Pi X^T on the matrix cores (v_mfma_f64_16x16x4f64: A = 16
     // rows x 4 columns of Pi in lane r + 16 k, B = 4 coordinates x 16 tokens in
@@ -164,18 +177,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
     const int w = gw[0];
     const double *thr = hd->thr[w - 1];
-    const double sd = sqrt((double)kHeadDim);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
         const int t = 16 * bt + lr;
-        const double nn = nrm[0][t];
+        const double zf = ninv[0][t];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * (2 * wave + a) + lk + 4 * e;
-          const double y = nn > 0.0 ? acc[a][bt][e] / nn : 0.0;
-          const double z = sd * y;
+          const double z = acc[a][bt][e] * zf;
           int code = 0;
           for (int kk = 0; kk < (1 << w) - 1; ++kk) code += thr[kk] < z ? 1 : 0;
           cs(t, i) = (uint8_t)code;
@@ -218,15 +229,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       // LDS by bisection; values: one width, the thresholds read through the
       // scalar cache and counted
       const double *thr = IS_V ? hd->thr[w - 1] : thr_s[w - 1];
-      const double sd = sqrt((double)d);
   #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const double nn = nrm[gi][u0 + u];
+        const double zf = ninv[gi][u0 + u];
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (i0 + r >= d) continue;
-          const double y = nn > 0.0 ? acc[r][u] / nn : 0.0;
-          const double z = sd * y;
+          const double z = acc[r][u] * zf;
           // code = #{k : thr[k] < z} over the ascending thresholds
           int code = 0;
           if constexpr (IS_V) {
