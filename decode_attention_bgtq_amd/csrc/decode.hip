@@ -2,27 +2,33 @@
 // packed-cache serving path of "RoPE-Aware Bit Allocation for KV-Cache
 // Quantization", Abstract, and of the Block-GTQ README backend table).
 //
-// Two launches per call.  The decode kernel, one workgroup of 16 waves (one
-// per CU; 8 waves where four waves per SIMD do not fit) per (split of the
-// sequence, KV head, sequence):
-//  prologue  the plan's decode tables into LDS; the G queries of the KV head
-//            rotated once per key width group (fp32 MFMA over the head's
-//            block-diagonal rotation) into the scaled 4-bit-group queries and
-//            the k-step operands of the width-1..3 groups (prep.h), in LDS.
-//            The first tile is requested once the small loads of the
-//            preparation have arrived, so that they are not queued behind it.
-//  tiles     per 64-token tile (lane = token): key words read coalesced
-//            (word-major); logits on the matrix cores (the 4-bit group one
-//            fp32 4x4x1 step per code, the width-1..3 groups one fp16 4x4x4
-//            k-step per four codes, both with LDS centroid lookups, the
-//            lookups of the next batch in flight during the products) times
-//            the group norms, in log2 units; online softmax with wavefront
-//            reductions; the value codes (lane = coordinate) accumulated on the
-//            matrix cores against the fp16 softmax weights in the rotated value
-//            space.  The waves of a workgroup merge into one partial
-//            (m, l, acc[128]) per query head.
-// The merge kernel, one workgroup per (query head, sequence): log-sum-exp
-// merge of the splits, normalisation, un-rotation by Pi_V^T, fp16 output.
+// Three launches per call.
+//  prep_kernel    one workgroup of 8 waves per (KV head, sequence): the G
+//                 queries rotated once per key width group (fp32 MFMA over the
+//                 head's block-diagonal rotation, prep.h), scaled into the
+//                 4-bit-group operands and the k-step operands of the
+//                 width-1..3 groups, written as the decode kernel's register
+//                 image (one 64-lane row per register).  In the serving step
+//                 the same workgroups run beside the new token's append
+//                 (step_front_kernel).
+//  decode_kernel  one workgroup per CU (16 waves, or 12 where four waves per
+//                 SIMD do not fit the registers) per (split of the sequence,
+//                 KV head, sequence).  Prologue: the plan's decode tables into
+//                 LDS (lookup rows), the query registers from the image, the
+//                 first tiles requested.  Per 64-token tile (lane = token):
+//                 key words read coalesced (word-major); logits on the matrix
+//                 cores (the 4-bit group one fp32 4x4x1 step per code, the
+//                 width-1..3 groups one fp16 4x4x4 k-step per four codes, both
+//                 with LDS centroid lookups, the lookups of the next batch in
+//                 flight during the products) times the group norms, in log2
+//                 units; online softmax with wavefront reductions; the value
+//                 codes (lane = coordinate) accumulated on the matrix cores
+//                 against the fp16 softmax weights in the rotated value space.
+//                 The waves of a workgroup merge into one partial
+//                 (m, l, acc[128]) per query head.
+//  merge_kernel   one workgroup per (query head, sequence): log-sum-exp merge
+//                 of the splits, normalisation, un-rotation by Pi_V^T, fp16
+//                 output.
 // (Merging inside the decode kernel, by the last workgroup to arrive, costs
 // more: its chain of device-coherent stores, atomics and loads sits on the
 // critical path at the end of the grid.)
@@ -55,7 +61,7 @@ struct StreamOcc {
 };
 
 // Waves per workgroup: one workgroup per CU (one copy of the lookup rows per
-// CU, every wave of the CU the same age), four waves per SIMD.
+// CU, every wave of the CU the same age), StreamOcc::v waves per SIMD.
 template <int G, int VB, int WK>
 struct StreamCfg {
   static constexpr int waves = 4 * StreamOcc<G, VB, WK>::v;

@@ -1,10 +1,11 @@
 // Query preparation for the fused decode: rotation of the queries once per
 // key width group and their matrix-core operands for the tile loop
 // ("RoPE-Aware Bit Allocation for KV-Cache Quantization", Abstract; Block-GTQ
-// README, backend table).  Internal header.  The decode kernel prepares the
-// queries of its (sequence, KV head) in its own prologue, and the
-// query-rotation entry point rotates batches of queries, both with fp32 MFMA
-// over the block-diagonal matrix of the group rotations.
+// README, backend table).  Internal header.  The preparation kernel (and the
+// serving step's front kernel) prepares the queries of each (sequence, KV
+// head) once per call, and the query-rotation entry point rotates batches of
+// queries, both with fp32 MFMA over the block-diagonal matrix of the group
+// rotations.
 #pragma once
 
 #include "device.h"
@@ -46,7 +47,7 @@ __device__ __forceinline__ void rot_rows(const float *R, int wave, int lane, Rot
   }
 }
 
-// The decode prologue fetches only the nonzero part of R: the row-table
+// The preparation fetches only the nonzero part of R: the row-table
 // entries of the lane's rows first (rot_keys; y = d_g | pos_g << 8 | ..., 0
 // past d_nz), then (rot_rows_sparse) the lane's four columns of each step
 // from R when they meet its row's group [pos_g, pos_g + d_g), else from the
