@@ -217,6 +217,15 @@ def test_decode_group_and_value_widths(bg, g, vb):
     _decode_check(bg, cfg, 777)
 
 
+@pytest.mark.parametrize("g,kb,vb", [(8, 4, 3), (8, 3, 4), (6, 4, 4), (4, 4, 3), (8, 3, 3)])
+def test_decode_wide_tiles(bg, g, kb, vb):
+    """Key and value widths whose tiles decide the occupancy: eight heads at K4V3, K3V4 and K4V4
+    (two waves per SIMD, query operands in registers), four heads at K4V3 (three waves per SIMD,
+    12-wave workgroups), eight heads at K3V3 (three waves, query operands in LDS)."""
+    cfg = synth.small(2, seq_len=1500, n_kv_heads=2, n_q_heads=2 * g, v_bits=vb, k_bits=kb)
+    _decode_check(bg, cfg, 1500)
+
+
 def test_decode_zero_bit_keys(bg):
     """avg 0 bits for keys: every logit is 0, attention is the mean of the values."""
     cfg = synth.small(2, seq_len=200, k_bits=0)
