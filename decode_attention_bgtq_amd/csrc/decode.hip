@@ -126,7 +126,6 @@ __global__ __launch_bounds__(256) void qrot_kernel(const uint8_t *__restrict__ c
 //                    byte moved to bits 8..15 and the slot offset put below
 //                    it, one v_perm_b32.
 //   [vcomp, ..)      one-bit value table (16 bytes per code byte), VB = 1 only
-//   [pt, ..)         per wave: the tile's softmax weights x value norm, fp16 [G][64]
 //   [kw, ..)         per wave: the tile's key words [WK + 2][64] (the last two rows zero)
 //   [qimg, ..)       query operands in LDS only: the (sequence, KV head)'s query
 //                    register image (the preparation kernel's rows, read by
@@ -140,9 +139,8 @@ struct StreamLds {
   static constexpr int rep = kt_bytes, rep_bytes = 256 * 256;
   static constexpr int vslot = VB == 2 ? 8 : 4;                 // bytes per value slot (VB 2..4)
   static constexpr int vcomp = rep + rep_bytes;
-  static constexpr int pt = vcomp + (VB == 1 ? VLut<1>::entries * VLut<1>::bytes : 0);
   static constexpr int W = StreamCfg<G, VB, WK>::waves;
-  static constexpr int kw = pt + W * G * kTile * 2;
+  static constexpr int kw = vcomp + (VB == 1 ? VLut<1>::entries * VLut<1>::bytes : 0);
   static constexpr int kw_rows = WK + 2;  // key words of the tile, then two zero rows
   static constexpr bool qlds = StreamOcc<G, VB, WK>::qlds;
   static constexpr int qimg = kw + W * kw_rows * kTile * 4;
@@ -153,7 +151,7 @@ struct StreamLds {
   static constexpr int alloc = total;
   static_assert(t2 % 2048 == 0 && t1 % 128 == 0 && t3 % 256 == 0 && rep % 256 == 0, "table bases above the index bits");
   static_assert(rep < 65536, "lookup rows addressed by the instruction offset plus a 16-bit row address");
-  static_assert(pt % 16 == 0 && kw % 16 == 0 && qimg % 16 == 0, "16-byte aligned areas");
+  static_assert(kw % 16 == 0 && qimg % 16 == 0, "16-byte aligned areas");
   static_assert(alloc <= 160 * 1024, "LDS of one CU");
 };
 
@@ -227,7 +225,6 @@ struct StreamState {
   uint32_t c4slot;    // this lane's slot offset in the centroid-pair half of a lookup row
   uint32_t cgrp;      // first k-step of the width-3, 2, 1 groups (bytes 0..2), k-step count (byte 3)
   uint32_t gbit;      // first stream bit of the width-3, 2, 1 groups (10 bits each)
-  uint32_t ptw;       // LDS byte offset of this wave's weight rows
   int wk, n4w;
   int lo;       // first token of the packed range
   uint32_t nv;  // tokens in the packed range [lo, lo + nv)
@@ -599,8 +596,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   // E of the token's fp16 value norm.  Without a rescale p = 2^(l - m) stays
   // below 2^(8 - dv), so P' = p * value norm stays below 2^15 (the norm is
   // below 2^(E - 14)); after one, p <= 1 and P' <= the norm.  So the fp16
-  // operand P' is finite for every finite norm.  P' goes to the wave's LDS
-  // rows [h][token].
+  // operand P' is finite for every finite norm.
   const float dv = (float)min(max((int)((r.nv >> 10) & 31u) - 21, 0), 8);
   float l[G];
   bool up = false;
@@ -626,18 +622,32 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
       mth[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn + kRescaleSlack)));
     }
   }
+  _Float16 pw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float p = __builtin_amdgcn_exp2f(l[h] - mrun[h]);
     lsum[h] += p;
-    *(__attribute__((address_space(3))) _Float16 *)(size_t)(st.ptw + h * (2 * kTile) + 2 * lane) = (_Float16)(p * nv);
+    pw[h] = (_Float16)(p * nv);
   }
   // A operands: lane 4k + m holds head m's weights of tokens 4k .. 4k + 3 (heads
-  // past G repeat a valid row; their output rows are never read)
+  // past G repeat a valid row; their output rows are never read): the 4 x 4
+  // block (token, head) of a lane quad transposed, first the 2 x 2 blocks
+  // within lane pairs, then the pairs across the quad
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+  const bool lo2 = (lane & 2) == 0;
   h4v pa[VQuads<G>::v];
 #pragma unroll
-  for (int g = 0; g < VQuads<G>::v; ++g)
-    pa[g] = lds_at<h4v>(st.ptw + ((4 * g + (lane & 3)) & (G - 1)) * (2 * kTile) + (lane >> 2) * 8);
+  for (int g = 0; g < VQuads<G>::v; ++g) {
+    const uint32_t d0 = __builtin_bit_cast(uint32_t, (h2v){pw[(4 * g) & (G - 1)], pw[(4 * g + 1) & (G - 1)]});
+    const uint32_t d1 = __builtin_bit_cast(uint32_t, (h2v){pw[(4 * g + 2) & (G - 1)], pw[(4 * g + 3) & (G - 1)]});
+    const uint32_t n0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    const uint32_t n1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, true);
+    const uint32_t e0 = __builtin_amdgcn_perm(n0, d0, sel), e1 = __builtin_amdgcn_perm(n1, d1, sel);
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)e0, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)e1, 0x4E, 0xF, 0xF, true);
+    pa[g] = __builtin_bit_cast(h4v, (u2v){lo2 ? e0 : p1, lo2 ? p0 : e1});
+  }
   // ---- values: lane = coordinates lane and lane + 64
   typedef StreamLds<G, VB, WK> L;
   h4v x0[kVBatch], x1[kVBatch], y0[kVBatch], y1[kVBatch];
@@ -924,7 +934,6 @@ void decode_kernel(const DecodeArgs a) {
   st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
   st.vslot = (uint32_t)(lane & (128 / Lds::vslot - 1)) * Lds::vslot;
   st.c4slot = 128u + (uint32_t)(lane & 15) * 8u;
-  st.ptw = (uint32_t)(Lds::pt + wave * (G * kTile * 2));
   st.n4w = n4w;
   st.cgrp = cgrp;
   st.gbit = gbit;
