@@ -20,8 +20,10 @@ namespace bgtq {
 //
 // Four waves per SIMD (registers at most 128, 28 KB of LDS per workgroup): the
 // rows are staged as their fp16 pairs and widened where they are read, and the
-// key codes sit coordinate-major in LDS, so that the packing's reads (lanes =
-// tokens) hit consecutive bytes.  (With fp32 rows and token-major codes the
+// codes sit coordinate-major in LDS, so that the key packing's reads (lanes =
+// tokens) hit consecutive bytes; the value rows are padded to 68 bytes, so
+// that the value quantiser's byte writes (16 tokens x 4 coordinates per wave
+// instruction) spread over the banks.  (With fp32 rows and token-major codes the
 // workgroups took 44 KB and 149 registers, three per CU, and the 128K layer's
 // prefill encode took 17% longer for the keys and 10% for the values.)
 template <bool IS_V>
@@ -30,8 +32,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     int64_t n_new, int split, uint32_t *__restrict__ codes, uint16_t *__restrict__ norms) {
   __shared__ uint32_t xs2[kTile][kHeadDim / 2 + 1];  // fp16 pairs; row stride 65 words
   const auto xs = [&](int t, int c) -> float { return h2f((uint16_t)(xs2[t][c >> 1] >> (16 * (c & 1)))); };
-  __shared__ uint8_t cs_[kTile * kHeadDim];  // values [token][coordinate], keys [coordinate][token]
-  const auto cs = [&](int t, int c) -> uint8_t & { return cs_[IS_V ? t * kHeadDim + c : c * kTile + t]; };
+  __shared__ uint8_t cs_[kHeadDim * (kTile + 4)];  // [coordinate][token]; value rows padded to 68 bytes
+  const auto cs = [&](int t, int c) -> uint8_t & { return cs_[c * (IS_V ? kTile + 4 : kTile) + t]; };
   __shared__ double ninv[kMaxGroups][kTile];  // sqrt(d_g) / n (0 for a zero group)
   __shared__ uint16_t nrm16[kTile][4];
   __shared__ int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
