@@ -212,14 +212,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   #pragma unroll 2
       for (int k = 0; k < d; ++k) {
         const int c = IS_V ? k : cds[pos + k];
-        // unconditional loads (rows past d re-read row d - 1 and are zeroed), so
-        // that the loads of the unrolled iterations are issued together
+        // unconditional loads, so that the loads of the unrolled iterations are
+        // issued together: rows past d re-read row d - 1, and their accumulators
+        // are never quantised
         double pr[4];
   #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const double pv = pt[(size_t)k * d + min(i0 + r, d - 1)];
-          pr[r] = i0 + r < d ? pv : 0.0;
-        }
+        for (int r = 0; r < 4; ++r) pr[r] = pt[(size_t)k * d + min(i0 + r, d - 1)];
   #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const double xv = (double)xs(u0 + u, c);
