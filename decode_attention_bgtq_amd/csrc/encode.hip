@@ -196,22 +196,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
       }
   } else {
     const int tb0 = lo >> 3, ntb = ((hi + 7) >> 3) - tb0;  // token blocks of eight overlapping [lo, hi)
-    for (int item = tid; item < total_rb * ntb; item += 256) {
-      const int grb = item / ntb, tb = tb0 + item % ntb;
-      int gi = 0;
-  #pragma unroll
-      for (int jg = 1; jg < kMaxGroups; ++jg) gi += (jg < n_groups && grb >= gpre[jg]) ? 1 : 0;
+    // Work units.  In half-tile workgroups (an append of a few thousand tokens,
+    // bound by each workgroup's chain), the items (row block of four, token block
+    // of eight) of a group with d_g > kSplitD are split in two halves of the k
+    // range: a wave-slot of 64 units holds 32 items, lane l (< 32) the first
+    // half, lane l + 32 the second; the halves are summed across the lanes
+    // before the quantiser.  The split slots come first (whole waves), then the
+    // other groups' items.  (In the prefill, with whole tiles and several
+    // workgroups per CU, splitting cost a fifth of the key rate: a second round
+    // of units and the idle halves of the last slots.)
+    constexpr int kSplitD = 24;
+    const int split_d = split > 1 ? kSplitD : kHeadDim;  // whole tiles: no group is split
+    int spre[kMaxGroups], upre[kMaxGroups];
+    int n_ss = 0, n_us = 0;
+#pragma unroll
+    for (int gi = 0; gi < kMaxGroups; ++gi) {
+      const int items = gi < n_groups ? (gd[gi] + 3) / 4 * ntb : 0;
+      const bool halves = gi < n_groups && gd[gi] > split_d;
+      spre[gi] = n_ss;
+      upre[gi] = n_us;
+      n_ss += halves ? (items + 31) / 32 : 0;
+      n_us += halves ? 0 : items;
+    }
+    const int n_units = 64 * n_ss + n_us;
+    for (int unit = tid; unit < n_units; unit += 256) {
+      const bool in_split = unit < 64 * n_ss;  // uniform per wave
+      int gi = 0, item, kbeg, kend;
+      bool valid = true, first = true;
+      if (in_split) {
+        const int slot = unit >> 6, l = unit & 63;
+#pragma unroll
+        for (int jg = 0; jg < kMaxGroups; ++jg)  // the last split group starting at or before slot
+          if (jg < n_groups && gd[jg] > split_d && slot >= spre[jg]) gi = jg;
+        item = (slot - sel(spre, gi)) * 32 + (l & 31);
+        const int dg = sel(gd, gi), items = (dg + 3) / 4 * ntb;
+        valid = item < items;
+        first = l < 32;
+        const int h = dg >> 1;
+        kbeg = valid ? (first ? 0 : h) : 0;
+        kend = valid ? (first ? h : dg) : 0;
+        item = valid ? item : 0;
+      } else {
+        const int v = unit - 64 * n_ss;
+#pragma unroll
+        for (int jg = 0; jg < kMaxGroups; ++jg)  // the last unsplit group starting at or before v
+          if (jg < n_groups && gd[jg] <= split_d && v >= upre[jg]) gi = jg;
+        item = v - sel(upre, gi);
+        kbeg = 0;
+        kend = sel(gd, gi);
+      }
+      const int grb_l = item / ntb, tb = tb0 + item % ntb;
       const int w = sel(gw, gi), d = sel(gd, gi), pos = sel(gpos, gi);
       const double *pt = gi == 0 ? gpt[0] : gi == 1 ? gpt[1] : gi == 2 ? gpt[2] : gpt[3];
-      const int i0 = 4 * (grb - sel(gpre, gi)), u0 = 8 * tb;
+      const int i0 = 4 * grb_l, u0 = 8 * tb;
       double acc[4][8];
   #pragma unroll
       for (int r = 0; r < 4; ++r)
   #pragma unroll
         for (int u = 0; u < 8; ++u) acc[r][u] = 0.0;
   #pragma unroll 2
-      for (int k = 0; k < d; ++k) {
-        const int c = IS_V ? k : cds[pos + k];
+      for (int k = kbeg; k < kend; ++k) {
+        const int c = cds[pos + k];
         // unconditional loads, so that the loads of the unrolled iterations are
         // issued together: rows past d re-read row d - 1, and their accumulators
         // are never quantised
@@ -225,6 +270,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
           for (int r = 0; r < 4; ++r) acc[r][u] = fma(pr[r], xv, acc[r][u]);
         }
       }
+      if (in_split) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r)
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) acc[r][u] += __shfl_xor(acc[r][u], 32);
+      }
+      if (!valid || !first) continue;
       // keys: a wave mixes groups of different widths, so the thresholds come from
       // LDS by bisection; values: one width, the thresholds read through the
       // scalar cache and counted
