@@ -21,11 +21,32 @@ struct AppendArgs {
   int hkv, wk, v_bits;
 };
 
-// Sum over the 64 lanes of a wave (integer, so the order does not matter).
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+// One DPP step of a wave sum of doubles: v + (v moved by the DPP pattern; lanes
+// the pattern does not write add 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave of integers below 2^40 held as doubles (every
+// partial sum is an integer below 2^47, so the fp64 additions are exact and the
+// order does not matter): quad, half-row, row steps, then the row broadcasts;
+// the total is read from lane 63.
+__device__ __forceinline__ uint64_t wave_sum_int40(uint64_t x) {
+  double v = (double)x;
+  v = dpp_add_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add_f64<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add_f64<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add_f64<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_add_f64<0x143, 0xC>(v);  // row_bcast:31
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return (uint64_t)__builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Tokens lo..hi-1 of cache tile `tile` of (sequence b, KV head kvh); token t
@@ -34,8 +55,8 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 // rotation row; that quarter of the fp64 rotation row is loaded into registers
 // once, before the token loop, and the four partial dot products are added in
 // quarter order.  Group norms are exact: the fp16 squares as integers
-// (|x| 2^24)^2, split at bit 40 and summed per wave, then rounded once to
-// float64.  Codes are OR-ed into the token's key words in LDS.
+// (|x| 2^24)^2, split at bit 40 and summed per wave (DPP steps on the halves
+// below 2^40, added exactly in fp64), then rounded once to float64.  Codes are OR-ed into the token's key words in LDS.
 template <bool IS_V>
 __device__ __forceinline__ void append_role(const AppendArgs &a, int64_t tile, int kvh, int b, int lo, int hi,
                                             int64_t row0) {
@@ -99,7 +120,7 @@ __device__ __forceinline__ void append_role(const AppendArgs &a, int64_t tile, i
         slo = (uint64_t)sq & ((1ull << 40) - 1);
       }
       for (int g = 0; g < n_groups; ++g) {
-        const uint64_t h = wave_sum_u64(g == gi ? shi : 0), l = wave_sum_u64(g == gi ? slo : 0);
+        const uint64_t h = wave_sum_int40(g == gi ? shi : 0), l = wave_sum_int40(g == gi ? slo : 0);
         if (lane == 0) gsum[tid >> 6][g][0] = h, gsum[tid >> 6][g][1] = l;
       }
     }
