@@ -30,6 +30,7 @@ EXPORTED = [
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
     "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc", "bgtq_key_logits",
+    "bgtq_encode_kv", "bgtq_encode_kv_paged",
 ]
 
 
@@ -99,6 +100,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_decode_attn_buffered": (I32, [P, P, P, P, P, P, P, I64, P, I32, I64, ctypes.c_float,
                                             P, P, I32, P, P, I32, P, P, SZ, P]),
         "bgtq_buffer_append": (I32, [P, P, I32, I64, I64, I32, P, P, I32, P, P, I32, P]),
+        "bgtq_encode_kv": (I32, [P, P, P, P, I32, I64, I64, I64, P, P, P, P, P]),
+        "bgtq_encode_kv_paged": (I32, [P, P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P, P, P]),
         "bgtq_encode_k_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
         "bgtq_encode_v_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
         "bgtq_decode_attn_paged": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
@@ -325,6 +328,21 @@ class Plan:
         _check(load().bgtq_encode_v(self._h, _ptr(consts), _ptr(v), b, capacity, t0, n,
                                     _ptr(v_codes), _ptr(v_norms), _stream(stream)))
 
+    def encode_kv(self, consts, k, v, capacity: int, t0: int, k_codes, k_norms, v_codes, v_norms,
+                  stream=None) -> None:
+        """Keys and values of the same tokens in one call (bit-identical to encode_k then encode_v)."""
+        self._check_tokens(k, "k")
+        self._check_tokens(v, "v")
+        _need(v, "v", shape=tuple(k.shape))
+        _need(k_codes, "k_codes", elem=4)
+        _need(k_norms, "k_norms", elem=2)
+        _need(v_codes, "v_codes", elem=4)
+        _need(v_norms, "v_norms", elem=2)
+        _gpu(k=k, v=v, k_codes=k_codes, k_norms=k_norms, v_codes=v_codes, v_norms=v_norms)
+        b, n = k.shape[0], k.shape[1]
+        _check(load().bgtq_encode_kv(self._h, _ptr(consts), _ptr(k), _ptr(v), b, capacity, t0, n, _ptr(k_codes),
+                                     _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _stream(stream)))
+
     def rotate_queries(self, consts, q, q_rot, stream=None) -> None:
         import torch
         _need(q, "q", elem=2, shape=(None, self.n_q_heads, HEAD_DIM))
@@ -391,6 +409,16 @@ class Plan:
         pg = pages.desc()
         _check(load().bgtq_encode_k_paged(self._h, _ptr(consts), _ptr(k), k.shape[0], ctypes.byref(pg), t0,
                                           k.shape[1], _ptr(pages.k_codes), _ptr(pages.k_norms), _stream(stream)))
+
+    def encode_kv_paged(self, consts, k, v, pages: "PagedCache", t0: int, stream=None) -> None:
+        self._check_tokens(k, "k")
+        self._check_tokens(v, "v")
+        _need(v, "v", shape=tuple(k.shape))
+        _gpu(k=k, v=v)
+        pg = pages.desc()
+        _check(load().bgtq_encode_kv_paged(self._h, _ptr(consts), _ptr(k), _ptr(v), k.shape[0], ctypes.byref(pg),
+                                           t0, k.shape[1], _ptr(pages.k_codes), _ptr(pages.k_norms),
+                                           _ptr(pages.v_codes), _ptr(pages.v_norms), _stream(stream)))
 
     def encode_v_paged(self, consts, v, pages: "PagedCache", t0: int, stream=None) -> None:
         self._check_tokens(v, "v")
@@ -518,6 +546,9 @@ class PagedCache:
         self.plan.encode_k_paged(self.consts, k, self, t0, stream)
         self.plan.encode_v_paged(self.consts, v, self, t0, stream)
 
+    def encode_kv(self, k, v, t0: int, stream=None) -> None:
+        self.plan.encode_kv_paged(self.consts, k, v, self, t0, stream)
+
 
 class Buffer:
     """fp16 sink and recent-window buffers of one layer (caller-owned torch tensors):
@@ -574,6 +605,10 @@ class Cache:
     def encode(self, k, v, t0: int, stream=None) -> None:
         self.plan.encode_k(self.consts, k, self.capacity, t0, self.k_codes, self.k_norms, stream)
         self.plan.encode_v(self.consts, v, self.capacity, t0, self.v_codes, self.v_norms, stream)
+
+    def encode_kv(self, k, v, t0: int, stream=None) -> None:
+        self.plan.encode_kv(self.consts, k, v, self.capacity, t0, self.k_codes, self.k_norms, self.v_codes,
+                            self.v_norms, stream)
 
     def step(self, q, k_new, v_new, pos, max_seq_len: int, out, workspace, softmax_scale=None, stream=None) -> None:
         self.plan.decode_step(self.consts, q, k_new, v_new, pos, max_seq_len, self.k_codes, self.k_norms,

@@ -27,9 +27,10 @@ namespace bgtq {
 // workgroups took 44 KB and 149 registers, three per CU, and the 128K layer's
 // prefill encode took 17% longer for the keys and 10% for the values.)
 template <bool IS_V>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(
-    const uint8_t *__restrict__ consts, const uint16_t *__restrict__ x, const TileMap map, int64_t t0,
-    int64_t n_new, int split, uint32_t *__restrict__ codes, uint16_t *__restrict__ norms) {
+__device__ __forceinline__ void encode_body(const uint8_t *__restrict__ consts, const uint16_t *__restrict__ x,
+                                            const TileMap &map, int64_t t0, int64_t n_new, int split,
+                                            uint32_t *__restrict__ codes, uint16_t *__restrict__ norms, int bx,
+                                            int kvh, int b) {
   __shared__ uint32_t xs2[kTile][kHeadDim / 2 + 1];  // fp16 pairs; row stride 65 words
   const auto xs = [&](int t, int c) -> float { return h2f((uint16_t)(xs2[t][c >> 1] >> (16 * (c & 1)))); };
   __shared__ uint8_t cs_[kHeadDim * (kTile + 4)];  // [coordinate][token]; value rows padded to 68 bytes
@@ -40,9 +41,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   __shared__ double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
   const ConstHeader *hd = hdr_of(consts);
   const int hkv = hd->n_kv_heads;
-  const int64_t tile = t0 / kTile + blockIdx.x / split;
-  const int part = blockIdx.x % split, span = kTile / split;
-  const int kvh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t tile = t0 / kTile + bx / split;
+  const int part = bx % split, span = kTile / split;
+  const int tid = threadIdx.x;
   const int64_t tok0 = tile * kTile;
   const int lo = (int)(std::max(std::max(t0, tok0 + part * span), tok0) - tok0);
   const int hi = (int)(std::min(t0 + n_new, tok0 + (part + 1) * span) - tok0);
@@ -364,6 +365,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   }
 }
 
+template <bool IS_V>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(
+    const uint8_t *__restrict__ consts, const uint16_t *__restrict__ x, const TileMap map, int64_t t0,
+    int64_t n_new, int split, uint32_t *__restrict__ codes, uint16_t *__restrict__ norms) {
+  encode_body<IS_V>(consts, x, map, t0, n_new, split, codes, norms, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Keys and values of the same tokens in one launch: grid.y = 2 Hkv, the keys
+// of KV head y, then the values of head y - Hkv.  The key encode is bound by
+// the issue of fp64 VALU work, the value encode by the fp64 matrix cores; a
+// key and a value workgroup side by side on a compute unit overlap the two,
+// and an append of a few thousand tokens fills twice the compute units that
+// one of its encodes fills.  Each role keeps its own LDS (the kernel holds
+// both, 56 KB: two workgroups per compute unit).
+struct KvCache {
+  uint32_t *kc;
+  uint16_t *kn;
+  uint32_t *vc;
+  uint16_t *vn;
+};
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void encode_kv_kernel(
+    const uint8_t *__restrict__ consts, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const TileMap map, int64_t t0, int64_t n_new, int split, int hkv, const KvCache o) {
+  const int y = blockIdx.y;
+  if (y < hkv)
+    encode_body<false>(consts, k, map, t0, n_new, split, o.kc, o.kn, blockIdx.x, y, blockIdx.z);
+  else
+    encode_body<true>(consts, v, map, t0, n_new, split, o.vc, o.vn, blockIdx.x, y - hkv, blockIdx.z);
+}
+
 // Append path for a few tokens per tile (uniform start t0 for the batch): one
 // workgroup per (tile, KV head, sequence), see append_role.
 template <bool IS_V>
@@ -435,6 +466,46 @@ bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_cons
   return launch_status(nm);
 }
 
+// Keys and values of the same tokens: one launch of encode_kv_kernel where the
+// two encodes together fill at most one round of compute units (half tiles
+// when that still leaves half of them idle), else the two encodes one after
+// the other, as bgtq_encode_k and bgtq_encode_v would run them.
+bgtq_status encode_kv_common(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, const uint16_t *v,
+                             int32_t batch, int64_t capacity, int64_t t0, int64_t n_new, uint32_t *k_codes,
+                             uint16_t *k_norms, uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream,
+                             const bgtq_pages *pages = nullptr) {
+  const char *nm = pages ? "bgtq_encode_kv_paged" : "bgtq_encode_kv";
+  if (pages) {
+    const bgtq_status ps = pages_check(pages, nm);
+    if (ps != BGTQ_OK) return ps;
+    capacity = (int64_t)kTile * pages->max_pages;
+  }
+  const bool no_codes = plan && plan->p.hdr.wk == 0;  // zero-bit keys store no code words
+  if (!plan || !dev_consts || (!k_codes && !no_codes) || !k_norms || !v_codes || !v_norms ||
+      ((!k || !v) && n_new > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  if (batch < 1 || n_new < 0 || capacity < 0) return fail(BGTQ_EINVAL, std::string(nm) + ": bad batch or count");
+  if (t0 < 0 || t0 + n_new > capacity) return fail(BGTQ_ECAPACITY, std::string(nm) + ": tokens beyond capacity");
+  if (((uintptr_t)k | (uintptr_t)v) & 15) return fail(BGTQ_EINVAL, std::string(nm) + ": k / v must be 16-byte aligned");
+  if (n_new == 0) return BGTQ_OK;
+  const int hkv = plan->p.desc.n_kv_heads;
+  const int64_t tiles = (t0 + n_new - 1) / kTile - t0 / kTile + 1;
+  const int64_t units = tiles * hkv * batch;  // workgroups of one encode in whole tiles
+  const int cus = device_cus();
+  if (n_new <= 8 || no_codes || units > cus) {
+    const bgtq_status sk = encode_common(false, plan, dev_consts, k, batch, capacity, t0, n_new, k_codes, k_norms,
+                                         stream, pages);
+    if (sk != BGTQ_OK) return sk;
+    return encode_common(true, plan, dev_consts, v, batch, capacity, t0, n_new, v_codes, v_norms, stream, pages);
+  }
+  const TileMap map = pages ? paged_map(plan->p, pages) : contiguous_map(hkv, capacity);
+  const int split = 4 * units <= 2 * (int64_t)cus ? 2 : 1;
+  const dim3 egrid((unsigned)(tiles * split), 2 * hkv, batch);
+  encode_kv_kernel<<<egrid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)dev_consts, k, v, map, t0, n_new, split,
+                                                            hkv, KvCache{k_codes, k_norms, v_codes, v_norms});
+  return launch_status(nm);
+}
+
 }  // namespace
 
 extern "C" {
@@ -449,6 +520,22 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
                           int64_t capacity, int64_t t0, int64_t n_new, uint32_t *v_codes, uint16_t *v_norms,
                           bgtq_stream stream) {
   return encode_common(true, plan, dev_consts, v, batch, capacity, t0, n_new, v_codes, v_norms, stream);
+}
+
+bgtq_status bgtq_encode_kv(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, const uint16_t *v,
+                           int32_t batch, int64_t capacity, int64_t t0, int64_t n_new, uint32_t *k_codes,
+                           uint16_t *k_norms, uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream) {
+  return encode_kv_common(plan, dev_consts, k, v, batch, capacity, t0, n_new, k_codes, k_norms, v_codes, v_norms,
+                          stream);
+}
+
+bgtq_status bgtq_encode_kv_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k,
+                                 const uint16_t *v, int32_t batch, const bgtq_pages *pages, int64_t t0,
+                                 int64_t n_new, uint32_t *k_codes, uint16_t *k_norms, uint32_t *v_codes,
+                                 uint16_t *v_norms, bgtq_stream stream) {
+  if (!pages) return fail(BGTQ_EINVAL, "bgtq_encode_kv_paged: null pages");
+  return encode_kv_common(plan, dev_consts, k, v, batch, 0, t0, n_new, k_codes, k_norms, v_codes, v_norms, stream,
+                          pages);
 }
 
 bgtq_status bgtq_encode_k_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, int32_t batch,

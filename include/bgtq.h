@@ -198,6 +198,17 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
                           int32_t batch, int64_t capacity, int64_t t0, int64_t n_new,
                           uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
 
+/* (4) for keys and values of the same tokens in one call: the caches are
+ * written exactly as bgtq_encode_k followed by bgtq_encode_v would write them
+ * (same codes and norms, bit for bit).  An append small enough that the two
+ * encodes together fill at most one round of compute units runs them in one
+ * launch, side by side; larger encodes run them one after the other.
+ * Arguments, errors and the 16-byte alignment of k and v as bgtq_encode_k/v.
+ */
+bgtq_status bgtq_encode_kv(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, const uint16_t *v,
+                           int32_t batch, int64_t capacity, int64_t t0, int64_t n_new, uint32_t *k_codes,
+                           uint16_t *k_norms, uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
+
 /*
  * (5) Query rotation (the fused decode's query side; Abstract: logits are
  * sums over RoPE frequency blocks, and a TurboQuant-MSE code lives in its
@@ -373,6 +384,12 @@ bgtq_status bgtq_encode_k_paged(const bgtq_plan *plan, const void *dev_consts, c
 bgtq_status bgtq_encode_v_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *v,
                                 int32_t batch, const bgtq_pages *pages, int64_t t0, int64_t n_new,
                                 uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream);
+/* bgtq_encode_kv on a paged pool: as bgtq_encode_k_paged followed by
+ * bgtq_encode_v_paged. */
+bgtq_status bgtq_encode_kv_paged(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k,
+                                 const uint16_t *v, int32_t batch, const bgtq_pages *pages, int64_t t0,
+                                 int64_t n_new, uint32_t *k_codes, uint16_t *k_norms, uint32_t *v_codes,
+                                 uint16_t *v_norms, bgtq_stream stream);
 
 /* (6) on a paged pool: everything as bgtq_decode_attn, capacity 64 * max_pages
  * (the same workspace size).  Errors: as (6); EINVAL for bad pages. */

@@ -79,6 +79,36 @@ def test_paged_encode_and_decode(bg, cid, seq_len, batch):
         assert rel_l2(got[s], ref).max() <= TOL
 
 
+@pytest.mark.parametrize("cid,seq_len,batch", [(5, 2048, 1), (4, 700, 3)])
+def test_paged_encode_kv_equals_two_encodes(bg, cid, seq_len, batch):
+    """bgtq_encode_kv_paged writes every page exactly as the paged key and value encodes do."""
+    import torch
+    cfg = synth.small(cid, seq_len=seq_len, batch=batch)
+    log("paged encode_kv config %d T=%d batch %d" % (cid, seq_len, batch))
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    n_tiles = (seq_len + 63) // 64
+    n_pages = batch * n_tiles + 5
+    table = np.random.default_rng(7).permutation(n_pages)[:batch * n_tiles].reshape(batch, n_tiles)
+    table = table.astype(np.int32)
+    fused, two = bg.PagedCache(plan, n_pages, table), bg.PagedCache(plan, n_pages, table)
+    ks = np.stack([synth.keys(cfg, seq=s, count=seq_len) for s in range(batch)])
+    vs = np.stack([synth.values(cfg, seq=s, count=seq_len) for s in range(batch)])
+    bounds = [0, 3, 64, 700, seq_len] if seq_len > 700 else [0, 3, 64, seq_len]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        fused.encode_kv(to_dev(ks[:, a:b]), to_dev(vs[:, a:b]), a)
+        two.encode(to_dev(ks[:, a:b]), to_dev(vs[:, a:b]), a)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        assert torch.equal(getattr(fused, name), getattr(two, name)), name
+    for s in range(batch):
+        for h in range(cfg.n_kv_heads):
+            ref = OracleHead(ks[s, :, h], vs[s, :, h], bits[h], cfg.v_bits, cfg.seed, 0, h).packed(n_tiles)
+            got = np.stack([_pool_tile(fused.v_codes, h, table[s, j]) for j in range(n_tiles)])
+            assert np.array_equal(got.view(ref[2].dtype), ref[2]), (s, h)
+
+
 def test_paged_writer_skips_entries_outside_the_pool(bg):
     """A table entry outside [0, n_pages) makes the encode skip that tile (the pool is unchanged)."""
     import torch

@@ -86,9 +86,10 @@ def test_allocation_budgets_and_uniform(bg):
         assert np.all(got[1] == avg)
 
 
-def _encode_case(bg, cfg, seq_len, batch=1, capacity=None, bits=None, chunks=None):
-    """Encode `seq_len` tokens per sequence on the GPU (optionally in several appends) and
-    compare every packed array with the oracle's."""
+def _encode_case(bg, cfg, seq_len, batch=1, capacity=None, bits=None, chunks=None, fused=False):
+    """Encode `seq_len` tokens per sequence on the GPU (optionally in several appends; with
+    `fused`, keys and values in one bgtq_encode_kv call) and compare every packed array with
+    the oracle's."""
     import torch
     capacity = capacity or seq_len
     if bits is None:
@@ -100,7 +101,10 @@ def _encode_case(bg, cfg, seq_len, batch=1, capacity=None, bits=None, chunks=Non
     vs = np.stack([synth.values(cfg, seq=s, count=seq_len) for s in range(batch)])
     bounds = chunks or [0, seq_len]
     for a, b in zip(bounds[:-1], bounds[1:]):
-        cache.encode(to_dev(ks[:, a:b]), to_dev(vs[:, a:b]), a)
+        if fused:
+            cache.encode_kv(to_dev(ks[:, a:b]), to_dev(vs[:, a:b]), a)
+        else:
+            cache.encode(to_dev(ks[:, a:b]), to_dev(vs[:, a:b]), a)
     torch.cuda.synchronize()
     heads = {}
     for s in range(batch):
@@ -127,6 +131,27 @@ def test_encode_batched_and_appended(bg):
     cfg = synth.small(4, seq_len=300, batch=3)
     log("encode batch 3, appends at 0/37/64/101/200")
     _encode_case(bg, cfg, 300, batch=3, capacity=320, chunks=[0, 37, 64, 101, 200, 300])
+
+
+# bgtq_encode_kv: one launch for keys and values where the two encodes fill at most one round
+# of compute units (half tiles below half a round), else the two encodes in turn; every case
+# bit-exact against the oracle.  (3, 3000): 47 tiles x 8 heads takes the two-launch path;
+# the chunked batch mixes appends of 5, 27, 37 and 199 tokens (the few-token path at 5).
+@pytest.mark.parametrize("cid,seq_len,batch,chunks", [
+    (5, 4096, 1, None), (3, 700, 1, None), (2, 1000, 1, None), (1, 63, 1, None), (3, 3000, 1, None),
+    (4, 300, 3, [0, 5, 32, 69, 101, 300])])
+def test_encode_kv_bitexact(bg, cid, seq_len, batch, chunks):
+    log("encode_kv config %d T=%d batch %d" % (cid, seq_len, batch))
+    cfg = synth.small(cid, seq_len=seq_len, batch=batch)
+    _encode_case(bg, cfg, seq_len, batch=batch, capacity=seq_len + 20, chunks=chunks, fused=True)
+
+
+def test_encode_kv_append_at_offset(bg):
+    """A 4096-token append at position 8192 behind a prefill (the long-context workload's
+    append, reduced), keys and values in one call."""
+    cfg = synth.small(5, seq_len=8192 + 4096)
+    log("encode_kv append of 4096 at 8192")
+    _encode_case(bg, cfg, 8192 + 4096, capacity=8192 + 4096 + 64, chunks=[0, 8192, 8192 + 4096], fused=True)
 
 
 def test_encode_zero_and_uniform(bg):

@@ -153,6 +153,18 @@ def test_device_calls_reject_bad_arguments_before_launch(bg):
     assert lib.bgtq_encode_k(h, 256, 256, 1, 100, 90, 20, 256, 256, None) == bg.ECAPACITY
     assert lib.bgtq_encode_v(h, 256, 256, 1, 100, -1, 20, 256, 256, None) == bg.ECAPACITY
     assert lib.bgtq_encode_k(h, None, 256, 1, 100, 0, 20, 256, 256, None) == bg.EINVAL
+    # the fused key + value encode: every check of the two encodes, before any launch
+    kv = [h, 256, 256, 256, 1, 100]
+    assert lib.bgtq_encode_kv(*kv, 90, 20, 256, 256, 256, 256, None) == bg.ECAPACITY
+    assert lib.bgtq_encode_kv(*kv, -1, 20, 256, 256, 256, 256, None) == bg.ECAPACITY
+    assert lib.bgtq_encode_kv(h, 256, 256, None, 1, 100, 0, 20, 256, 256, 256, 256, None) == bg.EINVAL
+    assert lib.bgtq_encode_kv(*kv, 0, 20, 256, 256, None, 256, None) == bg.EINVAL
+    assert lib.bgtq_encode_kv(h, 256, 256, 264, 1, 100, 0, 20, 256, 256, 256, 256, None) == bg.EINVAL  # align
+    assert lib.bgtq_encode_kv(h, 256, 256, 256, 0, 100, 0, 20, 256, 256, 256, 256, None) == bg.EINVAL
+    pg = bg._Pages(None, 4, 10)
+    assert lib.bgtq_encode_kv_paged(h, 256, 256, 256, 1, ctypes.byref(pg), 0, 10, 256, 256, 256, 256,
+                                    None) == bg.EINVAL
+    assert lib.bgtq_encode_kv_paged(h, 256, 256, 256, 1, None, 0, 10, 256, 256, 256, 256, None) == bg.EINVAL
     args = [h, 256, 256, 256, 256, 256, 256]
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 101, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
     assert lib.bgtq_decode_attn(*args, 100, 256, 1, 0, 0.1, 256, 256, 1 << 30, None) == bg.ECAPACITY
