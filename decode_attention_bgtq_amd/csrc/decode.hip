@@ -963,9 +963,11 @@ void decode_kernel(const DecodeArgs a) {
     wave_priority((tile_hi - 1 - tile) / kStreamWaves);
     process_tile<G, VB, WK>(ra, tile, st, qr, rinv, mrun, mth, lsum, acc0, acc1, lane);
     ra = rb;
-    const size_t bn = head_base + (paged ? pnext : (size_t)min(tile + 2 * kStreamWaves, tile_hi - 1));
-    load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
-    if (paged) pnext = page_of(min(tile + 3 * kStreamWaves, tile_hi - 1));
+    if (tile + 2 * kStreamWaves < tile_hi) {
+      const size_t bn = head_base + (paged ? pnext : (size_t)(tile + 2 * kStreamWaves));
+      load_tile(rb, kcodes, kstride, a.kn, a.vc, a.vn, bn, lane);
+      if (paged) pnext = page_of(min(tile + 3 * kStreamWaves, tile_hi - 1));
+    }
   }
 
   __builtin_amdgcn_s_setprio(0);

@@ -26,19 +26,29 @@ namespace bgtq {
 // instruction) spread over the banks.  (With fp32 rows and token-major codes the
 // workgroups took 44 KB and 149 registers, three per CU, and the 128K layer's
 // prefill encode took 17% longer for the keys and 10% for the values.)
+// LDS of one encode workgroup (28.6 KB; key and value workgroups use the same layout).
+struct EncLds {
+  uint32_t xs2[kTile][kHeadDim / 2 + 1];  // fp16 pairs; row stride 65 words
+  uint8_t cs_[kHeadDim * (kTile + 4)];     // [coordinate][token]; value rows padded to 68 bytes
+  double ninv[kMaxGroups][kTile];          // sqrt(d_g) / n (0 for a zero group)
+  uint16_t nrm16[kTile][4];
+  int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
+  double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
+};
+
 template <bool IS_V>
-__device__ __forceinline__ void encode_body(const uint8_t *__restrict__ consts, const uint16_t *__restrict__ x,
-                                            const TileMap &map, int64_t t0, int64_t n_new, int split,
-                                            uint32_t *__restrict__ codes, uint16_t *__restrict__ norms, int bx,
-                                            int kvh, int b) {
-  __shared__ uint32_t xs2[kTile][kHeadDim / 2 + 1];  // fp16 pairs; row stride 65 words
+__device__ __forceinline__ void encode_body(EncLds &L, const uint8_t *__restrict__ consts,
+                                            const uint16_t *__restrict__ x, const TileMap &map, int64_t t0,
+                                            int64_t n_new, int split, uint32_t *__restrict__ codes,
+                                            uint16_t *__restrict__ norms, int bx, int kvh, int b) {
+  auto &xs2 = L.xs2;
   const auto xs = [&](int t, int c) -> float { return h2f((uint16_t)(xs2[t][c >> 1] >> (16 * (c & 1)))); };
-  __shared__ uint8_t cs_[kHeadDim * (kTile + 4)];  // [coordinate][token]; value rows padded to 68 bytes
+  auto &cs_ = L.cs_;
   const auto cs = [&](int t, int c) -> uint8_t & { return cs_[c * (IS_V ? kTile + 4 : kTile) + t]; };
-  __shared__ double ninv[kMaxGroups][kTile];  // sqrt(d_g) / n (0 for a zero group)
-  __shared__ uint16_t nrm16[kTile][4];
-  __shared__ int16_t cds[kHeadDim];  // the head's group-order coordinates (keys)
-  __shared__ double thr_s[4][16];    // interior thresholds of the b-bit quantisers, row b - 1
+  auto &ninv = L.ninv;
+  auto &nrm16 = L.nrm16;
+  auto &cds = L.cds;
+  auto &thr_s = L.thr_s;
   const ConstHeader *hd = hdr_of(consts);
   const int hkv = hd->n_kv_heads;
   const int64_t tile = t0 / kTile + bx / split;
@@ -369,30 +379,32 @@ template <bool IS_V>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(
     const uint8_t *__restrict__ consts, const uint16_t *__restrict__ x, const TileMap map, int64_t t0,
     int64_t n_new, int split, uint32_t *__restrict__ codes, uint16_t *__restrict__ norms) {
-  encode_body<IS_V>(consts, x, map, t0, n_new, split, codes, norms, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ EncLds lds;
+  encode_body<IS_V>(lds, consts, x, map, t0, n_new, split, codes, norms, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Keys and values of the same tokens in one launch: grid.y = 2 Hkv, the keys
-// of KV head y, then the values of head y - Hkv.  The key encode is bound by
-// the issue of fp64 VALU work, the value encode by the fp64 matrix cores; a
-// key and a value workgroup side by side on a compute unit overlap the two,
-// and an append of a few thousand tokens fills twice the compute units that
-// one of its encodes fills.  Each role keeps its own LDS (the kernel holds
-// both, 56 KB: two workgroups per compute unit).
+// Keys and values of the same tokens in one launch: workgroup x takes the
+// keys (x even) or the values (x odd) of tile unit x / 2, so that the
+// dispatcher deals key and value workgroups alternately to the compute units.
+// The key encode is bound by the issue of fp64 VALU work, the value encode by
+// the fp64 matrix cores: side by side on a compute unit they overlap, and an
+// append of a few thousand tokens fills twice the compute units that one of
+// its encodes fills.
 struct KvCache {
   uint32_t *kc;
   uint16_t *kn;
   uint32_t *vc;
   uint16_t *vn;
 };
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void encode_kv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void encode_kv_kernel(
     const uint8_t *__restrict__ consts, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const TileMap map, int64_t t0, int64_t n_new, int split, int hkv, const KvCache o) {
-  const int y = blockIdx.y;
-  if (y < hkv)
-    encode_body<false>(consts, k, map, t0, n_new, split, o.kc, o.kn, blockIdx.x, y, blockIdx.z);
+    const TileMap map, int64_t t0, int64_t n_new, int split, const KvCache o) {
+  __shared__ EncLds lds;
+  const int u = blockIdx.x >> 1;
+  if ((blockIdx.x & 1) == 0)
+    encode_body<false>(lds, consts, k, map, t0, n_new, split, o.kc, o.kn, u, blockIdx.y, blockIdx.z);
   else
-    encode_body<true>(consts, v, map, t0, n_new, split, o.vc, o.vn, blockIdx.x, y - hkv, blockIdx.z);
+    encode_body<true>(lds, consts, v, map, t0, n_new, split, o.vc, o.vn, u, blockIdx.y, blockIdx.z);
 }
 
 // Append path for a few tokens per tile (uniform start t0 for the batch): one
@@ -467,9 +479,11 @@ bgtq_status encode_common(bool is_v, const bgtq_plan *plan, const void *dev_cons
 }
 
 // Keys and values of the same tokens: one launch of encode_kv_kernel where the
-// two encodes together fill at most one round of compute units (half tiles
-// when that still leaves half of them idle), else the two encodes one after
-// the other, as bgtq_encode_k and bgtq_encode_v would run them.
+// two encodes in whole tiles together fill at most two workgroups per compute
+// unit (in half tiles below that), else the two encodes one after the other
+// as bgtq_encode_k and bgtq_encode_v run them (a prefill of the 128K layer:
+// 692 M token-heads/s so, 634 M in one interleaved launch); appends of a few
+// tokens per tile take the two few-token launches.
 bgtq_status encode_kv_common(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, const uint16_t *v,
                              int32_t batch, int64_t capacity, int64_t t0, int64_t n_new, uint32_t *k_codes,
                              uint16_t *k_norms, uint32_t *v_codes, uint16_t *v_norms, bgtq_stream stream,
@@ -490,6 +504,7 @@ bgtq_status encode_kv_common(const bgtq_plan *plan, const void *dev_consts, cons
   if (n_new == 0) return BGTQ_OK;
   const int hkv = plan->p.desc.n_kv_heads;
   const int64_t tiles = (t0 + n_new - 1) / kTile - t0 / kTile + 1;
+  if (tiles > 0x3FFFFFFF || batch > 65535 || hkv > 65535) return fail(BGTQ_EINVAL, std::string(nm) + ": grid too large");
   const int64_t units = tiles * hkv * batch;  // workgroups of one encode in whole tiles
   const int cus = device_cus();
   if (n_new <= 8 || no_codes || units > cus) {
@@ -499,10 +514,10 @@ bgtq_status encode_kv_common(const bgtq_plan *plan, const void *dev_consts, cons
     return encode_common(true, plan, dev_consts, v, batch, capacity, t0, n_new, v_codes, v_norms, stream, pages);
   }
   const TileMap map = pages ? paged_map(plan->p, pages) : contiguous_map(hkv, capacity);
-  const int split = 4 * units <= 2 * (int64_t)cus ? 2 : 1;
-  const dim3 egrid((unsigned)(tiles * split), 2 * hkv, batch);
+  const int split = units >= cus ? 1 : 2;
+  const dim3 egrid((unsigned)(2 * tiles * split), hkv, batch);
   encode_kv_kernel<<<egrid, 256, 0, (hipStream_t)stream>>>((const uint8_t *)dev_consts, k, v, map, t0, n_new, split,
-                                                            hkv, KvCache{k_codes, k_norms, v_codes, v_norms});
+                                                            KvCache{k_codes, k_norms, v_codes, v_norms});
   return launch_status(nm);
 }
 

@@ -200,9 +200,10 @@ bgtq_status bgtq_encode_v(const bgtq_plan *plan, const void *dev_consts, const u
 
 /* (4) for keys and values of the same tokens in one call: the caches are
  * written exactly as bgtq_encode_k followed by bgtq_encode_v would write them
- * (same codes and norms, bit for bit).  An append small enough that the two
- * encodes together fill at most one round of compute units runs them in one
- * launch, side by side; larger encodes run them one after the other.
+ * (same codes and norms, bit for bit).  Where the tiles of the range times
+ * KV heads times sequences are at most the compute-unit count (an append of a
+ * few thousand tokens), the two encodes run in one launch, side by side;
+ * larger encodes run them one after the other.
  * Arguments, errors and the 16-byte alignment of k and v as bgtq_encode_k/v.
  */
 bgtq_status bgtq_encode_kv(const bgtq_plan *plan, const void *dev_consts, const uint16_t *k, const uint16_t *v,
