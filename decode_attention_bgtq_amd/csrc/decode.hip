@@ -144,7 +144,7 @@ struct StreamLds {
   static constexpr int kw_rows = WK + 2;  // key words of the tile, then two zero rows
   static constexpr bool qlds = StreamOcc<G, VB, WK>::qlds;
   static constexpr int qimg = kw + W * kw_rows * kTile * 4;
-  static constexpr int qimg_bytes = qlds ? 8 * 2 * kTile * 4 + 3 * 2 * 2 * kTile * 8 + 256 : 0;
+  static constexpr int qimg_bytes = qlds ? 3 * 2 * 2 * kTile * 8 + 256 + 8 * kTile * 16 : 0;
   static constexpr int end = qimg + qimg_bytes;
   static constexpr int merge = W * G * kPartStride * 4;
   static constexpr int total = end > merge ? end : merge;
@@ -221,6 +221,7 @@ __device__ __forceinline__ void load_tile(TileRegs<VB, WK> &r, const uint32_t *_
 
 struct StreamState {
   uint32_t kwl;       // LDS byte address of this lane's word 0 in this wave's key-word rows
+  uint32_t kwb;       // (16x16x32 4-bit group) of row lane / 32, token lane % 16 in those rows
   uint32_t vslot;     // this lane's slot offset in the value half of a lookup row
   uint32_t c4slot;    // this lane's slot offset in the centroid-pair half of a lookup row
   uint32_t cgrp;      // first k-step of the width-3, 2, 1 groups (bytes 0..2), k-step count (byte 3)
@@ -245,9 +246,9 @@ struct VQuads {
 //  kq[r][j][g]  lane 4b + m: head 4g + m's four fp16 query values of k-step
 //               16j + b of the width-(3 - r) group
 // They stay in registers for the whole loop (L false), or (eight heads at three
-// waves per SIMD) are read from the image in LDS next to their use (q4a, kqa:
-// the LDS byte addresses of the lane's column of rows q4[0][0] and
-// kq[0][0][0]), which leaves the registers of the third wave.
+// waves per SIMD) are read from the image in LDS next to their use, which
+// leaves the registers of the third wave; those kernels take the 4-bit group
+// on the 16x16x32 matrix cores (key4_wide) instead of the q4 steps.
 template <int G, bool L>
 struct QueryRegs;
 
@@ -260,20 +261,14 @@ struct QueryRegs<G, false> {
 
 template <int G>
 struct QueryRegs<G, true> {
-  uint32_t q4a, kqa;
+  uint32_t kqa;  // LDS byte address of the lane's column of kq[0][0][0]
+  uint32_t qaa;  // LDS byte address of the lane's qa operand of chunk 0
 };
 
 template <int G, int K>
 __device__ __forceinline__ void query_q4(const QueryRegs<G, false> &qr, float (&o)[VQuads<G>::v]) {
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) o[g] = qr.q4[K][g];
-}
-
-template <int G, int K>
-__device__ __forceinline__ void query_q4(const QueryRegs<G, true> &qr, float (&o)[VQuads<G>::v]) {
-#pragma unroll
-  for (int g = 0; g < VQuads<G>::v; ++g)
-    o[g] = *(const __attribute__((address_space(3))) float *)(size_t)(qr.q4a + (K * VQuads<G>::v + g) * kTile * 4);
 }
 
 template <int G, int R>
@@ -356,6 +351,86 @@ __device__ __forceinline__ void key4_group(const uint32_t (&w)[WK], int n4w, uin
     query_q4<G, 0>(qr, qx);
     key4_words<G, VB, WK, 0>(w, n4w, c4slot, cx, cy, qx, qy, qr, a4);
   }
+}
+
+// 4-bit group of the eight-head kernels that read their query operands from
+// LDS, on the 16x16x32 fp16 matrix cores with the query and the centroid each
+// split into two fp16 parts, q = q_hi + q_lo (q scaled per head by a power of
+// two into fp16 range) and c = c_hi + c_lo: q_hi c_hi + q_hi c_lo + q_lo c_hi
+// keeps ~22 bits of every product (the logits of the widest group need more
+// than fp16 operands give), at a quarter of the fp32 steps' matrix-core time.
+// Per chunk of 16 codes and token group tg (tokens 16 tg .. 16 tg + 15), one
+// product D += A B:
+//  A (16 x 32, the chunk's qa operand from the image in LDS): row 4r + j is
+//    head 2r + j / 2 with part j % 2 (q_hi, q_lo); k-slots 8 kb .. 8 kb + 7
+//    are codes 8 (kb / 2) .. + 7 of the chunk against c_hi (kb even) or c_lo
+//    (kb odd), where the q_lo rows are zero;
+//  B (32 x 16): lane 16 kb + n holds token 16 tg + n's key word 2 chunk + kb / 2
+//    (from this wave's key-word rows in LDS), its four code bytes looked up as
+//    fp16 pairs, c_hi or c_lo by the lane's slot (the two halves of an 8-byte
+//    lookup slot);
+//  D: lane 16 r + n, register j: head 2r + j / 2, part j % 2, token 16 tg + n.
+// The parts are added in the lane; two 4 x 4 transposes of 16-lane row blocks
+// over the four token groups (permlane16 / permlane32 swaps) then put head h
+// of token t into lane t (a4[h / 4][h % 4]), the layout of the other groups.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void rows_transpose(float (&x)[4]) {
+  uint32_t a0 = __builtin_bit_cast(uint32_t, x[0]), a1 = __builtin_bit_cast(uint32_t, x[1]);
+  uint32_t a2 = __builtin_bit_cast(uint32_t, x[2]), a3 = __builtin_bit_cast(uint32_t, x[3]);
+  auto p = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
+  a0 = p[0], a1 = p[1];
+  p = __builtin_amdgcn_permlane16_swap(a2, a3, false, false);
+  a2 = p[0], a3 = p[1];
+  p = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
+  a0 = p[0], a2 = p[1];
+  p = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
+  a1 = p[0], a3 = p[1];
+  x[0] = __builtin_bit_cast(float, a0), x[1] = __builtin_bit_cast(float, a1);
+  x[2] = __builtin_bit_cast(float, a2), x[3] = __builtin_bit_cast(float, a3);
+}
+
+template <class L>
+__device__ __forceinline__ h8v wide_b(uint32_t word, uint32_t slot) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 v = {lds_at<uint32_t>(L::rep + row_addr<0>(word, slot)), lds_at<uint32_t>(L::rep + row_addr<1>(word, slot)),
+                lds_at<uint32_t>(L::rep + row_addr<2>(word, slot)), lds_at<uint32_t>(L::rep + row_addr<3>(word, slot))};
+  return __builtin_bit_cast(h8v, v);
+}
+
+// kwb: LDS byte address of (row lane / 32, token lane % 16) of this wave's key
+// words; qaa: of the lane's qa operand of chunk 0; slot: the lane's lookup slot.
+template <int G, int VB, int WK>
+__device__ __forceinline__ void key4_wide(int n4w, uint32_t kwb, uint32_t qaa, uint32_t slot, f4v (&a4)[2]) {
+  typedef StreamLds<G, VB, WK> L;
+  f4v acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = (f4v){0.f, 0.f, 0.f, 0.f};
+  const int nch = (n4w + 1) >> 1;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (c >= nch) break;
+    const h8v a = *(const __attribute__((address_space(3))) h8v *)(size_t)(qaa + c * 64 * 16);
+    uint32_t wd[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wd[t] = lds_at<uint32_t>(kwb + c * 512 + t * 64);
+    h8v b0 = wide_b<L>(wd[0], slot), b1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t + 1 < 4) ((t & 1) ? b0 : b1) = wide_b<L>(wd[t + 1], slot);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, (t & 1) ? b1 : b0, acc[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float u0[4], u1[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) u0[t] = acc[t][0] + acc[t][1], u1[t] = acc[t][2] + acc[t][3];
+  rows_transpose(u0);  // u0[r]: head 2r
+  rows_transpose(u1);  // u1[r]: head 2r + 1
+  a4[0] = (f4v){u0[0], u1[0], u0[1], u1[1]};
+  a4[1] = (f4v){u0[2], u1[2], u0[3], u1[3]};
 }
 
 // Width-1..3 groups on the matrix cores: per k-step (four positions of one
@@ -559,19 +634,23 @@ __device__ __forceinline__ void v_mfma_steps(const uint32_t (&va)[2 * VB], const
 
 template <int G, int VB, int WK, class QR>
 __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile, const StreamState &st,
-                                             const QR &qr, const float (&rinv)[G], float (&mrun)[G],
+                                             const QR &qr, const float (&rinv)[G], const float (&rinv4)[G],
+                                             float (&mrun)[G],
                                              float (&mth)[G], float (&lsum)[G], f4v (&acc0)[VQuads<G>::v],
                                              f4v (&acc1)[VQuads<G>::v], int lane) {
-  // ---- keys, lane = token.  4-bit group: one fp32 step per code.
+  // ---- keys, lane = token.  4-bit group: one fp32 step per code, or (query
+  // operands in LDS) the split-fp16 16x16x32 products from the staged words.
+  // The key words are staged in this wave's LDS rows for the k-steps of
+  // widths 3, 2, 1 (norm slots 1, 2, 3): lr = sum_w n_w acc_w.
+  constexpr bool kWide = StreamLds<G, VB, WK>::qlds;
   f4v a4[VQuads<G>::v];
 #pragma unroll
   for (int g = 0; g < VQuads<G>::v; ++g) a4[g] = (f4v){0.f, 0.f, 0.f, 0.f};
-  key4_group<G, VB, WK>(r.w, st.n4w, st.c4slot, qr, a4);
-  // widths 3, 2, 1 (norm slots 1, 2, 3): fp16 k-steps, lr = sum_w n_w acc_w,
-  // from the key words staged in this wave's LDS rows
+  if constexpr (!kWide) key4_group<G, VB, WK>(r.w, st.n4w, st.c4slot, qr, a4);
 #pragma unroll
   for (int j = 0; j < WK; ++j)
     *(__attribute__((address_space(3))) uint32_t *)(size_t)(st.kwl + 256 * j) = r.w[j];
+  if constexpr (kWide) key4_wide<G, VB, WK>(st.n4w, st.kwb, qr.qaa, st.c4slot, a4);
   float lr[G];
   {
     f4v ak[VQuads<G>::v];
@@ -602,7 +681,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
   bool up = false;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] = valid ? fmaf(n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
+    l[h] = valid ? fmaf(kWide ? n4 * rinv4[h] : n4, a4[h >> 2][h & 3], lr[h] * rinv[h]) : -INFINITY;
     up = up || l[h] + dv > mth[h];
   }
   if (__builtin_amdgcn_ballot_w64(up) != 0) {
@@ -662,14 +741,23 @@ __device__ __forceinline__ void process_tile(const TileRegs<VB, WK> &r, int tile
 // as the preparation kernel writes them to the workspace: one 64-lane row per
 // register, so that the decode kernel loads each register with one coalesced
 // load whose address does not depend on loaded data.
+//
+// Eight heads also get the 4-bit group as the A operands of the 16x16x32 fp16
+// products (qa, see key4_wide); the kernels that keep their query operands in
+// LDS copy the image up to q4 (kq, the scales and qa) and read the rest of
+// their operands there.
 template <int G>
 struct QueryImage {
   static constexpr int VQ = VQuads<G>::v;
-  static constexpr int q4 = 0;                             // float [8][VQ][64]
-  static constexpr int kq = q4 + 8 * VQ * kTile * 4;       // h4v [3][2][VQ][64]
-  static constexpr int rinv = kq + 3 * 2 * VQ * kTile * 8; // float [G], 1 / the k-step operands' scale
-  static constexpr int bytes = rinv + 256;
-  static_assert(bytes % 256 == 0 && G <= 64, "256-byte slots");
+  static constexpr bool wide = G == 8;
+  static constexpr int kq = 0;                               // h4v [3][2][VQ][64]
+  static constexpr int rinv = kq + 3 * 2 * VQ * kTile * 8;   // float [G]: 1 / the k-step operands' scale;
+  static constexpr int rinv4 = rinv + 128;                   // float [G]: 1 / the qa operands' scale
+  static constexpr int qa = rinv + 256;                      // (eight heads) fp16 [8 chunks][64][8]
+  static constexpr int q4 = qa + (wide ? 8 * kTile * 16 : 0);  // float [8][VQ][64]
+  static constexpr int bytes = q4 + 8 * VQ * kTile * 4;
+  static constexpr int lds_bytes = q4;
+  static_assert(bytes % 256 == 0 && G <= 32, "256-byte slots");
 };
 
 constexpr int kPrepWaves = 8;
@@ -719,6 +807,37 @@ __device__ __forceinline__ void prep_role(const PrepArgs &pa, int kvh, int b) {
     ((uint2 *)(img + QI::kq))[i] = ((const uint2 *)(out + PO::qr))[(k * VQ + g) * 4 + (l & 3)];
   }
   if (tid < G) ((float *)(img + QI::rinv))[tid] = ((const float *)(out + PO::rinv))[tid];
+  if constexpr (QI::wide) {
+    // qa: the 4-bit group as the 16x16x32 A operands (key4_wide), head h's
+    // values scaled by the power of two fac[h] that brings their largest
+    // magnitude to [2^13, 2^14) and split as q = q_hi + q_lo in fp16.
+    // Wave h finds head h's scale (eight waves, eight heads).
+    static_assert(kPrepWaves == G, "one wave per head");
+    float *fac = (float *)(scr + PrepScratch<G>::hm);
+    const float *q4 = (const float *)(out + PO::q4);
+    const float m = wave_max(fmaxf(fabsf(q4[wave * kHeadDim + lane]), fabsf(q4[wave * kHeadDim + lane + 64])));
+    int e = 0;
+    (void)frexpf(m, &e);
+    e = m > 0.f ? e : 0;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    if (lane == 0) {
+      fac[wave] = ldexpf(1.f, 14 - e);
+      ((float *)(img + QI::rinv4))[wave] = ldexpf(1.f, e - 14);
+    }
+    __syncthreads();
+    // element i = (chunk c, lane l, e): row l % 16 = 4r + j is head 2r + j / 2,
+    // part j % 2; k-slot 8 (l / 16) + e is code 16 c + 8 (l / 32) + e against
+    // c_hi (l / 16 even) or c_lo (odd; the q_lo rows are zero there)
+    _Float16 *qa = (_Float16 *)(img + QI::qa);
+    for (int i = tid; i < 8 * kTile * 8; i += T) {
+      const int el = i & 7, l = (i >> 3) & 63, c = i >> 9;
+      const int row = l & 15, kb = l >> 4;
+      const int h = 2 * (row >> 2) + ((row >> 1) & 1);
+      const float v = q4[h * kHeadDim + 16 * c + 8 * (kb >> 1) + el] * fac[h];
+      const _Float16 hi = (_Float16)v, lo = (_Float16)(v - (float)hi);
+      qa[i] = (row & 1) == 0 ? hi : ((kb & 1) ? (_Float16)0.f : lo);
+    }
+  }
 }
 
 // One workgroup per (KV head, sequence).
@@ -850,14 +969,14 @@ void decode_kernel(const DecodeArgs a) {
   QueryRegs<G, Lds::qlds> qr;
   constexpr int kImg16 = Lds::qimg_bytes / 16;  // 16-byte pieces of the image copied to LDS (eight heads)
   constexpr int kImgRounds = (kImg16 + kStreamThreads - 1) / kStreamThreads;
-  uint4 qimg[kImgRounds > 0 ? kImgRounds : 1];
+  static_assert(kImgRounds <= 2, "two rounds of image loads");
+  uint4 qimg0 = make_uint4(0u, 0u, 0u, 0u), qimg1 = qimg0;  // (scalars: an array of them went to scratch)
   if constexpr (Lds::qlds) {
-    static_assert(QI::bytes == Lds::qimg_bytes, "query image in LDS");
-#pragma unroll
-    for (int i = 0; i < kImgRounds; ++i)
-      qimg[i] = ((const uint4 *)img)[min(tid + i * kStreamThreads, kImg16 - 1)];
-    qr.q4a = (uint32_t)(Lds::qimg + QI::q4 + lane * 4);
+    static_assert(QI::lds_bytes == Lds::qimg_bytes && QI::wide, "query image in LDS");
+    qimg0 = ((const uint4 *)img)[min(tid, kImg16 - 1)];
+    if constexpr (kImgRounds > 1) qimg1 = ((const uint4 *)img)[min(tid + kStreamThreads, kImg16 - 1)];
     qr.kqa = (uint32_t)(Lds::qimg + QI::kq + lane * 8);
+    qr.qaa = (uint32_t)(Lds::qimg + QI::qa + lane * 16);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -872,9 +991,12 @@ void decode_kernel(const DecodeArgs a) {
           qr.kq[r][j][g] =
               __builtin_bit_cast(h4v, ((const uint2 *)(img + QI::kq))[((2 * r + j) * VQ + g) * kTile + lane]);
   }
-  float rinv[G];
+  float rinv[G], rinv4[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) rinv[h] = ((const float *)(img + QI::rinv))[h];
+  for (int h = 0; h < G; ++h) {
+    rinv[h] = ((const float *)(img + QI::rinv))[h];
+    rinv4[h] = Lds::qlds ? ((const float *)(img + QI::rinv4))[h] : 1.f;
+  }
   // ---- tiles of this wave: tile_lo + wave, + W, ... (W waves); two in flight
   // in registers, their range bounded by max_seq_len (in memory)
   const int tile_lo = split * a.tiles_base + min(split, a.tiles_extra);
@@ -908,7 +1030,14 @@ void decode_kernel(const DecodeArgs a) {
   for (int rr = 0; rr < kRowRounds; ++rr) {
     const int e = (tid >> 2) + rr * (kStreamThreads / 4), part = tid & 3;
     if (e >= 256) break;
-    const uint2 v = rsrc[rr];
+    uint2 v = rsrc[rr];
+    if (Lds::qlds && part >= 2) {  // the pair (c, c') as fp16 (c_hi, c'_hi) and (c_lo, c'_lo)
+      const float c0 = __builtin_bit_cast(float, v.x), c1 = __builtin_bit_cast(float, v.y);
+      const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+      const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+      typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+      v = make_uint2(__builtin_bit_cast(uint32_t, (h2t){h0, h1}), __builtin_bit_cast(uint32_t, (h2t){l0, l1}));
+    }
     // 64 bytes of row e: slots of 8 bytes (two copies per 16-byte store) or of 4 bytes (four)
     const uint4 q = (part >= 2 || VB == 2) ? make_uint4(v.x, v.y, v.x, v.y) : make_uint4(v.x, v.x, v.x, v.x);
     uint4 *dst = (uint4 *)(smem + Lds::rep + 256 * e + 64 * part);
@@ -922,9 +1051,9 @@ void decode_kernel(const DecodeArgs a) {
   if constexpr (VB == 1)
     if (tid < kVEntries) *(uint4 *)(smem + Lds::vcomp + 16 * tid) = vcomp;
   if constexpr (Lds::qlds) {
-#pragma unroll
-    for (int i = 0; i < kImgRounds; ++i)
-      if (tid + i * kStreamThreads < kImg16) *(uint4 *)(smem + Lds::qimg + 16 * (tid + i * kStreamThreads)) = qimg[i];
+    if (tid < kImg16) *(uint4 *)(smem + Lds::qimg + 16 * tid) = qimg0;
+    if (kImgRounds > 1 && tid + kStreamThreads < kImg16)
+      *(uint4 *)(smem + Lds::qimg + 16 * (tid + kStreamThreads)) = qimg1;
   }
   StreamState st;
   st.seq = (seq_raw < 0 ? 0 : (seq_raw > a.max_seq_len ? a.max_seq_len : seq_raw)) - a.n_recent;
@@ -932,8 +1061,9 @@ void decode_kernel(const DecodeArgs a) {
   st.nv = (uint32_t)(st.seq > st.lo ? st.seq - st.lo : 0);
   st.wk = a.wk;
   st.kwl = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + lane * 4);
+  st.kwb = (uint32_t)(Lds::kw + wave * (Lds::kw_rows * kTile * 4) + (lane >> 5) * kTile * 4 + (lane & 15) * 4);
   st.vslot = (uint32_t)(lane & (128 / Lds::vslot - 1)) * Lds::vslot;
-  st.c4slot = 128u + (uint32_t)(lane & 15) * 8u;
+  st.c4slot = 128u + (uint32_t)(lane & 15) * 8u + (Lds::qlds ? 4u * (uint32_t)((lane >> 4) & 1) : 0u);
   st.n4w = n4w;
   st.cgrp = cgrp;
   st.gbit = gbit;
@@ -961,7 +1091,7 @@ void decode_kernel(const DecodeArgs a) {
   // limit.)
   for (; tile < tile_hi; tile += kStreamWaves) {
     wave_priority((tile_hi - 1 - tile) / kStreamWaves);
-    process_tile<G, VB, WK>(ra, tile, st, qr, rinv, mrun, mth, lsum, acc0, acc1, lane);
+    process_tile<G, VB, WK>(ra, tile, st, qr, rinv, rinv4, mrun, mth, lsum, acc0, acc1, lane);
     ra = rb;
     if (tile + 2 * kStreamWaves < tile_hi) {
       const size_t bn = head_base + (paged ? pnext : (size_t)(tile + 2 * kStreamWaves));
