@@ -828,14 +828,21 @@ __device__ __forceinline__ void prep_role(const PrepArgs &pa, int kvh, int b) {
     // element i = (chunk c, lane l, e): row l % 16 = 4r + j is head 2r + j / 2,
     // part j % 2; k-slot 8 (l / 16) + e is code 16 c + 8 (l / 32) + e against
     // c_hi (l / 16 even) or c_lo (odd; the q_lo rows are zero there)
-    _Float16 *qa = (_Float16 *)(img + QI::qa);
-    for (int i = tid; i < 8 * kTile * 8; i += T) {
-      const int el = i & 7, l = (i >> 3) & 63, c = i >> 9;
+    // (one 16-byte operand per thread and round)
+    for (int i = tid; i < 8 * kTile; i += T) {
+      const int l = i & 63, c = i >> 6;
       const int row = l & 15, kb = l >> 4;
       const int h = 2 * (row >> 2) + ((row >> 1) & 1);
-      const float v = q4[h * kHeadDim + 16 * c + 8 * (kb >> 1) + el] * fac[h];
-      const _Float16 hi = (_Float16)v, lo = (_Float16)(v - (float)hi);
-      qa[i] = (row & 1) == 0 ? hi : ((kb & 1) ? (_Float16)0.f : lo);
+      const float f = fac[h];
+      const float *src = q4 + h * kHeadDim + 16 * c + 8 * (kb >> 1);
+      h8v o;
+#pragma unroll
+      for (int el = 0; el < 8; ++el) {
+        const float v = src[el] * f;
+        const _Float16 hi = (_Float16)v, lo = (_Float16)(v - (float)hi);
+        o[el] = (row & 1) == 0 ? hi : ((kb & 1) ? (_Float16)0.f : lo);
+      }
+      ((h8v *)(img + QI::qa))[i] = o;
     }
   }
 }
