@@ -17,8 +17,9 @@
 //                 LDS (lookup rows), the query registers from the image, the
 //                 first tiles requested.  Per 64-token tile (lane = token):
 //                 key words read coalesced (word-major); logits on the matrix
-//                 cores (the 4-bit group one fp32 4x4x1 step per code, the
-//                 width-1..3 groups one fp16 4x4x4 k-step per four codes, both
+//                 cores (the 4-bit group one fp32 4x4x1 step per code, or for
+//                 eight heads split-fp16 16x16x32 products per 16 codes, the
+//                 width-1..3 groups one fp16 4x4x4 k-step per four codes, all
 //                 with LDS centroid lookups, the lookups of the next batch in
 //                 flight during the products) times the group norms, in log2
 //                 units; online softmax with wavefront reductions; the value
