@@ -5,8 +5,13 @@
 // benchmark).  Same split-sequence structure as the packed decode, same online
 // softmax and split merge, fp32 accumulation:
 //  * one workgroup of 4 waves per (split, KV head, sequence); per 64-token tile
-//    of a wave, lane = token reads its key row (256 bytes) and forms the G
-//    logits with v_dot2 (fp16 products, fp32 sums) against the queries in LDS;
+//    of a wave, the logits on the 16x16x32 fp16 matrix cores (fp16 products,
+//    fp32 sums): per group of 16 tokens and 32 coordinates one product whose B
+//    operand is 16 bytes of a key row per lane (each load instruction reads 64
+//    contiguous bytes of 16 rows) and whose A operand (the queries, from LDS)
+//    has its rows at the token group's row block, so that the four groups'
+//    results land in one accumulator with lane = token (a lane-per-row read
+//    of the keys moved 8x the key bytes through the caches);
 //  * the softmax weights go to the wave's LDS row; lane (j, c) then sums the
 //    value rows of the tokens 4u + j, u < 16, over its 8 coordinates 8c..8c+7
 //    (16-byte loads, fp32 accumulation), and the four token phases j are
@@ -37,22 +42,38 @@ struct F16Args {
   float kscale;       // softmax scale * log2(e)
 };
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int G>
 __global__ __launch_bounds__(kF16Threads) void f16_decode_kernel(const F16Args a) {
-  __shared__ __attribute__((aligned(16))) uint32_t qs[G * 64];               // fp16 pairs
+  constexpr int P = (G + 3) / 4;  // passes of four heads
+  // A operands [pass][token group][32-coordinate chunk][lane]: lane l holds row
+  // l % 16 = 4 tg' + m (head 4 pass + m if tg' is the token group, else zero),
+  // coordinates 32 kc + 8 (l / 16) .. + 7
+  // (after the tile loop the same LDS holds the wave merge: four workgroups
+  // per compute unit fit with eight heads)
+  constexpr int kQaBytes = P * 16 * 64 * 16, kMrgBytes = kF16Waves * G * kPartStride * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t qa_mrg[kQaBytes > kMrgBytes ? kQaBytes : kMrgBytes];
+  f16x8(*qa)[4][4][64] = (f16x8(*)[4][4][64])qa_mrg;
+  float *mrg = (float *)qa_mrg;
   __shared__ __attribute__((aligned(16))) float pw[kF16Waves][G][kTile];     // softmax weights
-  __shared__ __attribute__((aligned(16))) float mrg[kF16Waves * G * kPartStride];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t *qg = (const uint32_t *)(a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim);
-  for (int i = tid; i < G * 64; i += kF16Threads) qs[i] = qg[i];
+  const uint16_t *qg = a.q + ((size_t)b * a.hq + (size_t)kvh * G) * kHeadDim;
+  for (int i = tid; i < P * 16 * 64; i += kF16Threads) {
+    const int l = i & 63, kc = (i >> 6) & 3, tg = (i >> 8) & 3, pass = i >> 10;
+    const int r = l & 15, h = 4 * pass + (r & 3);
+    f16x8 v;
+    if ((r >> 2) == tg && h < G) {
+      const uint4 w = *(const uint4 *)(qg + (size_t)h * kHeadDim + 32 * kc + 8 * (l >> 4));
+      v = __builtin_bit_cast(f16x8, w);
+    } else {
+      v = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    qa[pass][tg][kc][l] = v;
+  }
   int64_t seq = a.seq_lens[b];
   seq = seq < 0 ? 0 : (seq > a.max_seq_len ? a.max_seq_len : seq);
   __syncthreads();
@@ -72,25 +93,33 @@ __global__ __launch_bounds__(kF16Threads) void f16_decode_kernel(const F16Args a
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
   for (int tile = tile_lo + wave; tile < tile_hi; tile += kF16Waves) {
-    // ---- logits, lane = token (rows past the sequence read its last token)
+    // ---- logits: token group tg = lanes' tokens 16 tg .. 16 tg + 15; lane l
+    // reads 16 bytes of row 16 tg + l % 16 at byte 64 kc + 16 (l / 16) (rows
+    // past the sequence read its last token); the result has lane = token
     const int64_t t = (int64_t)tile * kTile + lane;
     const bool valid = t < seq;
-    const uint4 *kr = (const uint4 *)(kb + (size_t)(valid ? t : seq - 1) * tstride);
+    uint4 kv[4][4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int64_t tr = (int64_t)tile * kTile + 16 * tg + (lane & 15);
+      const uint4 *kr = (const uint4 *)(kb + (size_t)(tr < seq ? tr : seq - 1) * tstride) + (lane >> 4);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) kv[tg][kc] = kr[4 * kc];
+    }
+    f32x4 sacc[P];
+#pragma unroll
+    for (int pass = 0; pass < P; ++pass) {
+      sacc[pass] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          sacc[pass] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[pass][tg][kc][lane],
+                                                             __builtin_bit_cast(f16x8, kv[tg][kc]), sacc[pass], 0, 0, 0);
+    }
     float sc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint4 kv = kr[c];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint4 qv = *(const uint4 *)&qs[h * 64 + 4 * c];
-        sc[h] = dot2(kv.x, qv.x, sc[h]);
-        sc[h] = dot2(kv.y, qv.y, sc[h]);
-        sc[h] = dot2(kv.z, qv.z, sc[h]);
-        sc[h] = dot2(kv.w, qv.w, sc[h]);
-      }
-    }
+    for (int h = 0; h < G; ++h) sc[h] = sacc[h >> 2][h & 3];
     // ---- online softmax (log2 domain), lazy rescale as in the packed decode
     float l[G];
     bool up = false;
@@ -137,6 +166,7 @@ __global__ __launch_bounds__(kF16Threads) void f16_decode_kernel(const F16Args a
     wave_sync_lds();  // the weights row is rewritten by the next tile
   }
   // ---- the four token phases of each coordinate, then the waves of the split
+  __syncthreads();  // every wave is past its last read of the query operands
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     lsum[h] = wave_sum(lsum[h]);
