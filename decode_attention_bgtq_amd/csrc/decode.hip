@@ -415,13 +415,14 @@ __device__ __forceinline__ void key4_wide(int n4w, uint32_t kwb, uint32_t qaa, u
     uint32_t wd[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) wd[t] = lds_at<uint32_t>(kwb + c * 512 + t * 64);
-    h8v b0 = wide_b<L>(wd[0], slot), b1;
+    h8v bb[2];  // B operands of token groups t (in use) and t + 1 (in flight)
+    bb[0] = wide_b<L>(wd[0], slot);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t + 1 < 4) ((t & 1) ? b0 : b1) = wide_b<L>(wd[t + 1], slot);
+      if (t + 1 < 4) bb[(t + 1) & 1] = wide_b<L>(wd[t + 1], slot);
       __builtin_amdgcn_sched_barrier(0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, (t & 1) ? b1 : b0, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb[t & 1], acc[t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -263,6 +263,19 @@ def test_decode_zero_bit_keys(bg):
         assert rel_l2(got[0, h], ref) <= TOL
 
 
+def test_encode_kv_zero_bit_keys(bg):
+    """bgtq_encode_kv with a zero-bit key plan: no key words, zero key norms, the values
+    bit-exact, and the decode the mean of the values."""
+    cfg = synth.small(2, seq_len=200, k_bits=0)
+    bits = np.zeros((cfg.n_kv_heads, 64), np.int8)
+    plan, cache, _, ks, vs, heads = _encode_case(bg, cfg, 200, bits=bits, fused=True)
+    q = synth.query(cfg)[None]
+    got = decode_gpu(plan, cache, q, [200], 200)
+    for h in range(cfg.n_q_heads):
+        ref = heads[(0, h // cfg.group)].v_hat().mean(0)
+        assert rel_l2(got[0, h], ref) <= TOL
+
+
 def test_decode_deterministic(bg):
     cfg = synth.small(3, seq_len=5000)
     plan, cache, q, got = _decode_check(bg, cfg, 5000)
