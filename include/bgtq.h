@@ -255,13 +255,15 @@ bgtq_status bgtq_key_logits(const bgtq_plan *plan, const void *dev_consts, const
  *   l_t = softmax_scale * q . k_hat_t,  o = sum_t softmax(l)_t v_hat_t
  * over t < seq_len, where k_hat, v_hat are the TurboQuant-MSE reconstructions
  * (fp16 norm * Pi^T (centroid / sqrt(d_g))).  Computed without
- * materialising k_hat or v_hat, in two launches: the decode kernel rotates the
- * queries once per key group, takes the logits in the rotated space from LDS
- * centroid lookups on the matrix cores (fp32 for the 4-bit group, fp16
- * operands with fp32 accumulation for widths 1..3), keeps an online softmax
- * and accumulates the values in the rotated value space, one partial per
- * split of the sequence; the merge kernel combines the splits and un-rotates
- * once per head.  fp32 accumulation throughout.  The value operand (softmax
+ * materialising k_hat or v_hat, in three launches: a preparation kernel
+ * rotates the queries once per key group; the decode kernel takes the logits
+ * in the rotated space from LDS centroid lookups on the matrix cores (fp32
+ * products for the 4-bit group -- with eight query heads per KV head, query and
+ * centroid each split into two fp16 parts -- and fp16 operands for widths
+ * 1..3), keeps an online softmax and accumulates the values in the rotated
+ * value space, one partial per split of the sequence; the merge kernel
+ * combines the splits and un-rotates once per head.  fp32 accumulation
+ * throughout.  The value operand (softmax
  * weight x fp16 value norm) is kept finite for every finite value norm (the
  * running maximum is raised early for tokens whose norm is 128 or more); a
  * value whose norm overflowed fp16 at encode (+inf) makes the output NaN, as
