@@ -30,7 +30,7 @@ EXPORTED = [
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
     "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc", "bgtq_key_logits",
-    "bgtq_encode_kv", "bgtq_encode_kv_paged",
+    "bgtq_encode_kv", "bgtq_encode_kv_paged", "bgtq_decode_attn_paged_buffered",
 ]
 
 
@@ -106,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bgtq_encode_v_paged": (I32, [P, P, P, I32, ctypes.POINTER(_Pages), I64, I64, P, P, P]),
         "bgtq_decode_attn_paged": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
                                          ctypes.c_float, P, P, SZ, P]),
+        "bgtq_decode_attn_paged_buffered": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
+                                                  ctypes.c_float, P, P, I32, P, P, I32, P, P, SZ, P]),
         "bgtq_decode_step_paged": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, ctypes.POINTER(_Pages),
                                          ctypes.c_float, P, P, SZ, P]),
         "bgtq_noalloc_scratch_bytes": (SZ, []),
@@ -438,6 +440,22 @@ class Plan:
         _check(load().bgtq_decode_attn_paged(
             self._h, _ptr(consts), _ptr(q), _ptr(pages.k_codes), _ptr(pages.k_norms), _ptr(pages.v_codes),
             _ptr(pages.v_norms), ctypes.byref(pg), _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale,
+            _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+    def decode_attn_paged_buffered(self, consts, q, pages: "PagedCache", seq_lens, max_seq_len: int,
+                                   buf: "Buffer", out, workspace, softmax_scale: float | None = None,
+                                   stream=None) -> None:
+        """decode_attn_paged with the fp16 sink and recent-window tokens of ``buf`` taken from fp16."""
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, seq_lens, out, workspace)
+        _gpu(q=q, seq_lens=seq_lens, out=out, workspace=workspace)
+        pg = pages.desc()
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_attn_paged_buffered(
+            self._h, _ptr(consts), _ptr(q), _ptr(pages.k_codes), _ptr(pages.k_norms), _ptr(pages.v_codes),
+            _ptr(pages.v_norms), ctypes.byref(pg), _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale,
+            _ptr(buf.k_sink), _ptr(buf.v_sink), buf.n_sink, _ptr(buf.k_recent), _ptr(buf.v_recent), buf.n_recent,
             _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
     def decode_step_paged(self, consts, q, k_new, v_new, pos, max_seq_len: int, pages: "PagedCache", out,

@@ -1420,6 +1420,38 @@ static bgtq_status scratch_address(void **out) {
 
 using namespace bgtq;
 
+// The buffered decode on a contiguous cache (pages null) or a paged pool.
+static bgtq_status decode_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                   const uint32_t *k_codes, const uint16_t *k_norms, const uint32_t *v_codes,
+                                   const uint16_t *v_norms, int64_t capacity, const bgtq_pages *pages,
+                                   const int32_t *seq_lens, int32_t batch, int64_t max_seq_len, float softmax_scale,
+                                   const uint16_t *k_sink, const uint16_t *v_sink, int32_t n_sink,
+                                   const uint16_t *k_recent, const uint16_t *v_recent, int32_t n_recent,
+                                   uint16_t *out, void *workspace, size_t ws_bytes, bgtq_stream stream,
+                                   const char *nm) {
+  if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace ||
+      (!k_codes && plan->p.hdr.wk > 0))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
+  if (n_sink < 0 || n_sink > kMaxSink || n_recent < 0 || n_recent > kMaxRecent)
+    return fail(BGTQ_EINVAL, std::string(nm) + ": n_sink must be 0..64 and n_recent 0..65536");
+  if ((n_sink && (!k_sink || !v_sink)) || (n_recent && (!k_recent || !v_recent)))
+    return fail(BGTQ_EINVAL, std::string(nm) + ": null buffer with a non-zero count");
+  if (((uintptr_t)k_sink | (uintptr_t)v_sink | (uintptr_t)k_recent | (uintptr_t)v_recent | (uintptr_t)q) & 15)
+    return fail(BGTQ_EINVAL, std::string(nm) + ": q and the buffers must be 16-byte aligned");
+  const bgtq_status v = decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
+  if (v != BGTQ_OK) return v;
+  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
+               softmax_scale, out, workspace, stream};
+  c.k_sink = k_sink;
+  c.v_sink = v_sink;
+  c.k_recent = k_recent;
+  c.v_recent = v_recent;
+  c.n_sink = n_sink;
+  c.n_recent = n_recent;
+  c.pages = pages;
+  return decode_launch(plan->p, c);
+}
+
 extern "C" {
 
 size_t bgtq_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
@@ -1507,27 +1539,25 @@ bgtq_status bgtq_decode_attn_buffered(const bgtq_plan *plan, const void *dev_con
                                       const uint16_t *k_sink, const uint16_t *v_sink, int32_t n_sink,
                                       const uint16_t *k_recent, const uint16_t *v_recent, int32_t n_recent,
                                       uint16_t *out, void *workspace, size_t ws_bytes, bgtq_stream stream) {
-  const char *nm = "bgtq_decode_attn_buffered";
-  if (!plan || !dev_consts || !q || !k_norms || !v_codes || !v_norms || !seq_lens || !out || !workspace ||
-      (!k_codes && plan->p.hdr.wk > 0))
-    return fail(BGTQ_EINVAL, std::string(nm) + ": null pointer");
-  if (n_sink < 0 || n_sink > kMaxSink || n_recent < 0 || n_recent > kMaxRecent)
-    return fail(BGTQ_EINVAL, std::string(nm) + ": n_sink must be 0..64 and n_recent 0..65536");
-  if ((n_sink && (!k_sink || !v_sink)) || (n_recent && (!k_recent || !v_recent)))
-    return fail(BGTQ_EINVAL, std::string(nm) + ": null buffer with a non-zero count");
-  if (((uintptr_t)k_sink | (uintptr_t)v_sink | (uintptr_t)k_recent | (uintptr_t)v_recent | (uintptr_t)q) & 15)
-    return fail(BGTQ_EINVAL, std::string(nm) + ": q and the buffers must be 16-byte aligned");
-  const bgtq_status v = decode_check(plan->p, capacity, batch, max_seq_len, softmax_scale, workspace, ws_bytes, nm);
-  if (v != BGTQ_OK) return v;
-  DecodeCall c{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, seq_lens, 0, batch, max_seq_len,
-               softmax_scale, out, workspace, stream};
-  c.k_sink = k_sink;
-  c.v_sink = v_sink;
-  c.k_recent = k_recent;
-  c.v_recent = v_recent;
-  c.n_sink = n_sink;
-  c.n_recent = n_recent;
-  return decode_launch(plan->p, c);
+  return decode_buffered(plan, dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, nullptr, seq_lens, batch,
+                         max_seq_len, softmax_scale, k_sink, v_sink, n_sink, k_recent, v_recent, n_recent, out,
+                         workspace, ws_bytes, stream, "bgtq_decode_attn_buffered");
+}
+
+bgtq_status bgtq_decode_attn_paged_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                            const uint32_t *k_codes, const uint16_t *k_norms,
+                                            const uint32_t *v_codes, const uint16_t *v_norms,
+                                            const bgtq_pages *pages, const int32_t *seq_lens, int32_t batch,
+                                            int64_t max_seq_len, float softmax_scale, const uint16_t *k_sink,
+                                            const uint16_t *v_sink, int32_t n_sink, const uint16_t *k_recent,
+                                            const uint16_t *v_recent, int32_t n_recent, uint16_t *out,
+                                            void *workspace, size_t ws_bytes, bgtq_stream stream) {
+  const char *nm = "bgtq_decode_attn_paged_buffered";
+  const bgtq_status ps = pages_check(pages, nm);
+  if (ps != BGTQ_OK) return ps;
+  return decode_buffered(plan, dev_consts, q, k_codes, k_norms, v_codes, v_norms, (int64_t)kTile * pages->max_pages,
+                         pages, seq_lens, batch, max_seq_len, softmax_scale, k_sink, v_sink, n_sink, k_recent,
+                         v_recent, n_recent, out, workspace, ws_bytes, stream, nm);
 }
 
 }  // extern "C"

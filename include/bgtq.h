@@ -403,6 +403,19 @@ bgtq_status bgtq_decode_attn_paged(const bgtq_plan *plan, const void *dev_consts
                                    int64_t max_seq_len, float softmax_scale, uint16_t *out,
                                    void *workspace, size_t ws_bytes, bgtq_stream stream);
 
+/* (6) on a paged pool with the fp16 sink and recent window (6b): the packed
+ * tokens are read through the block table as in bgtq_decode_attn_paged, the
+ * buffered ones from the fp16 buffers as in bgtq_decode_attn_buffered.
+ * Arguments and errors: those two calls'. */
+bgtq_status bgtq_decode_attn_paged_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                            const uint32_t *k_codes, const uint16_t *k_norms,
+                                            const uint32_t *v_codes, const uint16_t *v_norms,
+                                            const bgtq_pages *pages, const int32_t *seq_lens, int32_t batch,
+                                            int64_t max_seq_len, float softmax_scale, const uint16_t *k_sink,
+                                            const uint16_t *v_sink, int32_t n_sink, const uint16_t *k_recent,
+                                            const uint16_t *v_recent, int32_t n_recent, uint16_t *out,
+                                            void *workspace, size_t ws_bytes, bgtq_stream stream);
+
 /*
  * (7) Decode step: appends one new key and value per sequence to the packed
  * cache and attends the new query over the cache including that token (the

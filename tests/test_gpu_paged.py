@@ -156,3 +156,39 @@ def test_paged_decode_step_equals_contiguous(bg):
         for s in range(3):
             for j in range(5):
                 assert np.array_equal(pa[:, table[s, j]], ca[s, :, j]), (name, s, j)
+
+
+@pytest.mark.parametrize("cid,seq_len,n_sink,n_recent", [(4, 700, 4, 128), (2, 900, 64, 300), (1, 300, 0, 64)])
+def test_paged_buffered_decode_equals_contiguous(bg, cid, seq_len, n_sink, n_recent):
+    """Paged pool + fp16 sink / recent window: the output equals the contiguous buffered decode's
+    bit for bit (two sequences, a shuffled block table; the contiguous buffered decode is checked
+    against the oracle in test_gpu_buffer)."""
+    import torch
+    batch = 2
+    cfg = synth.small(cid, seq_len=seq_len, batch=batch)
+    log("paged buffered decode config %d T=%d sink %d recent %d" % (cid, seq_len, n_sink, n_recent))
+    q_cal, k_cal = synth.calibration(cfg)
+    _, bits = ref_bits(q_cal, k_cal, cfg.n_kv_heads, cfg.k_bits)
+    plan = bg.Plan(bits, cfg.k_bits, cfg.v_bits, cfg.n_q_heads, seed=cfg.seed)
+    n_tiles = (seq_len + 63) // 64
+    n_pages = batch * n_tiles + 2
+    table = np.random.default_rng(11).permutation(n_pages)[:batch * n_tiles].reshape(batch, n_tiles)
+    table = table.astype(np.int32)
+    pool = bg.PagedCache(plan, n_pages, table)
+    cont = bg.Cache(plan, batch, seq_len)
+    ks = np.stack([synth.keys(cfg, seq=s, count=seq_len) for s in range(batch)])
+    vs = np.stack([synth.values(cfg, seq=s, count=seq_len) for s in range(batch)])
+    pool.encode_kv(to_dev(ks), to_dev(vs), 0)
+    cont.encode(to_dev(ks), to_dev(vs), 0)
+    buf = bg.Buffer(batch, cfg.n_kv_heads, n_sink, n_recent, device=dev())
+    buf.append(to_dev(ks), to_dev(vs), 0)
+    seq_lens = np.array([seq_len, seq_len], np.int32)  # the buffers hold the last tokens of both
+    q = np.stack([synth.query(cfg, seq=s) for s in range(batch)])
+    out_p = torch.empty((batch, cfg.n_q_heads, 128), dtype=torch.int16, device=dev())
+    out_c = torch.empty_like(out_p)
+    ws = torch.empty(plan.workspace_size(batch, seq_len), dtype=torch.uint8, device=dev())
+    plan.decode_attn_paged_buffered(pool.consts, to_dev(q), pool, to_dev(seq_lens), seq_len, buf, out_p, ws)
+    plan.decode_attn_buffered(cont.consts, to_dev(q), cont.k_codes, cont.k_norms, cont.v_codes, cont.v_norms, seq_len,
+                              to_dev(seq_lens), seq_len, buf, out_c, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_p.cpu().numpy(), out_c.cpu().numpy())

@@ -138,6 +138,16 @@ def test_paged_calls_reject_bad_arguments_before_launch(bg):
                                       None) == bg.ECAPACITY
     assert lib.bgtq_decode_attn_paged(*args, ctypes.byref(bad[1]), 256, 1, 100, 0.1, 256, 256, 1 << 30,
                                       None) == bg.EINVAL
+    # paged with the fp16 buffers: the pool checks and the buffer checks, before any launch
+    pb = [256, 256, 4, 256, 256, 128]
+    assert lib.bgtq_decode_attn_paged_buffered(*args, None, 256, 1, 100, 0.1, *pb, 256, 256, 1 << 30,
+                                               None) == bg.EINVAL
+    assert lib.bgtq_decode_attn_paged_buffered(*args, ctypes.byref(pg), 256, 1, 257, 0.1, *pb, 256, 256, 1 << 30,
+                                               None) == bg.ECAPACITY
+    assert lib.bgtq_decode_attn_paged_buffered(*args, ctypes.byref(pg), 256, 1, 100, 0.1, 256, 256, 65, 256, 256,
+                                               128, 256, 256, 1 << 30, None) == bg.EINVAL   # n_sink > 64
+    assert lib.bgtq_decode_attn_paged_buffered(*args, ctypes.byref(pg), 256, 1, 100, 0.1, None, 256, 4, 256, 256,
+                                               128, 256, 256, 1 << 30, None) == bg.EINVAL   # null sink
 
 
 def test_device_calls_reject_bad_arguments_before_launch(bg):
