@@ -30,7 +30,7 @@ EXPORTED = [
     "bgtq_fp16_decode_workspace_size", "bgtq_fp16_decode_attn", "bgtq_decode_attn_buffered",
     "bgtq_buffer_append", "bgtq_encode_k_paged", "bgtq_encode_v_paged", "bgtq_decode_attn_paged",
     "bgtq_decode_step_paged", "bgtq_noalloc_scratch_bytes", "bgtq_decode_attn_noalloc", "bgtq_key_logits",
-    "bgtq_encode_kv", "bgtq_encode_kv_paged", "bgtq_decode_attn_paged_buffered",
+    "bgtq_encode_kv", "bgtq_encode_kv_paged", "bgtq_decode_attn_paged_buffered", "bgtq_decode_step_buffered",
 ]
 
 
@@ -108,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.c_float, P, P, SZ, P]),
         "bgtq_decode_attn_paged_buffered": (I32, [P, P, P, P, P, P, P, ctypes.POINTER(_Pages), P, I32, I64,
                                                   ctypes.c_float, P, P, I32, P, P, I32, P, P, SZ, P]),
+        "bgtq_decode_step_buffered": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, I64, ctypes.c_float,
+                                            P, P, I32, P, P, I32, P, P, SZ, P]),
         "bgtq_decode_step_paged": (I32, [P, P, P, P, P, P, I32, I64, P, P, P, P, ctypes.POINTER(_Pages),
                                          ctypes.c_float, P, P, SZ, P]),
         "bgtq_noalloc_scratch_bytes": (SZ, []),
@@ -457,6 +459,25 @@ class Plan:
             _ptr(pages.v_norms), ctypes.byref(pg), _ptr(seq_lens), q.shape[0], max_seq_len, softmax_scale,
             _ptr(buf.k_sink), _ptr(buf.v_sink), buf.n_sink, _ptr(buf.k_recent), _ptr(buf.v_recent), buf.n_recent,
             _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+    def decode_step_buffered(self, consts, q, k_new, v_new, pos, max_seq_len: int, k_codes, k_norms, v_codes,
+                             v_norms, capacity: int, buf: "Buffer", out, workspace,
+                             softmax_scale: float | None = None, stream=None) -> None:
+        """decode_step that also copies the new token into ``buf`` and attends with its fp16 sink and
+        recent window (decode_attn_buffered over pos[b] + 1 tokens)."""
+        if softmax_scale is None:
+            softmax_scale = HEAD_DIM ** -0.5
+        self._check_decode(q, pos, out, workspace, "pos")
+        self._check_new(q, k_new, v_new)
+        self._check_cache(k_codes, k_norms, v_codes, v_norms)
+        _gpu(q=q, k_new=k_new, v_new=v_new, pos=pos, out=out, workspace=workspace, k_codes=k_codes,
+             k_norms=k_norms, v_codes=v_codes, v_norms=v_norms)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _check(load().bgtq_decode_step_buffered(
+            self._h, _ptr(consts), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), q.shape[0], max_seq_len,
+            _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), capacity, softmax_scale, _ptr(buf.k_sink),
+            _ptr(buf.v_sink), buf.n_sink, _ptr(buf.k_recent), _ptr(buf.v_recent), buf.n_recent, _ptr(out),
+            _ptr(workspace), ws_bytes, _stream(stream)))
 
     def decode_step_paged(self, consts, q, k_new, v_new, pos, max_seq_len: int, pages: "PagedCache", out,
                           workspace, softmax_scale: float | None = None, stream=None) -> None:

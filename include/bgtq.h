@@ -440,6 +440,21 @@ bgtq_status bgtq_decode_step(const bgtq_plan *plan, const void *dev_consts, cons
                              uint16_t *v_norms, int64_t capacity, float softmax_scale, uint16_t *out,
                              void *workspace, size_t ws_bytes, bgtq_stream stream);
 
+/* (7) with the fp16 sink and recent window (6b): the new token of sequence b is
+ * appended to the packed cache as in bgtq_decode_step and copied into the
+ * buffers as bgtq_buffer_append would copy token pos[b] (sink row pos[b] when
+ * below n_sink, ring row pos[b] % n_recent; nothing for pos[b] < 0), then the
+ * output is bgtq_decode_attn_buffered's over pos[b] + 1 tokens.
+ *   k_sink ... n_recent   as for bgtq_decode_attn_buffered (written, then read)
+ * Errors: as bgtq_decode_step and bgtq_decode_attn_buffered. */
+bgtq_status bgtq_decode_step_buffered(const bgtq_plan *plan, const void *dev_consts, const uint16_t *q,
+                                      const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos,
+                                      int32_t batch, int64_t max_seq_len, uint32_t *k_codes, uint16_t *k_norms,
+                                      uint32_t *v_codes, uint16_t *v_norms, int64_t capacity, float softmax_scale,
+                                      uint16_t *k_sink, uint16_t *v_sink, int32_t n_sink, uint16_t *k_recent,
+                                      uint16_t *v_recent, int32_t n_recent, uint16_t *out, void *workspace,
+                                      size_t ws_bytes, bgtq_stream stream);
+
 /* (7) on a paged pool (6d): the new token of sequence b goes to page
  * block_table[b][pos[b] / 64] (sequences with pos[b] outside
  * [0, 64 * max_pages) append nothing), then bgtq_decode_attn_paged over

@@ -101,3 +101,42 @@ def test_decode_step_equals_separate_calls(bg):
         for g, e in zip(gpu_arrays(caches[0], 0, h), gpu_arrays(caches[1], 0, h)):
             assert np.array_equal(g, e)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("cid,n_sink,n_recent", [(4, 4, 128), (2, 64, 300), (1, 0, 64)])
+def test_decode_step_buffered_equals_separate_calls(bg, cid, n_sink, n_recent):
+    """bgtq_decode_step_buffered equals, bit for bit, the encode of the new token, its copy into
+    the fp16 buffers (bgtq_buffer_append) and the buffered decode over T + 1 tokens; both
+    buffers and both caches end up identical."""
+    import torch
+    prefix, capacity, batch = 500, 576, 2
+    cfg = synth.small(cid, seq_len=prefix + 1, batch=batch)
+    log("buffered decode step config %d sink %d recent %d" % (cid, n_sink, n_recent))
+    plan, _ = _plan(bg, cfg)
+    caches = [bg.Cache(plan, batch, capacity, device="cuda") for _ in range(2)]
+    bufs = [bg.Buffer(batch, cfg.n_kv_heads, n_sink, n_recent, device="cuda") for _ in range(2)]
+    ks = np.stack([synth.keys(cfg, seq=s, count=prefix + 1) for s in range(batch)])
+    vs = np.stack([synth.values(cfg, seq=s, count=prefix + 1) for s in range(batch)])
+    for c, bf in zip(caches, bufs):
+        c.encode(to_dev(ks[:, :prefix]), to_dev(vs[:, :prefix]), 0)
+        bf.append(to_dev(ks[:, :prefix]), to_dev(vs[:, :prefix]), 0)
+    q = to_dev(np.stack([synth.query(cfg, seq=s) for s in range(batch)]))
+    k_new, v_new = to_dev(ks[:, prefix]), to_dev(vs[:, prefix])
+    pos = to_dev(np.full(batch, prefix, np.int32))
+    out_s = torch.empty((batch, cfg.n_q_heads, 128), dtype=torch.int16, device="cuda")
+    out_r = torch.empty_like(out_s)
+    ws = torch.empty(plan.workspace_size(batch, prefix + 1), dtype=torch.uint8, device="cuda")
+    c0, c1 = caches
+    plan.decode_step_buffered(c0.consts, q, k_new, v_new, pos, prefix + 1, c0.k_codes, c0.k_norms, c0.v_codes,
+                              c0.v_norms, capacity, bufs[0], out_s, ws)
+    c1.encode(to_dev(ks[:, prefix:]), to_dev(vs[:, prefix:]), prefix)
+    bufs[1].append(to_dev(ks[:, prefix:]), to_dev(vs[:, prefix:]), prefix)
+    plan.decode_attn_buffered(c1.consts, q, c1.k_codes, c1.k_norms, c1.v_codes, c1.v_norms, capacity,
+                              to_dev(np.full(batch, prefix + 1, np.int32)), prefix + 1, bufs[1], out_r, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_s.cpu().numpy(), out_r.cpu().numpy())
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        assert torch.equal(getattr(c0, name), getattr(c1, name)), name
+    for name in ("k_sink", "v_sink", "k_recent", "v_recent"):
+        a, b = getattr(bufs[0], name), getattr(bufs[1], name)
+        assert (a is None and b is None) or torch.equal(a, b), name

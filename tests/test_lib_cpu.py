@@ -138,6 +138,13 @@ def test_paged_calls_reject_bad_arguments_before_launch(bg):
                                       None) == bg.ECAPACITY
     assert lib.bgtq_decode_attn_paged(*args, ctypes.byref(bad[1]), 256, 1, 100, 0.1, 256, 256, 1 << 30,
                                       None) == bg.EINVAL
+    # the buffered decode step: the step's checks and the buffer checks, before any launch
+    sb = [h, 256, 256, 256, 256, 256, 1, 100, 256, 256, 256, 256, 100, 0.1]
+    assert lib.bgtq_decode_step_buffered(*sb, 256, 256, 65, 256, 256, 128, 256, 256, 1 << 30, None) == bg.EINVAL
+    assert lib.bgtq_decode_step_buffered(*sb, 256, 256, 4, None, 256, 128, 256, 256, 1 << 30, None) == bg.EINVAL
+    assert lib.bgtq_decode_step_buffered(*sb, 264, 256, 4, 256, 256, 128, 256, 256, 1 << 30, None) == bg.EINVAL
+    assert lib.bgtq_decode_step_buffered(*sb[:7], 101, *sb[8:], 256, 256, 4, 256, 256, 128, 256, 256, 1 << 30,
+                                         None) == bg.ECAPACITY
     # paged with the fp16 buffers: the pool checks and the buffer checks, before any launch
     pb = [256, 256, 4, 256, 256, 128]
     assert lib.bgtq_decode_attn_paged_buffered(*args, None, 256, 1, 100, 0.1, *pb, 256, 256, 1 << 30,
