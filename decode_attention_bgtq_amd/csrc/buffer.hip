@@ -40,47 +40,6 @@ __global__ __launch_bounds__(256) void buffer_append_kernel(const uint4 *__restr
   }
 }
 
-// One new token per sequence (rows k_new / v_new [batch][hkv][128]) at
-// position pos[b]: into sink row pos[b] when it is below n_sink, and into ring
-// row pos[b] % n_recent (a sequence with pos[b] < 0 copies nothing).  Block b;
-// one 16-byte chunk per thread and step over the token's n_kv_heads rows.
-__global__ __launch_bounds__(256) void buffer_append_pos_kernel(const uint4 *__restrict__ k,
-                                                                const uint4 *__restrict__ v,
-                                                                const int32_t *__restrict__ pos, int hkv,
-                                                                uint4 *k_sink, uint4 *v_sink, int n_sink,
-                                                                uint4 *k_recent, uint4 *v_recent, int n_recent) {
-  const int b = blockIdx.x;
-  const int64_t t = pos[b];
-  if (t < 0) return;  // uniform per workgroup
-  const int per = hkv * (kHeadDim / 8);
-  const uint4 *ks = k + (size_t)b * per, *vs = v + (size_t)b * per;
-  for (int c = threadIdx.x; c < per; c += blockDim.x) {
-    const int h = c / (kHeadDim / 8), w = c % (kHeadDim / 8);
-    const uint4 kx = ks[c], vx = vs[c];
-    if (t < n_sink) {
-      const size_t dst = (((size_t)b * hkv + h) * n_sink + t) * (kHeadDim / 8) + w;
-      k_sink[dst] = kx;
-      v_sink[dst] = vx;
-    }
-    if (n_recent > 0) {
-      const size_t dst = (((size_t)b * hkv + h) * n_recent + (size_t)(t % n_recent)) * (kHeadDim / 8) + w;
-      k_recent[dst] = kx;
-      v_recent[dst] = vx;
-    }
-  }
-}
-
-// Launch of buffer_append_pos_kernel on `stream` (arguments checked by the caller).
-bgtq_status buffer_append_at(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, int32_t batch,
-                             int32_t n_kv_heads, uint16_t *k_sink, uint16_t *v_sink, int32_t n_sink,
-                             uint16_t *k_recent, uint16_t *v_recent, int32_t n_recent, bgtq_stream stream) {
-  if (n_sink == 0 && n_recent == 0) return BGTQ_OK;
-  buffer_append_pos_kernel<<<dim3((unsigned)batch), 256, 0, (hipStream_t)stream>>>(
-      (const uint4 *)k_new, (const uint4 *)v_new, pos, n_kv_heads, (uint4 *)k_sink, (uint4 *)v_sink, n_sink,
-      (uint4 *)k_recent, (uint4 *)v_recent, n_recent);
-  return launch_status("buffer append");
-}
-
 }  // namespace bgtq
 
 using namespace bgtq;

@@ -855,18 +855,54 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(const PrepArgs pa
   prep_role<G>(pa, blockIdx.x, blockIdx.y);
 }
 
+static_assert(kAppendThreads == 64 * kPrepWaves, "one workgroup size for all roles");
+
+// The buffered step's copy of the new token of sequence b into the fp16 sink
+// (row pos[b] when below n_sink) and recent window (ring row pos[b] %
+// n_recent); a sequence with pos[b] < 0 copies nothing.
+struct BufCopy {
+  const uint4 *k, *v;  // [batch][hkv][128] fp16, 16-byte chunks
+  uint4 *k_sink, *v_sink, *k_recent, *v_recent;
+  int n_sink, n_recent;
+};
+
+__device__ __forceinline__ void buffer_copy_role(const BufCopy &bc, const int32_t *__restrict__ pos, int hkv, int b) {
+  const int64_t t = pos[b];
+  if (t < 0) return;  // uniform per workgroup
+  const int per = hkv * (kHeadDim / 8);
+  for (int c = threadIdx.x; c < per; c += blockDim.x) {
+    const int h = c / (kHeadDim / 8), w = c % (kHeadDim / 8);
+    const uint4 kx = bc.k[(size_t)b * per + c], vx = bc.v[(size_t)b * per + c];
+    if (t < bc.n_sink) {
+      const size_t dst = (((size_t)b * hkv + h) * bc.n_sink + t) * (kHeadDim / 8) + w;
+      bc.k_sink[dst] = kx;
+      bc.v_sink[dst] = vx;
+    }
+    if (bc.n_recent > 0) {
+      const size_t dst = (((size_t)b * hkv + h) * bc.n_recent + (size_t)(t % bc.n_recent)) * (kHeadDim / 8) + w;
+      bc.k_recent[dst] = kx;
+      bc.v_recent[dst] = vx;
+    }
+  }
+}
+
 // The front of a serving step in one launch: the new token's key and value
 // appended to the cache and the queries prepared, side by side (the two are
 // independent; the decode kernel after them needs both).  Workgroups [0, n):
 // key append of (sequence, KV head) = (r / hkv, r % hkv); [n, 2n): value
-// append; [2n, 3n): query preparation.  n = batch * hkv.
-static_assert(kAppendThreads == 64 * kPrepWaves, "one workgroup size for both roles");
+// append; [2n, 3n): query preparation.  n = batch * hkv.  A buffered step adds
+// [3n, 3n + batch): the fp16 buffer copy of sequence role - 3n (read only by
+// the merge, two launches later).
 template <int G>
 __global__ __launch_bounds__(64 * kPrepWaves) void step_front_kernel(const PrepArgs pa, const AppendArgs ka,
                                                                      const AppendArgs va,
                                                                      const int32_t *__restrict__ pos,
-                                                                     int64_t capacity, int n) {
+                                                                     int64_t capacity, int n, const BufCopy bc) {
   const int role = blockIdx.x, hkv = ka.hkv;
+  if (role >= 3 * n) {
+    buffer_copy_role(bc, pos, hkv, role - 3 * n);
+    return;
+  }
   const int r = role < n ? role : role < 2 * n ? role - n : role - 2 * n;
   const int kvh = r % hkv, b = r / hkv;
   if (role >= 2 * n) {
@@ -1335,9 +1371,13 @@ bgtq_status decode_launch(const Plan &p, const DecodeCall &c) {
     const PrepArgs pa{a.consts, c.q, a.hq, a.hkv, G, a.off_zero, a.kscale, ws + lay.img_off};
     if (c.step) {
       const int n = c.batch * p.desc.n_kv_heads;
-      const unsigned blocks = (unsigned)(3 * n);
+      const StepAppend &sa = *c.step;
+      const bool copy = sa.n_sink > 0 || sa.n_recent > 0;
+      const BufCopy bc{(const uint4 *)sa.k_new, (const uint4 *)sa.v_new, (uint4 *)sa.k_sink, (uint4 *)sa.v_sink,
+                       (uint4 *)sa.k_recent, (uint4 *)sa.v_recent, sa.n_sink, sa.n_recent};
+      const unsigned blocks = (unsigned)(3 * n + (copy ? c.batch : 0));
 #define BGTQ_FRONT(GK) \
-  step_front_kernel<GK><<<blocks, 64 * kPrepWaves, 0, st>>>(pa, *c.step->ka, *c.step->va, c.step->pos, c.step->capacity, n)
+  step_front_kernel<GK><<<blocks, 64 * kPrepWaves, 0, st>>>(pa, *sa.ka, *sa.va, sa.pos, sa.capacity, n, bc)
       switch (kernel_group(G)) {
         case 1: BGTQ_FRONT(1); break;
         case 2: BGTQ_FRONT(2); break;

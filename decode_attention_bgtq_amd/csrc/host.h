@@ -32,6 +32,12 @@ struct StepAppend {
   const AppendArgs *ka, *va;
   const int32_t *pos;
   int64_t capacity;
+  // buffered step: the new token (rows [batch][hkv][128]) also copied into the
+  // fp16 sink (row pos[b] when below n_sink) and recent window (ring row
+  // pos[b] % n_recent); counts 0: no copy
+  const uint16_t *k_new = nullptr, *v_new = nullptr;
+  uint16_t *k_sink = nullptr, *v_sink = nullptr, *k_recent = nullptr, *v_recent = nullptr;
+  int n_sink = 0, n_recent = 0;
 };
 
 // Decode launches shared by bgtq_decode_attn and bgtq_decode_step.

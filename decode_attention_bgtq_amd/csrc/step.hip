@@ -8,12 +8,6 @@
 #include "host.h"
 #include "merge.h"
 
-namespace bgtq {
-bgtq_status buffer_append_at(const uint16_t *k_new, const uint16_t *v_new, const int32_t *pos, int32_t batch,
-                             int32_t n_kv_heads, uint16_t *k_sink, uint16_t *v_sink, int32_t n_sink,
-                             uint16_t *k_recent, uint16_t *v_recent, int32_t n_recent, bgtq_stream stream);
-}  // namespace bgtq
-
 using namespace bgtq;
 
 namespace {
@@ -49,16 +43,16 @@ bgtq_status step_common(const char *nm, const bgtq_plan *plan, const void *dev_c
   const uint8_t *c = (const uint8_t *)dev_consts;
   const AppendArgs ka = append_args(p, c, k_new, k_codes, k_norms, map, false);
   const AppendArgs va = append_args(p, c, v_new, v_codes, v_norms, map, true);
-  const StepAppend sa{&ka, &va, pos, capacity};
+  StepAppend sa{&ka, &va, pos, capacity};
   DecodeCall dc{dev_consts, q, k_codes, k_norms, v_codes, v_norms, capacity, pos, 1, batch, max_seq_len,
                 softmax_scale, out, workspace, stream};
   dc.pages = pages;
   dc.step = &sa;
   if (bf.n_sink || bf.n_recent) {
-    // the new token into the fp16 buffers first (the buffered merge reads them)
-    const bgtq_status bs = buffer_append_at(k_new, v_new, pos, batch, p.desc.n_kv_heads, bf.k_sink, bf.v_sink,
-                                            bf.n_sink, bf.k_recent, bf.v_recent, bf.n_recent, stream);
-    if (bs != BGTQ_OK) return bs;
+    // the new token into the fp16 buffers in the step's front launch (the buffered merge reads them)
+    sa.k_new = k_new, sa.v_new = v_new;
+    sa.k_sink = bf.k_sink, sa.v_sink = bf.v_sink, sa.k_recent = bf.k_recent, sa.v_recent = bf.v_recent;
+    sa.n_sink = bf.n_sink, sa.n_recent = bf.n_recent;
     dc.k_sink = bf.k_sink;
     dc.v_sink = bf.v_sink;
     dc.k_recent = bf.k_recent;
